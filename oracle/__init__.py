@@ -1,0 +1,152 @@
+"""fp64 CPU oracle for headwise-chunked causal GQA attention (fwd + bwd).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, the smoke check in
+``__graft_entry__.py`` and the CPU-baseline leg of ``bench.py`` may import this
+package.  It shares no code with the GPU library and never touches a GPU.
+
+The arithmetic lives in ``upipe_oracle.cpp`` (plain fp64 loops, unchunked; see
+its header for the passages of the pages on "Untied Ulysses: Memory-Efficient
+Context Parallelism via Headwise Chunking" it follows).  This module only
+builds that file with g++ and marshals numpy arrays to it.
+
+Input arrays may be float64, float32, or uint16 holding bf16 bit patterns;
+every element is decoded exactly into fp64 before any arithmetic.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "upipe_oracle.cpp")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with g++ (plain -O2, no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-pthread",
+               "-ffp-contract=off", _SRC, "-o", tmp]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        i64, i32, vp, dp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p
+        lib.oracle_forward.argtypes = [i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, dp, dp, i32]
+        lib.oracle_forward.restype = i32
+        lib.oracle_forward_rows.argtypes = [i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp,
+                                            vp, i64, dp, dp, i32]
+        lib.oracle_forward_rows.restype = i32
+        lib.oracle_backward.argtypes = [i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                        dp, dp, dp, dp, dp, dp, i32]
+        lib.oracle_backward.restype = i32
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _enc(a: np.ndarray) -> int:
+    if a.dtype == np.uint16:
+        return 0
+    if a.dtype == np.float32:
+        return 1
+    if a.dtype == np.float64:
+        return 2
+    raise TypeError("oracle inputs must be uint16 (bf16 bits), float32 or float64, got %s" % a.dtype)
+
+
+def _prep(arrs):
+    arrs = [np.ascontiguousarray(a) for a in arrs]
+    enc = {_enc(a) for a in arrs}
+    if len(enc) != 1:
+        raise TypeError("all oracle inputs must share one encoding")
+    return arrs, enc.pop()
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def forward(X, Wq, Wk, Wv, H: int, G: int, d: int, causal: bool = True, nthreads: int | None = None):
+    """Return (O [S][H*d], LSE [H][S]) in fp64."""
+    (X, Wq, Wk, Wv), enc = _prep([X, Wq, Wk, Wv])
+    S, D = X.shape
+    _check_shapes(S, D, H, G, d, Wq, Wk, Wv)
+    O = np.empty((S, H * d), np.float64)
+    LSE = np.empty((H, S), np.float64)
+    rc = _load().oracle_forward(S, D, H, G, d, int(bool(causal)), enc, _ptr(X), _ptr(Wq), _ptr(Wk),
+                                _ptr(Wv), _ptr(O), _ptr(LSE), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_forward rejected the shape")
+    return O, LSE
+
+
+def forward_rows(X, Wq, Wk, Wv, H: int, G: int, d: int, rows, causal: bool = True,
+                 nthreads: int | None = None):
+    """Forward at the token rows `rows` only: (O_rows [n][H*d], LSE_rows [H][n]) in fp64."""
+    (X, Wq, Wk, Wv), enc = _prep([X, Wq, Wk, Wv])
+    S, D = X.shape
+    _check_shapes(S, D, H, G, d, Wq, Wk, Wv)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    n = rows.shape[0]
+    O = np.empty((n, H * d), np.float64)
+    LSE = np.empty((H, n), np.float64)
+    rc = _load().oracle_forward_rows(S, D, H, G, d, int(bool(causal)), enc, _ptr(X), _ptr(Wq),
+                                     _ptr(Wk), _ptr(Wv), _ptr(rows), n, _ptr(O), _ptr(LSE),
+                                     nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_forward_rows rejected the shape or rows")
+    return O, LSE
+
+
+def backward(X, Wq, Wk, Wv, dO, H: int, G: int, d: int, causal: bool = True,
+             nthreads: int | None = None):
+    """Forward + backward of L = sum(O * dO).
+
+    Returns a dict of fp64 arrays: O, LSE, dX, dWq, dWk, dWv.
+    """
+    (X, Wq, Wk, Wv, dO), enc = _prep([X, Wq, Wk, Wv, dO])
+    S, D = X.shape
+    _check_shapes(S, D, H, G, d, Wq, Wk, Wv)
+    if dO.shape != (S, H * d):
+        raise ValueError("dO must be [S][H*d]")
+    out = {
+        "O": np.empty((S, H * d), np.float64),
+        "LSE": np.empty((H, S), np.float64),
+        "dX": np.empty((S, D), np.float64),
+        "dWq": np.empty((H * d, D), np.float64),
+        "dWk": np.empty((G * d, D), np.float64),
+        "dWv": np.empty((G * d, D), np.float64),
+    }
+    rc = _load().oracle_backward(S, D, H, G, d, int(bool(causal)), enc, _ptr(X), _ptr(Wq), _ptr(Wk),
+                                 _ptr(Wv), _ptr(dO), _ptr(out["O"]), _ptr(out["LSE"]),
+                                 _ptr(out["dX"]), _ptr(out["dWq"]), _ptr(out["dWk"]),
+                                 _ptr(out["dWv"]), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_backward rejected the shape")
+    return out
+
+
+def _check_shapes(S, D, H, G, d, Wq, Wk, Wv):
+    if H % G != 0:
+        raise ValueError("G must divide H")
+    if Wq.shape != (H * d, D) or Wk.shape != (G * d, D) or Wv.shape != (G * d, D):
+        raise ValueError("weight shapes must be Wq [H*d][D], Wk/Wv [G*d][D]")

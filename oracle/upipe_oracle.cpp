@@ -1,0 +1,352 @@
+// upipe_oracle.cpp -- fp64 CPU oracle for one GPU's share of a causal GQA
+// self-attention layer (forward and backward), unchunked.
+//
+// TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+// benchmark's CPU-baseline leg load this library.  It shares no source,
+// header, table or helper with the GPU library, and the GPU library never
+// calls it.
+//
+// What it follows (pages on "Untied Ulysses: Memory-Efficient Context
+// Parallelism via Headwise Chunking"):
+//  * paper.rainbus.top summary, section 前置知识 / DeepSpeed Ulysses: after the
+//    sequence-to-head exchange a device holds every position for a subset of
+//    heads and computes full attention for those heads on its own.
+//  * same page, section 前置知识 / 分组查询注意力 (GQA): H query heads, G key/value
+//    heads, each block of H/G consecutive query heads shares one KV head.
+//  * same page, sections 核心方法 and 方法步骤详情: headwise chunking only splits
+//    the H heads into H/U stages; each stage projects its heads' Q, K, V from X
+//    and runs attention over the full sequence.  Stages partition independent
+//    per-head work, so the chunked layer reaches exactly the unchunked result:
+//    this oracle is that unchunked definition and U does not appear in it.
+//  * fugumt.com abstract: chunking happens "at the attention head level".
+//
+// Readings where the pages are silent (each one listed in the design notes):
+//  softmax scale tau = 1/sqrt(d_head); causal mask j <= i (diagonal kept);
+//  no RoPE, bias, dropout or output projection; batch 1; query head h uses KV
+//  head floor(h / (H/G)); LSE is the natural log of sum_j exp(tau q_i.k_j);
+//  the backward is that of L = sum(O * dO) (dO given), with gradients for
+//  X, Wq, Wk, Wv.
+//
+// Arithmetic: every input element is decoded exactly into an fp64 value
+// (bf16 bits, fp32 or fp64 storage) and everything after that is fp64, in
+// plain loops: a row's softmax is two passes (max, then exp/sum), there is
+// no tiling and no online rescaling.  Work is spread over threads by output
+// row only; each output element is produced by exactly one thread with a
+// fixed loop order, so results do not depend on the thread count.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <thread>
+#include <vector>
+#include <algorithm>
+#include <functional>
+
+namespace {
+
+// ---------------------------------------------------------------- decoding
+// enc: 0 = bf16 bit patterns (uint16), 1 = fp32, 2 = fp64.
+double decode_one(const void* p, int enc, int64_t i) {
+  if (enc == 0) {
+    uint16_t h = static_cast<const uint16_t*>(p)[i];
+    uint32_t u = static_cast<uint32_t>(h) << 16;
+    float f;
+    std::memcpy(&f, &u, 4);
+    return static_cast<double>(f);
+  }
+  if (enc == 1) return static_cast<double>(static_cast<const float*>(p)[i]);
+  return static_cast<const double*>(p)[i];
+}
+
+std::vector<double> decode(const void* p, int enc, int64_t n) {
+  std::vector<double> out(static_cast<size_t>(n));
+  for (int64_t i = 0; i < n; ++i) out[i] = decode_one(p, enc, i);
+  return out;
+}
+
+// ---------------------------------------------------------------- threads
+void parallel_for(int64_t n, int nthreads, const std::function<void(int64_t)>& body) {
+  if (nthreads < 1) nthreads = 1;
+  if (n <= 0) return;
+  int64_t t = std::min<int64_t>(nthreads, n);
+  if (t == 1) {
+    for (int64_t i = 0; i < n; ++i) body(i);
+    return;
+  }
+  std::vector<std::thread> pool;
+  for (int64_t w = 0; w < t; ++w) {
+    pool.emplace_back([&, w]() {
+      // interleaved assignment balances the triangular causal work
+      for (int64_t i = w; i < n; i += t) body(i);
+    });
+  }
+  for (auto& th : pool) th.join();
+}
+
+double dot(const double* a, const double* b, int64_t n) {
+  double s = 0.0;
+  for (int64_t k = 0; k < n; ++k) s += a[k] * b[k];
+  return s;
+}
+
+struct Shape {
+  int64_t S, D;
+  int H, G, d, causal;
+  int r() const { return H / G; }
+  int kv(int h) const { return h / r(); }
+  double tau() const { return 1.0 / std::sqrt(static_cast<double>(d)); }
+  // keys visible to query row i: [0, last(i)]
+  int64_t last(int64_t i) const { return causal ? i : S - 1; }
+};
+
+bool shape_ok(const Shape& s) {
+  return s.S >= 1 && s.D >= 1 && s.H >= 1 && s.G >= 1 && s.d >= 1 && (s.H % s.G) == 0;
+}
+
+// Project rows [0, nrows) of X ([S][D]) through the rows of W that belong to
+// head `head` (W is [nh*d][D], head h = rows h*d .. h*d+d-1):
+// out[i][c] = sum_k X[i][k] * W[head*d + c][k]   (out is [nrows][d]).
+void project_head(const std::vector<double>& X, const std::vector<double>& W, const Shape& s,
+                  int head, int64_t nrows, const int64_t* rows, double* out, int nthreads) {
+  parallel_for(nrows, nthreads, [&](int64_t t) {
+    int64_t i = rows ? rows[t] : t;
+    const double* x = &X[static_cast<size_t>(i * s.D)];
+    for (int c = 0; c < s.d; ++c) {
+      const double* w = &W[static_cast<size_t>((static_cast<int64_t>(head) * s.d + c) * s.D)];
+      out[t * s.d + c] = dot(x, w, s.D);
+    }
+  });
+}
+
+// Row i of one head's attention, given q_i, all K and V of the KV head.
+// Writes o (d values) and returns LSE.  Two passes over the visible keys.
+double attend_row(const double* q, const double* K, const double* V, const Shape& s, int64_t i,
+                  double* o, std::vector<double>& scores) {
+  int64_t n = s.last(i) + 1;
+  scores.resize(static_cast<size_t>(n));
+  double m = -INFINITY;
+  for (int64_t j = 0; j < n; ++j) {
+    scores[j] = s.tau() * dot(q, K + j * s.d, s.d);
+    m = std::max(m, scores[j]);
+  }
+  double sum = 0.0;
+  for (int64_t j = 0; j < n; ++j) sum += std::exp(scores[j] - m);
+  double lse = m + std::log(sum);
+  for (int c = 0; c < s.d; ++c) o[c] = 0.0;
+  for (int64_t j = 0; j < n; ++j) {
+    double p = std::exp(scores[j] - lse);
+    for (int c = 0; c < s.d; ++c) o[c] += p * V[j * s.d + c];
+  }
+  return lse;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Forward.  X [S][D], Wq [H*d][D], Wk/Wv [G*d][D] in encoding `enc`.
+// Outputs (fp64, caller-owned): O [S][H*d] (column h*d+c), LSE [H][S].
+// Returns 0, or 1 on an invalid shape.
+int oracle_forward(int64_t S, int64_t D, int H, int G, int d, int causal, int enc,
+                   const void* Xp, const void* Wqp, const void* Wkp, const void* Wvp,
+                   double* O, double* LSE, int nthreads) {
+  Shape s{S, D, H, G, d, causal};
+  if (!shape_ok(s)) return 1;
+  std::vector<double> X = decode(Xp, enc, S * D);
+  std::vector<double> Wq = decode(Wqp, enc, static_cast<int64_t>(H) * d * D);
+  std::vector<double> Wk = decode(Wkp, enc, static_cast<int64_t>(G) * d * D);
+  std::vector<double> Wv = decode(Wvp, enc, static_cast<int64_t>(G) * d * D);
+  std::vector<double> K(static_cast<size_t>(S * d)), V(static_cast<size_t>(S * d)),
+      Q(static_cast<size_t>(S * d));
+  for (int g = 0; g < G; ++g) {
+    project_head(X, Wk, s, g, S, nullptr, K.data(), nthreads);
+    project_head(X, Wv, s, g, S, nullptr, V.data(), nthreads);
+    for (int h = g * s.r(); h < (g + 1) * s.r(); ++h) {
+      project_head(X, Wq, s, h, S, nullptr, Q.data(), nthreads);
+      parallel_for(S, nthreads, [&](int64_t i) {
+        std::vector<double> scores;
+        std::vector<double> o(static_cast<size_t>(d));
+        LSE[static_cast<int64_t>(h) * S + i] =
+            attend_row(&Q[i * d], K.data(), V.data(), s, i, o.data(), scores);
+        for (int c = 0; c < d; ++c) O[i * (static_cast<int64_t>(H) * d) + h * d + c] = o[c];
+      });
+    }
+  }
+  return 0;
+}
+
+// Forward on a subset of query rows (all heads).  rows[0..nrows) are token
+// indices; keys/values are projected only for the positions those rows see.
+// Outputs: Orows [nrows][H*d], LSErows [H][nrows] (fp64).
+int oracle_forward_rows(int64_t S, int64_t D, int H, int G, int d, int causal, int enc,
+                        const void* Xp, const void* Wqp, const void* Wkp, const void* Wvp,
+                        const int64_t* rows, int64_t nrows, double* Orows, double* LSErows,
+                        int nthreads) {
+  Shape s{S, D, H, G, d, causal};
+  if (!shape_ok(s) || nrows < 0) return 1;
+  int64_t need = 0;  // keys needed: [0, need)
+  for (int64_t t = 0; t < nrows; ++t) {
+    if (rows[t] < 0 || rows[t] >= S) return 1;
+    need = std::max(need, s.last(rows[t]) + 1);
+  }
+  // Decode only the X rows that are used.
+  std::vector<double> X(static_cast<size_t>(need * D));
+  for (int64_t i = 0; i < need * D; ++i) X[i] = decode_one(Xp, enc, i);
+  std::vector<double> Xq(static_cast<size_t>(nrows * D));
+  for (int64_t t = 0; t < nrows; ++t)
+    for (int64_t k = 0; k < D; ++k) Xq[t * D + k] = decode_one(Xp, enc, rows[t] * D + k);
+  std::vector<double> Wq = decode(Wqp, enc, static_cast<int64_t>(H) * d * D);
+  std::vector<double> Wk = decode(Wkp, enc, static_cast<int64_t>(G) * d * D);
+  std::vector<double> Wv = decode(Wvp, enc, static_cast<int64_t>(G) * d * D);
+  Shape sk = s;
+  sk.S = need;
+  std::vector<double> K(static_cast<size_t>(need * d)), V(static_cast<size_t>(need * d)),
+      Q(static_cast<size_t>(nrows * d));
+  Shape sq = s;
+  sq.S = nrows;
+  for (int g = 0; g < G; ++g) {
+    project_head(X, Wk, sk, g, need, nullptr, K.data(), nthreads);
+    project_head(X, Wv, sk, g, need, nullptr, V.data(), nthreads);
+    for (int h = g * s.r(); h < (g + 1) * s.r(); ++h) {
+      project_head(Xq, Wq, sq, h, nrows, nullptr, Q.data(), nthreads);
+      parallel_for(nrows, nthreads, [&](int64_t t) {
+        std::vector<double> scores;
+        std::vector<double> o(static_cast<size_t>(d));
+        LSErows[static_cast<int64_t>(h) * nrows + t] =
+            attend_row(&Q[t * d], K.data(), V.data(), s, rows[t], o.data(), scores);
+        for (int c = 0; c < d; ++c) Orows[t * (static_cast<int64_t>(H) * d) + h * d + c] = o[c];
+      });
+    }
+  }
+  return 0;
+}
+
+// Forward + backward of L = sum(O * dO).
+// Inputs in encoding `enc`: X, Wq, Wk, Wv, dO [S][H*d].
+// Outputs (fp64): O, LSE as in oracle_forward; dX [S][D]; dWq [H*d][D];
+// dWk, dWv [G*d][D].
+//
+// With P = softmax(tau Q K^T) (masked) and D_i = <dO_i, O_i>:
+//   dP_ij = <dO_i, V_j>,  dS_ij = P_ij (dP_ij - D_i)
+//   dQ_i = tau sum_j dS_ij K_j,   dK_j = tau sum_{h in group} sum_i dS_ij Q_i,
+//   dV_j = sum_{h in group} sum_i P_ij dO_i
+//   dW* = d*^T X,   dX = sum_h dQ_h Wq_h + sum_g (dK_g Wk_g + dV_g Wv_g)
+// Row quantities (dQ) are computed by a pass over query rows, column
+// quantities (dK, dV) by a pass over key rows; each recomputes P and dP from
+// Q, K, V, LSE and dO, so no two threads ever write the same element.
+int oracle_backward(int64_t S, int64_t D, int H, int G, int d, int causal, int enc,
+                    const void* Xp, const void* Wqp, const void* Wkp, const void* Wvp,
+                    const void* dOp, double* O, double* LSE, double* dX, double* dWq,
+                    double* dWk, double* dWv, int nthreads) {
+  Shape s{S, D, H, G, d, causal};
+  if (!shape_ok(s)) return 1;
+  const int64_t Hd = static_cast<int64_t>(H) * d;
+  const int r = s.r();
+  std::vector<double> X = decode(Xp, enc, S * D);
+  std::vector<double> Wq = decode(Wqp, enc, Hd * D);
+  std::vector<double> Wk = decode(Wkp, enc, static_cast<int64_t>(G) * d * D);
+  std::vector<double> Wv = decode(Wvp, enc, static_cast<int64_t>(G) * d * D);
+  std::vector<double> dO = decode(dOp, enc, S * Hd);
+
+  // Projections for every head (the oracle is not memory-frugal).
+  std::vector<double> Q(static_cast<size_t>(H * S * d)), K(static_cast<size_t>(G * S * d)),
+      V(static_cast<size_t>(G * S * d));
+  for (int h = 0; h < H; ++h) project_head(X, Wq, s, h, S, nullptr, &Q[h * S * d], nthreads);
+  for (int g = 0; g < G; ++g) {
+    project_head(X, Wk, s, g, S, nullptr, &K[g * S * d], nthreads);
+    project_head(X, Wv, s, g, S, nullptr, &V[g * S * d], nthreads);
+  }
+
+  // Forward (O, LSE) and D.
+  std::vector<double> Dv(static_cast<size_t>(H * S));
+  for (int h = 0; h < H; ++h) {
+    const int g = s.kv(h);
+    parallel_for(S, nthreads, [&](int64_t i) {
+      std::vector<double> scores;
+      std::vector<double> o(static_cast<size_t>(d));
+      LSE[h * S + i] = attend_row(&Q[(h * S + i) * d], &K[g * S * d], &V[g * S * d], s, i,
+                                  o.data(), scores);
+      double dd = 0.0;
+      for (int c = 0; c < d; ++c) {
+        O[i * Hd + h * d + c] = o[c];
+        dd += dO[i * Hd + h * d + c] * o[c];
+      }
+      Dv[h * S + i] = dd;
+    });
+  }
+
+  auto prob = [&](int h, int64_t i, int64_t j) {  // P_ij for head h
+    const int g = s.kv(h);
+    double sc = s.tau() * dot(&Q[(h * S + i) * d], &K[(g * S + j) * d], d);
+    return std::exp(sc - LSE[h * S + i]);
+  };
+  auto dprob = [&](int h, int64_t i, int64_t j) {  // dP_ij for head h
+    const int g = s.kv(h);
+    return dot(&dO[i * Hd + h * d], &V[(g * S + j) * d], d);
+  };
+
+  // dQ: pass over query rows.
+  std::vector<double> dQ(static_cast<size_t>(H * S * d), 0.0);
+  for (int h = 0; h < H; ++h) {
+    const int g = s.kv(h);
+    parallel_for(S, nthreads, [&](int64_t i) {
+      double* dq = &dQ[(h * S + i) * d];
+      for (int64_t j = 0; j <= s.last(i); ++j) {
+        double dsij = prob(h, i, j) * (dprob(h, i, j) - Dv[h * S + i]);
+        for (int c = 0; c < d; ++c) dq[c] += s.tau() * dsij * K[(g * S + j) * d + c];
+      }
+    });
+  }
+
+  // dK, dV: pass over key rows; query heads of the group in ascending order.
+  std::vector<double> dK(static_cast<size_t>(G * S * d), 0.0), dV(static_cast<size_t>(G * S * d), 0.0);
+  for (int g = 0; g < G; ++g) {
+    parallel_for(S, nthreads, [&](int64_t j) {
+      double* dk = &dK[(g * S + j) * d];
+      double* dv = &dV[(g * S + j) * d];
+      for (int h = g * r; h < (g + 1) * r; ++h) {
+        // query rows that see key j
+        int64_t i0 = causal ? j : 0;
+        for (int64_t i = i0; i < S; ++i) {
+          double p = prob(h, i, j);
+          double dsij = p * (dprob(h, i, j) - Dv[h * S + i]);
+          for (int c = 0; c < d; ++c) {
+            dk[c] += s.tau() * dsij * Q[(h * S + i) * d + c];
+            dv[c] += p * dO[i * Hd + h * d + c];
+          }
+        }
+      }
+    });
+  }
+
+  // Weight gradients: dW[row][k] = sum_i grad[i][row] * X[i][k].
+  auto weight_grad = [&](const std::vector<double>& grad, int nheads, double* dW) {
+    parallel_for(static_cast<int64_t>(nheads) * d, nthreads, [&](int64_t row) {
+      const int64_t h = row / d, c = row % d;
+      for (int64_t k = 0; k < D; ++k) {
+        double acc = 0.0;
+        for (int64_t i = 0; i < S; ++i) acc += grad[(h * S + i) * d + c] * X[i * D + k];
+        dW[row * D + k] = acc;
+      }
+    });
+  };
+  weight_grad(dQ, H, dWq);
+  weight_grad(dK, G, dWk);
+  weight_grad(dV, G, dWv);
+
+  // Input gradient: dX[i][k] = sum over projected rows of grad * W.
+  parallel_for(S, nthreads, [&](int64_t i) {
+    for (int64_t k = 0; k < D; ++k) {
+      double acc = 0.0;
+      for (int h = 0; h < H; ++h)
+        for (int c = 0; c < d; ++c) acc += dQ[(h * S + i) * d + c] * Wq[(h * d + c) * D + k];
+      for (int g = 0; g < G; ++g)
+        for (int c = 0; c < d; ++c)
+          acc += dK[(g * S + i) * d + c] * Wk[(g * d + c) * D + k] +
+                 dV[(g * S + i) * d + c] * Wv[(g * d + c) * D + k];
+      dX[i * D + k] = acc;
+    }
+  });
+  return 0;
+}
+
+}  // extern "C"

@@ -1,0 +1,254 @@
+"""Pins for the fp64 oracle, each against something other than the oracle itself.
+
+* torch CPU fp64 scaled_dot_product_attention + autograd (a library routine the
+  oracle never calls) for every output, causal and full, GQA/MHA/single head;
+* brute force: the whole masked S x S score matrix softmaxed at once (scipy);
+* central finite differences of L = sum(O * dO) for the backward;
+* closed forms: S = 1, row 0, uniform attention when Wq = 0 (prefix means,
+  LSE = ln(i+1), dWk = 0 exactly, dWv from prefix sums);
+* causal invariance (future rows do not change earlier outputs, bitwise);
+* softmax rows sum to one; scaling identities that hold at any size;
+* independence of the thread count (bitwise).
+
+The definition being pinned: paper.rainbus.top summary of "Untied Ulysses",
+section 前置知识 (Ulysses: full attention per head over all positions; GQA:
+H/G consecutive query heads share a KV head) and section 方法步骤详情 (each
+stage projects its heads' Q, K, V from X, then attends over the full sequence).
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+SHAPES = [
+    # S, D, H, G, d
+    (37, 24, 4, 2, 8),     # GQA, ragged S
+    (64, 32, 6, 3, 16),    # GQA r=2
+    (29, 16, 3, 3, 8),     # MHA (G = H)
+    (33, 20, 1, 1, 12),    # single head
+    (50, 24, 8, 1, 8),     # MQA (G = 1)
+]
+
+
+def draw(S, D, H, G, d, seed=0, wq_zero=False):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((S, D))
+    Wq = rng.standard_normal((H * d, D)) / math.sqrt(D)
+    Wk = rng.standard_normal((G * d, D)) / math.sqrt(D)
+    Wv = rng.standard_normal((G * d, D)) / math.sqrt(D)
+    dO = rng.standard_normal((S, H * d))
+    if wq_zero:
+        Wq[:] = 0.0
+    return X, Wq, Wk, Wv, dO
+
+
+def torch_layer(X, Wq, Wk, Wv, dO, H, G, d, causal):
+    """The same layer built from torch library calls, fp64, autograd backward."""
+    t = {k: torch.tensor(v, dtype=torch.float64, requires_grad=(k != "dO"))
+         for k, v in dict(X=X, Wq=Wq, Wk=Wk, Wv=Wv, dO=dO).items()}
+    S = X.shape[0]
+    q = (t["X"] @ t["Wq"].T).reshape(S, H, d).transpose(0, 1)
+    k = (t["X"] @ t["Wk"].T).reshape(S, G, d).transpose(0, 1)
+    v = (t["X"] @ t["Wv"].T).reshape(S, G, d).transpose(0, 1)
+    k = k.repeat_interleave(H // G, dim=0)
+    v = v.repeat_interleave(H // G, dim=0)
+    o = torch.nn.functional.scaled_dot_product_attention(q[None], k[None], v[None],
+                                                         is_causal=causal)[0]
+    O = o.transpose(0, 1).reshape(S, H * d)
+    (O * t["dO"]).sum().backward()
+    scores = (q @ k.transpose(1, 2)) / math.sqrt(d)
+    if causal:
+        mask = torch.ones(S, S, dtype=torch.bool).tril()
+        scores = scores.masked_fill(~mask, float("-inf"))
+    lse = torch.logsumexp(scores, dim=-1)
+    return dict(O=O.detach().numpy(), LSE=lse.detach().numpy(), dX=t["X"].grad.numpy(),
+                dWq=t["Wq"].grad.numpy(), dWk=t["Wk"].grad.numpy(), dWv=t["Wv"].grad.numpy())
+
+
+def close(a, b, tol=1e-10):
+    scale = max(1.0, float(np.max(np.abs(b))))
+    err = float(np.max(np.abs(a - b))) / scale
+    assert err <= tol, "max rel err %.3e > %.1e" % (err, tol)
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("causal", [True, False])
+def test_against_torch_library(oracle_mod, shape, causal):
+    S, D, H, G, d = shape
+    X, Wq, Wk, Wv, dO = draw(S, D, H, G, d, seed=S)
+    got = oracle_mod.backward(X, Wq, Wk, Wv, dO, H, G, d, causal=causal)
+    ref = torch_layer(X, Wq, Wk, Wv, dO, H, G, d, causal)
+    for name in ("O", "LSE", "dX", "dWq", "dWk", "dWv"):
+        close(got[name], ref[name])
+    # forward entry point agrees with the forward half of the backward one
+    O, LSE = oracle_mod.forward(X, Wq, Wk, Wv, H, G, d, causal=causal)
+    np.testing.assert_array_equal(O, got["O"])
+    np.testing.assert_array_equal(LSE, got["LSE"])
+
+
+@pytest.mark.parametrize("shape", SHAPES[:3])
+def test_brute_force_score_matrix(oracle_mod, shape):
+    S, D, H, G, d = shape
+    X, Wq, Wk, Wv, _ = draw(S, D, H, G, d, seed=1)
+    O, LSE = oracle_mod.forward(X, Wq, Wk, Wv, H, G, d)
+    r = H // G
+    mask = np.tril(np.ones((S, S), bool))
+    for h in range(H):
+        g = h // r
+        q = X @ Wq[h * d:(h + 1) * d].T
+        k = X @ Wk[g * d:(g + 1) * d].T
+        v = X @ Wv[g * d:(g + 1) * d].T
+        sc = np.where(mask, (q @ k.T) / math.sqrt(d), -np.inf)
+        P = scipy.special.softmax(sc, axis=1)
+        close(O[:, h * d:(h + 1) * d], P @ v, 1e-12)
+        close(LSE[h], scipy.special.logsumexp(sc, axis=1), 1e-12)
+        # rows of the softmax sum to one, with the oracle's own LSE
+        Pl = np.where(mask, np.exp(sc - LSE[h][:, None]), 0.0)
+        assert np.max(np.abs(Pl.sum(axis=1) - 1.0)) <= 1e-12
+
+
+@pytest.mark.parametrize("shape", [(23, 12, 4, 2, 6), (19, 10, 2, 1, 5)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_finite_differences(oracle_mod, shape, causal):
+    S, D, H, G, d = shape
+    X, Wq, Wk, Wv, dO = draw(S, D, H, G, d, seed=7)
+    g = oracle_mod.backward(X, Wq, Wk, Wv, dO, H, G, d, causal=causal)
+    params = dict(X=X, Wq=Wq, Wk=Wk, Wv=Wv)
+    rng = np.random.default_rng(3)
+
+    def loss(p):
+        O, _ = oracle_mod.forward(p["X"], p["Wq"], p["Wk"], p["Wv"], H, G, d, causal=causal,
+                                  nthreads=1)
+        return float(np.sum(O * dO))
+
+    for name, grad in (("X", "dX"), ("Wq", "dWq"), ("Wk", "dWk"), ("Wv", "dWv")):
+        for _ in range(20):
+            idx = tuple(int(rng.integers(0, n)) for n in params[name].shape)
+            base = params[name][idx]
+            eps = 1e-6 * max(1.0, abs(base))
+            plus = {k: v.copy() for k, v in params.items()}
+            minus = {k: v.copy() for k, v in params.items()}
+            plus[name][idx] = base + eps
+            minus[name][idx] = base - eps
+            fd = (loss(plus) - loss(minus)) / (2 * eps)
+            an = g[grad][idx]
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, idx, fd, an)
+
+
+def test_single_token(oracle_mod):
+    S, D, H, G, d = 1, 16, 4, 2, 8
+    X, Wq, Wk, Wv, _ = draw(S, D, H, G, d, seed=11)
+    O, LSE = oracle_mod.forward(X, Wq, Wk, Wv, H, G, d)
+    for h in range(H):
+        g = h // 2
+        q = X[0] @ Wq[h * d:(h + 1) * d].T
+        k = X[0] @ Wk[g * d:(g + 1) * d].T
+        v = X[0] @ Wv[g * d:(g + 1) * d].T
+        close(O[0, h * d:(h + 1) * d], v, 1e-14)
+        close(LSE[h, 0], q @ k / math.sqrt(d), 1e-14)
+
+
+def test_row_zero_is_first_value(oracle_mod):
+    S, D, H, G, d = 40, 16, 4, 1, 8
+    X, Wq, Wk, Wv, _ = draw(S, D, H, G, d, seed=12)
+    O, _ = oracle_mod.forward(X, Wq, Wk, Wv, H, G, d)
+    v0 = X[0] @ Wv[0:d].T
+    for h in range(H):
+        close(O[0, h * d:(h + 1) * d], v0, 1e-14)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_uniform_attention_when_wq_zero(oracle_mod, causal):
+    """Wq = 0 makes every score 0: P_ij = 1/n_i, O is a (prefix) mean of V,
+    LSE = ln n_i, Q = 0 so dK = 0 and dWk = 0 exactly, and
+    dV_j = sum_h sum_{i sees j} dO_i / n_i."""
+    S, D, H, G, d = 31, 12, 4, 2, 6
+    X, Wq, Wk, Wv, dO = draw(S, D, H, G, d, seed=13, wq_zero=True)
+    out = oracle_mod.backward(X, Wq, Wk, Wv, dO, H, G, d, causal=causal)
+    n = np.arange(1, S + 1, dtype=np.float64) if causal else np.full(S, float(S))
+    r = H // G
+    for h in range(H):
+        g = h // r
+        v = X @ Wv[g * d:(g + 1) * d].T
+        mean = np.cumsum(v, axis=0) / n[:, None] if causal else np.broadcast_to(v.mean(0), v.shape)
+        close(out["O"][:, h * d:(h + 1) * d], mean, 1e-13)
+        close(out["LSE"][h], np.log(n), 1e-14)
+    assert np.all(out["dWk"] == 0.0)
+    for g in range(G):
+        w = np.zeros((S, d))
+        for h in range(g * r, (g + 1) * r):
+            w += dO[:, h * d:(h + 1) * d] / n[:, None]
+        # dV_j = sum_{i >= j} w_i (causal) or sum_i w_i (full): a reverse prefix sum
+        dV = np.cumsum(w[::-1], axis=0)[::-1] if causal else np.broadcast_to(w.sum(0), w.shape)
+        close(out["dWv"][g * d:(g + 1) * d], dV.T @ X, 1e-12)
+
+
+def test_causal_invariance(oracle_mod):
+    S, D, H, G, d = 48, 16, 4, 2, 8
+    X, Wq, Wk, Wv, _ = draw(S, D, H, G, d, seed=14)
+    O1, L1 = oracle_mod.forward(X, Wq, Wk, Wv, H, G, d)
+    t = 20
+    X2 = X.copy()
+    X2[t + 1:] = np.random.default_rng(99).standard_normal(X2[t + 1:].shape)
+    O2, L2 = oracle_mod.forward(X2, Wq, Wk, Wv, H, G, d)
+    np.testing.assert_array_equal(O1[:t + 1], O2[:t + 1])
+    np.testing.assert_array_equal(L1[:, :t + 1], L2[:, :t + 1])
+    assert not np.array_equal(O1[t + 1:], O2[t + 1:])
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_scaling_identities(oracle_mod, causal):
+    """<dWv,Wv> = <dO,O> (O is linear in Wv); <dWq,Wq> = <dWk,Wk> (scores are
+    unchanged by Wq*a, Wk/a); <dX,X> = sum of <dW,W> (X*a equals all W*a)."""
+    S, D, H, G, d = 45, 20, 6, 2, 8
+    X, Wq, Wk, Wv, dO = draw(S, D, H, G, d, seed=15)
+    o = oracle_mod.backward(X, Wq, Wk, Wv, dO, H, G, d, causal=causal)
+    ip = lambda a, b: float(np.sum(a * b))
+    assert abs(ip(o["dWv"], Wv) - ip(dO, o["O"])) <= 1e-10 * abs(ip(dO, o["O"])) + 1e-10
+    assert abs(ip(o["dWq"], Wq) - ip(o["dWk"], Wk)) <= 1e-10 * abs(ip(o["dWq"], Wq)) + 1e-10
+    tot = ip(o["dWq"], Wq) + ip(o["dWk"], Wk) + ip(o["dWv"], Wv)
+    assert abs(ip(o["dX"], X) - tot) <= 1e-10 * abs(tot) + 1e-10
+
+
+def test_thread_count_independent(oracle_mod):
+    S, D, H, G, d = 41, 16, 4, 2, 8
+    X, Wq, Wk, Wv, dO = draw(S, D, H, G, d, seed=16)
+    a = oracle_mod.backward(X, Wq, Wk, Wv, dO, H, G, d, nthreads=1)
+    b = oracle_mod.backward(X, Wq, Wk, Wv, dO, H, G, d, nthreads=5)
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k])
+
+
+def test_sampled_rows_match_full(oracle_mod):
+    S, D, H, G, d = 70, 16, 4, 2, 8
+    X, Wq, Wk, Wv, _ = draw(S, D, H, G, d, seed=17)
+    O, LSE = oracle_mod.forward(X, Wq, Wk, Wv, H, G, d)
+    rows = [0, 1, 33, 69, 5]
+    Or, Lr = oracle_mod.forward_rows(X, Wq, Wk, Wv, H, G, d, rows)
+    np.testing.assert_array_equal(Or, O[rows])
+    np.testing.assert_array_equal(Lr, LSE[:, rows])
+
+
+def test_input_encodings_decode_exactly(oracle_mod):
+    """bf16 bit patterns and fp32 storage decode to the values they hold."""
+    S, D, H, G, d = 20, 16, 2, 1, 8
+    X, Wq, Wk, Wv, dO = draw(S, D, H, G, d, seed=18)
+    tb = [torch.tensor(a, dtype=torch.float32).to(torch.bfloat16) for a in (X, Wq, Wk, Wv, dO)]
+    bits = [t.view(torch.int16).numpy().view(np.uint16) for t in tb]
+    vals = [t.to(torch.float64).numpy() for t in tb]
+    a = oracle_mod.backward(*bits, H, G, d)
+    b = oracle_mod.backward(*vals, H, G, d)
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k])
+    f32 = [np.asarray(v, np.float32) for v in (X, Wq, Wk, Wv)]
+    c = oracle_mod.forward(*f32, H, G, d)
+    e = oracle_mod.forward(*[v.astype(np.float64) for v in f32], H, G, d)
+    np.testing.assert_array_equal(c[0], e[0])
+
+
+def test_rejects_bad_shapes(oracle_mod):
+    X, Wq, Wk, Wv, _ = draw(8, 8, 3, 2, 4)  # G does not divide H
+    with pytest.raises(ValueError):
+        oracle_mod.forward(X, Wq, Wk, Wv, 3, 2, 4)

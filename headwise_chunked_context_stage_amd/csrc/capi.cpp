@@ -1,0 +1,355 @@
+// capi.cpp -- the C ABI: validation, the stage loop of the forward and the
+// backward, and optional per-launch timing.
+//
+// Stage loop (paper.rainbus.top summary of "Untied Ulysses", section
+// 方法步骤详情, steps (1) and (3); the all-to-all steps (2) and (4) move data
+// between devices and have no counterpart on one GPU):
+//   forward,  stage s:  project Q of its U heads (and K, V when it opens a
+//                       KV group) into the stage buffers, then attention over
+//                       the full sequence into the stage's columns of O.
+//   backward, stage s:  recompute the same projections, D = rowsum(dO*O),
+//                       dK/dV (carried in fp32 across the stages of a group),
+//                       dQ, the weight gradients of the stage's heads, and
+//                       dX += (gradients) x (weights) with dX itself as the
+//                       running fp32 sum.
+// All work is enqueued on the caller's stream; nothing here synchronises.
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "upipe_internal.h"
+
+using namespace upipe;
+
+struct upipe_plan {
+  Plan p;
+};
+
+namespace {
+
+// ------------------------------------------------------------------ timing
+struct TimingRec {
+  int kind;
+  hipEvent_t a, b;
+};
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<TimingRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+TimingRec g_open{-1, nullptr, nullptr};
+
+hipEvent_t take_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool ptr_ok(const void* p) { return p != nullptr && aligned(p, 16); }
+
+char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
+const char* at(const void* base, size_t off) { return static_cast<const char*>(base) + off; }
+
+#define UPIPE_TRY(expr)                  \
+  do {                                   \
+    hipError_t e_ = (expr);              \
+    if (e_ != hipSuccess) return UPIPE_ERR_HIP; \
+  } while (0)
+
+// Launch wrappers: time the launch when timing is on.
+template <typename F>
+hipError_t timed(int kind, hipStream_t st, F&& f) {
+  timing_begin(kind, st);
+  hipError_t e = f();
+  timing_end(kind, st);
+  return e;
+}
+
+struct Kernels {
+  decltype(&bf16::proj) proj;
+  decltype(&bf16::attn_fwd) attn_fwd;
+  decltype(&bf16::bwd_pre) bwd_pre;
+  decltype(&bf16::attn_dkv) attn_dkv;
+  decltype(&bf16::attn_dq) attn_dq;
+  decltype(&bf16::dw) dw;
+  decltype(&bf16::dx) dx;
+};
+
+Kernels kernels_for(int dtype) {
+  if (dtype == UPIPE_BF16)
+    return {bf16::proj, bf16::attn_fwd, bf16::bwd_pre, bf16::attn_dkv, bf16::attn_dq, bf16::dw,
+            bf16::dx};
+  return {f32::proj, f32::attn_fwd, f32::bwd_pre, f32::attn_dkv, f32::attn_dq, f32::dw, f32::dx};
+}
+
+// Project the stage's query heads (and its KV heads when it opens their group)
+// into the stage buffers.  Chunks: one per head, d rows of the weight each.
+hipError_t stage_projection(const Plan& p, const Stage& st, const Kernels& K, const void* X,
+                            const void* Wq, const void* Wk, const void* Wv, void* ws,
+                            hipStream_t s) {
+  const size_t e = p.elem();
+  const size_t wrows = static_cast<size_t>(p.d) * p.D * e;  // bytes of one head's weight rows
+  const size_t hbuf = static_cast<size_t>(p.S) * p.d * e;   // bytes of one head's [S][d] buffer
+  std::vector<std::pair<const void*, void*>> jobs;
+  for (int h = 0; h < st.nq; ++h)
+    jobs.push_back({at(Wq, (st.q0 + h) * wrows), at(ws, p.ws.q + h * hbuf)});
+  if (st.load) {
+    for (int g = 0; g < st.nkv; ++g) {
+      jobs.push_back({at(Wk, (st.kv0 + g) * wrows), at(ws, p.ws.k + g * hbuf)});
+      jobs.push_back({at(Wv, (st.kv0 + g) * wrows), at(ws, p.ws.v + g * hbuf)});
+    }
+  }
+  for (size_t b = 0; b < jobs.size(); b += kMaxChunks) {
+    ChunkTable t;
+    std::memset(&t, 0, sizeof(t));
+    t.n = static_cast<int>(std::min<size_t>(kMaxChunks, jobs.size() - b));
+    for (int i = 0; i < t.n; ++i) {
+      t.w[i] = jobs[b + i].first;
+      t.a[i] = jobs[b + i].second;
+    }
+    hipError_t err = timed(UPIPE_K_PROJ, s, [&] { return K.proj(X, p.S, p.D, p.d, t, s); });
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+AttnArgs attn_args(const Plan& p, const Stage& st, void* ws) {
+  AttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.S = p.S;
+  a.H = p.H;
+  a.d = p.d;
+  a.causal = p.causal;
+  a.nq = st.nq;
+  a.q_head0 = st.q0;
+  a.r = p.r;
+  a.kv_head0 = st.kv0;
+  a.q = at(ws, p.ws.q);
+  a.k = at(ws, p.ws.k);
+  a.v = at(ws, p.ws.v);
+  a.first_of_group = st.load ? 1 : 0;
+  a.last_of_group = st.done ? 1 : 0;
+  return a;
+}
+
+}  // namespace
+
+namespace upipe {
+
+void timing_begin(int kind, hipStream_t st) {
+  if (!g_timing) return;
+  std::lock_guard<std::mutex> g(g_tmu);
+  g_open.kind = kind;
+  g_open.a = take_event();
+  g_open.b = take_event();
+  if (g_open.a) hipEventRecord(g_open.a, st);
+}
+
+void timing_end(int kind, hipStream_t st) {
+  if (!g_timing) return;
+  std::lock_guard<std::mutex> g(g_tmu);
+  if (g_open.kind != kind || !g_open.a || !g_open.b) return;
+  hipEventRecord(g_open.b, st);
+  g_recs.push_back(g_open);
+  g_open = TimingRec{-1, nullptr, nullptr};
+}
+
+}  // namespace upipe
+
+extern "C" {
+
+int upipe_create(upipe_plan** out, int64_t S, int64_t d_model, int H, int G, int d_head, int U,
+                 int causal, int dtype) {
+  if (!out) return UPIPE_ERR_ARG;
+  *out = nullptr;
+  upipe_plan* h = new (std::nothrow) upipe_plan;
+  if (!h) return UPIPE_ERR_ARG;
+  int rc = make_plan(h->p, S, d_model, H, G, d_head, U, causal, dtype);
+  if (rc != UPIPE_OK) {
+    delete h;
+    return rc;
+  }
+  *out = h;
+  return UPIPE_OK;
+}
+
+void upipe_destroy(upipe_plan* p) { delete p; }
+
+size_t upipe_peak_bytes(const upipe_plan* p) {
+  if (!p) return 0;
+  return std::max(p->p.ws.fwd_bytes, p->p.ws.bwd_bytes);
+}
+
+size_t upipe_peak_bytes_phase(const upipe_plan* p, int phase) {
+  if (!p) return 0;
+  return phase == 0 ? p->p.ws.fwd_bytes : p->p.ws.bwd_bytes;
+}
+
+int upipe_num_stages(const upipe_plan* p) { return p ? static_cast<int>(p->p.stages.size()) : 0; }
+
+int upipe_stage_info(const upipe_plan* p, int s, int* q_first, int* q_count, int* kv_first,
+                     int* kv_count, int* kv_load, int* kv_done) {
+  if (!p || s < 0 || s >= static_cast<int>(p->p.stages.size())) return UPIPE_ERR_ARG;
+  const Stage& st = p->p.stages[s];
+  if (q_first) *q_first = st.q0;
+  if (q_count) *q_count = st.nq;
+  if (kv_first) *kv_first = st.kv0;
+  if (kv_count) *kv_count = st.nkv;
+  if (kv_load) *kv_load = st.load ? 1 : 0;
+  if (kv_done) *kv_done = st.done ? 1 : 0;
+  return UPIPE_OK;
+}
+
+const char* upipe_strerror(int code) {
+  switch (code) {
+    case UPIPE_OK: return "ok";
+    case UPIPE_ERR_ARG: return "invalid argument";
+    case UPIPE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case UPIPE_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case UPIPE_ERR_HIP: return "HIP call failed";
+    default: return "unknown error";
+  }
+}
+
+int upipe_fwd(const upipe_plan* h, const void* X, const void* Wq, const void* Wk, const void* Wv,
+              void* O, float* LSE, void* ws, size_t ws_bytes, void* stream) {
+  if (!h) return UPIPE_ERR_ARG;
+  const Plan& p = h->p;
+  if (p.S == 0) return UPIPE_OK;
+  if (!ptr_ok(X) || !ptr_ok(Wq) || !ptr_ok(Wk) || !ptr_ok(Wv) || !ptr_ok(O) || !ptr_ok(LSE))
+    return UPIPE_ERR_ARG;
+  if (!ws || !aligned(ws, kAlign) || ws_bytes < p.ws.fwd_bytes) return UPIPE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Kernels K = kernels_for(p.dtype);
+  for (const Stage& st : p.stages) {
+    UPIPE_TRY(stage_projection(p, st, K, X, Wq, Wk, Wv, ws, s));
+    AttnArgs a = attn_args(p, st, ws);
+    a.o = O;
+    a.lse = LSE;
+    UPIPE_TRY(timed(UPIPE_K_ATTN_FWD, s, [&] { return K.attn_fwd(a, s); }));
+  }
+  return UPIPE_OK;
+}
+
+int upipe_bwd(const upipe_plan* h, const void* dO, const void* X, const void* Wq, const void* Wk,
+              const void* Wv, const void* O, const float* LSE, float* dX, float* dWq, float* dWk,
+              float* dWv, void* ws, size_t ws_bytes, void* stream) {
+  if (!h) return UPIPE_ERR_ARG;
+  const Plan& p = h->p;
+  if (!ptr_ok(dWq) || !ptr_ok(dWk) || !ptr_ok(dWv)) return UPIPE_ERR_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t wq_bytes = static_cast<size_t>(p.H) * p.d * p.D * 4;
+  const size_t wkv_bytes = static_cast<size_t>(p.G) * p.d * p.D * 4;
+  if (p.S == 0) {  // empty sequence: every weight gradient is an empty sum
+    UPIPE_TRY(timed(UPIPE_K_FILL, s, [&] { return fill_zero(dWq, wq_bytes, s); }));
+    UPIPE_TRY(timed(UPIPE_K_FILL, s, [&] { return fill_zero(dWk, wkv_bytes, s); }));
+    UPIPE_TRY(timed(UPIPE_K_FILL, s, [&] { return fill_zero(dWv, wkv_bytes, s); }));
+    return UPIPE_OK;
+  }
+  if (!ptr_ok(dO) || !ptr_ok(X) || !ptr_ok(Wq) || !ptr_ok(Wk) || !ptr_ok(Wv) || !ptr_ok(O) ||
+      !ptr_ok(LSE) || !ptr_ok(dX))
+    return UPIPE_ERR_ARG;
+  if (!ws || !aligned(ws, kAlign) || ws_bytes < p.ws.bwd_bytes) return UPIPE_ERR_WORKSPACE;
+  const Kernels K = kernels_for(p.dtype);
+  const size_t e = p.elem();
+  const size_t wrows = static_cast<size_t>(p.d) * p.D * e;
+  const size_t dwrows = static_cast<size_t>(p.d) * p.D;  // fp32 elements of one head's dW rows
+  const size_t hbuf = static_cast<size_t>(p.S) * p.d * e;
+
+  UPIPE_TRY(timed(UPIPE_K_FILL, s,
+                  [&] { return fill_zero(dX, static_cast<size_t>(p.S) * p.D * 4, s); }));
+  for (const Stage& st : p.stages) {
+    UPIPE_TRY(stage_projection(p, st, K, X, Wq, Wk, Wv, ws, s));
+    AttnArgs a = attn_args(p, st, ws);
+    a.dO = dO;
+    a.o_in = O;
+    a.lse_in = LSE;
+    a.dd = reinterpret_cast<float*>(at(ws, p.ws.dd));
+    a.dq = at(ws, p.ws.dq);
+    a.dk = at(ws, p.ws.dk);
+    a.dv = at(ws, p.ws.dv);
+    if (p.ws.dk_acc) {
+      a.dk_acc = reinterpret_cast<float*>(at(ws, p.ws.dk_acc));
+      a.dv_acc = reinterpret_cast<float*>(at(ws, p.ws.dv_acc));
+    }
+    UPIPE_TRY(timed(UPIPE_K_BWD_PRE, s, [&] { return K.bwd_pre(a, s); }));
+    UPIPE_TRY(timed(UPIPE_K_ATTN_DKV, s, [&] { return K.attn_dkv(a, s); }));
+    UPIPE_TRY(timed(UPIPE_K_ATTN_DQ, s, [&] { return K.attn_dq(a, s); }));
+
+    // Gradient chunks in the one global order used for dX: inside each KV
+    // group, its query heads ascending, then the group's dK, then its dV.
+    // Every U walks this same sequence, so dX is summed in the same order.
+    struct Chunk {
+      void* a;
+      const void* w;
+      float* dw;
+    };
+    std::vector<Chunk> chunks;
+    auto add_q = [&](int hq) {
+      chunks.push_back({at(a.dq, (hq - st.q0) * hbuf), at(Wq, hq * wrows), dWq + hq * dwrows});
+    };
+    auto add_kv = [&](int g) {
+      chunks.push_back({at(a.dk, (g - st.kv0) * hbuf), at(Wk, g * wrows), dWk + g * dwrows});
+      chunks.push_back({at(a.dv, (g - st.kv0) * hbuf), at(Wv, g * wrows), dWv + g * dwrows});
+    };
+    for (int hq = st.q0; hq < st.q0 + st.nq; ++hq) {
+      add_q(hq);
+      const bool group_end = ((hq + 1) % p.r) == 0;
+      if (group_end && st.done) add_kv(hq / p.r);
+    }
+    for (size_t b = 0; b < chunks.size(); b += kMaxChunks) {
+      ChunkTable t;
+      std::memset(&t, 0, sizeof(t));
+      t.n = static_cast<int>(std::min<size_t>(kMaxChunks, chunks.size() - b));
+      for (int i = 0; i < t.n; ++i) {
+        t.a[i] = chunks[b + i].a;
+        t.w[i] = chunks[b + i].w;
+        t.dw[i] = chunks[b + i].dw;
+      }
+      UPIPE_TRY(timed(UPIPE_K_DW, s, [&] { return K.dw(X, p.S, p.D, p.d, t, s); }));
+      UPIPE_TRY(timed(UPIPE_K_DX, s, [&] { return K.dx(dX, p.S, p.D, p.d, t, s); }));
+    }
+  }
+  return UPIPE_OK;
+}
+
+int upipe_timing_enable(int on) {
+  std::lock_guard<std::mutex> g(g_tmu);
+  g_timing = on != 0;
+  return UPIPE_OK;
+}
+
+int upipe_timing_read(double* ms, int64_t* launches, int n) {
+  std::lock_guard<std::mutex> g(g_tmu);
+  int rc = UPIPE_OK;
+  for (TimingRec& r : g_recs) {
+    float t = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess)
+      rc = UPIPE_ERR_HIP;
+    if (r.kind >= 0 && r.kind < n) {
+      if (ms) ms[r.kind] += t;
+      if (launches) launches[r.kind] += 1;
+    }
+    g_pool.push_back(r.a);
+    g_pool.push_back(r.b);
+  }
+  g_recs.clear();
+  return rc;
+}
+
+const char* upipe_kernel_name(int kind) {
+  static const char* names[UPIPE_K_COUNT] = {"proj", "attn_fwd", "bwd_pre", "attn_dkv",
+                                             "attn_dq", "dw", "dx", "fill"};
+  if (kind < 0 || kind >= UPIPE_K_COUNT) return "unknown";
+  return names[kind];
+}
+
+}  // extern "C"

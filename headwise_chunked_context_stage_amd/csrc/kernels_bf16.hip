@@ -1,0 +1,923 @@
+// kernels_bf16.hip -- bf16 kernels of the stage loop for gfx950 (CDNA4).
+//
+// Every dense contraction runs on v_mfma_f32_32x32x16_bf16 (bf16 inputs, fp32
+// accumulation).  Operand layout of that instruction, as used throughout:
+//   A (32 x 16, M x K): lane l supplies row m = l % 32 and the 8 k-slots
+//                       8*(l/32) .. 8*(l/32)+7 (one 16-byte register quad);
+//   B (16 x 32, K x N): lane l supplies column n = l % 32 and the same slots;
+//   C (32 x 32 fp32):   lane l holds column l % 32; register i holds row
+//                       8*(i/4) + 4*(l/32) + (i%4).
+// A and B pair their k-slots identically, so a contraction may visit its k
+// indices in any fixed order.  This is what lets an fp32 C result feed the
+// next product straight from registers: the 8 registers 8t..8t+7 of a C block
+// in lane half h hold the rows 16t + {4h..4h+3, 8+4h..8+4h+3}, and an operand
+// read from LDS must present the same rows in its slots 8h..8h+7.  Tiles that
+// are read "transposed" (k along a row of the source) are therefore staged
+// into LDS with that row order inside every 16-row group ("slot order"), by an
+// in-register 8x8 transpose during the global->LDS copy.
+//
+// Attention (flash formulation; the per-stage attention of the pages,
+// paper.rainbus.top summary of "Untied Ulysses", section 方法步骤详情 step (3)):
+// scores s = q.k / sqrt(d), softmax in the log2 domain with the hardware exp2,
+// online max/sum in fp32, LSE returned in natural log.  Backward recomputes P
+// from LSE: P = exp(s - LSE), dS = P (dP - D), D = rowsum(dO * O).
+//
+// Rounding points (bf16, round-to-nearest-even): stage Q/K/V, O, P and dS at
+// the MFMA inputs, dQ/dK/dV before the weight/input-gradient GEMMs.  All
+// accumulation is fp32.  No atomics: every output element has one owner and a
+// fixed summation order, so results are identical run to run and for every U.
+#include <hip/hip_runtime.h>
+
+#include "upipe_internal.h"
+
+namespace upipe {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int DH = 128;  // head dimension of the bf16 path
+
+__device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ bf16x8 frag(const u16* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+// Hardware exp2 (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+__device__ __forceinline__ unsigned pack2(float lo, float hi) {
+  __bf16 a = static_cast<__bf16>(lo), b = static_cast<__bf16>(hi);
+  return static_cast<unsigned>(__builtin_bit_cast(u16, a)) |
+         (static_cast<unsigned>(__builtin_bit_cast(u16, b)) << 16);
+}
+
+// Registers 8t..8t+7 of a C block -> an 8-slot bf16 operand.
+__device__ __forceinline__ bf16x8 pack8(const f32x16& c, int t) {
+  u32x4 r;
+  r[0] = pack2(c[8 * t + 0], c[8 * t + 1]);
+  r[1] = pack2(c[8 * t + 2], c[8 * t + 3]);
+  r[2] = pack2(c[8 * t + 4], c[8 * t + 5]);
+  r[3] = pack2(c[8 * t + 6], c[8 * t + 7]);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// 8x8 bf16 transpose: in[j] = row j (8 elements), out[c] = column c.
+__device__ __forceinline__ void transpose8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int k = c / 2;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const unsigned a = in[2 * m][k], b = in[2 * m + 1][k];
+      out[c][m] = (c & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+    }
+  }
+}
+
+// Row (within a 16-row group) of slot m of the 8-slot half `hh`.
+__device__ __forceinline__ int slot_row(int hh, int m) { return m < 4 ? 4 * hh + m : 8 + 4 * hh + (m - 4); }
+
+// Map a workgroup id so that each XCD (ids are dealt round-robin over 8 XCDs)
+// runs one contiguous range of logical ids.
+__device__ __forceinline__ int xcd_remap(int id, int total) {
+  const int x = id % 8, local = id / 8;
+  const int per = total / 8, rem = total % 8;
+  return x * per + min(x, rem) + local;
+}
+
+// ===================================================================== GEMMs
+// 128 x 128 output tile, 64-wide k steps, 4 waves as 2 x 2 (64 x 64 each),
+// LDS double-buffered with register prefetch.
+constexpr int GB = 128, GK = 64, GS = GK + 8;  // tile, k step, LDS row stride (elements)
+constexpr int GBUF = 2 * GB * GS;             // elements per buffer (two operand tiles)
+
+// ---- projection: out[i][c] = sum_k X[i][k] W[c][k] for one head (d = 128).
+__global__ __launch_bounds__(256, 2) void proj_kernel(const u16* __restrict__ X, int64_t S,
+                                                      int64_t D, ChunkTable t, int nrb) {
+  __shared__ __attribute__((aligned(16))) u16 lds[2 * GBUF];
+  const int total = nrb * t.n;
+  const int lid = xcd_remap(blockIdx.x, total);
+  const int rb = lid / t.n, ch = lid % t.n;
+  const u16* W = static_cast<const u16*>(t.w[ch]);
+  u16* out = static_cast<u16*>(t.a[ch]);
+  const int64_t i0 = static_cast<int64_t>(rb) * GB;
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, col = lane % 32, hf = lane / 32;
+  const int wm = wave / 2, wn = wave % 2;
+
+  u32x4 rx[4], rw[4];
+  auto load = [&](int64_t k0) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int row = tid / 8 + 32 * m, chunk = tid % 8;
+      const int64_t gi = i0 + row;
+      rx[m] = gi < S ? ld16(X + gi * D + k0 + chunk * 8) : u32x4{0, 0, 0, 0};
+      rw[m] = ld16(W + static_cast<int64_t>(row) * D + k0 + chunk * 8);
+    }
+  };
+  auto store = [&](int b) {
+    u16* xs = lds + b * GBUF;
+    u16* ws = xs + GB * GS;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int row = tid / 8 + 32 * m, chunk = tid % 8;
+      st16(xs + row * GS + chunk * 8, rx[m]);
+      st16(ws + row * GS + chunk * 8, rw[m]);
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = zero16();
+
+  const int nk = static_cast<int>(D / GK);
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kb = 0; kb < nk; ++kb) {
+    const int cur = kb & 1;
+    if (kb + 1 < nk) load(static_cast<int64_t>(kb + 1) * GK);
+    const u16* xs = lds + cur * GBUF;
+    const u16* ws = xs + GB * GS;
+#pragma unroll
+    for (int t4 = 0; t4 < GK / 16; ++t4) {
+      bf16x8 fa[2], fb[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) fa[mb] = frag(xs + (64 * wm + 32 * mb + col) * GS + 16 * t4 + 8 * hf);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) fb[nb] = frag(ws + (64 * wn + 32 * nb + col) * GS + 16 * t4 + 8 * hf);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma(fa[mb], fb[nb], acc[mb][nb]);
+    }
+    if (kb + 1 < nk) store(cur ^ 1);
+    __syncthreads();
+  }
+  // Epilogue: C (bf16) -> LDS tile [128][136] -> coalesced 16-byte stores.
+  constexpr int CS = GB + 8;
+  u16* cs = lds;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 64 * wm + 32 * mb + 8 * (i / 4) + 4 * hf + (i % 4);
+        const int c = 64 * wn + 32 * nb + col;
+        cs[row * CS + c] = __builtin_bit_cast(u16, static_cast<__bf16>(acc[mb][nb][i]));
+      }
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const int e = tid + 256 * m, row = e / 16, chunk = e % 16;
+    const int64_t gi = i0 + row;
+    if (gi < S) st16(out + gi * DH + chunk * 8, ld16(cs + row * CS + chunk * 8));
+  }
+}
+
+// ---- weight gradient: dW[c][k] = sum_i A[i][c] X[i][k] (one chunk, K = S).
+// Both operands are read with i along the k-slots, so both tiles are staged
+// transposed (identity slot order).
+__global__ __launch_bounds__(256, 2) void dw_kernel(const u16* __restrict__ X, int64_t S, int64_t D,
+                                                    ChunkTable t, int ncb) {
+  __shared__ __attribute__((aligned(16))) u16 lds[2 * GBUF];
+  const int total = ncb * t.n;
+  const int lid = xcd_remap(blockIdx.x, total);
+  const int cb = lid / t.n, ch = lid % t.n;
+  const u16* A = static_cast<const u16*>(t.a[ch]);
+  float* dW = t.dw[ch];
+  const int64_t k0 = static_cast<int64_t>(cb) * GB;  // column block of D
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, col = lane % 32, hf = lane / 32;
+  const int wm = wave / 2, wn = wave % 2;
+  // staging role: threads 0..127 stage A (rows of S x 128 head columns),
+  // 128..255 stage X (rows of S x 128 columns of D); each one 8x8 block.
+  const int st = tid % 128, rg = st / 16, cc = st % 16;
+  const bool isA = tid < 128;
+
+  u32x4 rr[8];
+  auto load = [&](int64_t s0) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int64_t gi = s0 + rg * 8 + m;
+      if (gi < S)
+        rr[m] = isA ? ld16(A + gi * DH + cc * 8) : ld16(X + gi * D + k0 + cc * 8);
+      else
+        rr[m] = u32x4{0, 0, 0, 0};
+    }
+  };
+  auto store = [&](int b) {
+    u16* base = lds + b * GBUF + (isA ? 0 : GB * GS);
+    u32x4 tc[8];
+    transpose8(rr, tc);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) st16(base + (cc * 8 + c) * GS + rg * 8, tc[c]);
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = zero16();
+
+  const int nk = static_cast<int>((S + GK - 1) / GK);
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kb = 0; kb < nk; ++kb) {
+    const int cur = kb & 1;
+    if (kb + 1 < nk) load(static_cast<int64_t>(kb + 1) * GK);
+    const u16* as = lds + cur * GBUF;
+    const u16* xs = as + GB * GS;
+#pragma unroll
+    for (int t4 = 0; t4 < GK / 16; ++t4) {
+      bf16x8 fa[2], fb[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) fa[mb] = frag(as + (64 * wm + 32 * mb + col) * GS + 16 * t4 + 8 * hf);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) fb[nb] = frag(xs + (64 * wn + 32 * nb + col) * GS + 16 * t4 + 8 * hf);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma(fa[mb], fb[nb], acc[mb][nb]);
+    }
+    if (kb + 1 < nk) store(cur ^ 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int c = 64 * wm + 32 * mb + 8 * (i / 4) + 4 * hf + (i % 4);
+        const int64_t k = k0 + 64 * wn + 32 * nb + col;
+        dW[static_cast<int64_t>(c) * D + k] = acc[mb][nb][i];
+      }
+}
+
+// ---- input gradient: dX[i][k] += sum over chunks (table order) of
+// sum_c A[i][c] W[c][k].  dX itself is the fp32 running sum (the MFMA C input).
+__global__ __launch_bounds__(256, 2) void dx_kernel(float* __restrict__ dX, int64_t S, int64_t D,
+                                                    ChunkTable t, int nrb, int ncb) {
+  __shared__ __attribute__((aligned(16))) u16 lds[2 * GBUF];
+  const int lid = xcd_remap(blockIdx.x, nrb * ncb);
+  const int rb = lid / ncb, cb = lid % ncb;
+  const int64_t i0 = static_cast<int64_t>(rb) * GB;
+  const int64_t k0 = static_cast<int64_t>(cb) * GB;
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, col = lane % 32, hf = lane / 32;
+  const int wm = wave / 2, wn = wave % 2;
+  const int rg = (tid % 128) / 16, cc = tid % 16;  // W staging block (threads 0..127)
+
+  u32x4 ra[4], rw[8];
+  auto load = [&](int step) {
+    const int ch = step / (DH / GK), c0 = (step % (DH / GK)) * GK;
+    const u16* A = static_cast<const u16*>(t.a[ch]);
+    const u16* W = static_cast<const u16*>(t.w[ch]);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int row = tid / 8 + 32 * m, chunk = tid % 8;
+      const int64_t gi = i0 + row;
+      ra[m] = gi < S ? ld16(A + gi * DH + c0 + chunk * 8) : u32x4{0, 0, 0, 0};
+    }
+    if (tid < 128) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) rw[m] = ld16(W + static_cast<int64_t>(c0 + rg * 8 + m) * D + k0 + cc * 8);
+    }
+  };
+  auto store = [&](int b) {
+    u16* as = lds + b * GBUF;
+    u16* wt = as + GB * GS;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int row = tid / 8 + 32 * m, chunk = tid % 8;
+      st16(as + row * GS + chunk * 8, ra[m]);
+    }
+    if (tid < 128) {
+      u32x4 tc[8];
+      transpose8(rw, tc);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) st16(wt + (cc * 8 + c) * GS + rg * 8, tc[c]);
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t gi = i0 + 64 * wm + 32 * mb + 8 * (i / 4) + 4 * hf + (i % 4);
+        const int64_t k = k0 + 64 * wn + 32 * nb + col;
+        acc[mb][nb][i] = gi < S ? dX[gi * D + k] : 0.f;
+      }
+
+  const int nsteps = t.n * (DH / GK);
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int sidx = 0; sidx < nsteps; ++sidx) {
+    const int cur = sidx & 1;
+    if (sidx + 1 < nsteps) load(sidx + 1);
+    const u16* as = lds + cur * GBUF;
+    const u16* wt = as + GB * GS;
+#pragma unroll
+    for (int t4 = 0; t4 < GK / 16; ++t4) {
+      bf16x8 fa[2], fb[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) fa[mb] = frag(as + (64 * wm + 32 * mb + col) * GS + 16 * t4 + 8 * hf);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) fb[nb] = frag(wt + (64 * wn + 32 * nb + col) * GS + 16 * t4 + 8 * hf);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma(fa[mb], fb[nb], acc[mb][nb]);
+    }
+    if (sidx + 1 < nsteps) store(cur ^ 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t gi = i0 + 64 * wm + 32 * mb + 8 * (i / 4) + 4 * hf + (i % 4);
+        const int64_t k = k0 + 64 * wn + 32 * nb + col;
+        if (gi < S) dX[gi * D + k] = acc[mb][nb][i];
+      }
+}
+
+// ================================================================= attention
+// ---- forward.  Workgroup: 128 query rows of one head (4 waves x 32 rows);
+// key/value tiles of 64 rows.  Each wave computes S^T = K Q^T (lane = query
+// row, registers = keys), so row statistics are per lane plus one exchange
+// between the two lane halves, and O^T = V^T P^T keeps O with the query in
+// the lane (the online rescale is a per-lane scalar).
+namespace fw {
+constexpr int BM = 128, BN = 64;
+constexpr int KS = DH + 8;   // K tile row stride (row-major [key][d])
+constexpr int VS = BN + 8;   // V^T tile row stride ([d][key], slot order)
+constexpr int KE = BN * KS;  // elements of the K tile
+constexpr int BUF = KE + DH * VS;
+}  // namespace fw
+
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
+  using namespace fw;
+  __shared__ __attribute__((aligned(16))) u16 lds[2 * BUF];
+  const int64_t S = a.S;
+  const int nqb = static_cast<int>((S + BM - 1) / BM);
+  const int qb = nqb - 1 - static_cast<int>(blockIdx.x) / a.nq;  // longest rows first
+  const int u = blockIdx.x % a.nq;
+  const int h = a.q_head0 + u;
+  const int gl = h / a.r - a.kv_head0;
+  const u16* Q = static_cast<const u16*>(a.q) + static_cast<int64_t>(u) * S * DH;
+  const u16* K = static_cast<const u16*>(a.k) + static_cast<int64_t>(gl) * S * DH;
+  const u16* V = static_cast<const u16*>(a.v) + static_cast<int64_t>(gl) * S * DH;
+
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, col = lane % 32, hf = lane / 32;
+  const int64_t qfirst = static_cast<int64_t>(qb) * BM;
+  const int64_t wq0 = qfirst + 32 * wave;
+  const int64_t myq = wq0 + col;
+  const float c = kLog2e / sqrtf(static_cast<float>(DH));
+
+  bf16x8 qf[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+    qf[t] = __builtin_bit_cast(bf16x8, myq < S ? ld16(Q + myq * DH + 16 * t + 8 * hf) : u32x4{0, 0, 0, 0});
+
+  const int64_t kv_end = a.causal ? min(S, qfirst + BM) : S;
+  const int ntiles = static_cast<int>((kv_end + BN - 1) / BN);
+
+  // staging roles: threads 0..127 copy K rows; 128..255 transpose V blocks.
+  const bool isK = tid < 128;
+  const int vt = tid - 128, vdc = vt % 16, vrg = vt / 16, vs16 = vrg / 2, vhh = vrg % 2;
+  u32x4 rr[8];
+  auto load = [&](int j) {
+    const int64_t kv0 = static_cast<int64_t>(j) * BN;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      if (isK) {
+        const int row = tid / 16 + 8 * m, chunk = tid % 16;
+        const int64_t kv = kv0 + row;
+        rr[m] = kv < S ? ld16(K + kv * DH + chunk * 8) : u32x4{0, 0, 0, 0};
+      } else {
+        const int64_t kv = kv0 + 16 * vs16 + slot_row(vhh, m);
+        rr[m] = kv < S ? ld16(V + kv * DH + vdc * 8) : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store = [&](int b) {
+    u16* ks = lds + b * BUF;
+    u16* vts = ks + KE;
+    if (isK) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) st16(ks + (tid / 16 + 8 * m) * KS + (tid % 16) * 8, rr[m]);
+    } else {
+      u32x4 tc[8];
+      transpose8(rr, tc);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) st16(vts + (vdc * 8 + e) * VS + 16 * vs16 + 8 * vhh, tc[e]);
+    }
+  };
+
+  f32x16 oacc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) oacc[i] = zero16();
+  float m_run = -INFINITY, l_run = 0.f;
+
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int j = 0; j < ntiles; ++j) {
+    const int cur = j & 1;
+    if (j + 1 < ntiles) load(j + 1);
+    const int64_t kv0 = static_cast<int64_t>(j) * BN;
+    const bool active = !a.causal || kv0 <= wq0 + 31;
+    if (active) {
+      const u16* ks = lds + cur * BUF;
+      const u16* vts = ks + KE;
+      f32x16 s[2] = {zero16(), zero16()};
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) s[b] = mfma(frag(ks + (32 * b + col) * KS + 16 * t + 8 * hf), qf[t], s[b]);
+      }
+      const bool need_mask = a.causal ? (kv0 + BN - 1 > wq0) : (kv0 + BN > S);
+      float mt = -INFINITY;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float x = s[b][i] * c;
+          if (need_mask) {
+            const int64_t kv = kv0 + 32 * b + 8 * (i / 4) + 4 * hf + (i % 4);
+            if (a.causal ? (kv > myq) : (kv >= S)) x = -INFINITY;
+          }
+          s[b][i] = x;
+          mt = fmaxf(mt, x);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = ex2(m_run - m_new);
+      float ls = 0.f;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = ex2(s[b][i] - m_new);
+          s[b][i] = p;
+          ls += p;
+        }
+      l_run = l_run * alpha + ls;
+      m_run = m_new;
+#pragma unroll
+      for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[d4][i] *= alpha;
+      bf16x8 pb[4];
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) pb[k4] = pack8(s[k4 / 2], k4 % 2);
+#pragma unroll
+      for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4)
+          oacc[d4] = mfma(frag(vts + (32 * d4 + col) * VS + 16 * k4 + 8 * hf), pb[k4], oacc[d4]);
+    }
+    if (j + 1 < ntiles) store(cur ^ 1);
+    __syncthreads();
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = 1.f / l_tot;
+  if (myq < S) {
+    u16* O = static_cast<u16*>(a.o) + myq * static_cast<int64_t>(a.H) * DH + static_cast<int64_t>(h) * DH;
+#pragma unroll
+    for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        u32x2 v;
+        v[0] = pack2(oacc[d4][4 * g4 + 0] * inv, oacc[d4][4 * g4 + 1] * inv);
+        v[1] = pack2(oacc[d4][4 * g4 + 2] * inv, oacc[d4][4 * g4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(O + 32 * d4 + 8 * g4 + 4 * hf) = v;
+      }
+    if (hf == 0) a.lse[static_cast<int64_t>(h) * S + myq] = (m_run + log2f(l_tot)) * kLn2;
+  }
+}
+
+// ---- D = rowsum(dO * O) for the stage's heads (fp32).  16 lanes per row.
+__global__ __launch_bounds__(256) void bwd_pre_kernel(AttnArgs a) {
+  const int u = blockIdx.y;
+  const int h = a.q_head0 + u;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 16 + threadIdx.x / 16;
+  const int part = threadIdx.x % 16;
+  float acc = 0.f;
+  if (row < a.S) {
+    const int64_t off = row * static_cast<int64_t>(a.H) * DH + static_cast<int64_t>(h) * DH + part * 8;
+    const u32x4 g = ld16(static_cast<const u16*>(a.dO) + off);
+    const u32x4 o = ld16(static_cast<const u16*>(a.o_in) + off);
+    const bf16x8 gb = __builtin_bit_cast(bf16x8, g), ob = __builtin_bit_cast(bf16x8, o);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += static_cast<float>(gb[e]) * static_cast<float>(ob[e]);
+  }
+  acc += __shfl_xor(acc, 8);
+  acc += __shfl_xor(acc, 4);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 1);
+  if (row < a.S && part == 0) a.dd[static_cast<int64_t>(u) * a.S + row] = acc;
+}
+
+// ---- dK, dV.  Workgroup: 128 key rows of one KV head (4 waves x 32 keys),
+// looping over the stage's query heads of that group (ascending) and over
+// 32-row query tiles.  Each wave computes S = Q K^T with the key in the lane
+// (registers = query rows), so P^T and dS^T are A operands straight from
+// registers; Q and dO are staged both row-major (for S and dP) and transposed
+// in slot order (for dV += P^T dO and dK += dS^T Q).  The fp32 sums are kept
+// in registers, and across the stages of a group in the fp32 carry buffers.
+namespace kv {
+constexpr int BN = 128, BM = 32;
+constexpr int RS = DH + 8;  // row-major tile stride
+constexpr int TS = BM + 8;  // transposed tile stride
+constexpr int QS_OFF = 0, DOS_OFF = BM * RS, QT_OFF = 2 * BM * RS, DOT_OFF = QT_OFF + DH * TS;
+constexpr int BUF = DOT_OFF + DH * TS;  // bf16 elements
+}  // namespace kv
+
+__global__ __launch_bounds__(256, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
+  using namespace kv;
+  __shared__ __attribute__((aligned(16))) u16 lds[2 * BUF];
+  __shared__ __attribute__((aligned(16))) float stat[2][2][BM];  // [buffer][lse2, D][row]
+  const int64_t S = a.S;
+  const int kt = blockIdx.x / nkv, gl = blockIdx.x % nkv;  // key tile 0 (most work) first
+  const int g = a.kv_head0 + gl;
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, col = lane % 32, hf = lane / 32;
+  const int64_t wk0 = static_cast<int64_t>(kt) * BN + 32 * wave;
+  const int64_t myk = wk0 + col;
+  const float tau = 1.f / sqrtf(static_cast<float>(DH));
+  const float c = kLog2e * tau;
+  const int64_t ldo = static_cast<int64_t>(a.H) * DH;
+
+  bf16x8 kf[8], vf[8];
+  {
+    const u16* K = static_cast<const u16*>(a.k) + static_cast<int64_t>(gl) * S * DH;
+    const u16* V = static_cast<const u16*>(a.v) + static_cast<int64_t>(gl) * S * DH;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      kf[t] = __builtin_bit_cast(bf16x8, myk < S ? ld16(K + myk * DH + 16 * t + 8 * hf) : u32x4{0, 0, 0, 0});
+      vf[t] = __builtin_bit_cast(bf16x8, myk < S ? ld16(V + myk * DH + 16 * t + 8 * hf) : u32x4{0, 0, 0, 0});
+    }
+  }
+
+  // accumulators: C layout, lane = d column (within 32-block d4), registers = key rows
+  f32x16 dk[4], dv[4];
+  if (a.first_of_group) {
+#pragma unroll
+    for (int d4 = 0; d4 < 4; ++d4) dk[d4] = dv[d4] = zero16();
+  } else {
+#pragma unroll
+    for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t kr = wk0 + 8 * (i / 4) + 4 * hf + (i % 4);
+        const int64_t off = (static_cast<int64_t>(gl) * S + kr) * DH + 32 * d4 + col;
+        dk[d4][i] = kr < S ? a.dk_acc[off] : 0.f;
+        dv[d4][i] = kr < S ? a.dv_acc[off] : 0.f;
+      }
+  }
+
+  const int h_lo = max(a.q_head0, g * a.r), h_hi = min(a.q_head0 + a.nq, (g + 1) * a.r);
+  const int nqt = static_cast<int>((S + BM - 1) / BM);
+  const int qt0 = a.causal ? static_cast<int>((static_cast<int64_t>(kt) * BN) / BM) : 0;
+  const int per_head = nqt - qt0;
+  const int niter = (h_hi - h_lo) * per_head;
+
+  // staging roles: 0..63 Q blocks, 64..127 dO blocks (8x8 each, both layouts),
+  // 128..159 lse2, 160..191 D.
+  const int sb = tid % 64, srg = sb / 16, sdc = sb % 16, ss16 = srg / 2, shh = srg % 2;
+  u32x4 rr[8];
+  float rs = 0.f;
+  auto load = [&](int it) {
+    const int h = h_lo + it / per_head;
+    const int u = h - a.q_head0;
+    const int64_t q0 = static_cast<int64_t>(qt0 + it % per_head) * BM;
+    if (tid < 128) {
+      const bool isQ = tid < 64;
+      const u16* src = isQ ? static_cast<const u16*>(a.q) + static_cast<int64_t>(u) * S * DH
+                           : static_cast<const u16*>(a.dO) + static_cast<int64_t>(h) * DH;
+      const int64_t ld = isQ ? DH : ldo;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int64_t q = q0 + 16 * ss16 + slot_row(shh, m);
+        rr[m] = q < S ? ld16(src + q * ld + sdc * 8) : u32x4{0, 0, 0, 0};
+      }
+    } else if (tid < 160) {
+      const int64_t q = q0 + (tid - 128);
+      rs = q < S ? a.lse_in[static_cast<int64_t>(h) * S + q] * kLog2e : INFINITY;
+    } else if (tid < 192) {
+      const int64_t q = q0 + (tid - 160);
+      rs = q < S ? a.dd[static_cast<int64_t>(u) * S + q] : 0.f;
+    }
+  };
+  auto store = [&](int b) {
+    u16* base = lds + b * BUF;
+    if (tid < 128) {
+      const bool isQ = tid < 64;
+      u16* rowm = base + (isQ ? QS_OFF : DOS_OFF);
+      u16* tr = base + (isQ ? QT_OFF : DOT_OFF);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) st16(rowm + (16 * ss16 + slot_row(shh, m)) * RS + sdc * 8, rr[m]);
+      u32x4 tc[8];
+      transpose8(rr, tc);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) st16(tr + (sdc * 8 + e) * TS + 16 * ss16 + 8 * shh, tc[e]);
+    } else if (tid < 160) {
+      stat[b][0][tid - 128] = rs;
+    } else if (tid < 192) {
+      stat[b][1][tid - 160] = rs;
+    }
+  };
+
+  if (niter > 0) {
+    load(0);
+    store(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < niter; ++it) {
+    const int cur = it & 1;
+    if (it + 1 < niter) load(it + 1);
+    const int64_t q0 = static_cast<int64_t>(qt0 + it % per_head) * BM;
+    const bool active = !a.causal || q0 + BM - 1 >= wk0;
+    if (active) {
+      const u16* base = lds + cur * BUF;
+      f32x16 sacc = zero16(), dpacc = zero16();
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        sacc = mfma(frag(base + QS_OFF + col * RS + 16 * t + 8 * hf), kf[t], sacc);
+        dpacc = mfma(frag(base + DOS_OFF + col * RS + 16 * t + 8 * hf), vf[t], dpacc);
+      }
+      const bool need_mask = a.causal && q0 < wk0 + 31;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int r0 = 8 * g4 + 4 * hf;  // rows r0..r0+3 of the tile
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&stat[cur][0][r0]);
+        const f32x4 d4v = *reinterpret_cast<const f32x4*>(&stat[cur][1][r0]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * g4 + e;
+          float p = ex2(sacc[i] * c - l4[e]);
+          if (need_mask && myk > q0 + r0 + e) p = 0.f;
+          sacc[i] = p;
+          dpacc[i] = p * (dpacc[i] - d4v[e]);
+        }
+      }
+      bf16x8 pa[2], dsa[2];
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        pa[k2] = pack8(sacc, k2);
+        dsa[k2] = pack8(dpacc, k2);
+      }
+#pragma unroll
+      for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          dv[d4] = mfma(pa[k2], frag(base + DOT_OFF + (32 * d4 + col) * TS + 16 * k2 + 8 * hf), dv[d4]);
+          dk[d4] = mfma(dsa[k2], frag(base + QT_OFF + (32 * d4 + col) * TS + 16 * k2 + 8 * hf), dk[d4]);
+        }
+    }
+    if (it + 1 < niter) store(cur ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int64_t kr = wk0 + 8 * (i / 4) + 4 * hf + (i % 4);
+      if (kr >= S) continue;
+      const int64_t off = (static_cast<int64_t>(gl) * S + kr) * DH + 32 * d4 + col;
+      if (a.last_of_group) {
+        static_cast<u16*>(a.dk)[off] = __builtin_bit_cast(u16, static_cast<__bf16>(dk[d4][i] * tau));
+        static_cast<u16*>(a.dv)[off] = __builtin_bit_cast(u16, static_cast<__bf16>(dv[d4][i]));
+      } else {
+        a.dk_acc[off] = dk[d4][i];
+        a.dv_acc[off] = dv[d4][i];
+      }
+    }
+}
+
+// ---- dQ.  Workgroup: 128 query rows of one head (4 waves x 32 rows); key
+// tiles of 64 rows.  Orientation as in the forward (lane = query row): S^T
+// and dP^T from registers Q, dO against K, V tiles, then dQ^T += K^T dS^T with
+// K also staged transposed in slot order.
+namespace dqk {
+constexpr int BM = 128, BN = 64;
+constexpr int RS = DH + 8, TS = BN + 8;
+constexpr int KS_OFF = 0, VS_OFF = BN * RS, KT_OFF = 2 * BN * RS;
+constexpr int BUF = KT_OFF + DH * TS;
+}  // namespace dqk
+
+__global__ __launch_bounds__(256, 1) void attn_dq_kernel(AttnArgs a) {
+  using namespace dqk;
+  __shared__ __attribute__((aligned(16))) u16 lds[2 * BUF];
+  const int64_t S = a.S;
+  const int nqb = static_cast<int>((S + BM - 1) / BM);
+  const int qb = nqb - 1 - static_cast<int>(blockIdx.x) / a.nq;
+  const int u = blockIdx.x % a.nq;
+  const int h = a.q_head0 + u;
+  const int gl = h / a.r - a.kv_head0;
+  const u16* K = static_cast<const u16*>(a.k) + static_cast<int64_t>(gl) * S * DH;
+  const u16* V = static_cast<const u16*>(a.v) + static_cast<int64_t>(gl) * S * DH;
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, col = lane % 32, hf = lane / 32;
+  const int64_t qfirst = static_cast<int64_t>(qb) * BM;
+  const int64_t wq0 = qfirst + 32 * wave;
+  const int64_t myq = wq0 + col;
+  const float tau = 1.f / sqrtf(static_cast<float>(DH));
+  const float c = kLog2e * tau;
+
+  bf16x8 qf[8], gf[8];
+  {
+    const u16* Q = static_cast<const u16*>(a.q) + static_cast<int64_t>(u) * S * DH;
+    const u16* dO = static_cast<const u16*>(a.dO) + static_cast<int64_t>(h) * DH;
+    const int64_t ldo = static_cast<int64_t>(a.H) * DH;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      qf[t] = __builtin_bit_cast(bf16x8, myq < S ? ld16(Q + myq * DH + 16 * t + 8 * hf) : u32x4{0, 0, 0, 0});
+      gf[t] = __builtin_bit_cast(bf16x8, myq < S ? ld16(dO + myq * ldo + 16 * t + 8 * hf) : u32x4{0, 0, 0, 0});
+    }
+  }
+  const float lse2 = myq < S ? a.lse_in[static_cast<int64_t>(h) * S + myq] * kLog2e : INFINITY;
+  const float Dq = myq < S ? a.dd[static_cast<int64_t>(u) * S + myq] : 0.f;
+
+  const int64_t kv_end = a.causal ? min(S, qfirst + BM) : S;
+  const int ntiles = static_cast<int>((kv_end + BN - 1) / BN);
+
+  // staging roles: 0..127 K blocks (row-major + transposed), 128..255 V rows.
+  const bool isK = tid < 128;
+  const int krg = (tid % 128) / 16, kdc = tid % 16, ks16 = krg / 2, khh = krg % 2;
+  u32x4 rr[8];
+  auto load = [&](int j) {
+    const int64_t kv0 = static_cast<int64_t>(j) * BN;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      if (isK) {
+        const int64_t kvr = kv0 + 16 * ks16 + slot_row(khh, m);
+        rr[m] = kvr < S ? ld16(K + kvr * DH + kdc * 8) : u32x4{0, 0, 0, 0};
+      } else {
+        const int row = (tid - 128) / 16 + 8 * m, chunk = tid % 16;
+        const int64_t kvr = kv0 + row;
+        rr[m] = kvr < S ? ld16(V + kvr * DH + chunk * 8) : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store = [&](int b) {
+    u16* base = lds + b * BUF;
+    if (isK) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) st16(base + KS_OFF + (16 * ks16 + slot_row(khh, m)) * RS + kdc * 8, rr[m]);
+      u32x4 tc[8];
+      transpose8(rr, tc);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) st16(base + KT_OFF + (kdc * 8 + e) * TS + 16 * ks16 + 8 * khh, tc[e]);
+    } else {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) st16(base + VS_OFF + ((tid - 128) / 16 + 8 * m) * RS + (tid % 16) * 8, rr[m]);
+    }
+  };
+
+  f32x16 dq[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dq[i] = zero16();
+
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int j = 0; j < ntiles; ++j) {
+    const int cur = j & 1;
+    if (j + 1 < ntiles) load(j + 1);
+    const int64_t kv0 = static_cast<int64_t>(j) * BN;
+    const bool active = !a.causal || kv0 <= wq0 + 31;
+    if (active) {
+      const u16* base = lds + cur * BUF;
+      f32x16 s[2] = {zero16(), zero16()}, dp[2] = {zero16(), zero16()};
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          s[b] = mfma(frag(base + KS_OFF + (32 * b + col) * RS + 16 * t + 8 * hf), qf[t], s[b]);
+          dp[b] = mfma(frag(base + VS_OFF + (32 * b + col) * RS + 16 * t + 8 * hf), gf[t], dp[b]);
+        }
+      const bool need_mask = a.causal ? (kv0 + BN - 1 > wq0) : (kv0 + BN > S);
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float p = ex2(s[b][i] * c - lse2);
+          if (need_mask) {
+            const int64_t kvr = kv0 + 32 * b + 8 * (i / 4) + 4 * hf + (i % 4);
+            if (a.causal ? (kvr > myq) : (kvr >= S)) p = 0.f;
+          }
+          dp[b][i] = p * (dp[b][i] - Dq);
+        }
+      bf16x8 dsb[4];
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) dsb[k4] = pack8(dp[k4 / 2], k4 % 2);
+#pragma unroll
+      for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4)
+          dq[d4] = mfma(frag(base + KT_OFF + (32 * d4 + col) * TS + 16 * k4 + 8 * hf), dsb[k4], dq[d4]);
+    }
+    if (j + 1 < ntiles) store(cur ^ 1);
+    __syncthreads();
+  }
+
+  if (myq < S) {
+    u16* out = static_cast<u16*>(a.dq) + (static_cast<int64_t>(u) * S + myq) * DH;
+#pragma unroll
+    for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        u32x2 v;
+        v[0] = pack2(dq[d4][4 * g4 + 0] * tau, dq[d4][4 * g4 + 1] * tau);
+        v[1] = pack2(dq[d4][4 * g4 + 2] * tau, dq[d4][4 * g4 + 3] * tau);
+        *reinterpret_cast<u32x2*>(out + 32 * d4 + 8 * g4 + 4 * hf) = v;
+      }
+  }
+}
+
+inline unsigned cdiv(int64_t a, int64_t b) { return static_cast<unsigned>((a + b - 1) / b); }
+
+}  // namespace
+
+namespace bf16 {
+
+hipError_t proj(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t, hipStream_t st) {
+  if (d != DH || D % GK != 0) return hipErrorInvalidValue;
+  const int nrb = static_cast<int>(cdiv(S, GB));
+  hipLaunchKernelGGL(proj_kernel, dim3(nrb * t.n), dim3(256), 0, st, static_cast<const u16*>(X), S,
+                     D, t, nrb);
+  return hipGetLastError();
+}
+
+hipError_t dw(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t, hipStream_t st) {
+  if (d != DH || D % GB != 0) return hipErrorInvalidValue;
+  const int ncb = static_cast<int>(D / GB);
+  hipLaunchKernelGGL(dw_kernel, dim3(ncb * t.n), dim3(256), 0, st, static_cast<const u16*>(X), S, D,
+                     t, ncb);
+  return hipGetLastError();
+}
+
+hipError_t dx(float* dX, int64_t S, int64_t D, int d, const ChunkTable& t, hipStream_t st) {
+  if (d != DH || D % GB != 0) return hipErrorInvalidValue;
+  const int nrb = static_cast<int>(cdiv(S, GB)), ncb = static_cast<int>(D / GB);
+  hipLaunchKernelGGL(dx_kernel, dim3(nrb * ncb), dim3(256), 0, st, dX, S, D, t, nrb, ncb);
+  return hipGetLastError();
+}
+
+hipError_t attn_fwd(const AttnArgs& a, hipStream_t st) {
+  if (a.d != DH) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_fwd_kernel, dim3(cdiv(a.S, fw::BM) * a.nq), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t bwd_pre(const AttnArgs& a, hipStream_t st) {
+  if (a.d != DH) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bwd_pre_kernel, dim3(cdiv(a.S, 16), a.nq), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t attn_dkv(const AttnArgs& a, hipStream_t st) {
+  if (a.d != DH) return hipErrorInvalidValue;
+  const int nkv = a.nq >= a.r ? a.nq / a.r : 1;
+  hipLaunchKernelGGL(attn_dkv_kernel, dim3(cdiv(a.S, kv::BN) * nkv), dim3(256), 0, st, a, nkv);
+  return hipGetLastError();
+}
+
+hipError_t attn_dq(const AttnArgs& a, hipStream_t st) {
+  if (a.d != DH) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_dq_kernel, dim3(cdiv(a.S, dqk::BM) * a.nq), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace bf16
+}  // namespace upipe

@@ -1,0 +1,96 @@
+// plan.cpp -- head schedule and stage-buffer allocator (host only).
+//
+// paper.rainbus.top summary of "Untied Ulysses", section 方法步骤详情: the
+// layer runs in H/U stages; stage i handles heads iU .. (i+1)U-1 and the
+// QKV buffers are reused by every stage, so the peak is O(U), not O(H).
+// Section 技术新颖性: distinct KV heads are moved once (the GQA-aware
+// schedule).  On one GPU the schedule is ascending head order: groups are
+// contiguous, so a KV head is projected in the first stage of its group and
+// kept until the group's last query head has been processed.
+//
+// Legal U on one GPU (the pages' rule "U divisible by the device count",
+// section 局限与改进, concerns several devices): U divides H, and either U
+// divides the group size r = H/G (a stage lies inside one group) or r divides
+// U (a stage holds whole groups).  No stage ever cuts a group unevenly.
+#include <algorithm>
+
+#include "upipe_internal.h"
+
+namespace upipe {
+
+int make_plan(Plan& p, int64_t S, int64_t D, int H, int G, int d, int U, int causal, int dtype) {
+  if (S < 0 || D <= 0 || H <= 0 || G <= 0 || d <= 0 || U <= 0) return UPIPE_ERR_ARG;
+  if (causal != 0 && causal != 1) return UPIPE_ERR_ARG;
+  if (dtype != UPIPE_BF16 && dtype != UPIPE_F32) return UPIPE_ERR_ARG;
+  if (H % G != 0) return UPIPE_ERR_ARG;
+  const int r = H / G;
+  if (H % U != 0) return UPIPE_ERR_ARG;
+  if (!(r % U == 0 || U % r == 0)) return UPIPE_ERR_ARG;
+  if (d != 64 && d != 128) return UPIPE_ERR_UNSUPPORTED;
+  if (dtype == UPIPE_BF16 && d != 128) return UPIPE_ERR_UNSUPPORTED;
+  if (dtype == UPIPE_BF16 && D % 128 != 0) return UPIPE_ERR_UNSUPPORTED;
+  if (dtype == UPIPE_F32 && D % 64 != 0) return UPIPE_ERR_UNSUPPORTED;
+  // The fp32 variant is the small exact-precision path (one thread per row).
+  if (dtype == UPIPE_F32 && S > 65536) return UPIPE_ERR_UNSUPPORTED;
+  // Token indices and the [S][D] / [S][H*d] offsets are 64-bit in every kernel;
+  // per-row counts stay below 2^31.
+  if (S > (int64_t(1) << 31) - 256) return UPIPE_ERR_UNSUPPORTED;
+  if (D > (int64_t(1) << 20)) return UPIPE_ERR_UNSUPPORTED;
+
+  p.S = S;
+  p.D = D;
+  p.H = H;
+  p.G = G;
+  p.d = d;
+  p.U = U;
+  p.r = r;
+  p.causal = causal;
+  p.dtype = dtype;
+  p.kv_per_stage = std::max(1, U / r);
+
+  p.stages.clear();
+  for (int s = 0; s < H / U; ++s) {
+    Stage st;
+    st.q0 = s * U;
+    st.nq = U;
+    st.kv0 = st.q0 / r;
+    st.nkv = p.kv_per_stage;
+    if (U >= r) {
+      st.load = st.done = true;
+    } else {
+      st.load = (st.q0 % r) == 0;
+      st.done = ((st.q0 + U) % r) == 0;
+    }
+    p.stages.push_back(st);
+  }
+
+  // Stage buffers: one region each, reused by every stage.
+  const size_t e = p.elem();
+  const size_t Sd = static_cast<size_t>(S) * d;
+  const size_t nkv = p.kv_per_stage;
+  WsLayout& w = p.ws;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  w.q = take(U * Sd * e);
+  w.k = take(nkv * Sd * e);
+  w.v = take(nkv * Sd * e);
+  w.fwd_bytes = off;
+  w.dd = take(static_cast<size_t>(U) * S * 4);
+  w.dq = take(U * Sd * e);
+  w.dk = take(nkv * Sd * e);
+  w.dv = take(nkv * Sd * e);
+  if (dtype == UPIPE_BF16 && U < r) {
+    w.dk_acc = take(Sd * 4);
+    w.dv_acc = take(Sd * 4);
+  } else {
+    w.dk_acc = w.dv_acc = 0;
+  }
+  w.bwd_bytes = off;
+  return UPIPE_OK;
+}
+
+}  // namespace upipe

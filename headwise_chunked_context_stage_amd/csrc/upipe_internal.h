@@ -1,0 +1,119 @@
+// upipe_internal.h -- host-side plan, stage-buffer layout and the launch
+// interface between the C ABI and the kernels.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "../../include/upipe.h"
+
+namespace upipe {
+
+constexpr size_t kAlign = 256;  // every workspace region starts on a 256-byte boundary
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// One stage of the head schedule: query heads [q0, q0+nq) and the KV heads
+// [kv0, kv0+nkv) they read.  `load`: the stage is the first of those KV heads'
+// group, so it projects K and V; `done`: it is the last, so it finishes their
+// gradients.  Stages run in ascending head order; with groups contiguous this
+// projects every KV head exactly once per group.
+struct Stage {
+  int q0, nq;
+  int kv0, nkv;
+  bool load, done;
+};
+
+// Byte offsets of the stage buffers inside the caller's workspace.
+struct WsLayout {
+  size_t q, k, v;              // Q [U][S][d], K [kv][S][d], V [kv][S][d]   (element type)
+  size_t dd;                   // D = rowsum(dO*O) [U][S] fp32                 (backward)
+  size_t dq;                   // dQ [U][S][d] (element type)                  (backward)
+  size_t dk, dv;               // dK, dV [kv][S][d] (element type)             (backward)
+  size_t dk_acc, dv_acc;       // fp32 carry of dK, dV across a group's stages (bf16 and U < r)
+  size_t fwd_bytes, bwd_bytes;
+};
+
+struct Plan {
+  int64_t S, D;
+  int H, G, d, U, r, causal, dtype;
+  int kv_per_stage;  // max(1, U / r)
+  std::vector<Stage> stages;
+  WsLayout ws;
+  size_t elem() const { return dtype == UPIPE_BF16 ? 2 : 4; }
+};
+
+// Validates and builds; returns a UPIPE_* code.
+int make_plan(Plan& p, int64_t S, int64_t D, int H, int G, int d, int U, int causal, int dtype);
+
+// ------------------------------------------------------------------ launch
+// A list of [S][d] operand buffers with matching weight row blocks.  Used for
+// the projection (out[i] = X * W[i]^T), the weight gradient
+// (dW[i] = a[i]^T X) and the input gradient (dX += sum_i a[i] W[i]).
+constexpr int kMaxChunks = 64;
+struct ChunkTable {
+  int n;
+  const void* w[kMaxChunks];  // weight rows [d][D] of this chunk
+  void* a[kMaxChunks];        // [S][d] activation / gradient buffer of this chunk
+  float* dw[kMaxChunks];      // [d][D] fp32 weight-gradient rows (dW launches only)
+};
+
+struct AttnArgs {
+  int64_t S;
+  int H;          // total query heads (row stride of O/dO is H*d)
+  int d;
+  int causal;
+  int nq;         // query heads in this launch
+  int q_head0;    // global index of the first query head
+  int r;          // query heads per KV group
+  const void* q;  // Q [nq][S][d]
+  const void* k;  // K of the first KV head touched, [nkv][S][d]
+  const void* v;
+  int kv_head0;   // global index of the first KV head in k/v
+  // forward
+  void* o;        // O [S][H*d]
+  float* lse;     // LSE [H][S]
+  // backward
+  const void* dO;       // [S][H*d]
+  const void* o_in;     // [S][H*d]
+  const float* lse_in;  // [H][S]
+  float* dd;            // D [nq][S]
+  void* dq;             // dQ [nq][S][d]
+  void* dk;             // dK [nkv][S][d], element type (written when the group is done)
+  void* dv;
+  float* dk_acc;        // fp32 carry (bf16 only), may be null when not needed
+  float* dv_acc;
+  int first_of_group;   // this launch starts the group's dK/dV accumulation
+  int last_of_group;    // this launch completes it
+};
+
+// Kernel launchers (one set per element type).  Return hipSuccess or the
+// launch error.  `S` is the number of tokens; X is [S][D].
+namespace bf16 {
+hipError_t proj(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t, hipStream_t st);
+hipError_t attn_fwd(const AttnArgs& a, hipStream_t st);
+hipError_t bwd_pre(const AttnArgs& a, hipStream_t st);
+hipError_t attn_dkv(const AttnArgs& a, hipStream_t st);
+hipError_t attn_dq(const AttnArgs& a, hipStream_t st);
+hipError_t dw(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t, hipStream_t st);
+hipError_t dx(float* dX, int64_t S, int64_t D, int d, const ChunkTable& t, hipStream_t st);
+}  // namespace bf16
+namespace f32 {
+hipError_t proj(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t, hipStream_t st);
+hipError_t attn_fwd(const AttnArgs& a, hipStream_t st);
+hipError_t bwd_pre(const AttnArgs& a, hipStream_t st);
+hipError_t attn_dkv(const AttnArgs& a, hipStream_t st);
+hipError_t attn_dq(const AttnArgs& a, hipStream_t st);
+hipError_t dw(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t, hipStream_t st);
+hipError_t dx(float* dX, int64_t S, int64_t D, int d, const ChunkTable& t, hipStream_t st);
+}  // namespace f32
+hipError_t fill_zero(void* p, size_t bytes, hipStream_t st);
+
+// Kernel timing hooks (capi.cpp).
+void timing_begin(int kind, hipStream_t st);
+void timing_end(int kind, hipStream_t st);
+
+}  // namespace upipe

@@ -1,0 +1,46 @@
+"""Caller-side helpers: allocate the tensors the C ABI writes (torch is used for
+device memory and streams only) and run the layer through the binding."""
+from __future__ import annotations
+
+import torch
+
+from . import upipe
+from .synth import torch_dtype
+
+
+def alloc_outputs(plan: "upipe.Plan", device, backward: bool = True, ws_extra: int = 0):
+    """O, LSE, the workspace (peak_bytes, 256-byte aligned by torch's allocator)
+    and, for the backward, dX and the three weight gradients (fp32)."""
+    S, D, H, G, d = plan.S, plan.D, plan.H, plan.G, plan.d
+    td = torch_dtype(plan.dtype)
+    out = {
+        "O": torch.empty((S, H * d), dtype=td, device=device),
+        "LSE": torch.empty((H, S), dtype=torch.float32, device=device),
+        "ws": torch.empty((max(1, plan.peak_bytes + ws_extra),), dtype=torch.uint8, device=device),
+    }
+    if backward:
+        out["dX"] = torch.empty((S, D), dtype=torch.float32, device=device)
+        out["dWq"] = torch.empty((H * d, D), dtype=torch.float32, device=device)
+        out["dWk"] = torch.empty((G * d, D), dtype=torch.float32, device=device)
+        out["dWv"] = torch.empty((G * d, D), dtype=torch.float32, device=device)
+    return out
+
+
+def forward(plan, inp, out, stream=None):
+    plan.fwd(inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], out["O"], out["LSE"], out["ws"],
+             stream=stream)
+
+
+def backward(plan, inp, out, stream=None):
+    plan.bwd(inp["dO"], inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], out["O"], out["LSE"], out["dX"],
+             out["dWq"], out["dWk"], out["dWv"], out["ws"], stream=stream)
+
+
+def run(plan, inp, backward_pass: bool = True, stream=None):
+    """Forward (and backward) on the current stream; returns the output dict."""
+    dev = inp["X"].device
+    out = alloc_outputs(plan, dev, backward=backward_pass)
+    forward(plan, inp, out, stream)
+    if backward_pass:
+        backward(plan, inp, out, stream)
+    return out

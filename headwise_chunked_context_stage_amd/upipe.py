@@ -1,0 +1,222 @@
+"""Thin ctypes binding of the upipe C ABI (include/upipe.h).
+
+Argument marshalling only: every step of the layer runs in the HIP library.
+Tensors may be passed as torch tensors (their data_ptr is used) or as raw
+integer device addresses.  The library must have been built
+(``python -m headwise_chunked_context_stage_amd.build``); there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libupipe.so")
+
+UPIPE_BF16, UPIPE_F32 = 0, 1
+UPIPE_OK, UPIPE_ERR_ARG, UPIPE_ERR_UNSUPPORTED, UPIPE_ERR_WORKSPACE, UPIPE_ERR_HIP = 0, 1, 2, 3, 4
+KERNEL_KINDS = ("proj", "attn_fwd", "bwd_pre", "attn_dkv", "attn_dq", "dw", "dx", "fill")
+
+EXPORTS = ("upipe_create", "upipe_destroy", "upipe_peak_bytes", "upipe_peak_bytes_phase",
+           "upipe_fwd", "upipe_bwd", "upipe_strerror", "upipe_num_stages", "upipe_stage_info",
+           "upipe_timing_enable", "upipe_timing_read", "upipe_kernel_name")
+
+_lib = None
+
+
+class UpipeError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__("%s: %s (code %d)" % (where, strerror_text(code), code))
+
+
+def lib():
+    """Load libupipe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libupipe.so is not built: run `python -m "
+                           "headwise_chunked_context_stage_amd.build` (no CPU fallback exists)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    L.upipe_create.argtypes = [ctypes.POINTER(vp), i64, i64, i32, i32, i32, i32, i32, i32]
+    L.upipe_create.restype = i32
+    L.upipe_destroy.argtypes = [vp]
+    L.upipe_destroy.restype = None
+    L.upipe_peak_bytes.argtypes = [vp]
+    L.upipe_peak_bytes.restype = sz
+    L.upipe_peak_bytes_phase.argtypes = [vp, i32]
+    L.upipe_peak_bytes_phase.restype = sz
+    L.upipe_fwd.argtypes = [vp] * 8 + [sz, vp]
+    L.upipe_fwd.restype = i32
+    L.upipe_bwd.argtypes = [vp] * 13 + [sz, vp]
+    L.upipe_bwd.restype = i32
+    L.upipe_strerror.argtypes = [i32]
+    L.upipe_strerror.restype = ctypes.c_char_p
+    L.upipe_num_stages.argtypes = [vp]
+    L.upipe_num_stages.restype = i32
+    L.upipe_stage_info.argtypes = [vp, i32] + [ctypes.POINTER(i32)] * 6
+    L.upipe_stage_info.restype = i32
+    L.upipe_timing_enable.argtypes = [i32]
+    L.upipe_timing_enable.restype = i32
+    L.upipe_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64), i32]
+    L.upipe_timing_read.restype = i32
+    L.upipe_kernel_name.argtypes = [i32]
+    L.upipe_kernel_name.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def strerror_text(code: int) -> str:
+    try:
+        return lib().upipe_strerror(code).decode()
+    except Exception:  # pragma: no cover - only when the library is missing
+        return "error"
+
+
+def _addr(t) -> int:
+    if t is None:
+        return 0
+    if isinstance(t, int):
+        return t
+    return int(t.data_ptr())
+
+
+def _stream(stream, *tensors) -> int:
+    if stream is not None:
+        return stream if isinstance(stream, int) else int(stream.cuda_stream)
+    for t in tensors:
+        if hasattr(t, "is_cuda") and t.is_cuda:
+            import torch
+
+            return int(torch.cuda.current_stream(t.device).cuda_stream)
+    return 0
+
+
+def _check(code: int, where: str):
+    if code != UPIPE_OK:
+        raise UpipeError(code, where)
+
+
+def _dtype_code(dtype) -> int:
+    if dtype in (UPIPE_BF16, "bf16", "bfloat16"):
+        return UPIPE_BF16
+    if dtype in (UPIPE_F32, "f32", "fp32", "float32"):
+        return UPIPE_F32
+    try:
+        import torch
+
+        if dtype == torch.bfloat16:
+            return UPIPE_BF16
+        if dtype == torch.float32:
+            return UPIPE_F32
+    except ImportError:  # pragma: no cover
+        pass
+    return int(dtype)
+
+
+def upipe_create(S, d_model, H, G, d_head, U, causal=1, dtype="bf16") -> int:
+    h = ctypes.c_void_p()
+    _check(lib().upipe_create(ctypes.byref(h), S, d_model, H, G, d_head, U, int(causal),
+                              _dtype_code(dtype)), "upipe_create")
+    return h.value
+
+
+def upipe_destroy(plan) -> None:
+    lib().upipe_destroy(plan)
+
+
+def upipe_peak_bytes(plan) -> int:
+    return int(lib().upipe_peak_bytes(plan))
+
+
+def upipe_peak_bytes_phase(plan, phase: int) -> int:
+    return int(lib().upipe_peak_bytes_phase(plan, phase))
+
+
+def upipe_fwd(plan, X, Wq, Wk, Wv, O, LSE, ws, ws_bytes=None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if hasattr(ws, "numel") else 0
+    _check(lib().upipe_fwd(plan, _addr(X), _addr(Wq), _addr(Wk), _addr(Wv), _addr(O), _addr(LSE),
+                           _addr(ws), ws_bytes, _stream(stream, X, O)), "upipe_fwd")
+
+
+def upipe_bwd(plan, dO, X, Wq, Wk, Wv, O, LSE, dX, dWq, dWk, dWv, ws, ws_bytes=None,
+              stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if hasattr(ws, "numel") else 0
+    _check(lib().upipe_bwd(plan, _addr(dO), _addr(X), _addr(Wq), _addr(Wk), _addr(Wv), _addr(O),
+                           _addr(LSE), _addr(dX), _addr(dWq), _addr(dWk), _addr(dWv), _addr(ws),
+                           ws_bytes, _stream(stream, dX, dWq)), "upipe_bwd")
+
+
+def upipe_strerror(code: int) -> str:
+    return lib().upipe_strerror(code).decode()
+
+
+def upipe_num_stages(plan) -> int:
+    return int(lib().upipe_num_stages(plan))
+
+
+def upipe_stage_info(plan, s: int) -> dict:
+    vals = [ctypes.c_int() for _ in range(6)]
+    _check(lib().upipe_stage_info(plan, s, *[ctypes.byref(v) for v in vals]), "upipe_stage_info")
+    keys = ("q_first", "q_count", "kv_first", "kv_count", "kv_load", "kv_done")
+    return {k: v.value for k, v in zip(keys, vals)}
+
+
+def upipe_timing_enable(on: bool) -> None:
+    _check(lib().upipe_timing_enable(int(bool(on))), "upipe_timing_enable")
+
+
+def upipe_timing_read() -> dict:
+    """Per kernel kind: {"ms": total milliseconds, "launches": count}; resets."""
+    n = len(KERNEL_KINDS)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    _check(lib().upipe_timing_read(ms, cnt, n), "upipe_timing_read")
+    return {KERNEL_KINDS[i]: {"ms": ms[i], "launches": cnt[i]} for i in range(n)}
+
+
+def upipe_kernel_name(kind: int) -> str:
+    return lib().upipe_kernel_name(kind).decode()
+
+
+class Plan:
+    """Owns a plan handle; the layer's shape and stage size U are fixed here."""
+
+    def __init__(self, S, d_model, H, G, d_head, U, causal=True, dtype="bf16"):
+        self.S, self.D, self.H, self.G, self.d, self.U = S, d_model, H, G, d_head, U
+        self.causal = bool(causal)
+        self.dtype = "bf16" if _dtype_code(dtype) == UPIPE_BF16 else "f32"
+        self.handle = upipe_create(S, d_model, H, G, d_head, U, int(self.causal), dtype)
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            try:
+                upipe_destroy(h)
+            except Exception:  # pragma: no cover
+                pass
+            self.handle = None
+
+    @property
+    def peak_bytes(self) -> int:
+        return upipe_peak_bytes(self.handle)
+
+    def peak_bytes_phase(self, phase: int) -> int:
+        return upipe_peak_bytes_phase(self.handle, phase)
+
+    @property
+    def num_stages(self) -> int:
+        return upipe_num_stages(self.handle)
+
+    def stage_info(self, s: int) -> dict:
+        return upipe_stage_info(self.handle, s)
+
+    def fwd(self, X, Wq, Wk, Wv, O, LSE, ws, ws_bytes=None, stream=None):
+        upipe_fwd(self.handle, X, Wq, Wk, Wv, O, LSE, ws, ws_bytes, stream)
+
+    def bwd(self, dO, X, Wq, Wk, Wv, O, LSE, dX, dWq, dWk, dWv, ws, ws_bytes=None, stream=None):
+        upipe_bwd(self.handle, dO, X, Wq, Wk, Wv, O, LSE, dX, dWq, dWk, dWv, ws, ws_bytes, stream)

@@ -1,0 +1,136 @@
+/* upipe.h -- C ABI of the headwise-chunked causal GQA attention layer
+ * (one GPU's share), forward and backward, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (pages on "Untied Ulysses: Memory-Efficient Context
+ * Parallelism via Headwise Chunking"; paper.rainbus.top summary):
+ *  - section 前置知识 / 分组查询注意力: H query heads, G key/value heads; every
+ *    H/G consecutive query heads share one KV head (query head h reads KV head
+ *    floor(h / (H/G))).
+ *  - section 前置知识 / DeepSpeed Ulysses: each device computes full attention
+ *    over all positions for its own subset of heads; this library is that
+ *    per-device computation for one GPU's heads.
+ *  - sections 核心方法 and 方法步骤详情: the layer runs in H/U stages of U heads.
+ *    A stage projects X into Q, K, V of its heads, runs flash attention over
+ *    the full sequence and writes its slice of the output; the same stage
+ *    buffers are reused by every stage, so intermediate memory grows with U,
+ *    not with H.
+ *  - same page, section 技术新颖性: the GQA-aware schedule moves each distinct
+ *    KV head once.  On one GPU this becomes: each KV head is projected once
+ *    per group and kept while the group's query heads are processed.
+ *  - the all-to-all exchanges of steps (2) and (4) are between devices and are
+ *    not part of one GPU's share.
+ * Readings where the pages are silent: softmax scale 1/sqrt(d_head), causal
+ * mask j <= i, no RoPE / bias / output projection, batch 1, natural-log LSE,
+ * backward of L = sum(O * dO) with recomputation of each stage's Q, K, V.
+ *
+ * Layouts (row-major, batch 1, all tensor pointers are DEVICE pointers owned
+ * by the caller; element type `dtype` unless stated):
+ *   X  [S][D]            Wq [H*d][D]  (head h = rows h*d .. h*d+d-1)
+ *   Wk, Wv [G*d][D]      O, dO [S][H*d]  (head h = columns h*d .. h*d+d-1)
+ *   LSE [H][S] fp32      dX [S][D] fp32     dWq, dWk, dWv fp32, weight shapes
+ *   ws: workspace of at least upipe_peak_bytes() bytes, 256-byte aligned.
+ *
+ * Results do not depend on U: every legal U gives bit-identical O, LSE, dX,
+ * dWq, dWk and dWv, and repeated calls give identical bits.
+ *
+ * Errors: every entry point validates its arguments on the host before it
+ * enqueues anything; on failure it returns a nonzero code and enqueues
+ * nothing.  A failed HIP launch returns UPIPE_ERR_HIP.  Faults that happen on
+ * the device surface at the caller's next synchronisation.  No entry point
+ * allocates device memory, synchronises the stream or prints.
+ */
+#ifndef UPIPE_H
+#define UPIPE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct upipe_plan upipe_plan; /* opaque, immutable after create, host memory only */
+
+typedef enum { UPIPE_BF16 = 0, UPIPE_F32 = 1 } upipe_dtype;
+
+enum {
+  UPIPE_OK = 0,
+  UPIPE_ERR_ARG = 1,         /* invalid argument: shape, U, null or misaligned pointer */
+  UPIPE_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. bf16 with d_head != 128) */
+  UPIPE_ERR_WORKSPACE = 3,   /* ws too small or not 256-byte aligned */
+  UPIPE_ERR_HIP = 4          /* a HIP call failed */
+};
+
+/* Build a plan.  Host only: no device call, no allocation of device memory.
+ *   S >= 0 tokens (S = 0 is the empty sequence), d_model = D, H query heads,
+ *   G KV heads (G divides H), d_head in {64, 128} (bf16 needs 128),
+ *   U query heads per stage: U divides H and (U divides H/G or H/G divides U),
+ *   causal in {0, 1}, dtype a upipe_dtype.  D must be a multiple of 64 (bf16:
+ *   of 128).  *out receives the plan; release it with upipe_destroy. */
+int upipe_create(upipe_plan** out, int64_t S, int64_t d_model, int H, int G, int d_head, int U,
+                 int causal, int dtype);
+
+/* Release a plan (NULL is ignored). */
+void upipe_destroy(upipe_plan* p);
+
+/* Workspace bytes needed by both upipe_fwd and upipe_bwd: the stage buffers
+ * (Q of U heads, K and V of the KV heads a stage touches, and the backward's
+ * per-stage gradient buffers).  Grows linearly with U; independent of H. */
+size_t upipe_peak_bytes(const upipe_plan* p);
+
+/* Per phase: 0 = forward only, 1 = backward. */
+size_t upipe_peak_bytes_phase(const upipe_plan* p, int phase);
+
+/* Forward.  Writes O [S][H*d] and LSE [H][S] (natural log of the softmax
+ * denominator of the scaled scores).  Enqueued on `stream` (a hipStream_t;
+ * NULL = the null stream); asynchronous. */
+int upipe_fwd(const upipe_plan* p, const void* X, const void* Wq, const void* Wk, const void* Wv,
+              void* O, float* LSE, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of L = sum(O * dO), given the forward's O and LSE.  Overwrites
+ * dX [S][D], dWq, dWk, dWv (fp32).  Q, K, V are recomputed stage by stage
+ * from X.  Enqueued on `stream`; asynchronous. */
+int upipe_bwd(const upipe_plan* p, const void* dO, const void* X, const void* Wq, const void* Wk,
+              const void* Wv, const void* O, const float* LSE, float* dX, float* dWq, float* dWk,
+              float* dWv, void* ws, size_t ws_bytes, void* stream);
+
+/* Text for an error code (static storage). */
+const char* upipe_strerror(int code);
+
+/* ---- plan introspection (host only) ---- */
+
+/* Number of stages, H/U. */
+int upipe_num_stages(const upipe_plan* p);
+
+/* Stage s: its query heads [q_first, q_first + q_count), the KV heads it
+ * touches [kv_first, kv_first + kv_count), whether it projects them (first
+ * stage of their group: kv_load = 1) and whether it completes them (last
+ * stage of their group: kv_done = 1).  Returns UPIPE_ERR_ARG for a bad s. */
+int upipe_stage_info(const upipe_plan* p, int s, int* q_first, int* q_count, int* kv_first,
+                     int* kv_count, int* kv_load, int* kv_done);
+
+/* ---- kernel timing (for benchmarks) ----
+ * When enabled, every kernel launch is bracketed by hipEvents recorded on the
+ * stream it is launched on.  upipe_timing_read waits for those events, adds
+ * each launch's duration (ms) and count to ms[kind] and launches[kind] for
+ * kind < n, then forgets them.  Process-wide; not for concurrent callers. */
+enum {
+  UPIPE_K_PROJ = 0,     /* stage Q/K/V projection GEMM */
+  UPIPE_K_ATTN_FWD = 1, /* attention forward */
+  UPIPE_K_BWD_PRE = 2,  /* D = rowsum(dO * O) */
+  UPIPE_K_ATTN_DKV = 3, /* attention backward, dK and dV */
+  UPIPE_K_ATTN_DQ = 4,  /* attention backward, dQ */
+  UPIPE_K_DW = 5,       /* weight-gradient GEMM */
+  UPIPE_K_DX = 6,       /* input-gradient GEMM */
+  UPIPE_K_FILL = 7,     /* zero fill */
+  UPIPE_K_COUNT = 8
+};
+int upipe_timing_enable(int on);
+int upipe_timing_read(double* ms, int64_t* launches, int n);
+const char* upipe_kernel_name(int kind);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UPIPE_H */

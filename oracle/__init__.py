@@ -47,7 +47,7 @@ def _load():
         lib.oracle_forward.argtypes = [i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, dp, dp, i32]
         lib.oracle_forward.restype = i32
         lib.oracle_forward_rows.argtypes = [i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp,
-                                            vp, i64, dp, dp, i32]
+                                            vp, i64, i32, i32, dp, dp, i32]
         lib.oracle_forward_rows.restype = i32
         lib.oracle_backward.argtypes = [i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                                         dp, dp, dp, dp, dp, dp, i32]
@@ -100,18 +100,21 @@ def forward(X, Wq, Wk, Wv, H: int, G: int, d: int, causal: bool = True, nthreads
 
 
 def forward_rows(X, Wq, Wk, Wv, H: int, G: int, d: int, rows, causal: bool = True,
-                 nthreads: int | None = None):
-    """Forward at the token rows `rows` only: (O_rows [n][H*d], LSE_rows [H][n]) in fp64."""
+                 heads=None, nthreads: int | None = None):
+    """Forward at the token rows `rows` only, for query heads range(*heads)
+    (default: all): (O_rows [n][H*d], LSE_rows [H][n]) in fp64; entries of
+    heads outside the range are NaN."""
     (X, Wq, Wk, Wv), enc = _prep([X, Wq, Wk, Wv])
     S, D = X.shape
     _check_shapes(S, D, H, G, d, Wq, Wk, Wv)
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
     n = rows.shape[0]
-    O = np.empty((n, H * d), np.float64)
-    LSE = np.empty((H, n), np.float64)
+    h0, h1 = heads if heads is not None else (0, H)
+    O = np.full((n, H * d), np.nan, np.float64)
+    LSE = np.full((H, n), np.nan, np.float64)
     rc = _load().oracle_forward_rows(S, D, H, G, d, int(bool(causal)), enc, _ptr(X), _ptr(Wq),
-                                     _ptr(Wk), _ptr(Wv), _ptr(rows), n, _ptr(O), _ptr(LSE),
-                                     nthreads or default_threads())
+                                     _ptr(Wk), _ptr(Wv), _ptr(rows), n, int(h0), int(h1), _ptr(O),
+                                     _ptr(LSE), nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle_forward_rows rejected the shape or rows")
     return O, LSE

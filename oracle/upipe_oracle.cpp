@@ -174,15 +174,16 @@ int oracle_forward(int64_t S, int64_t D, int H, int G, int d, int causal, int en
   return 0;
 }
 
-// Forward on a subset of query rows (all heads).  rows[0..nrows) are token
-// indices; keys/values are projected only for the positions those rows see.
-// Outputs: Orows [nrows][H*d], LSErows [H][nrows] (fp64).
+// Forward on a subset of query rows and of query heads [h0, h1).  rows[0..nrows)
+// are token indices; keys/values are projected only for the KV heads of those
+// query heads and the positions those rows see.  Outputs: Orows [nrows][H*d],
+// LSErows [H][nrows] (fp64); entries of other heads are left untouched.
 int oracle_forward_rows(int64_t S, int64_t D, int H, int G, int d, int causal, int enc,
                         const void* Xp, const void* Wqp, const void* Wkp, const void* Wvp,
-                        const int64_t* rows, int64_t nrows, double* Orows, double* LSErows,
-                        int nthreads) {
+                        const int64_t* rows, int64_t nrows, int h0, int h1, double* Orows,
+                        double* LSErows, int nthreads) {
   Shape s{S, D, H, G, d, causal};
-  if (!shape_ok(s) || nrows < 0) return 1;
+  if (!shape_ok(s) || nrows < 0 || h0 < 0 || h1 > H || h0 >= h1) return 1;
   int64_t need = 0;  // keys needed: [0, need)
   for (int64_t t = 0; t < nrows; ++t) {
     if (rows[t] < 0 || rows[t] >= S) return 1;
@@ -203,10 +204,10 @@ int oracle_forward_rows(int64_t S, int64_t D, int H, int G, int d, int causal, i
       Q(static_cast<size_t>(nrows * d));
   Shape sq = s;
   sq.S = nrows;
-  for (int g = 0; g < G; ++g) {
+  for (int g = s.kv(h0); g <= s.kv(h1 - 1); ++g) {
     project_head(X, Wk, sk, g, need, nullptr, K.data(), nthreads);
     project_head(X, Wv, sk, g, need, nullptr, V.data(), nthreads);
-    for (int h = g * s.r(); h < (g + 1) * s.r(); ++h) {
+    for (int h = std::max(h0, g * s.r()); h < std::min(h1, (g + 1) * s.r()); ++h) {
       project_head(Xq, Wq, sq, h, nrows, nullptr, Q.data(), nthreads);
       parallel_for(nrows, nthreads, [&](int64_t t) {
         std::vector<double> scores;

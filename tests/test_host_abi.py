@@ -1,0 +1,178 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads and exports
+every declared symbol, plans are validated, the head schedule and the stage
+buffer sizes follow the pages, and bad arguments are rejected before any
+launch.
+
+Stage schedule: paper.rainbus.top summary of "Untied Ulysses", section
+方法步骤详情 (H/U stages of U consecutive heads, buffers reused by every stage)
+and section 技术新颖性 (each distinct KV head moved once).
+"""
+import json
+import os
+import re
+
+import pytest
+
+from headwise_chunked_context_stage_amd import upipe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "upipe.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "memory_closed_forms.json")
+
+
+def legal_us(H, G):
+    r = H // G
+    return [U for U in range(1, H + 1) if H % U == 0 and (r % U == 0 or U % r == 0)]
+
+
+def test_exports_every_declared_symbol():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    declared = set(re.findall(r"\b(upipe_[a-z_]+)\s*\(", text))
+    assert declared >= set(upipe.EXPORTS)
+    L = upipe.lib()
+    for name in sorted(declared):
+        assert hasattr(L, name), name
+
+
+def test_strerror():
+    assert upipe.upipe_strerror(0) == "ok"
+    for c in (1, 2, 3, 4):
+        assert upipe.upipe_strerror(c) not in ("ok", "unknown error")
+    assert upipe.upipe_strerror(99) == "unknown error"
+
+
+@pytest.mark.parametrize("args,code", [
+    ((128, 256, 4, 3, 64, 1, 1, "f32"), upipe.UPIPE_ERR_ARG),   # G does not divide H
+    ((128, 256, 32, 8, 128, 3, 1, "bf16"), upipe.UPIPE_ERR_ARG),  # U does not divide H
+    ((128, 256, 24, 4, 128, 4, 1, "bf16"), upipe.UPIPE_ERR_ARG),  # U=4 vs group size 6
+    ((128, 256, 24, 4, 128, 12, 1, "bf16"), upipe.UPIPE_OK),      # two whole groups
+    ((-1, 256, 4, 2, 64, 1, 1, "f32"), upipe.UPIPE_ERR_ARG),
+    ((128, 0, 4, 2, 64, 1, 1, "f32"), upipe.UPIPE_ERR_ARG),
+    ((128, 256, 4, 2, 64, 1, 2, "f32"), upipe.UPIPE_ERR_ARG),     # causal flag
+    ((128, 256, 4, 2, 64, 1, 1, 7), upipe.UPIPE_ERR_ARG),         # dtype
+    ((128, 256, 4, 2, 96, 1, 1, "f32"), upipe.UPIPE_ERR_UNSUPPORTED),
+    ((128, 256, 4, 2, 64, 1, 1, "bf16"), upipe.UPIPE_ERR_UNSUPPORTED),   # bf16 needs d=128
+    ((128, 192, 4, 2, 128, 1, 1, "bf16"), upipe.UPIPE_ERR_UNSUPPORTED),  # D % 128
+    ((128, 96, 4, 2, 64, 1, 1, "f32"), upipe.UPIPE_ERR_UNSUPPORTED),     # D % 64
+    ((0, 256, 4, 2, 64, 2, 1, "f32"), upipe.UPIPE_OK),                   # empty sequence
+])
+def test_create_validation(args, code):
+    if code == upipe.UPIPE_OK:
+        p = upipe.upipe_create(*args)
+        upipe.upipe_destroy(p)
+    else:
+        with pytest.raises(upipe.UpipeError) as e:
+            upipe.upipe_create(*args)
+        assert e.value.code == code
+
+
+@pytest.mark.parametrize("H,G", [(32, 8), (64, 8), (4, 2), (4, 1), (8, 8), (24, 4)])
+def test_schedule_covers_heads_and_loads_kv_once(H, G):
+    r = H // G
+    for U in legal_us(H, G):
+        p = upipe.Plan(1024, 1024, H, G, 128, U)
+        assert p.num_stages == H // U
+        seen_q, loads, dones = [], [], []
+        for s in range(p.num_stages):
+            st = p.stage_info(s)
+            assert st["q_first"] == s * U and st["q_count"] == U
+            qs = range(st["q_first"], st["q_first"] + U)
+            kvs = list(range(st["kv_first"], st["kv_first"] + st["kv_count"]))
+            assert sorted({h // r for h in qs}) == kvs  # exactly the KV heads it reads
+            seen_q += list(qs)
+            if st["kv_load"]:
+                loads += kvs
+                # a group is opened by the stage holding its first query head
+                assert all(g * r in qs for g in kvs)
+            if st["kv_done"]:
+                dones += kvs
+                assert all((g + 1) * r - 1 in qs for g in kvs)
+        assert seen_q == list(range(H))
+        assert loads == list(range(G)) and dones == list(range(G))
+
+
+def test_peak_bytes_closed_forms():
+    """Forward stage bytes = 2*S*d*(U + 2*kv_s) <= 6*S*U*d (the pages' per-stage
+    projection bytes, which count K and V at U heads); equal for MHA; linear in
+    U; independent of H."""
+    g = json.load(open(GOLDEN))
+    coeff, b = g["projection_coeff"], g["bytes_per_element"]
+    S, d = 4096, 128
+    for H, G in [(32, 8), (64, 8), (8, 8)]:
+        r = H // G
+        for U in legal_us(H, G):
+            p = upipe.Plan(S, 1024, H, G, d, U)
+            kv_s = max(1, U // r)
+            fwd = p.peak_bytes_phase(0)
+            assert fwd == b * S * d * (U + 2 * kv_s)
+            assert fwd <= coeff * S * U * d
+            if G == H:
+                assert fwd == coeff * S * U * d
+            assert p.peak_bytes == max(p.peak_bytes_phase(0), p.peak_bytes_phase(1))
+    # independent of H for the same U and group size
+    a = upipe.Plan(S, 1024, 32, 8, d, 4).peak_bytes
+    c = upipe.Plan(S, 1024, 64, 16, d, 4).peak_bytes
+    assert a == c
+    # linear in U for group-aligned U
+    p4, p8, p16 = (upipe.Plan(S, 1024, 64, 8, d, U).peak_bytes for U in (8, 16, 32))
+    assert p16 - p8 == 2 * (p8 - p4)
+
+
+def test_qwen3_32b_reduction_matches_pages():
+    """Qwen3-32B attention (H=64, G=8): one head per device per stage (U = C = 8)
+    vs all heads (U = H = 64) is 12 vs 96 (x S/C x d_head) = an 87.5% cut."""
+    g = json.load(open(GOLDEN))["qwen3_32b"]
+    S, D, d = 65536, 5120, 128
+    u_small = upipe.Plan(S, D, g["H"], 8, d, g["C"])
+    u_all = upipe.Plan(S, D, g["H"], 8, d, g["H"])
+    ratio = u_small.peak_bytes_phase(0) / u_all.peak_bytes_phase(0)
+    assert ratio == g["upipe_coeff"] / g["ulysses_coeff"]
+    assert 100.0 * (1.0 - ratio) == g["reduction_percent"]
+    # the backward's stage buffers scale the same way
+    assert u_small.peak_bytes_phase(1) / u_all.peak_bytes_phase(1) == pytest.approx(1 / 8, rel=1e-3)
+
+
+FAKE = 1 << 20  # a 256-aligned non-null address; never dereferenced (validation fails first)
+
+
+def test_fwd_bwd_reject_before_launch():
+    p = upipe.Plan(512, 256, 4, 2, 64, 2, dtype="f32")
+    need = p.peak_bytes
+    ok = [FAKE] * 6
+    with pytest.raises(upipe.UpipeError) as e:
+        upipe.upipe_fwd(p.handle, 0, *ok[1:], FAKE, need, 0)
+    assert e.value.code == upipe.UPIPE_ERR_ARG
+    with pytest.raises(upipe.UpipeError) as e:  # misaligned tensor
+        upipe.upipe_fwd(p.handle, FAKE + 2, *ok[1:], FAKE, need, 0)
+    assert e.value.code == upipe.UPIPE_ERR_ARG
+    with pytest.raises(upipe.UpipeError) as e:  # workspace too small
+        upipe.upipe_fwd(p.handle, *ok, FAKE, p.peak_bytes_phase(0) - 1, 0)
+    assert e.value.code == upipe.UPIPE_ERR_WORKSPACE
+    with pytest.raises(upipe.UpipeError) as e:  # workspace misaligned
+        upipe.upipe_fwd(p.handle, *ok, FAKE + 16, need, 0)
+    assert e.value.code == upipe.UPIPE_ERR_WORKSPACE
+    bw = [FAKE] * 12
+    with pytest.raises(upipe.UpipeError) as e:
+        upipe.upipe_bwd(p.handle, *bw[:7], 0, *bw[8:11], FAKE, need, 0)
+    assert e.value.code == upipe.UPIPE_ERR_ARG
+    with pytest.raises(upipe.UpipeError) as e:
+        upipe.upipe_bwd(p.handle, *bw[:11], FAKE, p.peak_bytes_phase(1) - 1, 0)
+    assert e.value.code == upipe.UPIPE_ERR_WORKSPACE
+    with pytest.raises(upipe.UpipeError) as e:
+        upipe.upipe_fwd(0, *ok, FAKE, need, 0)
+    assert e.value.code == upipe.UPIPE_ERR_ARG
+
+
+def test_empty_sequence_forward_is_a_no_op():
+    p = upipe.Plan(0, 256, 4, 2, 64, 2, dtype="f32")
+    assert p.peak_bytes == 0
+    upipe.upipe_fwd(p.handle, 0, 0, 0, 0, 0, 0, 0, 0, 0)  # nothing to do, nothing enqueued
+
+
+def test_stage_info_bad_index():
+    p = upipe.Plan(128, 256, 4, 2, 64, 2, dtype="f32")
+    with pytest.raises(upipe.UpipeError):
+        p.stage_info(2)
+    with pytest.raises(upipe.UpipeError):
+        p.stage_info(-1)

@@ -252,3 +252,14 @@ def test_rejects_bad_shapes(oracle_mod):
     X, Wq, Wk, Wv, _ = draw(8, 8, 3, 2, 4)  # G does not divide H
     with pytest.raises(ValueError):
         oracle_mod.forward(X, Wq, Wk, Wv, 3, 2, 4)
+
+
+def test_sampled_rows_head_subset(oracle_mod):
+    S, D, H, G, d = 40, 16, 6, 3, 8
+    X, Wq, Wk, Wv, _ = draw(S, D, H, G, d, seed=19)
+    O, LSE = oracle_mod.forward(X, Wq, Wk, Wv, H, G, d)
+    rows = [39, 0, 7]
+    Or, Lr = oracle_mod.forward_rows(X, Wq, Wk, Wv, H, G, d, rows, heads=(1, 4))
+    np.testing.assert_array_equal(Or[:, d:4 * d], O[rows][:, d:4 * d])
+    np.testing.assert_array_equal(Lr[1:4], LSE[1:4][:, rows])
+    assert np.all(np.isnan(Or[:, :d])) and np.all(np.isnan(Lr[4:]))

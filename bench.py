@@ -1,0 +1,267 @@
+"""Benchmark: one GPU's share of a headwise-chunked causal GQA attention layer,
+forward + backward, through the C ABI.
+
+Workload (default): Llama3-8B attention shape at long context -- S = 131072,
+d_model 4096, 32 query heads, 8 KV heads, d_head 128, U = 4 (one KV group per
+stage), causal, bf16; seed-0 Gaussian inputs drawn on the GPU (X ~ N(0,1),
+W ~ N(0, 1/d_model), dO ~ N(0,1)).  A step is one forward and one backward of
+the whole layer (every stage); inputs are resident in HBM before timing.
+
+Prints one JSON line.  `value` is causal attention fwd+bwd TFLOP/s on the
+step's wall clock (algorithmic flops 7*d*S*(S+1) per query head: 2 matmuls
+forward, 5 backward, causal pairs only), so projection and gradient GEMM time
+is counted against it.  Per-kernel times come from HIP events recorded around
+every launch on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "causal attn fwd+bwd TFLOP/s & % bf16 MFMA peak at S=128K; peak bytes vs U"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="llama8b_s128k")
+    ap.add_argument("--U", type=int, default=None)
+    ap.add_argument("--skip-cpu-baseline", action="store_true",
+                    help="omit the oracle timing (profiling runs only)")
+    ap.add_argument("--cpu-baseline-S", type=int, default=6144)
+    return ap.parse_args()
+
+
+def attn_flops(S, H, d, causal=True):
+    pairs = S * (S + 1) / 2 if causal else float(S) * S
+    return 14.0 * d * pairs * H  # 2 fwd + 5 bwd matmuls, 2*d flops each per pair
+
+
+def kernel_work(kind, S, D, d, U, r, causal=True):
+    """Algorithmic work of one launch of `kind` in a stage of U query heads
+    (U >= r: whole groups).  Returns (amount, unit)."""
+    pairs = S * (S + 1) / 2 if causal else float(S) * S
+    nkv = max(1, U // r)
+    if kind == "attn_fwd":
+        return 4.0 * d * pairs * U, "flop"        # S = QK^T, O = PV
+    if kind == "attn_dkv":
+        return 8.0 * d * pairs * U, "flop"        # QK^T, dO V^T, P^T dO, dS^T Q
+    if kind == "attn_dq":
+        return 2.0 * d * pairs * U, "flop"        # dS K
+    if kind == "proj":
+        return 2.0 * S * D * d * (U + 2 * nkv), "flop"
+    if kind == "dw":
+        return 2.0 * S * D * d * (U + 2 * nkv), "flop"
+    if kind == "dx":
+        return 2.0 * S * D * d * (U + 2 * nkv), "flop"
+    if kind == "bwd_pre":
+        return (2.0 * 2 * S * d + 4.0 * S) * U, "byte"  # read O, dO (bf16); write D (fp32)
+    if kind == "fill":
+        return 4.0 * S * D, "byte"
+    return 0.0, "flop"
+
+
+def source_sha():
+    p = os.path.join(ROOT, "headwise_chunked_context_stage_amd", "csrc", "kernels_bf16.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def traffic_for(kernel):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        t = json.load(open(p))
+    except ValueError:
+        return None
+    if t.get("source_sha") != source_sha():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(S_sample, D, d):
+    """The fp64 oracle on a bounded sample of the workload: one query head and
+    its KV head at S_sample tokens, full d_model, causal, forward + backward."""
+    import numpy as np
+
+    import oracle
+    from headwise_chunked_context_stage_amd.synth import LayerShape, make_inputs, to_numpy_exact
+
+    oracle.build(force=False)
+    shape = LayerShape(S=S_sample, D=D, H=1, G=1, d=d)
+    inp = make_inputs(shape, "bf16", seed=0, device="cpu")
+    arrs = [to_numpy_exact(inp[k]) for k in ("X", "Wq", "Wk", "Wv", "dO")]
+    nthreads = oracle.default_threads()
+    t0 = time.perf_counter()
+    out = oracle.backward(*arrs, 1, 1, d, causal=True, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(out["dX"]).all()
+    flops = attn_flops(S_sample, 1, d)
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": nthreads,
+        "kind": "oracle",
+        "sample": ("1 query head + its KV head, S=%d, d_model=%d, d_head=%d, causal, fwd+bwd "
+                   "incl. projections and weight/input gradients; %.1f s; TFLOP/s counts causal "
+                   "attention flops only, as for the GPU value" % (S_sample, D, d, dt)),
+        "seconds": dt,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU's share of the layer; runs on more than one GPU are "
+              "not part of this build (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from headwise_chunked_context_stage_amd import upipe
+    from headwise_chunked_context_stage_amd.layer import alloc_outputs, backward, forward
+    from headwise_chunked_context_stage_amd.synth import CONFIGS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    upipe.lib()
+    cfg = CONFIGS[args.config]
+    shape = cfg["shape"]
+    U = args.U or cfg["U"][0]
+    S, D, H, G, d = shape.S, shape.D, shape.H, shape.G, shape.d
+    r = H // G
+    dev = torch.device("cuda:0")
+    print("bench: %s S=%d D=%d H=%d G=%d d=%d U=%d" % (args.config, S, D, H, G, d, U),
+          file=sys.stderr, flush=True)
+
+    inp = make_inputs(shape, cfg["dtype"], seed=0, device="cuda")
+    plan = upipe.Plan(S, D, H, G, d, U, causal=True, dtype=cfg["dtype"])
+    out = alloc_outputs(plan, dev)
+    torch.cuda.synchronize()
+    mem_before = torch.cuda.memory_allocated()
+
+    def step():
+        forward(plan, inp, out)
+        backward(plan, inp, out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+
+    upipe.upipe_timing_enable(True)
+    upipe.upipe_timing_read()  # drop anything pending
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    upipe.upipe_timing_enable(False)
+    ktimes = upipe.upipe_timing_read()
+    high_water_delta = torch.cuda.max_memory_allocated() - mem_before
+    for k in ("O", "LSE", "dX", "dWq", "dWk", "dWv"):
+        assert torch.isfinite(out[k]).all(), k
+
+    ms_per_step = 1e3 * elapsed / args.steps
+    aflops = attn_flops(S, H, d)
+    value = aflops / (ms_per_step * 1e-3) / 1e12
+    proj_flops = 8.0 * S * D * (H + 2 * G) * d
+
+    kernels = {}
+    for kind, rec in ktimes.items():
+        if rec["launches"] == 0:
+            continue
+        n_per_step = rec["launches"] / args.steps
+        avg_ms = rec["ms"] / rec["launches"]
+        work, unit = kernel_work(kind, S, D, d, min(U, H), r)
+        ent = {"ms_per_step": rec["ms"] / args.steps, "launches_per_step": n_per_step,
+               "avg_launch_ms": avg_ms}
+        if kind in ("attn_fwd", "attn_dkv", "attn_dq", "proj", "dw", "dx") and U >= r:
+            ent["tflops"] = work / (avg_ms * 1e-3) / 1e12
+        elif kind in ("bwd_pre",):
+            ent["gbps"] = work / (avg_ms * 1e-3) / 1e9
+        kernels[kind] = ent
+    attn_ms = sum(kernels.get(k, {}).get("ms_per_step", 0.0)
+                  for k in ("attn_fwd", "bwd_pre", "attn_dkv", "attn_dq"))
+    dominant = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    dwork, dunit = kernel_work(dominant, S, D, d, min(U, H), r)
+    dk = kernels[dominant]
+    if dunit == "flop":
+        achieved = dwork / (dk["avg_launch_ms"] * 1e-3) / 1e12
+        roof = {"kernel": dominant, "bound": "mfma", "achieved": achieved,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                "traffic": traffic_for(dominant),
+                "work_per_launch": dwork, "avg_launch_ms": dk["avg_launch_ms"]}
+    else:
+        achieved = dwork / (dk["avg_launch_ms"] * 1e-3) / 1e9
+        roof = {"kernel": dominant, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic_for(dominant),
+                "work_per_launch": dwork, "avg_launch_ms": dk["avg_launch_ms"]}
+
+    peak_by_u = {}
+    for u in cfg["U"] + (1, H):
+        if H % u == 0 and (r % u == 0 or u % r == 0):
+            p = upipe.Plan(S, D, H, G, d, u, causal=True, dtype=cfg["dtype"])
+            peak_by_u[str(u)] = {"fwd": p.peak_bytes_phase(0), "bwd": p.peak_bytes_phase(1),
+                                 "pages_projection_form_6SUd": 6 * S * u * d}
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg["dtype"] == "bf16" else "f32",
+        "data": "synthetic (seed-0 Gaussian X, W, dO drawn on the GPU; no dataset or weights)",
+        "config": {"workload": "causal GQA attention layer fwd+bwd, one GPU, Llama3-8B attention "
+                               "shape" if args.config.startswith("llama") else args.config,
+                   "name": args.config, "S": S, "d_model": D, "H": H, "G": G, "d_head": d,
+                   "U": U, "causal": True, "seed": 0},
+        "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "attn_kernels_tflops": aflops / (attn_ms * 1e-3) / 1e12 if attn_ms > 0 else None,
+        "attn_kernels_pct_peak": (100.0 * aflops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
+                                  if attn_ms > 0 else None),
+        "layer_tflops_incl_projections": (aflops + proj_flops) / (ms_per_step * 1e-3) / 1e12,
+        "tokens_per_s_layer_fwd_bwd": S / (ms_per_step * 1e-3),
+        "peak_bytes": {"U": U, "ws_fwd": plan.peak_bytes_phase(0),
+                       "ws_bwd": plan.peak_bytes_phase(1),
+                       "device_high_water_delta_during_steps": high_water_delta,
+                       "by_U": peak_by_u},
+        "kernels": kernels,
+        "roofline": roof,
+        "kernel_source_sha": source_sha(),
+        "torch": torch.__version__,
+    }
+    if not args.skip_cpu_baseline:
+        print("bench: timing the oracle on the host (bounded sample)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(args.cpu_baseline_S, D, d)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

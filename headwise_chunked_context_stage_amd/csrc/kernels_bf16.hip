@@ -370,17 +370,87 @@ __global__ __launch_bounds__(256, 2) void dx_kernel(float* __restrict__ dX, int6
 }
 
 // ================================================================= attention
+// Tiles of 128-column bf16 rows live in LDS row-major with a padded row
+// stride (RS = 136 elements, 272 bytes) and a fixed permutation of the rows
+// inside every 16-row group: logical row 8a + 4b + c (a, b in {0,1}, c < 4)
+// sits at physical row 8b + 2c + a.  Two read patterns are then free of bank
+// conflicts and all their addresses are affine (immediate offsets):
+//  * row operand (ds_read_b128): each lane reads 8 columns of its own row; 16
+//    consecutive logical rows are 16 distinct physical rows;
+//  * column operand (ds_read_b64_tr_b16): a 16-lane group reads 4 logical
+//    rows 4b..4b+3 (physical rows two apart) x 32 bytes.
+// The transposing read gives lane i of each 16-lane group element (i % 4) of
+// the 8-byte rows addressed by lanes 4k + i/4 (k = 0..3).  When lane 4k + c of
+// the group addresses row R_k at columns n0 + 4c .. n0 + 4c + 3, lane i
+// receives column n0 + i of rows R_0..R_3: four k-slots of an MFMA operand
+// whose lane index is a column of the tile.  Two such reads fill the 8 slots
+// in the row order of a C block (rows 4h..4h+3, then 8+4h..8+4h+3 of each
+// 16-row step), so they pair with P or dS taken from registers.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+constexpr int RS = DH + 8;  // LDS row stride of attention tiles (elements)
+
+__device__ __forceinline__ int prow(int q) {
+  return (q & ~15) | (((q >> 2) & 1) << 3) | ((q & 3) << 1) | ((q >> 3) & 1);
+}
+
+// Element offset of (logical row q, column col) in a tile.
+__device__ __forceinline__ int toff(int q, int col) { return prow(q) * RS + col; }
+
+// Row operand: 8 columns [col, col + 8) of row q.
+__device__ __forceinline__ bf16x8 row_frag(const u16* t, int q, int col) { return frag(t + toff(q, col)); }
+
+// Column operand: column n0 + lane % 32 of the 16 rows r0 .. r0 + 15 (r0 a
+// multiple of 16), in the slot order of a C block (lane half h: rows
+// r0+4h..r0+4h+3, then r0+8+4h..r0+8+4h+3; the second set is one physical row
+// further).
+__device__ __forceinline__ bf16x8 col_frag(const u16* t, int r0, int n0, int lane) {
+  const int hf = lane >> 5, g16 = (lane >> 4) & 1, i16 = lane & 15;
+  const u16* p = t + toff(r0 + 4 * hf + (i16 >> 2), n0 + 16 * g16 + 4 * (i16 & 3));
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, p));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, p + RS));
+  u32x4 w;
+  w[0] = static_cast<unsigned>(static_cast<u16>(lo[0])) | (static_cast<unsigned>(static_cast<u16>(lo[1])) << 16);
+  w[1] = static_cast<unsigned>(static_cast<u16>(lo[2])) | (static_cast<unsigned>(static_cast<u16>(lo[3])) << 16);
+  w[2] = static_cast<unsigned>(static_cast<u16>(hi[0])) | (static_cast<unsigned>(static_cast<u16>(hi[1])) << 16);
+  w[3] = static_cast<unsigned>(static_cast<u16>(hi[2])) | (static_cast<unsigned>(static_cast<u16>(hi[3])) << 16);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// Copy rows [row0, row0 + nrows) of a [S][ld] bf16 matrix (128 columns from
+// `src`) into a tile; rows at or beyond S are zero.  NCH chunks of 16 bytes
+// per thread, thread t handling chunks t, t + 256, ...
+template <int NCH>
+struct TileLoad {
+  u32x4 r[NCH];
+  __device__ __forceinline__ void load(const u16* src, int64_t ld, int64_t row0, int64_t S, int first) {
+#pragma unroll
+    for (int m = 0; m < NCH; ++m) {
+      const int e = first + 256 * m, row = e >> 4, c = e & 15;
+      const int64_t g = row0 + row;
+      r[m] = g < S ? ld16(src + g * ld + c * 8) : u32x4{0, 0, 0, 0};
+    }
+  }
+  __device__ __forceinline__ void store(u16* tile, int first) const {
+#pragma unroll
+    for (int m = 0; m < NCH; ++m) {
+      const int e = first + 256 * m, row = e >> 4, c = e & 15;
+      st16(tile + toff(row, c * 8), r[m]);
+    }
+  }
+};
+
 // ---- forward.  Workgroup: 128 query rows of one head (4 waves x 32 rows);
-// key/value tiles of 64 rows.  Each wave computes S^T = K Q^T (lane = query
-// row, registers = keys), so row statistics are per lane plus one exchange
-// between the two lane halves, and O^T = V^T P^T keeps O with the query in
-// the lane (the online rescale is a per-lane scalar).
+// key/value tiles of 64 rows, double-buffered.  Each wave computes
+// S^T = K Q^T (lane = query row, registers = keys): row statistics are per
+// lane plus one exchange between the lane halves, and O^T = V^T P^T keeps the
+// query in the lane, so the online rescale is a per-lane scalar.
 namespace fw {
 constexpr int BM = 128, BN = 64;
-constexpr int KS = DH + 8;   // K tile row stride (row-major [key][d])
-constexpr int VS = BN + 8;   // V^T tile row stride ([d][key], slot order)
-constexpr int KE = BN * KS;  // elements of the K tile
-constexpr int BUF = KE + DH * VS;
+constexpr int TILE = BN * RS;   // elements of one 64-row tile
+constexpr int BUF = 2 * TILE;   // K and V
+constexpr float kLazy = 8.f;    // keep a stale running max while the new one exceeds it by <= 8 (log2)
 }  // namespace fw
 
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
@@ -410,36 +480,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   const int64_t kv_end = a.causal ? min(S, qfirst + BM) : S;
   const int ntiles = static_cast<int>((kv_end + BN - 1) / BN);
 
-  // staging roles: threads 0..127 copy K rows; 128..255 transpose V blocks.
-  const bool isK = tid < 128;
-  const int vt = tid - 128, vdc = vt % 16, vrg = vt / 16, vs16 = vrg / 2, vhh = vrg % 2;
-  u32x4 rr[8];
+  TileLoad<4> lk, lv;
   auto load = [&](int j) {
-    const int64_t kv0 = static_cast<int64_t>(j) * BN;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      if (isK) {
-        const int row = tid / 16 + 8 * m, chunk = tid % 16;
-        const int64_t kv = kv0 + row;
-        rr[m] = kv < S ? ld16(K + kv * DH + chunk * 8) : u32x4{0, 0, 0, 0};
-      } else {
-        const int64_t kv = kv0 + 16 * vs16 + slot_row(vhh, m);
-        rr[m] = kv < S ? ld16(V + kv * DH + vdc * 8) : u32x4{0, 0, 0, 0};
-      }
-    }
+    lk.load(K, DH, static_cast<int64_t>(j) * BN, S, tid);
+    lv.load(V, DH, static_cast<int64_t>(j) * BN, S, tid);
   };
   auto store = [&](int b) {
-    u16* ks = lds + b * BUF;
-    u16* vts = ks + KE;
-    if (isK) {
-#pragma unroll
-      for (int m = 0; m < 8; ++m) st16(ks + (tid / 16 + 8 * m) * KS + (tid % 16) * 8, rr[m]);
-    } else {
-      u32x4 tc[8];
-      transpose8(rr, tc);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) st16(vts + (vdc * 8 + e) * VS + 16 * vs16 + 8 * vhh, tc[e]);
-    }
+    lk.store(lds + b * BUF, tid);
+    lv.store(lds + b * BUF + TILE, tid);
   };
 
   f32x16 oacc[4];
@@ -457,53 +505,58 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     const bool active = !a.causal || kv0 <= wq0 + 31;
     if (active) {
       const u16* ks = lds + cur * BUF;
-      const u16* vts = ks + KE;
+      const u16* vs = ks + TILE;
       f32x16 s[2] = {zero16(), zero16()};
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b) s[b] = mfma(frag(ks + (32 * b + col) * KS + 16 * t + 8 * hf), qf[t], s[b]);
+        for (int b = 0; b < 2; ++b) s[b] = mfma(row_frag(ks, 32 * b + col, 16 * t + 8 * hf), qf[t], s[b]);
       }
       const bool need_mask = a.causal ? (kv0 + BN - 1 > wq0) : (kv0 + BN > S);
-      float mt = -INFINITY;
+      if (need_mask) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int64_t kv = kv0 + 32 * b + 8 * (i / 4) + 4 * hf + (i % 4);
+            if (a.causal ? (kv > myq) : (kv >= S)) s[b][i] = -INFINITY;
+          }
+      }
+      float mt = s[0][0];
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float x = s[b][i] * c;
-          if (need_mask) {
-            const int64_t kv = kv0 + 32 * b + 8 * (i / 4) + 4 * hf + (i % 4);
-            if (a.causal ? (kv > myq) : (kv >= S)) x = -INFINITY;
-          }
-          s[b][i] = x;
-          mt = fmaxf(mt, x);
-        }
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = ex2(m_run - m_new);
+        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[b][i]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32)) * c;
+      // Lazy running max: rescale only when the tile max exceeds it by more
+      // than kLazy (p <= 2^kLazy stays exact in fp32 and in bf16's exponent).
+      const float m_new = (mt > m_run + kLazy) ? mt : m_run;
+      if (__ballot(m_new != m_run)) {
+        const float alpha = ex2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[d4][i] *= alpha;
+        m_run = m_new;
+      }
       float ls = 0.f;
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = ex2(s[b][i] - m_new);
+          const float p = ex2(__builtin_fmaf(s[b][i], c, -m_run));
           s[b][i] = p;
           ls += p;
         }
-      l_run = l_run * alpha + ls;
-      m_run = m_new;
-#pragma unroll
-      for (int d4 = 0; d4 < 4; ++d4)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[d4][i] *= alpha;
+      l_run += ls;
       bf16x8 pb[4];
 #pragma unroll
       for (int k4 = 0; k4 < 4; ++k4) pb[k4] = pack8(s[k4 / 2], k4 % 2);
 #pragma unroll
       for (int d4 = 0; d4 < 4; ++d4)
 #pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4)
-          oacc[d4] = mfma(frag(vts + (32 * d4 + col) * VS + 16 * k4 + 8 * hf), pb[k4], oacc[d4]);
+        for (int k4 = 0; k4 < 4; ++k4) oacc[d4] = mfma(col_frag(vs, 16 * k4, 32 * d4, lane), pb[k4], oacc[d4]);
     }
     if (j + 1 < ntiles) store(cur ^ 1);
     __syncthreads();
@@ -550,17 +603,15 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(AttnArgs a) {
 
 // ---- dK, dV.  Workgroup: 128 key rows of one KV head (4 waves x 32 keys),
 // looping over the stage's query heads of that group (ascending) and over
-// 32-row query tiles.  Each wave computes S = Q K^T with the key in the lane
-// (registers = query rows), so P^T and dS^T are A operands straight from
-// registers; Q and dO are staged both row-major (for S and dP) and transposed
-// in slot order (for dV += P^T dO and dK += dS^T Q).  The fp32 sums are kept
-// in registers, and across the stages of a group in the fp32 carry buffers.
+// 64-row query tiles.  Each wave computes S = Q K^T and dP = dO V^T with the
+// key in the lane (registers = query rows), so P^T and dS^T are A operands
+// straight from registers; dV += P^T dO and dK += dS^T Q read dO and Q as
+// column operands of the same row-major tiles.  The fp32 sums stay in
+// registers, and across the stages of a group in the fp32 carry buffers.
 namespace kv {
-constexpr int BN = 128, BM = 32;
-constexpr int RS = DH + 8;  // row-major tile stride
-constexpr int TS = BM + 8;  // transposed tile stride
-constexpr int QS_OFF = 0, DOS_OFF = BM * RS, QT_OFF = 2 * BM * RS, DOT_OFF = QT_OFF + DH * TS;
-constexpr int BUF = DOT_OFF + DH * TS;  // bf16 elements
+constexpr int BN = 128, BM = 64;
+constexpr int TILE = BM * RS;
+constexpr int BUF = 2 * TILE;  // Q and dO tiles
 }  // namespace kv
 
 __global__ __launch_bounds__(256, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
@@ -611,50 +662,26 @@ __global__ __launch_bounds__(256, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
   const int per_head = nqt - qt0;
   const int niter = (h_hi - h_lo) * per_head;
 
-  // staging roles: 0..63 Q blocks, 64..127 dO blocks (8x8 each, both layouts),
-  // 128..159 lse2, 160..191 D.
-  const int sb = tid % 64, srg = sb / 16, sdc = sb % 16, ss16 = srg / 2, shh = srg % 2;
-  u32x4 rr[8];
+  TileLoad<4> lq, lo;
   float rs = 0.f;
   auto load = [&](int it) {
     const int h = h_lo + it / per_head;
     const int u = h - a.q_head0;
     const int64_t q0 = static_cast<int64_t>(qt0 + it % per_head) * BM;
-    if (tid < 128) {
-      const bool isQ = tid < 64;
-      const u16* src = isQ ? static_cast<const u16*>(a.q) + static_cast<int64_t>(u) * S * DH
-                           : static_cast<const u16*>(a.dO) + static_cast<int64_t>(h) * DH;
-      const int64_t ld = isQ ? DH : ldo;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int64_t q = q0 + 16 * ss16 + slot_row(shh, m);
-        rr[m] = q < S ? ld16(src + q * ld + sdc * 8) : u32x4{0, 0, 0, 0};
-      }
-    } else if (tid < 160) {
-      const int64_t q = q0 + (tid - 128);
+    lq.load(static_cast<const u16*>(a.q) + static_cast<int64_t>(u) * S * DH, DH, q0, S, tid);
+    lo.load(static_cast<const u16*>(a.dO) + static_cast<int64_t>(h) * DH, ldo, q0, S, tid);
+    if (tid < BM) {
+      const int64_t q = q0 + tid;
       rs = q < S ? a.lse_in[static_cast<int64_t>(h) * S + q] * kLog2e : INFINITY;
-    } else if (tid < 192) {
-      const int64_t q = q0 + (tid - 160);
+    } else if (tid < 2 * BM) {
+      const int64_t q = q0 + tid - BM;
       rs = q < S ? a.dd[static_cast<int64_t>(u) * S + q] : 0.f;
     }
   };
   auto store = [&](int b) {
-    u16* base = lds + b * BUF;
-    if (tid < 128) {
-      const bool isQ = tid < 64;
-      u16* rowm = base + (isQ ? QS_OFF : DOS_OFF);
-      u16* tr = base + (isQ ? QT_OFF : DOT_OFF);
-#pragma unroll
-      for (int m = 0; m < 8; ++m) st16(rowm + (16 * ss16 + slot_row(shh, m)) * RS + sdc * 8, rr[m]);
-      u32x4 tc[8];
-      transpose8(rr, tc);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) st16(tr + (sdc * 8 + e) * TS + 16 * ss16 + 8 * shh, tc[e]);
-    } else if (tid < 160) {
-      stat[b][0][tid - 128] = rs;
-    } else if (tid < 192) {
-      stat[b][1][tid - 160] = rs;
-    }
+    lq.store(lds + b * BUF, tid);
+    lo.store(lds + b * BUF + TILE, tid);
+    if (tid < 2 * BM) stat[b][tid / BM][tid % BM] = rs;
   };
 
   if (niter > 0) {
@@ -668,40 +695,45 @@ __global__ __launch_bounds__(256, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
     const int64_t q0 = static_cast<int64_t>(qt0 + it % per_head) * BM;
     const bool active = !a.causal || q0 + BM - 1 >= wk0;
     if (active) {
-      const u16* base = lds + cur * BUF;
-      f32x16 sacc = zero16(), dpacc = zero16();
+      const u16* qs = lds + cur * BUF;
+      const u16* gs = qs + TILE;
+      f32x16 sacc[2] = {zero16(), zero16()}, dpacc[2] = {zero16(), zero16()};
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        sacc = mfma(frag(base + QS_OFF + col * RS + 16 * t + 8 * hf), kf[t], sacc);
-        dpacc = mfma(frag(base + DOS_OFF + col * RS + 16 * t + 8 * hf), vf[t], dpacc);
-      }
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          sacc[qb] = mfma(row_frag(qs, 32 * qb + col, 16 * t + 8 * hf), kf[t], sacc[qb]);
+          dpacc[qb] = mfma(row_frag(gs, 32 * qb + col, 16 * t + 8 * hf), vf[t], dpacc[qb]);
+        }
       const bool need_mask = a.causal && q0 < wk0 + 31;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int r0 = 8 * g4 + 4 * hf;  // rows r0..r0+3 of the tile
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&stat[cur][0][r0]);
-        const f32x4 d4v = *reinterpret_cast<const f32x4*>(&stat[cur][1][r0]);
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * g4 + e;
-          float p = ex2(sacc[i] * c - l4[e]);
-          if (need_mask && myk > q0 + r0 + e) p = 0.f;
-          sacc[i] = p;
-          dpacc[i] = p * (dpacc[i] - d4v[e]);
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int r0 = 32 * qb + 8 * g4 + 4 * hf;  // rows r0..r0+3 of the tile
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&stat[cur][0][r0]);
+          const f32x4 d4v = *reinterpret_cast<const f32x4*>(&stat[cur][1][r0]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * g4 + e;
+            float p = ex2(__builtin_fmaf(sacc[qb][i], c, -l4[e]));
+            if (need_mask && myk > q0 + r0 + e) p = 0.f;
+            sacc[qb][i] = p;
+            dpacc[qb][i] = p * (dpacc[qb][i] - d4v[e]);
+          }
         }
-      }
-      bf16x8 pa[2], dsa[2];
+      bf16x8 pa[4], dsa[4];
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        pa[k2] = pack8(sacc, k2);
-        dsa[k2] = pack8(dpacc, k2);
+      for (int k4 = 0; k4 < 4; ++k4) {
+        pa[k4] = pack8(sacc[k4 / 2], k4 % 2);
+        dsa[k4] = pack8(dpacc[k4 / 2], k4 % 2);
       }
 #pragma unroll
       for (int d4 = 0; d4 < 4; ++d4)
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          dv[d4] = mfma(pa[k2], frag(base + DOT_OFF + (32 * d4 + col) * TS + 16 * k2 + 8 * hf), dv[d4]);
-          dk[d4] = mfma(dsa[k2], frag(base + QT_OFF + (32 * d4 + col) * TS + 16 * k2 + 8 * hf), dk[d4]);
+        for (int k4 = 0; k4 < 4; ++k4) {
+          dv[d4] = mfma(pa[k4], col_frag(gs, 16 * k4, 32 * d4, lane), dv[d4]);
+          dk[d4] = mfma(dsa[k4], col_frag(qs, 16 * k4, 32 * d4, lane), dk[d4]);
         }
     }
     if (it + 1 < niter) store(cur ^ 1);
@@ -727,16 +759,15 @@ __global__ __launch_bounds__(256, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
 
 // ---- dQ.  Workgroup: 128 query rows of one head (4 waves x 32 rows); key
 // tiles of 64 rows.  Orientation as in the forward (lane = query row): S^T
-// and dP^T from registers Q, dO against K, V tiles, then dQ^T += K^T dS^T with
-// K also staged transposed in slot order.
+// and dP^T from registers Q, dO against K and V row operands, then
+// dQ^T += K^T dS^T with K read as a column operand of the same tile.
 namespace dqk {
 constexpr int BM = 128, BN = 64;
-constexpr int RS = DH + 8, TS = BN + 8;
-constexpr int KS_OFF = 0, VS_OFF = BN * RS, KT_OFF = 2 * BN * RS;
-constexpr int BUF = KT_OFF + DH * TS;
+constexpr int TILE = BN * RS;
+constexpr int BUF = 2 * TILE;  // K and V
 }  // namespace dqk
 
-__global__ __launch_bounds__(256, 1) void attn_dq_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnArgs a) {
   using namespace dqk;
   __shared__ __attribute__((aligned(16))) u16 lds[2 * BUF];
   const int64_t S = a.S;
@@ -771,37 +802,14 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(AttnArgs a) {
   const int64_t kv_end = a.causal ? min(S, qfirst + BM) : S;
   const int ntiles = static_cast<int>((kv_end + BN - 1) / BN);
 
-  // staging roles: 0..127 K blocks (row-major + transposed), 128..255 V rows.
-  const bool isK = tid < 128;
-  const int krg = (tid % 128) / 16, kdc = tid % 16, ks16 = krg / 2, khh = krg % 2;
-  u32x4 rr[8];
+  TileLoad<4> lk, lv;
   auto load = [&](int j) {
-    const int64_t kv0 = static_cast<int64_t>(j) * BN;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      if (isK) {
-        const int64_t kvr = kv0 + 16 * ks16 + slot_row(khh, m);
-        rr[m] = kvr < S ? ld16(K + kvr * DH + kdc * 8) : u32x4{0, 0, 0, 0};
-      } else {
-        const int row = (tid - 128) / 16 + 8 * m, chunk = tid % 16;
-        const int64_t kvr = kv0 + row;
-        rr[m] = kvr < S ? ld16(V + kvr * DH + chunk * 8) : u32x4{0, 0, 0, 0};
-      }
-    }
+    lk.load(K, DH, static_cast<int64_t>(j) * BN, S, tid);
+    lv.load(V, DH, static_cast<int64_t>(j) * BN, S, tid);
   };
   auto store = [&](int b) {
-    u16* base = lds + b * BUF;
-    if (isK) {
-#pragma unroll
-      for (int m = 0; m < 8; ++m) st16(base + KS_OFF + (16 * ks16 + slot_row(khh, m)) * RS + kdc * 8, rr[m]);
-      u32x4 tc[8];
-      transpose8(rr, tc);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) st16(base + KT_OFF + (kdc * 8 + e) * TS + 16 * ks16 + 8 * khh, tc[e]);
-    } else {
-#pragma unroll
-      for (int m = 0; m < 8; ++m) st16(base + VS_OFF + ((tid - 128) / 16 + 8 * m) * RS + (tid % 16) * 8, rr[m]);
-    }
+    lk.store(lds + b * BUF, tid);
+    lv.store(lds + b * BUF + TILE, tid);
   };
 
   f32x16 dq[4];
@@ -817,35 +825,35 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(AttnArgs a) {
     const int64_t kv0 = static_cast<int64_t>(j) * BN;
     const bool active = !a.causal || kv0 <= wq0 + 31;
     if (active) {
-      const u16* base = lds + cur * BUF;
-      f32x16 s[2] = {zero16(), zero16()}, dp[2] = {zero16(), zero16()};
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          s[b] = mfma(frag(base + KS_OFF + (32 * b + col) * RS + 16 * t + 8 * hf), qf[t], s[b]);
-          dp[b] = mfma(frag(base + VS_OFF + (32 * b + col) * RS + 16 * t + 8 * hf), gf[t], dp[b]);
-        }
+      const u16* ks = lds + cur * BUF;
+      const u16* vs = ks + TILE;
       const bool need_mask = a.causal ? (kv0 + BN - 1 > wq0) : (kv0 + BN > S);
+      // two 32-key halves, one after the other (fewer live registers); each
+      // dQ^T column block still sums its four 16-key steps in order
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < 2; ++b) {
+        f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          s = mfma(row_frag(ks, 32 * b + col, 16 * t + 8 * hf), qf[t], s);
+          dp = mfma(row_frag(vs, 32 * b + col, 16 * t + 8 * hf), gf[t], dp);
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float p = ex2(s[b][i] * c - lse2);
+          float p = ex2(__builtin_fmaf(s[i], c, -lse2));
           if (need_mask) {
             const int64_t kvr = kv0 + 32 * b + 8 * (i / 4) + 4 * hf + (i % 4);
             if (a.causal ? (kvr > myq) : (kvr >= S)) p = 0.f;
           }
-          dp[b][i] = p * (dp[b][i] - Dq);
+          dp[i] = p * (dp[i] - Dq);
         }
-      bf16x8 dsb[4];
+        const bf16x8 ds0 = pack8(dp, 0), ds1 = pack8(dp, 1);
 #pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) dsb[k4] = pack8(dp[k4 / 2], k4 % 2);
-#pragma unroll
-      for (int d4 = 0; d4 < 4; ++d4)
-#pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4)
-          dq[d4] = mfma(frag(base + KT_OFF + (32 * d4 + col) * TS + 16 * k4 + 8 * hf), dsb[k4], dq[d4]);
+        for (int d4 = 0; d4 < 4; ++d4) {
+          dq[d4] = mfma(col_frag(ks, 32 * b, 32 * d4, lane), ds0, dq[d4]);
+          dq[d4] = mfma(col_frag(ks, 32 * b + 16, 32 * d4, lane), ds1, dq[d4]);
+        }
+      }
     }
     if (j + 1 < ntiles) store(cur ^ 1);
     __syncthreads();

@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--skip-cpu-baseline", action="store_true",
                     help="omit the oracle timing (profiling runs only)")
     ap.add_argument("--cpu-baseline-S", type=int, default=6144)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (HBM counter calibration)")
     return ap.parse_args()
 
 
@@ -151,6 +153,15 @@ def main():
     print("bench: %s S=%d D=%d H=%d G=%d d=%d U=%d" % (args.config, S, D, H, G, d, U),
           file=sys.stderr, flush=True)
 
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("bench: calibration copy of %d bytes" % n, file=sys.stderr, flush=True)
+        del src, dst
     inp = make_inputs(shape, cfg["dtype"], seed=0, device="cuda")
     plan = upipe.Plan(S, D, H, G, d, U, causal=True, dtype=cfg["dtype"])
     out = alloc_outputs(plan, dev)

@@ -28,6 +28,8 @@
 // fixed summation order, so results are identical run to run and for every U.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "upipe_internal.h"
 
 namespace upipe {
@@ -64,10 +66,13 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> one dword of two bf16 (round to nearest even): v_cvt_pk_bf16_f32.
 __device__ __forceinline__ unsigned pack2(float lo, float hi) {
-  __bf16 a = static_cast<__bf16>(lo), b = static_cast<__bf16>(hi);
-  return static_cast<unsigned>(__builtin_bit_cast(u16, a)) |
-         (static_cast<unsigned>(__builtin_bit_cast(u16, b)) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
 }
 
 // Registers 8t..8t+7 of a C block -> an 8-slot bf16 operand.
@@ -391,6 +396,8 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 constexpr int RS = DH + 8;  // LDS row stride of attention tiles (elements)
 
+typedef __attribute__((address_space(3))) u16 lds_u16;
+
 __device__ __forceinline__ int prow(int q) {
   return (q & ~15) | (((q >> 2) & 1) << 3) | ((q & 3) << 1) | ((q >> 3) & 1);
 }
@@ -398,23 +405,46 @@ __device__ __forceinline__ int prow(int q) {
 // Element offset of (logical row q, column col) in a tile.
 __device__ __forceinline__ int toff(int q, int col) { return prow(q) * RS + col; }
 
-// Row operand: 8 columns [col, col + 8) of row q.
-__device__ __forceinline__ bf16x8 row_frag(const u16* t, int q, int col) { return frag(t + toff(q, col)); }
+// Per-lane base addresses of one tile for the two read patterns.  They are
+// passed through an empty asm so the compiler keeps exactly one register per
+// pattern and folds every fragment's constant offset into the instruction,
+// instead of hoisting one address register per fragment out of the loop.
+struct TileAddr {
+  const lds_u16* row;  // + (32*blk)*RS + 16*t: row operand of rows 32*blk + lane%32, columns 16t + 8h..
+  const lds_u16* col;  // + r0*RS + n0: column operand (first 4 slots; the other 4 are one row further)
+};
+__device__ __forceinline__ const lds_u16* opaque(const lds_u16* p) {
+  unsigned v = static_cast<unsigned>(reinterpret_cast<uintptr_t>(p));
+  asm volatile("" : "+v"(v));
+  return reinterpret_cast<const lds_u16*>(static_cast<uintptr_t>(v));
+}
+__device__ __forceinline__ TileAddr tile_addr(const u16* tile, int lane) {
+  const lds_u16* t = (const lds_u16*)tile;  // generic -> LDS address space
+  const int hf = lane >> 5, g16 = (lane >> 4) & 1, i16 = lane & 15;
+  TileAddr ta;
+  ta.row = opaque(t + prow(lane & 31) * RS + 8 * hf);
+  ta.col = opaque(t + prow(4 * hf + (i16 >> 2)) * RS + 16 * g16 + 4 * (i16 & 3));
+  return ta;
+}
+
+// Row operand: row 32*blk + lane%32, columns 16t + 8h .. 16t + 8h + 7.
+__device__ __forceinline__ bf16x8 row_frag(const TileAddr& ta, int blk, int t) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                                        ta.row + 32 * blk * RS + 16 * t));
+}
 
 // Column operand: column n0 + lane % 32 of the 16 rows r0 .. r0 + 15 (r0 a
 // multiple of 16), in the slot order of a C block (lane half h: rows
 // r0+4h..r0+4h+3, then r0+8+4h..r0+8+4h+3; the second set is one physical row
 // further).
-__device__ __forceinline__ bf16x8 col_frag(const u16* t, int r0, int n0, int lane) {
-  const int hf = lane >> 5, g16 = (lane >> 4) & 1, i16 = lane & 15;
-  const u16* p = t + toff(r0 + 4 * hf + (i16 >> 2), n0 + 16 * g16 + 4 * (i16 & 3));
-  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, p));
-  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, p + RS));
-  u32x4 w;
-  w[0] = static_cast<unsigned>(static_cast<u16>(lo[0])) | (static_cast<unsigned>(static_cast<u16>(lo[1])) << 16);
-  w[1] = static_cast<unsigned>(static_cast<u16>(lo[2])) | (static_cast<unsigned>(static_cast<u16>(lo[3])) << 16);
-  w[2] = static_cast<unsigned>(static_cast<u16>(hi[0])) | (static_cast<unsigned>(static_cast<u16>(hi[1])) << 16);
-  w[3] = static_cast<unsigned>(static_cast<u16>(hi[2])) | (static_cast<unsigned>(static_cast<u16>(hi[3])) << 16);
+__device__ __forceinline__ bf16x8 col_frag(const TileAddr& ta, int r0, int n0) {
+  const lds_u16* p = ta.col + r0 * RS + n0;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) v4i16*>(const_cast<lds_u16*>(p)));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) v4i16*>(const_cast<lds_u16*>(p + RS)));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  const u32x4 w = {l2[0], l2[1], h2[0], h2[1]};
   return __builtin_bit_cast(bf16x8, w);
 }
 
@@ -425,12 +455,11 @@ template <int NCH>
 struct TileLoad {
   u32x4 r[NCH];
   __device__ __forceinline__ void load(const u16* src, int64_t ld, int64_t row0, int64_t S, int first) {
+    const int row = first >> 4, c = first & 15;  // rows row, row + 16, ... (256 chunks apart)
+    const u16* p = src + (row0 + row) * ld + c * 8;
+    const int64_t left = S - row0 - row;          // rows of this thread still inside S: m * 16 < left
 #pragma unroll
-    for (int m = 0; m < NCH; ++m) {
-      const int e = first + 256 * m, row = e >> 4, c = e & 15;
-      const int64_t g = row0 + row;
-      r[m] = g < S ? ld16(src + g * ld + c * 8) : u32x4{0, 0, 0, 0};
-    }
+    for (int m = 0; m < NCH; ++m) r[m] = 16 * m < left ? ld16(p + 16 * m * ld) : u32x4{0, 0, 0, 0};
   }
   __device__ __forceinline__ void store(u16* tile, int first) const {
 #pragma unroll
@@ -504,22 +533,37 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     const int64_t kv0 = static_cast<int64_t>(j) * BN;
     const bool active = !a.causal || kv0 <= wq0 + 31;
     if (active) {
-      const u16* ks = lds + cur * BUF;
-      const u16* vs = ks + TILE;
+      const TileAddr ka = tile_addr(lds + cur * BUF, lane);
+      const TileAddr va = tile_addr(lds + cur * BUF + TILE, lane);
+      // S^T = K Q^T: two accumulator chains; the K operands of step t + 2 are
+      // requested before the MFMAs of step t are issued.
       f32x16 s[2] = {zero16(), zero16()};
+      bf16x8 fa[3][2];
+      auto load_a = [&](int t, bf16x8 (&f)[2]) {
+        f[0] = row_frag(ka, 0, t);
+        f[1] = row_frag(ka, 1, t);
+      };
+      load_a(0, fa[0]);
+      load_a(1, fa[1]);
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b) s[b] = mfma(row_frag(ks, 32 * b + col, 16 * t + 8 * hf), qf[t], s[b]);
+        if (t + 2 < 8) load_a(t + 2, fa[(t + 2) % 3]);
+        __builtin_amdgcn_sched_barrier(0);
+        s[0] = mfma(fa[t % 3][0], qf[t], s[0]);
+        s[1] = mfma(fa[t % 3][1], qf[t], s[1]);
+        __builtin_amdgcn_sched_barrier(0);
       }
       const bool need_mask = a.causal ? (kv0 + BN - 1 > wq0) : (kv0 + BN > S);
       if (need_mask) {
+        // key kv0 + j is masked when j > myq - kv0 (causal) or j >= S - kv0
+        const int lim = static_cast<int>(a.causal ? min(myq - kv0, static_cast<int64_t>(BN)) :
+                                                    min(S - 1 - kv0, static_cast<int64_t>(BN)));
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int64_t kv = kv0 + 32 * b + 8 * (i / 4) + 4 * hf + (i % 4);
-            if (a.causal ? (kv > myq) : (kv >= S)) s[b][i] = -INFINITY;
+            const int j = 32 * b + 8 * (i / 4) + 4 * hf + (i % 4);
+            if (j > lim) s[b][i] = -INFINITY;
           }
       }
       float mt = s[0][0];
@@ -553,10 +597,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
       bf16x8 pb[4];
 #pragma unroll
       for (int k4 = 0; k4 < 4; ++k4) pb[k4] = pack8(s[k4 / 2], k4 % 2);
+      // O^T += V^T P^T: step k4 outermost so the four accumulators alternate
+      // (each still sums k4 = 0..3 in order); V operands requested 3 groups ahead.
+      bf16x8 fc[4];
+      auto load_c = [&](int gi) { return col_frag(va, 16 * (gi / 4), 32 * (gi % 4)); };
+      fc[0] = load_c(0);
+      fc[1] = load_c(1);
+      fc[2] = load_c(2);
 #pragma unroll
-      for (int d4 = 0; d4 < 4; ++d4)
-#pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) oacc[d4] = mfma(col_frag(vs, 16 * k4, 32 * d4, lane), pb[k4], oacc[d4]);
+      for (int gi = 0; gi < 16; ++gi) {
+        if (gi + 3 < 16) fc[(gi + 3) % 4] = load_c(gi + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        oacc[gi % 4] = mfma(fc[gi % 4], pb[gi / 4], oacc[gi % 4]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if (j + 1 < ntiles) store(cur ^ 1);
     __syncthreads();
@@ -612,12 +666,14 @@ namespace kv {
 constexpr int BN = 128, BM = 64;
 constexpr int TILE = BM * RS;
 constexpr int BUF = 2 * TILE;  // Q and dO tiles
+constexpr int NBUF = 2;        // double buffer: tile it (read), it + 1 (being filled)
 }  // namespace kv
 
 __global__ __launch_bounds__(256, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
   using namespace kv;
-  __shared__ __attribute__((aligned(16))) u16 lds[2 * BUF];
-  __shared__ __attribute__((aligned(16))) float stat[2][2][BM];  // [buffer][lse2, D][row]
+  __shared__ __attribute__((aligned(16))) u16 lds[NBUF * BUF];
+  __shared__ __attribute__((aligned(16))) u16 kvs[2 * BN * RS];  // this workgroup's K and V rows
+  __shared__ __attribute__((aligned(16))) float stat[NBUF][2][BM];  // [buffer][lse2, D][row]
   const int64_t S = a.S;
   const int kt = blockIdx.x / nkv, gl = blockIdx.x % nkv;  // key tile 0 (most work) first
   const int g = a.kv_head0 + gl;
@@ -628,16 +684,20 @@ __global__ __launch_bounds__(256, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
   const float c = kLog2e * tau;
   const int64_t ldo = static_cast<int64_t>(a.H) * DH;
 
-  bf16x8 kf[8], vf[8];
+  // K and V rows of this workgroup stay in LDS for the whole kernel (as B
+  // operands of S = Q K^T and dP = dO V^T); this keeps 64 registers per lane
+  // free for the S/dP accumulators.
   {
     const u16* K = static_cast<const u16*>(a.k) + static_cast<int64_t>(gl) * S * DH;
     const u16* V = static_cast<const u16*>(a.v) + static_cast<int64_t>(gl) * S * DH;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      kf[t] = __builtin_bit_cast(bf16x8, myk < S ? ld16(K + myk * DH + 16 * t + 8 * hf) : u32x4{0, 0, 0, 0});
-      vf[t] = __builtin_bit_cast(bf16x8, myk < S ? ld16(V + myk * DH + 16 * t + 8 * hf) : u32x4{0, 0, 0, 0});
-    }
+    TileLoad<8> lk, lv;
+    lk.load(K, DH, static_cast<int64_t>(kt) * BN, S, tid);
+    lv.load(V, DH, static_cast<int64_t>(kt) * BN, S, tid);
+    lk.store(kvs, tid);
+    lv.store(kvs + BN * RS, tid);
   }
+  const TileAddr kaddr = tile_addr(kvs + 32 * wave * RS, lane);
+  const TileAddr vaddr = tile_addr(kvs + BN * RS + 32 * wave * RS, lane);
 
   // accumulators: C layout, lane = d column (within 32-block d4), registers = key rows
   f32x16 dk[4], dv[4];
@@ -661,13 +721,14 @@ __global__ __launch_bounds__(256, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
   const int qt0 = a.causal ? static_cast<int>((static_cast<int64_t>(kt) * BN) / BM) : 0;
   const int per_head = nqt - qt0;
   const int niter = (h_hi - h_lo) * per_head;
+  auto tile_q0 = [&](int it) { return static_cast<int64_t>(qt0 + it % per_head) * BM; };
 
   TileLoad<4> lq, lo;
   float rs = 0.f;
   auto load = [&](int it) {
     const int h = h_lo + it / per_head;
     const int u = h - a.q_head0;
-    const int64_t q0 = static_cast<int64_t>(qt0 + it % per_head) * BM;
+    const int64_t q0 = tile_q0(it);
     lq.load(static_cast<const u16*>(a.q) + static_cast<int64_t>(u) * S * DH, DH, q0, S, tid);
     lo.load(static_cast<const u16*>(a.dO) + static_cast<int64_t>(h) * DH, ldo, q0, S, tid);
     if (tid < BM) {
@@ -690,53 +751,89 @@ __global__ __launch_bounds__(256, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
   }
   __syncthreads();
   for (int it = 0; it < niter; ++it) {
-    const int cur = it & 1;
-    if (it + 1 < niter) load(it + 1);
-    const int64_t q0 = static_cast<int64_t>(qt0 + it % per_head) * BM;
-    const bool active = !a.causal || q0 + BM - 1 >= wk0;
-    if (active) {
-      const u16* qs = lds + cur * BUF;
-      const u16* gs = qs + TILE;
-      f32x16 sacc[2] = {zero16(), zero16()}, dpacc[2] = {zero16(), zero16()};
+    const int b = it % NBUF;
+    const TileAddr qa = tile_addr(lds + b * BUF, lane);
+    const TileAddr ga = tile_addr(lds + b * BUF + TILE, lane);
+
+    // S = Q K^T and dP = dO V^T: four MFMA chains; the LDS operands of step
+    // t + 1 are requested before the MFMAs of step t are issued.
+    f32x16 sacc[2] = {zero16(), zero16()}, dpacc[2] = {zero16(), zero16()};
+    bf16x8 fa[2][6];
+    auto row_ops = [&](int t, bf16x8 (&f)[6]) {
+      f[0] = row_frag(qa, 0, t);
+      f[1] = row_frag(qa, 1, t);
+      f[2] = row_frag(ga, 0, t);
+      f[3] = row_frag(ga, 1, t);
+      f[4] = row_frag(kaddr, 0, t);
+      f[5] = row_frag(vaddr, 0, t);
+    };
+    row_ops(0, fa[0]);
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          sacc[qb] = mfma(row_frag(qs, 32 * qb + col, 16 * t + 8 * hf), kf[t], sacc[qb]);
-          dpacc[qb] = mfma(row_frag(gs, 32 * qb + col, 16 * t + 8 * hf), vf[t], dpacc[qb]);
-        }
-      const bool need_mask = a.causal && q0 < wk0 + 31;
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int r0 = 32 * qb + 8 * g4 + 4 * hf;  // rows r0..r0+3 of the tile
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&stat[cur][0][r0]);
-          const f32x4 d4v = *reinterpret_cast<const f32x4*>(&stat[cur][1][r0]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * g4 + e;
-            float p = ex2(__builtin_fmaf(sacc[qb][i], c, -l4[e]));
-            if (need_mask && myk > q0 + r0 + e) p = 0.f;
-            sacc[qb][i] = p;
-            dpacc[qb][i] = p * (dpacc[qb][i] - d4v[e]);
-          }
-        }
-      bf16x8 pa[4], dsa[4];
-#pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) {
-        pa[k4] = pack8(sacc[k4 / 2], k4 % 2);
-        dsa[k4] = pack8(dpacc[k4 / 2], k4 % 2);
-      }
-#pragma unroll
-      for (int d4 = 0; d4 < 4; ++d4)
-#pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) {
-          dv[d4] = mfma(pa[k4], col_frag(gs, 16 * k4, 32 * d4, lane), dv[d4]);
-          dk[d4] = mfma(dsa[k4], col_frag(qs, 16 * k4, 32 * d4, lane), dk[d4]);
-        }
+    for (int t = 0; t < 8; ++t) {
+      if (t + 1 < 8) row_ops(t + 1, fa[(t + 1) % 2]);
+      __builtin_amdgcn_sched_barrier(0);
+      sacc[0] = mfma(fa[t % 2][0], fa[t % 2][4], sacc[0]);
+      sacc[1] = mfma(fa[t % 2][1], fa[t % 2][4], sacc[1]);
+      dpacc[0] = mfma(fa[t % 2][2], fa[t % 2][5], dpacc[0]);
+      dpacc[1] = mfma(fa[t % 2][3], fa[t % 2][5], dpacc[1]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (it + 1 < niter) store(cur ^ 1);
+    // next tile: global loads in flight during the softmax and dV/dK phases
+    if (it + 1 < niter) load(it + 1);
+
+    // P = exp(S - LSE), dS = P (dP - D), masked above the diagonal.
+    const int64_t q0 = tile_q0(it);
+    const bool need_mask = a.causal && q0 < wk0 + 31;
+    const int mlim = need_mask ? static_cast<int>(myk - q0) : -(1 << 30);  // row r masked when r < mlim
+    bf16x8 pa[4], dsa[4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int r0 = 32 * qb + 8 * g4 + 4 * hf;  // tile rows r0..r0+3 = registers 4*g4..4*g4+3
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&stat[b][0][r0]);
+        const f32x4 d4v = *reinterpret_cast<const f32x4*>(&stat[b][1][r0]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * g4 + e;
+          sacc[qb][i] = ex2(__builtin_fmaf(sacc[qb][i], c, -l4[e]));
+        }
+        if (need_mask) {  // wave-uniform: only tiles that cross the diagonal
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (r0 + e < mlim) sacc[qb][4 * g4 + e] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * g4 + e;
+          dpacc[qb][i] = sacc[qb][i] * (dpacc[qb][i] - d4v[e]);
+        }
+        if (g4 & 1) {
+          pa[2 * qb + g4 / 2] = pack8(sacc[qb], g4 / 2);
+          dsa[2 * qb + g4 / 2] = pack8(dpacc[qb], g4 / 2);
+        }
+      }
+
+    // dV += P^T dO and dK += dS^T Q: step k4 outermost, so eight independent
+    // accumulators alternate (each still sums k4 = 0..3 in order); the column
+    // operands of group gi + 1 are requested before group gi's MFMAs.
+    bf16x8 fc[2][2];
+    auto col_ops = [&](int gi, bf16x8 (&f)[2]) {
+      const int k4 = gi / 4, d4 = gi % 4;
+      f[0] = col_frag(ga, 16 * k4, 32 * d4);
+      f[1] = col_frag(qa, 16 * k4, 32 * d4);
+    };
+    col_ops(0, fc[0]);
+#pragma unroll
+    for (int gi = 0; gi < 16; ++gi) {
+      if (gi + 1 < 16) col_ops(gi + 1, fc[(gi + 1) % 2]);
+      __builtin_amdgcn_sched_barrier(0);
+      const int k4 = gi / 4, d4 = gi % 4;
+      dv[d4] = mfma(pa[k4], fc[gi % 2][0], dv[d4]);
+      dk[d4] = mfma(dsa[k4], fc[gi % 2][1], dk[d4]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (it + 1 < niter) store((it + 1) % NBUF);
     __syncthreads();
   }
 
@@ -825,33 +922,53 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnArgs a) {
     const int64_t kv0 = static_cast<int64_t>(j) * BN;
     const bool active = !a.causal || kv0 <= wq0 + 31;
     if (active) {
-      const u16* ks = lds + cur * BUF;
-      const u16* vs = ks + TILE;
+      const TileAddr ks = tile_addr(lds + cur * BUF, lane);
+      const TileAddr vs = tile_addr(lds + cur * BUF + TILE, lane);
       const bool need_mask = a.causal ? (kv0 + BN - 1 > wq0) : (kv0 + BN > S);
+      // key kv0 + j is masked when j > lim
+      const int lim = static_cast<int>(a.causal ? min(myq - kv0, static_cast<int64_t>(BN)) :
+                                                  min(S - 1 - kv0, static_cast<int64_t>(BN)));
       // two 32-key halves, one after the other (fewer live registers); each
       // dQ^T column block still sums its four 16-key steps in order
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         f32x16 s = zero16(), dp = zero16();
+        bf16x8 fa[2][2];
+        auto load_a = [&](int t, bf16x8 (&f)[2]) {
+          f[0] = row_frag(ks, b, t);
+          f[1] = row_frag(vs, b, t);
+        };
+        load_a(0, fa[0]);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          s = mfma(row_frag(ks, 32 * b + col, 16 * t + 8 * hf), qf[t], s);
-          dp = mfma(row_frag(vs, 32 * b + col, 16 * t + 8 * hf), gf[t], dp);
+          if (t + 1 < 8) load_a(t + 1, fa[(t + 1) % 2]);
+          __builtin_amdgcn_sched_barrier(0);
+          s = mfma(fa[t % 2][0], qf[t], s);
+          dp = mfma(fa[t % 2][1], gf[t], dp);
+          __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float p = ex2(__builtin_fmaf(s[i], c, -lse2));
-          if (need_mask) {
-            const int64_t kvr = kv0 + 32 * b + 8 * (i / 4) + 4 * hf + (i % 4);
-            if (a.causal ? (kvr > myq) : (kvr >= S)) p = 0.f;
-          }
-          dp[i] = p * (dp[i] - Dq);
-        }
-        const bf16x8 ds0 = pack8(dp, 0), ds1 = pack8(dp, 1);
+        for (int i = 0; i < 16; ++i) s[i] = ex2(__builtin_fmaf(s[i], c, -lse2));
+        if (need_mask) {  // wave-uniform: only tiles that cross the diagonal or the end
 #pragma unroll
-        for (int d4 = 0; d4 < 4; ++d4) {
-          dq[d4] = mfma(col_frag(ks, 32 * b, 32 * d4, lane), ds0, dq[d4]);
-          dq[d4] = mfma(col_frag(ks, 32 * b + 16, 32 * d4, lane), ds1, dq[d4]);
+          for (int i = 0; i < 16; ++i)
+            if (32 * b + 8 * (i / 4) + 4 * hf + (i % 4) > lim) s[i] = 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dp[i] = s[i] * (dp[i] - Dq);
+        const bf16x8 ds[2] = {pack8(dp, 0), pack8(dp, 1)};
+        // step outermost: four alternating accumulators, each summing its
+        // 16-key steps in order; K operands requested 2 groups ahead
+        bf16x8 fc[3];
+        auto load_c = [&](int gi) { return col_frag(ks, 32 * b + 16 * (gi / 4), 32 * (gi % 4)); };
+        fc[0] = load_c(0);
+        fc[1] = load_c(1);
+#pragma unroll
+        for (int gi = 0; gi < 8; ++gi) {
+          if (gi + 2 < 8) fc[(gi + 2) % 3] = load_c(gi + 2);
+          __builtin_amdgcn_sched_barrier(0);
+          dq[gi % 4] = mfma(fc[gi % 3], ds[gi / 4], dq[gi % 4]);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }

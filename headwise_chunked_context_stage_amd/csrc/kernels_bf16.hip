@@ -109,6 +109,19 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
   return x * per + min(x, rem) + local;
 }
 
+// Rounds of 256 consecutive workgroup ids (one per CU at a time): within a
+// round, XCD x (ids are dealt round-robin over 8 XCDs) gets 32 consecutive
+// logical ids, and the order of the XCDs reverses every other round, so each
+// XCD's L2 serves neighbouring tiles while heavy and light tiles stay evenly
+// spread over the XCDs.  A trailing partial round keeps the identity map.
+__device__ __forceinline__ int xcd_snake(int id, int total) {
+  const int round = id >> 8, pos = id & 255;
+  if ((round << 8) + 256 > total) return id;
+  const int x = pos & 7, j = pos >> 3;
+  const int xx = (round & 1) ? 7 - x : x;
+  return (round << 8) + xx * 32 + j;
+}
+
 // ===================================================================== GEMMs
 // 128 x 128 output tile, 64-wide k steps, 4 waves as 2 x 2 (64 x 64 each),
 // LDS double-buffered with register prefetch.
@@ -376,14 +389,16 @@ __global__ __launch_bounds__(256, 2) void dx_kernel(float* __restrict__ dX, int6
 
 // ================================================================= attention
 // Tiles of 128-column bf16 rows live in LDS row-major with a padded row
-// stride (RS = 136 elements, 272 bytes) and a fixed permutation of the rows
-// inside every 16-row group: logical row 8a + 4b + c (a, b in {0,1}, c < 4)
-// sits at physical row 8b + 2c + a.  Two read patterns are then free of bank
-// conflicts and all their addresses are affine (immediate offsets):
+// stride (RS = 136 elements, 272 bytes: consecutive physical rows start 4
+// banks apart) and a fixed permutation of the rows inside every 16-row group:
+// logical row 8a + 4b + c (a, b in {0,1}, c < 4) sits at physical row
+// 4c + 2b + a.  Two read patterns are then free of bank conflicts and all
+// their addresses are affine (immediate offsets):
 //  * row operand (ds_read_b128): each lane reads 8 columns of its own row; 16
 //    consecutive logical rows are 16 distinct physical rows;
 //  * column operand (ds_read_b64_tr_b16): a 16-lane group reads 4 logical
-//    rows 4b..4b+3 (physical rows two apart) x 32 bytes.
+//    rows 4b..4b+3 (physical rows four apart, 16 banks apart) x 32 bytes, so
+//    the two groups of a half wave (columns 16 apart, 8 banks) interleave.
 // The transposing read gives lane i of each 16-lane group element (i % 4) of
 // the 8-byte rows addressed by lanes 4k + i/4 (k = 0..3).  When lane 4k + c of
 // the group addresses row R_k at columns n0 + 4c .. n0 + 4c + 3, lane i
@@ -399,7 +414,7 @@ constexpr int RS = DH + 8;  // LDS row stride of attention tiles (elements)
 typedef __attribute__((address_space(3))) u16 lds_u16;
 
 __device__ __forceinline__ int prow(int q) {
-  return (q & ~15) | (((q >> 2) & 1) << 3) | ((q & 3) << 1) | ((q >> 3) & 1);
+  return (q & ~15) | ((q & 3) << 2) | (((q >> 2) & 1) << 1) | ((q >> 3) & 1);
 }
 
 // Element offset of (logical row q, column col) in a tile.
@@ -675,7 +690,8 @@ __global__ __launch_bounds__(256, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
   __shared__ __attribute__((aligned(16))) u16 kvs[2 * BN * RS];  // this workgroup's K and V rows
   __shared__ __attribute__((aligned(16))) float stat[NBUF][2][BM];  // [buffer][lse2, D][row]
   const int64_t S = a.S;
-  const int kt = blockIdx.x / nkv, gl = blockIdx.x % nkv;  // key tile 0 (most work) first
+  const int lid = xcd_snake(blockIdx.x, gridDim.x);
+  const int kt = lid / nkv, gl = lid % nkv;  // key tile 0 (most work) first
   const int g = a.kv_head0 + gl;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, col = lane % 32, hf = lane / 32;
   const int64_t wk0 = static_cast<int64_t>(kt) * BN + 32 * wave;

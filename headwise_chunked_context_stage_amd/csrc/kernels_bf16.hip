@@ -466,20 +466,21 @@ __device__ __forceinline__ bf16x8 col_frag(const TileAddr& ta, int r0, int n0) {
 // Copy rows [row0, row0 + nrows) of a [S][ld] bf16 matrix (128 columns from
 // `src`) into a tile; rows at or beyond S are zero.  NCH chunks of 16 bytes
 // per thread, thread t handling chunks t, t + 256, ...
-template <int NCH>
+template <int NCH, int NT = 256>
 struct TileLoad {
   u32x4 r[NCH];
   __device__ __forceinline__ void load(const u16* src, int64_t ld, int64_t row0, int64_t S, int first) {
-    const int row = first >> 4, c = first & 15;  // rows row, row + 16, ... (256 chunks apart)
+    constexpr int RSTEP = NT / 16;                // rows between a thread's chunks
+    const int row = first >> 4, c = first & 15;  // rows row, row + RSTEP, ...
     const u16* p = src + (row0 + row) * ld + c * 8;
-    const int64_t left = S - row0 - row;          // rows of this thread still inside S: m * 16 < left
+    const int64_t left = S - row0 - row;          // rows of this thread still inside S: m * RSTEP < left
 #pragma unroll
-    for (int m = 0; m < NCH; ++m) r[m] = 16 * m < left ? ld16(p + 16 * m * ld) : u32x4{0, 0, 0, 0};
+    for (int m = 0; m < NCH; ++m) r[m] = RSTEP * m < left ? ld16(p + RSTEP * m * ld) : u32x4{0, 0, 0, 0};
   }
   __device__ __forceinline__ void store(u16* tile, int first) const {
 #pragma unroll
     for (int m = 0; m < NCH; ++m) {
-      const int e = first + 256 * m, row = e >> 4, c = e & 15;
+      const int e = first + NT * m, row = e >> 4, c = e & 15;
       st16(tile + toff(row, c * 8), r[m]);
     }
   }
@@ -670,66 +671,70 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(AttnArgs a) {
   if (row < a.S && part == 0) a.dd[static_cast<int64_t>(u) * a.S + row] = acc;
 }
 
-// ---- dK, dV.  Workgroup: 128 key rows of one KV head (4 waves x 32 keys),
-// looping over the stage's query heads of that group (ascending) and over
-// 64-row query tiles.  Each wave computes S = Q K^T and dP = dO V^T with the
-// key in the lane (registers = query rows), so P^T and dS^T are A operands
-// straight from registers; dV += P^T dO and dK += dS^T Q read dO and Q as
-// column operands of the same row-major tiles.  The fp32 sums stay in
+// ---- dK, dV.  Workgroup: 128 key rows of one KV head, looping over the
+// stage's query heads of that group (ascending) and over 64-row query tiles.
+// Eight waves: each 32-key block has a pair of waves on one SIMD.  With the
+// key in the lane (registers = query rows), the first wave of a pair computes
+// S = Q K^T, P = exp(S - LSE) and dV += P^T dO; the second computes
+// dP = dO V^T, dS = P (dP - D) with the first wave's fp32 P (exchanged
+// through LDS lane for lane) and dK += dS^T Q.  P^T and dS^T are A operands
+// straight from registers; dO and Q are read as column operands of the same
+// row-major tiles.  Each tile takes two barrier phases: in the first, the
+// second wave runs dK of the previous tile while the first wave evaluates the
+// exponentials, so the SIMD's matrix unit stays busy; in the second, the
+// first wave runs dV while the second forms dS.  The fp32 sums stay in
 // registers, and across the stages of a group in the fp32 carry buffers.
 namespace kv {
 constexpr int BN = 128, BM = 64;
-constexpr int TILE = BM * RS;
-constexpr int BUF = 2 * TILE;  // Q and dO tiles
-constexpr int NBUF = 2;        // double buffer: tile it (read), it + 1 (being filled)
+constexpr int TILE = BM * RS;  // one 64-row tile
+constexpr int NQ = 3;          // Q tiles it - 1 (dK), it (S), it + 1 (being filled)
+constexpr int NG = 2;          // dO tiles it (dP, dV), it + 1 (being filled)
 }  // namespace kv
 
-__global__ __launch_bounds__(256, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
+__global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
   using namespace kv;
-  __shared__ __attribute__((aligned(16))) u16 lds[NBUF * BUF];
-  __shared__ __attribute__((aligned(16))) u16 kvs[2 * BN * RS];  // this workgroup's K and V rows
-  __shared__ __attribute__((aligned(16))) float stat[NBUF][2][BM];  // [buffer][lse2, D][row]
+  __shared__ __attribute__((aligned(16))) u16 qs[NQ * TILE];
+  __shared__ __attribute__((aligned(16))) u16 gs[NG * TILE];
+  __shared__ __attribute__((aligned(16))) float stat[2][2][BM];  // [tile & 1][lse2, D][row]
+  __shared__ __attribute__((aligned(16))) f32x4 pxch[4][8][64];  // P of each key block: [block][reg/4][lane]
   const int64_t S = a.S;
   const int lid = xcd_snake(blockIdx.x, gridDim.x);
   const int kt = lid / nkv, gl = lid % nkv;  // key tile 0 (most work) first
   const int g = a.kv_head0 + gl;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, col = lane % 32, hf = lane / 32;
-  const int64_t wk0 = static_cast<int64_t>(kt) * BN + 32 * wave;
+  const int kb = wave & 3;      // key block of this wave (waves kb and kb + 4 share a SIMD)
+  const bool pwave = wave < 4;  // S, P, dV; the others dP, dS, dK
+  const int64_t wk0 = static_cast<int64_t>(kt) * BN + 32 * kb;
   const int64_t myk = wk0 + col;
   const float tau = 1.f / sqrtf(static_cast<float>(DH));
   const float c = kLog2e * tau;
   const int64_t ldo = static_cast<int64_t>(a.H) * DH;
 
-  // K and V rows of this workgroup stay in LDS for the whole kernel (as B
-  // operands of S = Q K^T and dP = dO V^T); this keeps 64 registers per lane
-  // free for the S/dP accumulators.
+  // K rows (first wave of a pair) or V rows (second) of this key block, as B operands.
+  bf16x8 kvf[8];
   {
-    const u16* K = static_cast<const u16*>(a.k) + static_cast<int64_t>(gl) * S * DH;
-    const u16* V = static_cast<const u16*>(a.v) + static_cast<int64_t>(gl) * S * DH;
-    TileLoad<8> lk, lv;
-    lk.load(K, DH, static_cast<int64_t>(kt) * BN, S, tid);
-    lv.load(V, DH, static_cast<int64_t>(kt) * BN, S, tid);
-    lk.store(kvs, tid);
-    lv.store(kvs + BN * RS, tid);
+    const u16* src = static_cast<const u16*>(pwave ? a.k : a.v) + static_cast<int64_t>(gl) * S * DH;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      kvf[t] = __builtin_bit_cast(bf16x8, myk < S ? ld16(src + myk * DH + 16 * t + 8 * hf) : u32x4{0, 0, 0, 0});
   }
-  const TileAddr kaddr = tile_addr(kvs + 32 * wave * RS, lane);
-  const TileAddr vaddr = tile_addr(kvs + BN * RS + 32 * wave * RS, lane);
 
-  // accumulators: C layout, lane = d column (within 32-block d4), registers = key rows
-  f32x16 dk[4], dv[4];
-  if (a.first_of_group) {
+  // dV (first wave) or dK (second) sums: C layout, lane = d column within
+  // the 32-column block d4, registers = key rows
+  f32x16 acc[4];
+  {
+    const float* carry = pwave ? a.dv_acc : a.dk_acc;
 #pragma unroll
-    for (int d4 = 0; d4 < 4; ++d4) dk[d4] = dv[d4] = zero16();
-  } else {
+    for (int d4 = 0; d4 < 4; ++d4) acc[d4] = zero16();
+    if (!a.first_of_group) {
 #pragma unroll
-    for (int d4 = 0; d4 < 4; ++d4)
+      for (int d4 = 0; d4 < 4; ++d4)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int64_t kr = wk0 + 8 * (i / 4) + 4 * hf + (i % 4);
-        const int64_t off = (static_cast<int64_t>(gl) * S + kr) * DH + 32 * d4 + col;
-        dk[d4][i] = kr < S ? a.dk_acc[off] : 0.f;
-        dv[d4][i] = kr < S ? a.dv_acc[off] : 0.f;
-      }
+        for (int i = 0; i < 16; ++i) {
+          const int64_t kr = wk0 + 8 * (i / 4) + 4 * hf + (i % 4);
+          if (kr < S) acc[d4][i] = carry[(static_cast<int64_t>(gl) * S + kr) * DH + 32 * d4 + col];
+        }
+    }
   }
 
   const int h_lo = max(a.q_head0, g * a.r), h_hi = min(a.q_head0 + a.nq, (g + 1) * a.r);
@@ -739,135 +744,164 @@ __global__ __launch_bounds__(256, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
   const int niter = (h_hi - h_lo) * per_head;
   auto tile_q0 = [&](int it) { return static_cast<int64_t>(qt0 + it % per_head) * BM; };
 
-  TileLoad<4> lq, lo;
-  float rs = 0.f;
+  // Tile it + 1 is loaded from global memory during tile it - 1 and written
+  // to LDS during tile it: each load has a whole tile of time to arrive.
+  TileLoad<2, 512> lq, lo;
+  float rs = 0.f;  // raw LSE (threads 0..63) or D (64..127) of the staged tile
   auto load = [&](int it) {
     const int h = h_lo + it / per_head;
     const int u = h - a.q_head0;
     const int64_t q0 = tile_q0(it);
     lq.load(static_cast<const u16*>(a.q) + static_cast<int64_t>(u) * S * DH, DH, q0, S, tid);
     lo.load(static_cast<const u16*>(a.dO) + static_cast<int64_t>(h) * DH, ldo, q0, S, tid);
-    if (tid < BM) {
-      const int64_t q = q0 + tid;
-      rs = q < S ? a.lse_in[static_cast<int64_t>(h) * S + q] * kLog2e : INFINITY;
-    } else if (tid < 2 * BM) {
-      const int64_t q = q0 + tid - BM;
-      rs = q < S ? a.dd[static_cast<int64_t>(u) * S + q] : 0.f;
+    if (tid < 2 * BM) {
+      const int64_t q = min(q0 + (tid % BM), S - 1);
+      rs = tid < BM ? a.lse_in[static_cast<int64_t>(h) * S + q] : a.dd[static_cast<int64_t>(u) * S + q];
     }
   };
-  auto store = [&](int b) {
-    lq.store(lds + b * BUF, tid);
-    lo.store(lds + b * BUF + TILE, tid);
-    if (tid < 2 * BM) stat[b][tid / BM][tid % BM] = rs;
+  auto store = [&](int it) {
+    lq.store(qs + (it % NQ) * TILE, tid);
+    lo.store(gs + (it % NG) * TILE, tid);
+    if (tid < 2 * BM) {
+      const bool in = tile_q0(it) + (tid % BM) < S;
+      stat[it & 1][tid / BM][tid % BM] = tid < BM ? (in ? rs * kLog2e : INFINITY) : (in ? rs : 0.f);
+    }
+  };
+  auto stage = [&](int it) {  // during tile it: tile it + 1 to LDS, tile it + 2 requested
+    if (it + 1 < niter) store(it + 1);
+    if (it + 2 < niter) load(it + 2);
+  };
+
+  // 32x64 C blocks of one tile: rows (query) x keys of this wave, two chains
+  // over the 128 head columns; row operands from LDS two steps ahead.
+  auto row_pass = [&](const TileAddr& xa, f32x16 (&sv)[2]) {
+    sv[0] = sv[1] = zero16();
+    bf16x8 fa[3][2];
+    auto row_ops = [&](int t, bf16x8 (&f)[2]) {
+      f[0] = row_frag(xa, 0, t);
+      f[1] = row_frag(xa, 1, t);
+    };
+    row_ops(0, fa[0]);
+    row_ops(1, fa[1]);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (t + 2 < 8) row_ops(t + 2, fa[(t + 2) % 3]);
+      __builtin_amdgcn_sched_barrier(0);
+      sv[0] = mfma(fa[t % 3][0], kvf[t], sv[0]);
+      sv[1] = mfma(fa[t % 3][1], kvf[t], sv[1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // acc += op^T Y over the 64 rows of a tile: Y read as column operands,
+  // step k4 outermost so the four accumulators alternate (each sums
+  // k4 = 0..3 in order); operands requested two groups ahead.
+  auto col_pass = [&](const TileAddr& ya, const bf16x8 (&op)[4]) {
+    bf16x8 fc[3];
+    auto col_op = [&](int gi) { return col_frag(ya, 16 * (gi / 4), 32 * (gi % 4)); };
+    fc[0] = col_op(0);
+    fc[1] = col_op(1);
+#pragma unroll
+    for (int gi = 0; gi < 16; ++gi) {
+      if (gi + 2 < 16) fc[(gi + 2) % 3] = col_op(gi + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      acc[gi % 4] = mfma(op[gi / 4], fc[gi % 3], acc[gi % 4]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   if (niter > 0) {
     load(0);
     store(0);
   }
+  if (niter > 1) load(1);
   __syncthreads();
-  for (int it = 0; it < niter; ++it) {
-    const int b = it % NBUF;
-    const TileAddr qa = tile_addr(lds + b * BUF, lane);
-    const TileAddr ga = tile_addr(lds + b * BUF + TILE, lane);
 
-    // S = Q K^T and dP = dO V^T: four MFMA chains; the LDS operands of step
-    // t + 1 are requested before the MFMAs of step t are issued.
-    f32x16 sacc[2] = {zero16(), zero16()}, dpacc[2] = {zero16(), zero16()};
-    bf16x8 fa[2][6];
-    auto row_ops = [&](int t, bf16x8 (&f)[6]) {
-      f[0] = row_frag(qa, 0, t);
-      f[1] = row_frag(qa, 1, t);
-      f[2] = row_frag(ga, 0, t);
-      f[3] = row_frag(ga, 1, t);
-      f[4] = row_frag(kaddr, 0, t);
-      f[5] = row_frag(vaddr, 0, t);
-    };
-    row_ops(0, fa[0]);
+  // Both waves of a pair run niter + 1 rounds of two barriers each.
+  if (pwave) {
+    for (int it = 0; it <= niter; ++it) {
+      bf16x8 op[4];  // P of tile it, packed
+      if (it < niter) {
+        // S = Q K^T; P = exp(S - LSE), masked above the diagonal; fp32 P to the partner
+        f32x16 sv[2];
+        row_pass(tile_addr(qs + (it % NQ) * TILE, lane), sv);
+        stage(it);
+        const int64_t q0 = tile_q0(it);
+        const bool need_mask = a.causal && q0 < wk0 + 31;
+        const int mlim = static_cast<int>(myk - q0);  // tile row r is masked when r < mlim
+        f32x4 l4[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      if (t + 1 < 8) row_ops(t + 1, fa[(t + 1) % 2]);
-      __builtin_amdgcn_sched_barrier(0);
-      sacc[0] = mfma(fa[t % 2][0], fa[t % 2][4], sacc[0]);
-      sacc[1] = mfma(fa[t % 2][1], fa[t % 2][4], sacc[1]);
-      dpacc[0] = mfma(fa[t % 2][2], fa[t % 2][5], dpacc[0]);
-      dpacc[1] = mfma(fa[t % 2][3], fa[t % 2][5], dpacc[1]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // next tile: global loads in flight during the softmax and dV/dK phases
-    if (it + 1 < niter) load(it + 1);
-
-    // P = exp(S - LSE), dS = P (dP - D), masked above the diagonal.
-    const int64_t q0 = tile_q0(it);
-    const bool need_mask = a.causal && q0 < wk0 + 31;
-    const int mlim = need_mask ? static_cast<int>(myk - q0) : -(1 << 30);  // row r masked when r < mlim
-    bf16x8 pa[4], dsa[4];
+        for (int j = 0; j < 8; ++j) l4[j] = *reinterpret_cast<const f32x4*>(&stat[it & 1][0][8 * j + 4 * hf]);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int r0 = 32 * qb + 8 * g4 + 4 * hf;  // tile rows r0..r0+3 = registers 4*g4..4*g4+3
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&stat[b][0][r0]);
-        const f32x4 d4v = *reinterpret_cast<const f32x4*>(&stat[b][1][r0]);
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int j = 4 * qb + g4, r0 = 8 * j + 4 * hf;  // tile rows r0..r0+3 = registers 4*g4..4*g4+3
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * g4 + e;
-          sacc[qb][i] = ex2(__builtin_fmaf(sacc[qb][i], c, -l4[e]));
-        }
-        if (need_mask) {  // wave-uniform: only tiles that cross the diagonal
+            for (int e = 0; e < 4; ++e) sv[qb][4 * g4 + e] = ex2(__builtin_fmaf(sv[qb][4 * g4 + e], c, -l4[j][e]));
+            if (need_mask) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (r0 + e < mlim) sacc[qb][4 * g4 + e] = 0.f;
-        }
+              for (int e = 0; e < 4; ++e)
+                if (r0 + e < mlim) sv[qb][4 * g4 + e] = 0.f;
+            }
+            pxch[kb][j][lane] = f32x4{sv[qb][4 * g4], sv[qb][4 * g4 + 1], sv[qb][4 * g4 + 2], sv[qb][4 * g4 + 3]};
+          }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * g4 + e;
-          dpacc[qb][i] = sacc[qb][i] * (dpacc[qb][i] - d4v[e]);
-        }
-        if (g4 & 1) {
-          pa[2 * qb + g4 / 2] = pack8(sacc[qb], g4 / 2);
-          dsa[2 * qb + g4 / 2] = pack8(dpacc[qb], g4 / 2);
-        }
+        for (int k4 = 0; k4 < 4; ++k4) op[k4] = pack8(sv[k4 / 2], k4 % 2);
       }
-
-    // dV += P^T dO and dK += dS^T Q: step k4 outermost, so eight independent
-    // accumulators alternate (each still sums k4 = 0..3 in order); the column
-    // operands of group gi + 1 are requested before group gi's MFMAs.
-    bf16x8 fc[2][2];
-    auto col_ops = [&](int gi, bf16x8 (&f)[2]) {
-      const int k4 = gi / 4, d4 = gi % 4;
-      f[0] = col_frag(ga, 16 * k4, 32 * d4);
-      f[1] = col_frag(qa, 16 * k4, 32 * d4);
-    };
-    col_ops(0, fc[0]);
-#pragma unroll
-    for (int gi = 0; gi < 16; ++gi) {
-      if (gi + 1 < 16) col_ops(gi + 1, fc[(gi + 1) % 2]);
-      __builtin_amdgcn_sched_barrier(0);
-      const int k4 = gi / 4, d4 = gi % 4;
-      dv[d4] = mfma(pa[k4], fc[gi % 2][0], dv[d4]);
-      dk[d4] = mfma(dsa[k4], fc[gi % 2][1], dk[d4]);
-      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      if (it < niter) col_pass(tile_addr(gs + (it % NG) * TILE, lane), op);  // dV += P^T dO
+      __syncthreads();
     }
-    if (it + 1 < niter) store((it + 1) % NBUF);
-    __syncthreads();
+  } else {
+    bf16x8 op[4];  // dS of the previous tile, packed
+    f32x16 sv[2];  // dP of the current tile
+    for (int it = 0; it <= niter; ++it) {
+      if (it < niter) {
+        row_pass(tile_addr(gs + (it % NG) * TILE, lane), sv);  // dP = dO V^T
+        stage(it);
+      }
+      if (it >= 1) col_pass(tile_addr(qs + ((it - 1) % NQ) * TILE, lane), op);  // dK += dS^T Q, tile it - 1
+      __syncthreads();
+      if (it < niter) {
+        // dS = P (dP - D) with the partner's fp32 P
+        f32x4 d4[8], p4[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          d4[j] = *reinterpret_cast<const f32x4*>(&stat[it & 1][1][8 * j + 4 * hf]);
+          p4[j] = pxch[kb][j][lane];
+        }
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int j = 4 * qb + g4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sv[qb][4 * g4 + e] = p4[j][e] * (sv[qb][4 * g4 + e] - d4[j][e]);
+          }
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) op[k4] = pack8(sv[k4 / 2], k4 % 2);
+      }
+      __syncthreads();
+    }
   }
 
+  {
+    float* carry = pwave ? a.dv_acc : a.dk_acc;
+    u16* out = static_cast<u16*>(pwave ? a.dv : a.dk);
+    const float scale = pwave ? 1.f : tau;
 #pragma unroll
-  for (int d4 = 0; d4 < 4; ++d4)
+    for (int d4 = 0; d4 < 4; ++d4)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int64_t kr = wk0 + 8 * (i / 4) + 4 * hf + (i % 4);
-      if (kr >= S) continue;
-      const int64_t off = (static_cast<int64_t>(gl) * S + kr) * DH + 32 * d4 + col;
-      if (a.last_of_group) {
-        static_cast<u16*>(a.dk)[off] = __builtin_bit_cast(u16, static_cast<__bf16>(dk[d4][i] * tau));
-        static_cast<u16*>(a.dv)[off] = __builtin_bit_cast(u16, static_cast<__bf16>(dv[d4][i]));
-      } else {
-        a.dk_acc[off] = dk[d4][i];
-        a.dv_acc[off] = dv[d4][i];
+      for (int i = 0; i < 16; ++i) {
+        const int64_t kr = wk0 + 8 * (i / 4) + 4 * hf + (i % 4);
+        if (kr >= S) continue;
+        const int64_t off = (static_cast<int64_t>(gl) * S + kr) * DH + 32 * d4 + col;
+        if (a.last_of_group)
+          out[off] = __builtin_bit_cast(u16, static_cast<__bf16>(acc[d4][i] * scale));
+        else
+          carry[off] = acc[d4][i];
       }
-    }
+  }
 }
 
 // ---- dQ.  Workgroup: 128 query rows of one head (4 waves x 32 rows); key
@@ -1050,7 +1084,7 @@ hipError_t bwd_pre(const AttnArgs& a, hipStream_t st) {
 hipError_t attn_dkv(const AttnArgs& a, hipStream_t st) {
   if (a.d != DH) return hipErrorInvalidValue;
   const int nkv = a.nq >= a.r ? a.nq / a.r : 1;
-  hipLaunchKernelGGL(attn_dkv_kernel, dim3(cdiv(a.S, kv::BN) * nkv), dim3(256), 0, st, a, nkv);
+  hipLaunchKernelGGL(attn_dkv_kernel, dim3(cdiv(a.S, kv::BN) * nkv), dim3(512), 0, st, a, nkv);
   return hipGetLastError();
 }
 

@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--U", type=int, default=None)
     ap.add_argument("--skip-cpu-baseline", action="store_true",
                     help="omit the oracle timing (profiling runs only)")
-    ap.add_argument("--cpu-baseline-S", type=int, default=6144)
+    ap.add_argument("--cpu-baseline-S", type=int, default=8192)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (HBM counter calibration)")
     return ap.parse_args()

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libupipe.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["plan.cpp", "capi.cpp", "kernels_f32.hip", "kernels_bf16.hip"]
+SOURCES = ["plan.cpp", "capi.cpp", "kernels_f32.hip", "kernels_bf16.hip", "kernels_dkv.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -22,7 +22,8 @@ COMMON = [
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # MFMA results in arch VGPRs: the softmax reads S/dP straight from the
-    # accumulators instead of copying them out of AGPRs
+    # accumulators instead of copying them out of AGPRs (the dK/dV kernel
+    # pins its long-lived sums to AGPRs explicitly)
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument",
 ]

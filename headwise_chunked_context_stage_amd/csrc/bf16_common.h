@@ -1,0 +1,200 @@
+// bf16_common.h -- shared device helpers of the bf16 kernels for gfx950
+// (CDNA4): MFMA wrapper, packing, XCD-aware workgroup order, and the LDS tile
+// layout with its two conflict-free read patterns used by the attention
+// kernels.  Included by each kernel source; everything has internal linkage.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace upipe {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int DH = 128;  // head dimension of the bf16 path
+
+__device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ bf16x8 frag(const u16* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+// Hardware exp2 (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> one dword of two bf16 (round to nearest even): v_cvt_pk_bf16_f32.
+__device__ __forceinline__ unsigned pack2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
+}
+
+// Registers 8t..8t+7 of a C block -> an 8-slot bf16 operand.
+__device__ __forceinline__ bf16x8 pack8(const f32x16& c, int t) {
+  u32x4 r;
+  r[0] = pack2(c[8 * t + 0], c[8 * t + 1]);
+  r[1] = pack2(c[8 * t + 2], c[8 * t + 3]);
+  r[2] = pack2(c[8 * t + 4], c[8 * t + 5]);
+  r[3] = pack2(c[8 * t + 6], c[8 * t + 7]);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// 8x8 bf16 transpose: in[j] = row j (8 elements), out[c] = column c.
+__device__ __forceinline__ void transpose8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int k = c / 2;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const unsigned a = in[2 * m][k], b = in[2 * m + 1][k];
+      out[c][m] = (c & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+    }
+  }
+}
+
+// Row (within a 16-row group) of slot m of the 8-slot half `hh`.
+__device__ __forceinline__ int slot_row(int hh, int m) { return m < 4 ? 4 * hh + m : 8 + 4 * hh + (m - 4); }
+
+// Map a workgroup id so that each XCD (ids are dealt round-robin over 8 XCDs)
+// runs one contiguous range of logical ids.
+__device__ __forceinline__ int xcd_remap(int id, int total) {
+  const int x = id % 8, local = id / 8;
+  const int per = total / 8, rem = total % 8;
+  return x * per + min(x, rem) + local;
+}
+
+// Rounds of 256 consecutive workgroup ids (one per CU at a time): within a
+// round, XCD x (ids are dealt round-robin over 8 XCDs) gets 32 consecutive
+// logical ids, and the order of the XCDs reverses every other round, so each
+// XCD's L2 serves neighbouring tiles while heavy and light tiles stay evenly
+// spread over the XCDs.  A trailing partial round keeps the identity map.
+__device__ __forceinline__ int xcd_snake(int id, int total) {
+  const int round = id >> 8, pos = id & 255;
+  if ((round << 8) + 256 > total) return id;
+  const int x = pos & 7, j = pos >> 3;
+  const int xx = (round & 1) ? 7 - x : x;
+  return (round << 8) + xx * 32 + j;
+}
+
+// ================================================================= attention
+// Tiles of 128-column bf16 rows live in LDS row-major with a padded row
+// stride (RS = 136 elements, 272 bytes: consecutive physical rows start 4
+// banks apart) and a fixed permutation of the rows inside every 16-row group:
+// logical row 8a + 4b + c (a, b in {0,1}, c < 4) sits at physical row
+// 4c + 2b + a.  Two read patterns are then free of bank conflicts and all
+// their addresses are affine (immediate offsets):
+//  * row operand (ds_read_b128): each lane reads 8 columns of its own row; 16
+//    consecutive logical rows are 16 distinct physical rows;
+//  * column operand (ds_read_b64_tr_b16): a 16-lane group reads 4 logical
+//    rows 4b..4b+3 (physical rows four apart, 16 banks apart) x 32 bytes, so
+//    the two groups of a half wave (columns 16 apart, 8 banks) interleave.
+// The transposing read gives lane i of each 16-lane group element (i % 4) of
+// the 8-byte rows addressed by lanes 4k + i/4 (k = 0..3).  When lane 4k + c of
+// the group addresses row R_k at columns n0 + 4c .. n0 + 4c + 3, lane i
+// receives column n0 + i of rows R_0..R_3: four k-slots of an MFMA operand
+// whose lane index is a column of the tile.  Two such reads fill the 8 slots
+// in the row order of a C block (rows 4h..4h+3, then 8+4h..8+4h+3 of each
+// 16-row step), so they pair with P or dS taken from registers.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+constexpr int RS = DH + 8;  // LDS row stride of attention tiles (elements)
+
+typedef __attribute__((address_space(3))) u16 lds_u16;
+
+__device__ __forceinline__ int prow(int q) {
+  return (q & ~15) | ((q & 3) << 2) | (((q >> 2) & 1) << 1) | ((q >> 3) & 1);
+}
+
+// Element offset of (logical row q, column col) in a tile.
+__device__ __forceinline__ int toff(int q, int col) { return prow(q) * RS + col; }
+
+// Per-lane base addresses of one tile for the two read patterns.  They are
+// passed through an empty asm so the compiler keeps exactly one register per
+// pattern and folds every fragment's constant offset into the instruction,
+// instead of hoisting one address register per fragment out of the loop.
+struct TileAddr {
+  const lds_u16* row;  // + (32*blk)*RS + 16*t: row operand of rows 32*blk + lane%32, columns 16t + 8h..
+  const lds_u16* col;  // + r0*RS + n0: column operand (first 4 slots; the other 4 are one row further)
+};
+__device__ __forceinline__ const lds_u16* opaque(const lds_u16* p) {
+  unsigned v = static_cast<unsigned>(reinterpret_cast<uintptr_t>(p));
+  asm volatile("" : "+v"(v));
+  return reinterpret_cast<const lds_u16*>(static_cast<uintptr_t>(v));
+}
+__device__ __forceinline__ TileAddr tile_addr(const u16* tile, int lane) {
+  const lds_u16* t = (const lds_u16*)tile;  // generic -> LDS address space
+  const int hf = lane >> 5, g16 = (lane >> 4) & 1, i16 = lane & 15;
+  TileAddr ta;
+  ta.row = opaque(t + prow(lane & 31) * RS + 8 * hf);
+  ta.col = opaque(t + prow(4 * hf + (i16 >> 2)) * RS + 16 * g16 + 4 * (i16 & 3));
+  return ta;
+}
+
+// Row operand: row 32*blk + lane%32, columns 16t + 8h .. 16t + 8h + 7.
+__device__ __forceinline__ bf16x8 row_frag(const TileAddr& ta, int blk, int t) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                                        ta.row + 32 * blk * RS + 16 * t));
+}
+
+// Column operand: column n0 + lane % 32 of the 16 rows r0 .. r0 + 15 (r0 a
+// multiple of 16), in the slot order of a C block (lane half h: rows
+// r0+4h..r0+4h+3, then r0+8+4h..r0+8+4h+3; the second set is one physical row
+// further).
+__device__ __forceinline__ bf16x8 col_frag(const TileAddr& ta, int r0, int n0) {
+  const lds_u16* p = ta.col + r0 * RS + n0;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) v4i16*>(const_cast<lds_u16*>(p)));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) v4i16*>(const_cast<lds_u16*>(p + RS)));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  const u32x4 w = {l2[0], l2[1], h2[0], h2[1]};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// Copy rows [row0, row0 + nrows) of a [S][ld] bf16 matrix (128 columns from
+// `src`) into a tile; rows at or beyond S are zero.  NCH chunks of 16 bytes
+// per thread, thread t handling chunks t, t + 256, ...
+template <int NCH, int NT = 256>
+struct TileLoad {
+  u32x4 r[NCH];
+  __device__ __forceinline__ void load(const u16* src, int64_t ld, int64_t row0, int64_t S, int first) {
+    constexpr int RSTEP = NT / 16;                // rows between a thread's chunks
+    const int row = first >> 4, c = first & 15;  // rows row, row + RSTEP, ...
+    const u16* p = src + (row0 + row) * ld + c * 8;
+    const int64_t left = S - row0 - row;          // rows of this thread still inside S: m * RSTEP < left
+#pragma unroll
+    for (int m = 0; m < NCH; ++m) r[m] = RSTEP * m < left ? ld16(p + RSTEP * m * ld) : u32x4{0, 0, 0, 0};
+  }
+  __device__ __forceinline__ void store(u16* tile, int first) const {
+#pragma unroll
+    for (int m = 0; m < NCH; ++m) {
+      const int e = first + NT * m, row = e >> 4, c = e & 15;
+      st16(tile + toff(row, c * 8), r[m]);
+    }
+  }
+};
+
+}  // namespace
+}  // namespace upipe

@@ -31,96 +31,10 @@
 #include <type_traits>
 
 #include "upipe_internal.h"
+#include "bf16_common.h"
 
 namespace upipe {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned short u16;
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr int DH = 128;  // head dimension of the bf16 path
-
-__device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
-__device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
-__device__ __forceinline__ bf16x8 frag(const u16* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
-}
-
-// Hardware exp2 (v_exp_f32); exp2(-inf) = 0.
-__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ f32x16 zero16() {
-  f32x16 z;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) z[i] = 0.f;
-  return z;
-}
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-// Two fp32 -> one dword of two bf16 (round to nearest even): v_cvt_pk_bf16_f32.
-__device__ __forceinline__ unsigned pack2(float lo, float hi) {
-  const f32x2 v = {lo, hi};
-  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
-}
-
-// Registers 8t..8t+7 of a C block -> an 8-slot bf16 operand.
-__device__ __forceinline__ bf16x8 pack8(const f32x16& c, int t) {
-  u32x4 r;
-  r[0] = pack2(c[8 * t + 0], c[8 * t + 1]);
-  r[1] = pack2(c[8 * t + 2], c[8 * t + 3]);
-  r[2] = pack2(c[8 * t + 4], c[8 * t + 5]);
-  r[3] = pack2(c[8 * t + 6], c[8 * t + 7]);
-  return __builtin_bit_cast(bf16x8, r);
-}
-
-// 8x8 bf16 transpose: in[j] = row j (8 elements), out[c] = column c.
-__device__ __forceinline__ void transpose8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int k = c / 2;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const unsigned a = in[2 * m][k], b = in[2 * m + 1][k];
-      out[c][m] = (c & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-    }
-  }
-}
-
-// Row (within a 16-row group) of slot m of the 8-slot half `hh`.
-__device__ __forceinline__ int slot_row(int hh, int m) { return m < 4 ? 4 * hh + m : 8 + 4 * hh + (m - 4); }
-
-// Map a workgroup id so that each XCD (ids are dealt round-robin over 8 XCDs)
-// runs one contiguous range of logical ids.
-__device__ __forceinline__ int xcd_remap(int id, int total) {
-  const int x = id % 8, local = id / 8;
-  const int per = total / 8, rem = total % 8;
-  return x * per + min(x, rem) + local;
-}
-
-// Rounds of 256 consecutive workgroup ids (one per CU at a time): within a
-// round, XCD x (ids are dealt round-robin over 8 XCDs) gets 32 consecutive
-// logical ids, and the order of the XCDs reverses every other round, so each
-// XCD's L2 serves neighbouring tiles while heavy and light tiles stay evenly
-// spread over the XCDs.  A trailing partial round keeps the identity map.
-__device__ __forceinline__ int xcd_snake(int id, int total) {
-  const int round = id >> 8, pos = id & 255;
-  if ((round << 8) + 256 > total) return id;
-  const int x = pos & 7, j = pos >> 3;
-  const int xx = (round & 1) ? 7 - x : x;
-  return (round << 8) + xx * 32 + j;
-}
 
 // ===================================================================== GEMMs
 // 128 x 128 output tile, 64-wide k steps, 4 waves as 2 x 2 (64 x 64 each),
@@ -233,21 +147,25 @@ __global__ __launch_bounds__(256, 2) void dw_kernel(const u16* __restrict__ X, i
   const int st = tid % 128, rg = st / 16, cc = st % 16;
   const bool isA = tid < 128;
 
-  u32x4 rr[8];
-  auto load = [&](int64_t s0) {
+  // One wave per SIMD for most of the launch (few output tiles, long k):
+  // global loads run three k-steps ahead through a ring of register sets,
+  // and LDS is double-buffered.
+  constexpr int NRR = 3;
+  u32x4 rr[NRR][8];
+  auto load = [&](int set, int64_t s0) {
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       const int64_t gi = s0 + rg * 8 + m;
       if (gi < S)
-        rr[m] = isA ? ld16(A + gi * DH + cc * 8) : ld16(X + gi * D + k0 + cc * 8);
+        rr[set][m] = isA ? ld16(A + gi * DH + cc * 8) : ld16(X + gi * D + k0 + cc * 8);
       else
-        rr[m] = u32x4{0, 0, 0, 0};
+        rr[set][m] = u32x4{0, 0, 0, 0};
     }
   };
-  auto store = [&](int b) {
+  auto store = [&](int set, int b) {
     u16* base = lds + b * GBUF + (isA ? 0 : GB * GS);
     u32x4 tc[8];
-    transpose8(rr, tc);
+    transpose8(rr[set], tc);
 #pragma unroll
     for (int c = 0; c < 8; ++c) st16(base + (cc * 8 + c) * GS + rg * 8, tc[c]);
   };
@@ -259,12 +177,16 @@ __global__ __launch_bounds__(256, 2) void dw_kernel(const u16* __restrict__ X, i
     for (int b = 0; b < 2; ++b) acc[a][b] = zero16();
 
   const int nk = static_cast<int>((S + GK - 1) / GK);
-  load(0);
-  store(0);
+  // k-step kb's data sits in register set kb % NRR until its LDS store
+  load(0, 0);
+  if (nk > 1) load(1, GK);
+  if (nk > 2) load(2, 2 * GK);
+  store(0, 0);
+  if (nk > 3) load(0, 3 * GK);
   __syncthreads();
-  for (int kb = 0; kb < nk; ++kb) {
+  auto body = [&](int kb, auto setc) {  // setc = (kb + 1) % NRR, a compile-time constant
+    constexpr int SN = decltype(setc)::value;
     const int cur = kb & 1;
-    if (kb + 1 < nk) load(static_cast<int64_t>(kb + 1) * GK);
     const u16* as = lds + cur * GBUF;
     const u16* xs = as + GB * GS;
 #pragma unroll
@@ -279,9 +201,19 @@ __global__ __launch_bounds__(256, 2) void dw_kernel(const u16* __restrict__ X, i
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma(fa[mb], fb[nb], acc[mb][nb]);
     }
-    if (kb + 1 < nk) store(cur ^ 1);
+    if (kb + 1 < nk) store(SN, cur ^ 1);
+    // the set just stored takes k-step kb + 1 + NRR
+    if (kb + 1 + NRR < nk) load(SN, static_cast<int64_t>(kb + 1 + NRR) * GK);
     __syncthreads();
+  };
+  int kb = 0;
+  for (; kb + NRR <= nk; kb += NRR) {
+    body(kb, std::integral_constant<int, 1>{});
+    body(kb + 1, std::integral_constant<int, 2>{});
+    body(kb + 2, std::integral_constant<int, 0>{});
   }
+  if (kb < nk) body(kb, std::integral_constant<int, 1>{});
+  if (kb + 1 < nk) body(kb + 1, std::integral_constant<int, 2>{});
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -386,105 +318,6 @@ __global__ __launch_bounds__(256, 2) void dx_kernel(float* __restrict__ dX, int6
         if (gi < S) dX[gi * D + k] = acc[mb][nb][i];
       }
 }
-
-// ================================================================= attention
-// Tiles of 128-column bf16 rows live in LDS row-major with a padded row
-// stride (RS = 136 elements, 272 bytes: consecutive physical rows start 4
-// banks apart) and a fixed permutation of the rows inside every 16-row group:
-// logical row 8a + 4b + c (a, b in {0,1}, c < 4) sits at physical row
-// 4c + 2b + a.  Two read patterns are then free of bank conflicts and all
-// their addresses are affine (immediate offsets):
-//  * row operand (ds_read_b128): each lane reads 8 columns of its own row; 16
-//    consecutive logical rows are 16 distinct physical rows;
-//  * column operand (ds_read_b64_tr_b16): a 16-lane group reads 4 logical
-//    rows 4b..4b+3 (physical rows four apart, 16 banks apart) x 32 bytes, so
-//    the two groups of a half wave (columns 16 apart, 8 banks) interleave.
-// The transposing read gives lane i of each 16-lane group element (i % 4) of
-// the 8-byte rows addressed by lanes 4k + i/4 (k = 0..3).  When lane 4k + c of
-// the group addresses row R_k at columns n0 + 4c .. n0 + 4c + 3, lane i
-// receives column n0 + i of rows R_0..R_3: four k-slots of an MFMA operand
-// whose lane index is a column of the tile.  Two such reads fill the 8 slots
-// in the row order of a C block (rows 4h..4h+3, then 8+4h..8+4h+3 of each
-// 16-row step), so they pair with P or dS taken from registers.
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
-
-constexpr int RS = DH + 8;  // LDS row stride of attention tiles (elements)
-
-typedef __attribute__((address_space(3))) u16 lds_u16;
-
-__device__ __forceinline__ int prow(int q) {
-  return (q & ~15) | ((q & 3) << 2) | (((q >> 2) & 1) << 1) | ((q >> 3) & 1);
-}
-
-// Element offset of (logical row q, column col) in a tile.
-__device__ __forceinline__ int toff(int q, int col) { return prow(q) * RS + col; }
-
-// Per-lane base addresses of one tile for the two read patterns.  They are
-// passed through an empty asm so the compiler keeps exactly one register per
-// pattern and folds every fragment's constant offset into the instruction,
-// instead of hoisting one address register per fragment out of the loop.
-struct TileAddr {
-  const lds_u16* row;  // + (32*blk)*RS + 16*t: row operand of rows 32*blk + lane%32, columns 16t + 8h..
-  const lds_u16* col;  // + r0*RS + n0: column operand (first 4 slots; the other 4 are one row further)
-};
-__device__ __forceinline__ const lds_u16* opaque(const lds_u16* p) {
-  unsigned v = static_cast<unsigned>(reinterpret_cast<uintptr_t>(p));
-  asm volatile("" : "+v"(v));
-  return reinterpret_cast<const lds_u16*>(static_cast<uintptr_t>(v));
-}
-__device__ __forceinline__ TileAddr tile_addr(const u16* tile, int lane) {
-  const lds_u16* t = (const lds_u16*)tile;  // generic -> LDS address space
-  const int hf = lane >> 5, g16 = (lane >> 4) & 1, i16 = lane & 15;
-  TileAddr ta;
-  ta.row = opaque(t + prow(lane & 31) * RS + 8 * hf);
-  ta.col = opaque(t + prow(4 * hf + (i16 >> 2)) * RS + 16 * g16 + 4 * (i16 & 3));
-  return ta;
-}
-
-// Row operand: row 32*blk + lane%32, columns 16t + 8h .. 16t + 8h + 7.
-__device__ __forceinline__ bf16x8 row_frag(const TileAddr& ta, int blk, int t) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-                                        ta.row + 32 * blk * RS + 16 * t));
-}
-
-// Column operand: column n0 + lane % 32 of the 16 rows r0 .. r0 + 15 (r0 a
-// multiple of 16), in the slot order of a C block (lane half h: rows
-// r0+4h..r0+4h+3, then r0+8+4h..r0+8+4h+3; the second set is one physical row
-// further).
-__device__ __forceinline__ bf16x8 col_frag(const TileAddr& ta, int r0, int n0) {
-  const lds_u16* p = ta.col + r0 * RS + n0;
-  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      reinterpret_cast<__attribute__((address_space(3))) v4i16*>(const_cast<lds_u16*>(p)));
-  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      reinterpret_cast<__attribute__((address_space(3))) v4i16*>(const_cast<lds_u16*>(p + RS)));
-  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-  const u32x4 w = {l2[0], l2[1], h2[0], h2[1]};
-  return __builtin_bit_cast(bf16x8, w);
-}
-
-// Copy rows [row0, row0 + nrows) of a [S][ld] bf16 matrix (128 columns from
-// `src`) into a tile; rows at or beyond S are zero.  NCH chunks of 16 bytes
-// per thread, thread t handling chunks t, t + 256, ...
-template <int NCH, int NT = 256>
-struct TileLoad {
-  u32x4 r[NCH];
-  __device__ __forceinline__ void load(const u16* src, int64_t ld, int64_t row0, int64_t S, int first) {
-    constexpr int RSTEP = NT / 16;                // rows between a thread's chunks
-    const int row = first >> 4, c = first & 15;  // rows row, row + RSTEP, ...
-    const u16* p = src + (row0 + row) * ld + c * 8;
-    const int64_t left = S - row0 - row;          // rows of this thread still inside S: m * RSTEP < left
-#pragma unroll
-    for (int m = 0; m < NCH; ++m) r[m] = RSTEP * m < left ? ld16(p + RSTEP * m * ld) : u32x4{0, 0, 0, 0};
-  }
-  __device__ __forceinline__ void store(u16* tile, int first) const {
-#pragma unroll
-    for (int m = 0; m < NCH; ++m) {
-      const int e = first + NT * m, row = e >> 4, c = e & 15;
-      st16(tile + toff(row, c * 8), r[m]);
-    }
-  }
-};
 
 // ---- forward.  Workgroup: 128 query rows of one head (4 waves x 32 rows);
 // key/value tiles of 64 rows, double-buffered.  Each wave computes
@@ -671,239 +504,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(AttnArgs a) {
   if (row < a.S && part == 0) a.dd[static_cast<int64_t>(u) * a.S + row] = acc;
 }
 
-// ---- dK, dV.  Workgroup: 128 key rows of one KV head, looping over the
-// stage's query heads of that group (ascending) and over 64-row query tiles.
-// Eight waves: each 32-key block has a pair of waves on one SIMD.  With the
-// key in the lane (registers = query rows), the first wave of a pair computes
-// S = Q K^T, P = exp(S - LSE) and dV += P^T dO; the second computes
-// dP = dO V^T, dS = P (dP - D) with the first wave's fp32 P (exchanged
-// through LDS lane for lane) and dK += dS^T Q.  P^T and dS^T are A operands
-// straight from registers; dO and Q are read as column operands of the same
-// row-major tiles.  Each tile takes two barrier phases: in the first, the
-// second wave runs dK of the previous tile while the first wave evaluates the
-// exponentials, so the SIMD's matrix unit stays busy; in the second, the
-// first wave runs dV while the second forms dS.  The fp32 sums stay in
-// registers, and across the stages of a group in the fp32 carry buffers.
-namespace kv {
-constexpr int BN = 128, BM = 64;
-constexpr int TILE = BM * RS;  // one 64-row tile
-constexpr int NQ = 3;          // Q tiles it - 1 (dK), it (S), it + 1 (being filled)
-constexpr int NG = 2;          // dO tiles it (dP, dV), it + 1 (being filled)
-}  // namespace kv
-
-__global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
-  using namespace kv;
-  __shared__ __attribute__((aligned(16))) u16 qs[NQ * TILE];
-  __shared__ __attribute__((aligned(16))) u16 gs[NG * TILE];
-  __shared__ __attribute__((aligned(16))) float stat[2][2][BM];  // [tile & 1][lse2, D][row]
-  __shared__ __attribute__((aligned(16))) f32x4 pxch[4][8][64];  // P of each key block: [block][reg/4][lane]
-  const int64_t S = a.S;
-  const int lid = xcd_snake(blockIdx.x, gridDim.x);
-  const int kt = lid / nkv, gl = lid % nkv;  // key tile 0 (most work) first
-  const int g = a.kv_head0 + gl;
-  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, col = lane % 32, hf = lane / 32;
-  const int kb = wave & 3;      // key block of this wave (waves kb and kb + 4 share a SIMD)
-  const bool pwave = wave < 4;  // S, P, dV; the others dP, dS, dK
-  const int64_t wk0 = static_cast<int64_t>(kt) * BN + 32 * kb;
-  const int64_t myk = wk0 + col;
-  const float tau = 1.f / sqrtf(static_cast<float>(DH));
-  const float c = kLog2e * tau;
-  const int64_t ldo = static_cast<int64_t>(a.H) * DH;
-
-  // K rows (first wave of a pair) or V rows (second) of this key block, as B operands.
-  bf16x8 kvf[8];
-  {
-    const u16* src = static_cast<const u16*>(pwave ? a.k : a.v) + static_cast<int64_t>(gl) * S * DH;
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-      kvf[t] = __builtin_bit_cast(bf16x8, myk < S ? ld16(src + myk * DH + 16 * t + 8 * hf) : u32x4{0, 0, 0, 0});
-  }
-
-  // dV (first wave) or dK (second) sums: C layout, lane = d column within
-  // the 32-column block d4, registers = key rows
-  f32x16 acc[4];
-  {
-    const float* carry = pwave ? a.dv_acc : a.dk_acc;
-#pragma unroll
-    for (int d4 = 0; d4 < 4; ++d4) acc[d4] = zero16();
-    if (!a.first_of_group) {
-#pragma unroll
-      for (int d4 = 0; d4 < 4; ++d4)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int64_t kr = wk0 + 8 * (i / 4) + 4 * hf + (i % 4);
-          if (kr < S) acc[d4][i] = carry[(static_cast<int64_t>(gl) * S + kr) * DH + 32 * d4 + col];
-        }
-    }
-  }
-
-  const int h_lo = max(a.q_head0, g * a.r), h_hi = min(a.q_head0 + a.nq, (g + 1) * a.r);
-  const int nqt = static_cast<int>((S + BM - 1) / BM);
-  const int qt0 = a.causal ? static_cast<int>((static_cast<int64_t>(kt) * BN) / BM) : 0;
-  const int per_head = nqt - qt0;
-  const int niter = (h_hi - h_lo) * per_head;
-  auto tile_q0 = [&](int it) { return static_cast<int64_t>(qt0 + it % per_head) * BM; };
-
-  // Tile it + 1 is loaded from global memory during tile it - 1 and written
-  // to LDS during tile it: each load has a whole tile of time to arrive.
-  TileLoad<2, 512> lq, lo;
-  float rs = 0.f;  // raw LSE (threads 0..63) or D (64..127) of the staged tile
-  auto load = [&](int it) {
-    const int h = h_lo + it / per_head;
-    const int u = h - a.q_head0;
-    const int64_t q0 = tile_q0(it);
-    lq.load(static_cast<const u16*>(a.q) + static_cast<int64_t>(u) * S * DH, DH, q0, S, tid);
-    lo.load(static_cast<const u16*>(a.dO) + static_cast<int64_t>(h) * DH, ldo, q0, S, tid);
-    if (tid < 2 * BM) {
-      const int64_t q = min(q0 + (tid % BM), S - 1);
-      rs = tid < BM ? a.lse_in[static_cast<int64_t>(h) * S + q] : a.dd[static_cast<int64_t>(u) * S + q];
-    }
-  };
-  auto store = [&](int it) {
-    lq.store(qs + (it % NQ) * TILE, tid);
-    lo.store(gs + (it % NG) * TILE, tid);
-    if (tid < 2 * BM) {
-      const bool in = tile_q0(it) + (tid % BM) < S;
-      stat[it & 1][tid / BM][tid % BM] = tid < BM ? (in ? rs * kLog2e : INFINITY) : (in ? rs : 0.f);
-    }
-  };
-  auto stage = [&](int it) {  // during tile it: tile it + 1 to LDS, tile it + 2 requested
-    if (it + 1 < niter) store(it + 1);
-    if (it + 2 < niter) load(it + 2);
-  };
-
-  // 32x64 C blocks of one tile: rows (query) x keys of this wave, two chains
-  // over the 128 head columns; row operands from LDS two steps ahead.
-  auto row_pass = [&](const TileAddr& xa, f32x16 (&sv)[2]) {
-    sv[0] = sv[1] = zero16();
-    bf16x8 fa[3][2];
-    auto row_ops = [&](int t, bf16x8 (&f)[2]) {
-      f[0] = row_frag(xa, 0, t);
-      f[1] = row_frag(xa, 1, t);
-    };
-    row_ops(0, fa[0]);
-    row_ops(1, fa[1]);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      if (t + 2 < 8) row_ops(t + 2, fa[(t + 2) % 3]);
-      __builtin_amdgcn_sched_barrier(0);
-      sv[0] = mfma(fa[t % 3][0], kvf[t], sv[0]);
-      sv[1] = mfma(fa[t % 3][1], kvf[t], sv[1]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  // acc += op^T Y over the 64 rows of a tile: Y read as column operands,
-  // step k4 outermost so the four accumulators alternate (each sums
-  // k4 = 0..3 in order); operands requested two groups ahead.
-  auto col_pass = [&](const TileAddr& ya, const bf16x8 (&op)[4]) {
-    bf16x8 fc[3];
-    auto col_op = [&](int gi) { return col_frag(ya, 16 * (gi / 4), 32 * (gi % 4)); };
-    fc[0] = col_op(0);
-    fc[1] = col_op(1);
-#pragma unroll
-    for (int gi = 0; gi < 16; ++gi) {
-      if (gi + 2 < 16) fc[(gi + 2) % 3] = col_op(gi + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      acc[gi % 4] = mfma(op[gi / 4], fc[gi % 3], acc[gi % 4]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  if (niter > 0) {
-    load(0);
-    store(0);
-  }
-  if (niter > 1) load(1);
-  __syncthreads();
-
-  // Both waves of a pair run niter + 1 rounds of two barriers each.
-  if (pwave) {
-    for (int it = 0; it <= niter; ++it) {
-      bf16x8 op[4];  // P of tile it, packed
-      if (it < niter) {
-        // S = Q K^T; P = exp(S - LSE), masked above the diagonal; fp32 P to the partner
-        f32x16 sv[2];
-        row_pass(tile_addr(qs + (it % NQ) * TILE, lane), sv);
-        stage(it);
-        const int64_t q0 = tile_q0(it);
-        const bool need_mask = a.causal && q0 < wk0 + 31;
-        const int mlim = static_cast<int>(myk - q0);  // tile row r is masked when r < mlim
-        f32x4 l4[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) l4[j] = *reinterpret_cast<const f32x4*>(&stat[it & 1][0][8 * j + 4 * hf]);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int j = 4 * qb + g4, r0 = 8 * j + 4 * hf;  // tile rows r0..r0+3 = registers 4*g4..4*g4+3
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sv[qb][4 * g4 + e] = ex2(__builtin_fmaf(sv[qb][4 * g4 + e], c, -l4[j][e]));
-            if (need_mask) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (r0 + e < mlim) sv[qb][4 * g4 + e] = 0.f;
-            }
-            pxch[kb][j][lane] = f32x4{sv[qb][4 * g4], sv[qb][4 * g4 + 1], sv[qb][4 * g4 + 2], sv[qb][4 * g4 + 3]};
-          }
-#pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) op[k4] = pack8(sv[k4 / 2], k4 % 2);
-      }
-      __syncthreads();
-      if (it < niter) col_pass(tile_addr(gs + (it % NG) * TILE, lane), op);  // dV += P^T dO
-      __syncthreads();
-    }
-  } else {
-    bf16x8 op[4];  // dS of the previous tile, packed
-    f32x16 sv[2];  // dP of the current tile
-    for (int it = 0; it <= niter; ++it) {
-      if (it < niter) {
-        row_pass(tile_addr(gs + (it % NG) * TILE, lane), sv);  // dP = dO V^T
-        stage(it);
-      }
-      if (it >= 1) col_pass(tile_addr(qs + ((it - 1) % NQ) * TILE, lane), op);  // dK += dS^T Q, tile it - 1
-      __syncthreads();
-      if (it < niter) {
-        // dS = P (dP - D) with the partner's fp32 P
-        f32x4 d4[8], p4[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          d4[j] = *reinterpret_cast<const f32x4*>(&stat[it & 1][1][8 * j + 4 * hf]);
-          p4[j] = pxch[kb][j][lane];
-        }
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int j = 4 * qb + g4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sv[qb][4 * g4 + e] = p4[j][e] * (sv[qb][4 * g4 + e] - d4[j][e]);
-          }
-#pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) op[k4] = pack8(sv[k4 / 2], k4 % 2);
-      }
-      __syncthreads();
-    }
-  }
-
-  {
-    float* carry = pwave ? a.dv_acc : a.dk_acc;
-    u16* out = static_cast<u16*>(pwave ? a.dv : a.dk);
-    const float scale = pwave ? 1.f : tau;
-#pragma unroll
-    for (int d4 = 0; d4 < 4; ++d4)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int64_t kr = wk0 + 8 * (i / 4) + 4 * hf + (i % 4);
-        if (kr >= S) continue;
-        const int64_t off = (static_cast<int64_t>(gl) * S + kr) * DH + 32 * d4 + col;
-        if (a.last_of_group)
-          out[off] = __builtin_bit_cast(u16, static_cast<__bf16>(acc[d4][i] * scale));
-        else
-          carry[off] = acc[d4][i];
-      }
-  }
-}
-
 // ---- dQ.  Workgroup: 128 query rows of one head (4 waves x 32 rows); key
 // tiles of 64 rows.  Orientation as in the forward (lane = query row): S^T
 // and dP^T from registers Q, dO against K and V row operands, then
@@ -1078,13 +678,6 @@ hipError_t attn_fwd(const AttnArgs& a, hipStream_t st) {
 hipError_t bwd_pre(const AttnArgs& a, hipStream_t st) {
   if (a.d != DH) return hipErrorInvalidValue;
   hipLaunchKernelGGL(bwd_pre_kernel, dim3(cdiv(a.S, 16), a.nq), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
-
-hipError_t attn_dkv(const AttnArgs& a, hipStream_t st) {
-  if (a.d != DH) return hipErrorInvalidValue;
-  const int nkv = a.nq >= a.r ? a.nq / a.r : 1;
-  hipLaunchKernelGGL(attn_dkv_kernel, dim3(cdiv(a.S, kv::BN) * nkv), dim3(512), 0, st, a, nkv);
   return hipGetLastError();
 }
 

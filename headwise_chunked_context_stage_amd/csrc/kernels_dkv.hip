@@ -1,0 +1,261 @@
+// kernels_dkv.hip -- dK/dV pass of the attention backward for gfx950 (CDNA4).
+//
+// Backward of the per-stage attention (paper.rainbus.top summary of "Untied
+// Ulysses", section 方法步骤详情 step (3); flash formulation): with the key in
+// the lane, P = exp(S - LSE) and dS = P (dP - D) are recomputed per query
+// tile, and dV += P^T dO, dK += dS^T Q accumulate in registers.
+#include <hip/hip_runtime.h>
+
+#include "upipe_internal.h"
+#include "bf16_common.h"
+
+namespace upipe {
+namespace {
+
+// ---- dK, dV.  Workgroup: 128 key rows of one KV head, looping over the
+// stage's query heads of that group (ascending) and over 64-row query tiles.
+// Eight waves: each 32-key block has a pair of waves on one SIMD.  With the
+// key in the lane (registers = query rows), the first wave of a pair computes
+// S = Q K^T, P = exp(S - LSE) and dV += P^T dO; the second computes
+// dP = dO V^T, dS = P (dP - D) with the first wave's fp32 P (exchanged
+// through LDS lane for lane) and dK += dS^T Q.  P^T and dS^T are A operands
+// straight from registers; dO and Q are read as column operands of the same
+// row-major tiles.  Each tile takes two barrier phases: in the first, the
+// second wave runs dK of the previous tile while the first wave evaluates the
+// exponentials, so the SIMD's matrix unit stays busy; in the second, the
+// first wave runs dV while the second forms dS.  The fp32 sums stay in
+// registers, and across the stages of a group in the fp32 carry buffers.
+namespace kv {
+constexpr int BN = 128, BM = 64;
+constexpr int TILE = BM * RS;  // one 64-row tile
+constexpr int NQ = 3;          // Q tiles it - 1 (dK), it (S), it + 1 (being filled)
+constexpr int NG = 2;          // dO tiles it (dP, dV), it + 1 (being filled)
+}  // namespace kv
+
+__global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
+  using namespace kv;
+  __shared__ __attribute__((aligned(16))) u16 qs[NQ * TILE];
+  __shared__ __attribute__((aligned(16))) u16 gs[NG * TILE];
+  __shared__ __attribute__((aligned(16))) float stat[2][2][BM];  // [tile & 1][lse2, D][row]
+  __shared__ __attribute__((aligned(16))) f32x4 pxch[4][8][64];  // P of each key block: [block][reg/4][lane]
+  const int64_t S = a.S;
+  const int lid = xcd_snake(blockIdx.x, gridDim.x);
+  const int kt = lid / nkv, gl = lid % nkv;  // key tile 0 (most work) first
+  const int g = a.kv_head0 + gl;
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, col = lane % 32, hf = lane / 32;
+  const int kb = wave & 3;      // key block of this wave (waves kb and kb + 4 share a SIMD)
+  const bool pwave = wave < 4;  // S, P, dV; the others dP, dS, dK
+  const int64_t wk0 = static_cast<int64_t>(kt) * BN + 32 * kb;
+  const int64_t myk = wk0 + col;
+  const float tau = 1.f / sqrtf(static_cast<float>(DH));
+  const float c = kLog2e * tau;
+  const int64_t ldo = static_cast<int64_t>(a.H) * DH;
+
+  // K rows (first wave of a pair) or V rows (second) of this key block, as B operands.
+  bf16x8 kvf[8];
+  {
+    const u16* src = static_cast<const u16*>(pwave ? a.k : a.v) + static_cast<int64_t>(gl) * S * DH;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      kvf[t] = __builtin_bit_cast(bf16x8, myk < S ? ld16(src + myk * DH + 16 * t + 8 * hf) : u32x4{0, 0, 0, 0});
+  }
+
+  // dV (first wave) or dK (second) sums: C layout, lane = d column within
+  // the 32-column block d4, registers = key rows
+  f32x16 acc[4];
+  {
+    const float* carry = pwave ? a.dv_acc : a.dk_acc;
+#pragma unroll
+    for (int d4 = 0; d4 < 4; ++d4) acc[d4] = zero16();
+    if (!a.first_of_group) {
+#pragma unroll
+      for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int64_t kr = wk0 + 8 * (i / 4) + 4 * hf + (i % 4);
+          if (kr < S) acc[d4][i] = carry[(static_cast<int64_t>(gl) * S + kr) * DH + 32 * d4 + col];
+        }
+    }
+  }
+
+  const int h_lo = max(a.q_head0, g * a.r), h_hi = min(a.q_head0 + a.nq, (g + 1) * a.r);
+  const int nqt = static_cast<int>((S + BM - 1) / BM);
+  const int qt0 = a.causal ? static_cast<int>((static_cast<int64_t>(kt) * BN) / BM) : 0;
+  const int per_head = nqt - qt0;
+  const int niter = (h_hi - h_lo) * per_head;
+  auto tile_q0 = [&](int it) { return static_cast<int64_t>(qt0 + it % per_head) * BM; };
+
+  // Tile it + 1 is loaded from global memory during tile it - 1 and written
+  // to LDS during tile it: each load has a whole tile of time to arrive.
+  TileLoad<2, 512> lq, lo;
+  float rs = 0.f;  // raw LSE (threads 0..63) or D (64..127) of the staged tile
+  auto load = [&](int it) {
+    const int h = h_lo + it / per_head;
+    const int u = h - a.q_head0;
+    const int64_t q0 = tile_q0(it);
+    lq.load(static_cast<const u16*>(a.q) + static_cast<int64_t>(u) * S * DH, DH, q0, S, tid);
+    lo.load(static_cast<const u16*>(a.dO) + static_cast<int64_t>(h) * DH, ldo, q0, S, tid);
+    if (tid < 2 * BM) {
+      const int64_t q = min(q0 + (tid % BM), S - 1);
+      rs = tid < BM ? a.lse_in[static_cast<int64_t>(h) * S + q] : a.dd[static_cast<int64_t>(u) * S + q];
+    }
+  };
+  auto store = [&](int it) {
+    lq.store(qs + (it % NQ) * TILE, tid);
+    lo.store(gs + (it % NG) * TILE, tid);
+    if (tid < 2 * BM) {
+      const bool in = tile_q0(it) + (tid % BM) < S;
+      stat[it & 1][tid / BM][tid % BM] = tid < BM ? (in ? rs * kLog2e : INFINITY) : (in ? rs : 0.f);
+    }
+  };
+  auto stage = [&](int it) {  // during tile it: tile it + 1 to LDS, tile it + 2 requested
+    if (it + 1 < niter) store(it + 1);
+    if (it + 2 < niter) load(it + 2);
+  };
+
+  // 32x64 C blocks of one tile: rows (query) x keys of this wave, two chains
+  // over the 128 head columns; row operands from LDS two steps ahead.
+  auto row_pass = [&](const TileAddr& xa, f32x16 (&sv)[2]) {
+    sv[0] = sv[1] = zero16();
+    bf16x8 fa[3][2];
+    auto row_ops = [&](int t, bf16x8 (&f)[2]) {
+      f[0] = row_frag(xa, 0, t);
+      f[1] = row_frag(xa, 1, t);
+    };
+    row_ops(0, fa[0]);
+    row_ops(1, fa[1]);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (t + 2 < 8) row_ops(t + 2, fa[(t + 2) % 3]);
+      __builtin_amdgcn_sched_barrier(0);
+      sv[0] = mfma(fa[t % 3][0], kvf[t], sv[0]);
+      sv[1] = mfma(fa[t % 3][1], kvf[t], sv[1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // acc += op^T Y over the 64 rows of a tile: Y read as column operands,
+  // step k4 outermost so the four accumulators alternate (each sums
+  // k4 = 0..3 in order); operands requested two groups ahead.
+  auto col_pass = [&](const TileAddr& ya, const bf16x8 (&op)[4]) {
+    bf16x8 fc[3];
+    auto col_op = [&](int gi) { return col_frag(ya, 16 * (gi / 4), 32 * (gi % 4)); };
+    fc[0] = col_op(0);
+    fc[1] = col_op(1);
+#pragma unroll
+    for (int gi = 0; gi < 16; ++gi) {
+      if (gi + 2 < 16) fc[(gi + 2) % 3] = col_op(gi + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      acc[gi % 4] = mfma(op[gi / 4], fc[gi % 3], acc[gi % 4]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  if (niter > 0) {
+    load(0);
+    store(0);
+  }
+  if (niter > 1) load(1);
+  __syncthreads();
+
+  // Both waves of a pair run niter + 1 rounds of two barriers each.
+  if (pwave) {
+    for (int it = 0; it <= niter; ++it) {
+      bf16x8 op[4];  // P of tile it, packed
+      if (it < niter) {
+        // S = Q K^T; P = exp(S - LSE), masked above the diagonal; fp32 P to the partner
+        f32x16 sv[2];
+        row_pass(tile_addr(qs + (it % NQ) * TILE, lane), sv);
+        stage(it);
+        const int64_t q0 = tile_q0(it);
+        const bool need_mask = a.causal && q0 < wk0 + 31;
+        const int mlim = static_cast<int>(myk - q0);  // tile row r is masked when r < mlim
+        f32x4 l4[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) l4[j] = *reinterpret_cast<const f32x4*>(&stat[it & 1][0][8 * j + 4 * hf]);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int j = 4 * qb + g4, r0 = 8 * j + 4 * hf;  // tile rows r0..r0+3 = registers 4*g4..4*g4+3
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sv[qb][4 * g4 + e] = ex2(__builtin_fmaf(sv[qb][4 * g4 + e], c, -l4[j][e]));
+            if (need_mask) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (r0 + e < mlim) sv[qb][4 * g4 + e] = 0.f;
+            }
+            pxch[kb][j][lane] = f32x4{sv[qb][4 * g4], sv[qb][4 * g4 + 1], sv[qb][4 * g4 + 2], sv[qb][4 * g4 + 3]};
+          }
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) op[k4] = pack8(sv[k4 / 2], k4 % 2);
+      }
+      __syncthreads();
+      if (it < niter) col_pass(tile_addr(gs + (it % NG) * TILE, lane), op);  // dV += P^T dO
+      __syncthreads();
+    }
+  } else {
+    bf16x8 op[4];  // dS of the previous tile, packed
+    f32x16 sv[2];  // dP of the current tile
+    for (int it = 0; it <= niter; ++it) {
+      if (it < niter) {
+        row_pass(tile_addr(gs + (it % NG) * TILE, lane), sv);  // dP = dO V^T
+        stage(it);
+      }
+      if (it >= 1) col_pass(tile_addr(qs + ((it - 1) % NQ) * TILE, lane), op);  // dK += dS^T Q, tile it - 1
+      __syncthreads();
+      if (it < niter) {
+        // dS = P (dP - D) with the partner's fp32 P
+        f32x4 d4[8], p4[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          d4[j] = *reinterpret_cast<const f32x4*>(&stat[it & 1][1][8 * j + 4 * hf]);
+          p4[j] = pxch[kb][j][lane];
+        }
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int j = 4 * qb + g4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sv[qb][4 * g4 + e] = p4[j][e] * (sv[qb][4 * g4 + e] - d4[j][e]);
+          }
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) op[k4] = pack8(sv[k4 / 2], k4 % 2);
+      }
+      __syncthreads();
+    }
+  }
+
+  {
+    float* carry = pwave ? a.dv_acc : a.dk_acc;
+    u16* out = static_cast<u16*>(pwave ? a.dv : a.dk);
+    const float scale = pwave ? 1.f : tau;
+#pragma unroll
+    for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t kr = wk0 + 8 * (i / 4) + 4 * hf + (i % 4);
+        if (kr >= S) continue;
+        const int64_t off = (static_cast<int64_t>(gl) * S + kr) * DH + 32 * d4 + col;
+        if (a.last_of_group)
+          out[off] = __builtin_bit_cast(u16, static_cast<__bf16>(acc[d4][i] * scale));
+        else
+          carry[off] = acc[d4][i];
+      }
+  }
+}
+
+}  // namespace
+
+namespace bf16 {
+
+hipError_t attn_dkv(const AttnArgs& a, hipStream_t st) {
+  if (a.d != DH) return hipErrorInvalidValue;
+  const int nkv = a.nq >= a.r ? a.nq / a.r : 1;
+  const unsigned nkt = static_cast<unsigned>((a.S + kv::BN - 1) / kv::BN);
+  hipLaunchKernelGGL(attn_dkv_kernel, dim3(nkt * nkv), dim3(512), 0, st, a, nkv);
+  return hipGetLastError();
+}
+
+}  // namespace bf16
+}  // namespace upipe

@@ -27,7 +27,7 @@ import torch
 
 import oracle
 from headwise_chunked_context_stage_amd import upipe
-from headwise_chunked_context_stage_amd.layer import run
+from headwise_chunked_context_stage_amd.layer import alloc_outputs, backward, forward, run
 from headwise_chunked_context_stage_amd.synth import CONFIGS, LayerShape, make_inputs, to_numpy_exact
 
 from bf16_floor import bf16_path_emulation
@@ -226,13 +226,20 @@ def test_causal_invariance_bitwise():
 
 
 # ---------------------------------------------------------------- full size
+def chunked_ip(a, b, rows=1 << 16):
+    """<a, b> accumulated in fp64 over row blocks (bounded temporaries at S = 1M)."""
+    tot = 0.0
+    for i in range(0, a.shape[0], rows):
+        tot += float((a[i:i + rows].double() * b[i:i + rows].double()).sum())
+    return tot
+
+
 def identities(out, inp):
     """Scaling identities that hold for the exact layer at any size:
     <dWv,Wv> = <dO,O>, <dWq,Wq> = <dWk,Wk>, <dX,X> = sum <dW,W>.
     Returns the three relative discrepancies (normalised by norm products)."""
-    f = lambda t: t.double()
-    ip = lambda a, b: float((f(a) * f(b)).sum())
-    nn = lambda a, b: float(f(a).norm() * f(b).norm())
+    ip = chunked_ip
+    nn = lambda a, b: math.sqrt(ip(a, a) * ip(b, b))
     e1 = abs(ip(out["dWv"], inp["Wv"]) - ip(inp["dO"], out["O"])) / nn(inp["dO"], out["O"])
     e2 = abs(ip(out["dWq"], inp["Wq"]) - ip(out["dWk"], inp["Wk"])) / (
         nn(out["dWq"], inp["Wq"]) + nn(out["dWk"], inp["Wk"]))
@@ -242,7 +249,10 @@ def identities(out, inp):
 
 
 def sampled_rows_check(shape, inp, out, rows_all, rows_late, late_heads):
-    np_in = [to_numpy_exact(inp[k]) for k in ("X", "Wq", "Wk", "Wv")]
+    """Forward rows against the oracle.  With causal masking row i depends only
+    on X rows 0..i, so the oracle gets X[:max_row + 1] (a shorter sequence)."""
+    n = max(rows_all + rows_late) + 1
+    np_in = [to_numpy_exact(inp["X"][:n])] + [to_numpy_exact(inp[k]) for k in ("Wq", "Wk", "Wv")]
     O = out["O"]
     LSE = out["LSE"]
     for rows, heads in ((rows_all, (0, shape.H)), (rows_late, late_heads)):
@@ -256,6 +266,24 @@ def sampled_rows_check(shape, inp, out, rows_all, rows_late, late_heads):
         compare("O", got_o, Or[:, c0:c1], 2e-2, 2e-3)
         assert np.isfinite(Or[:, c0:c1]).all()
         compare("LSE", got_l, Lr[heads[0]:heads[1]], 2e-2, 2e-3)
+
+
+def run_measured(shape, U, inp):
+    """fwd + bwd with the device high-water mark taken around the calls: the
+    library allocates nothing, so the only intermediate memory is the
+    caller's workspace of peak_bytes()."""
+    plan = upipe.Plan(shape.S, shape.D, shape.H, shape.G, shape.d, U, causal=True, dtype="bf16")
+    out = alloc_outputs(plan, inp["X"].device)
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    forward(plan, inp, out)
+    backward(plan, inp, out)
+    torch.cuda.synchronize()
+    assert torch.cuda.max_memory_allocated() == base, "device memory allocated during the calls"
+    assert out["ws"].numel() == plan.peak_bytes
+    out.pop("ws")
+    return out, (plan.peak_bytes_phase(0), plan.peak_bytes_phase(1))
 
 
 def test_full_size_llama8b_s32k_U_invariant():
@@ -288,6 +316,58 @@ def test_full_size_llama8b_s128k_bench_config():
     S = shape.S
     sampled_rows_check(shape, inp, out, [0, 1, 100, 1023, 1024, 2047],
                        [S - 1, S - 2, S - 129, S - 4096], (0, 4))
+    e = identities(out, inp)
+    say("  identities %.2e %.2e %.2e" % e)
+    assert max(e) < 1e-4
+    for k in OUTS:
+        assert torch.isfinite(out[k]).all(), k
+
+
+def test_full_size_qwen32b_s64k_U_invariant_and_peak_bytes():
+    """Qwen3-32B attention shape: bit-exact across U in {1, 8, 64}, forward rows
+    against the oracle, the scaling identities, and the stage workspace: the
+    QKV region is 2*S*d*(U + 2*kv_s) bytes, so U = 8 needs 1/8 of U = 64 (the
+    pages' 12 vs 96 S*d_head per device, 87.5% less; paper.rainbus.top summary
+    of "Untied Ulysses", sections 核心方法 and 复现评估)."""
+    cfg = CONFIGS["qwen32b_s64k"]
+    shape = cfg["shape"]
+    S, d, r = shape.S, shape.d, shape.H // shape.G
+    inp = make_inputs(shape, "bf16", seed=0, device="cuda")
+    first, ws = None, {}
+    for U in cfg["U"]:
+        say("qwen32b S=65536 U=%d" % U)
+        out, ws[U] = run_measured(shape, U, inp)
+        say("  workspace fwd %d bwd %d bytes" % ws[U])
+        assert ws[U][0] == 2 * S * d * (U + 2 * max(1, U // r))
+        if first is None:
+            first = out
+            sampled_rows_check(shape, inp, out, [0, 1, 100, 1023, 1024, 4095],
+                               [S - 1, S - 2, S - 1000], (0, r))
+            e = identities(out, inp)
+            say("  identities %.2e %.2e %.2e" % e)
+            assert max(e) < 1e-4
+            for k in OUTS:
+                assert torch.isfinite(out[k]).all(), k
+        else:
+            assert_same_bits(first, out, "U=%d" % U)
+            del out
+        torch.cuda.empty_cache()
+    assert 8 * ws[8][0] == ws[64][0]
+
+
+def test_full_size_llama8b_share_s1m():
+    """One GPU's share of Llama3-8B at S = 1M tokens (4 query heads + 1 KV
+    head, U = 1): forward rows against the oracle (early rows of all heads
+    and rows near 64K), the scaling identities, finite outputs and the
+    measured workspace."""
+    cfg = CONFIGS["llama8b_share_s1m"]
+    shape = cfg["shape"]
+    inp = make_inputs(shape, "bf16", seed=0, device="cuda")
+    say("llama8b share S=1048576 U=1")
+    out, ws = run_measured(shape, 1, inp)
+    say("  workspace fwd %d bwd %d bytes" % ws)
+    assert ws[0] == 2 * shape.S * shape.d * 3
+    sampled_rows_check(shape, inp, out, [0, 1, 1023, 4095], [65535, 65534, 32767], (0, 4))
     e = identities(out, inp)
     say("  identities %.2e %.2e %.2e" % e)
     assert max(e) < 1e-4

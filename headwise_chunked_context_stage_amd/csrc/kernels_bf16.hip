@@ -130,40 +130,50 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(const u16* __restrict__ X,
 
 // ---- weight gradient: dW[c][k] = sum_i A[i][c] X[i][k] (one chunk, K = S).
 // Both operands are read with i along the k-slots, so both tiles are staged
-// transposed (identity slot order).
-__global__ __launch_bounds__(256, 2) void dw_kernel(const u16* __restrict__ X, int64_t S, int64_t D,
+// transposed (identity slot order).  A launch has few output tiles and a long
+// contraction, so each workgroup splits K: two groups of four waves sum the
+// first and the second half of the k-steps (the split point depends on S
+// only), and the halves are added in that order through LDS.
+__global__ __launch_bounds__(512, 1) void dw_kernel(const u16* __restrict__ X, int64_t S, int64_t D,
                                                     ChunkTable t, int ncb) {
-  __shared__ __attribute__((aligned(16))) u16 lds[2 * GBUF];
+  __shared__ __attribute__((aligned(16))) u16 lds[2][2 * GBUF];  // [group][buffer]
   const int total = ncb * t.n;
   const int lid = xcd_remap(blockIdx.x, total);
   const int cb = lid / t.n, ch = lid % t.n;
   const u16* A = static_cast<const u16*>(t.a[ch]);
   float* dW = t.dw[ch];
   const int64_t k0 = static_cast<int64_t>(cb) * GB;  // column block of D
-  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, col = lane % 32, hf = lane / 32;
+  const int grp = threadIdx.x / 256, tid = threadIdx.x % 256;
+  const int wave = tid / 64, lane = tid % 64, col = lane % 32, hf = lane / 32;
   const int wm = wave / 2, wn = wave % 2;
-  // staging role: threads 0..127 stage A (rows of S x 128 head columns),
-  // 128..255 stage X (rows of S x 128 columns of D); each one 8x8 block.
+  // staging role: threads 0..127 of a group stage A (rows of S x 128 head
+  // columns), 128..255 stage X (rows of S x 128 columns of D); each one 8x8 block.
   const int st = tid % 128, rg = st / 16, cc = st % 16;
   const bool isA = tid < 128;
+  u16* gl = lds[grp];
 
-  // One wave per SIMD for most of the launch (few output tiles, long k):
-  // global loads run three k-steps ahead through a ring of register sets,
-  // and LDS is double-buffered.
+  // Global loads run three k-steps ahead through a ring of register sets;
+  // LDS is double-buffered.
   constexpr int NRR = 3;
   u32x4 rr[NRR][8];
-  auto load = [&](int set, int64_t s0) {
+  const int nk_all = static_cast<int>((S + GK - 1) / GK);
+  const int half = (nk_all + 1) / 2;
+  const int kfirst = grp ? half : 0;                  // first k-step of this group
+  const int nk = grp ? nk_all - half : half;          // k-steps of this group
+  const int nk_max = half;                            // rounds run by both groups
+  auto load = [&](int set, int kb) {
+    const int64_t s0 = static_cast<int64_t>(kfirst + kb) * GK;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       const int64_t gi = s0 + rg * 8 + m;
-      if (gi < S)
+      if (kb < nk && gi < S)
         rr[set][m] = isA ? ld16(A + gi * DH + cc * 8) : ld16(X + gi * D + k0 + cc * 8);
       else
         rr[set][m] = u32x4{0, 0, 0, 0};
     }
   };
   auto store = [&](int set, int b) {
-    u16* base = lds + b * GBUF + (isA ? 0 : GB * GS);
+    u16* base = gl + b * GBUF + (isA ? 0 : GB * GS);
     u32x4 tc[8];
     transpose8(rr[set], tc);
 #pragma unroll
@@ -176,54 +186,77 @@ __global__ __launch_bounds__(256, 2) void dw_kernel(const u16* __restrict__ X, i
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = zero16();
 
-  const int nk = static_cast<int>((S + GK - 1) / GK);
-  // k-step kb's data sits in register set kb % NRR until its LDS store
+  // k-step kb's data sits in register set kb % NRR until its LDS store.
+  // Steps beyond a group's range load zeros and are not accumulated.
   load(0, 0);
-  if (nk > 1) load(1, GK);
-  if (nk > 2) load(2, 2 * GK);
+  load(1, 1);
+  load(2, 2);
   store(0, 0);
-  if (nk > 3) load(0, 3 * GK);
+  load(0, 3);
   __syncthreads();
   auto body = [&](int kb, auto setc) {  // setc = (kb + 1) % NRR, a compile-time constant
     constexpr int SN = decltype(setc)::value;
     const int cur = kb & 1;
-    const u16* as = lds + cur * GBUF;
-    const u16* xs = as + GB * GS;
+    if (kb < nk) {
+      const u16* as = gl + cur * GBUF;
+      const u16* xs = as + GB * GS;
 #pragma unroll
-    for (int t4 = 0; t4 < GK / 16; ++t4) {
-      bf16x8 fa[2], fb[2];
+      for (int t4 = 0; t4 < GK / 16; ++t4) {
+        bf16x8 fa[2], fb[2];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) fa[mb] = frag(as + (64 * wm + 32 * mb + col) * GS + 16 * t4 + 8 * hf);
+        for (int mb = 0; mb < 2; ++mb) fa[mb] = frag(as + (64 * wm + 32 * mb + col) * GS + 16 * t4 + 8 * hf);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) fb[nb] = frag(xs + (64 * wn + 32 * nb + col) * GS + 16 * t4 + 8 * hf);
+        for (int nb = 0; nb < 2; ++nb) fb[nb] = frag(xs + (64 * wn + 32 * nb + col) * GS + 16 * t4 + 8 * hf);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma(fa[mb], fb[nb], acc[mb][nb]);
+          for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma(fa[mb], fb[nb], acc[mb][nb]);
+      }
     }
-    if (kb + 1 < nk) store(SN, cur ^ 1);
+    if (kb + 1 < nk_max) store(SN, cur ^ 1);
     // the set just stored takes k-step kb + 1 + NRR
-    if (kb + 1 + NRR < nk) load(SN, static_cast<int64_t>(kb + 1 + NRR) * GK);
+    if (kb + 1 + NRR < nk_max) load(SN, kb + 1 + NRR);
     __syncthreads();
   };
   int kb = 0;
-  for (; kb + NRR <= nk; kb += NRR) {
+  for (; kb + NRR <= nk_max; kb += NRR) {
     body(kb, std::integral_constant<int, 1>{});
     body(kb + 1, std::integral_constant<int, 2>{});
     body(kb + 2, std::integral_constant<int, 0>{});
   }
-  if (kb < nk) body(kb, std::integral_constant<int, 1>{});
-  if (kb + 1 < nk) body(kb + 1, std::integral_constant<int, 2>{});
+  if (kb < nk_max) body(kb, std::integral_constant<int, 1>{});
+  if (kb + 1 < nk_max) body(kb + 1, std::integral_constant<int, 2>{});
+
+  // second half to LDS (fp32, C layout per lane), then first + second in that order
+  float* red = reinterpret_cast<float*>(lds[1]);  // 64 KB of the second group's buffers
+  if (grp == 1) {
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int c = 64 * wm + 32 * mb + 8 * (i / 4) + 4 * hf + (i % 4);
-        const int64_t k = k0 + 64 * wn + 32 * nb + col;
-        dW[static_cast<int64_t>(c) * D + k] = acc[mb][nb][i];
-      }
+        for (int i4 = 0; i4 < 4; ++i4)
+          *reinterpret_cast<f32x4*>(red + (((wave * 4 + mb * 2 + nb) * 4 + i4) * 64 + lane) * 4) =
+              f32x4{acc[mb][nb][4 * i4], acc[mb][nb][4 * i4 + 1], acc[mb][nb][4 * i4 + 2], acc[mb][nb][4 * i4 + 3]};
+  }
+  __syncthreads();
+  if (grp == 0) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x4 o = *reinterpret_cast<const f32x4*>(red + (((wave * 4 + mb * 2 + nb) * 4 + i4) * 64 + lane) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * i4 + e;
+            const int c = 64 * wm + 32 * mb + 8 * (i / 4) + 4 * hf + (i % 4);
+            const int64_t k = k0 + 64 * wn + 32 * nb + col;
+            dW[static_cast<int64_t>(c) * D + k] = acc[mb][nb][i] + o[e];
+          }
+        }
+  }
 }
 
 // ---- input gradient: dX[i][k] += sum over chunks (table order) of
@@ -657,7 +690,7 @@ hipError_t proj(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t,
 hipError_t dw(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t, hipStream_t st) {
   if (d != DH || D % GB != 0) return hipErrorInvalidValue;
   const int ncb = static_cast<int>(D / GB);
-  hipLaunchKernelGGL(dw_kernel, dim3(ncb * t.n), dim3(256), 0, st, static_cast<const u16*>(X), S, D,
+  hipLaunchKernelGGL(dw_kernel, dim3(ncb * t.n), dim3(512), 0, st, static_cast<const u16*>(X), S, D,
                      t, ncb);
   return hipGetLastError();
 }

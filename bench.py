@@ -74,9 +74,15 @@ def kernel_work(kind, S, D, d, U, r, causal=True):
     return 0.0, "flop"
 
 
+KERNEL_SOURCES = ("bf16_common.h", "kernels_bf16.hip", "kernels_dkv.hip")
+
+
 def source_sha():
-    p = os.path.join(ROOT, "headwise_chunked_context_stage_amd", "csrc", "kernels_bf16.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    """First 16 hex digits of the sha256 over the bf16 kernel sources."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, "headwise_chunked_context_stage_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_for(kernel):
@@ -226,6 +232,18 @@ def main():
         roof = {"kernel": dominant, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic_for(dominant),
                 "work_per_launch": dwork, "avg_launch_ms": dk["avg_launch_ms"]}
+
+    # measured dense-MFMA ceiling of this chip (every CU, 2 waves per SIMD):
+    # context for frac, which stays against the published peak
+    ceiling = upipe.upipe_mfma_ceiling(2)
+    roof["measured_mfma_ceiling"] = ceiling
+    if dunit == "flop":
+        roof["frac_of_measured_ceiling"] = roof["achieved"] / ceiling
+    for k, ent in kernels.items():
+        if "tflops" in ent:
+            ent["frac_of_peak"] = ent["tflops"] / PEAK_BF16_TFLOPS
+        if k == "dx":  # fp32 dX read-modify-write per stage launch, against HBM
+            ent["dX_rmw_gbps"] = 8.0 * S * D / (ent["avg_launch_ms"] * 1e-3) / 1e9
 
     peak_by_u = {}
     for u in cfg["U"] + (1, H):

@@ -345,6 +345,13 @@ int upipe_timing_read(double* ms, int64_t* launches, int n) {
   return rc;
 }
 
+int upipe_mfma_ceiling(int waves_per_simd, int iters, double* tflops, void* stream) {
+  if (!tflops || waves_per_simd < 1 || waves_per_simd > 2 || iters < 8) return UPIPE_ERR_ARG;
+  return bf16::mfma_ceiling(waves_per_simd, iters, tflops, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? UPIPE_OK
+             : UPIPE_ERR_HIP;
+}
+
 const char* upipe_kernel_name(int kind) {
   static const char* names[UPIPE_K_COUNT] = {"proj", "attn_fwd", "bwd_pre", "attn_dkv",
                                              "attn_dq", "dw", "dx", "fill"};

@@ -673,6 +673,34 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnArgs a) {
   }
 }
 
+// ---- dense MFMA stream: four independent accumulator chains per wave,
+// operands in registers.  The result is stored only when iters < 0 (never),
+// which keeps the products live without any memory traffic.
+__global__ __launch_bounds__(256) void mfma_ceiling_kernel(float* sink, int iters) {
+  const unsigned lane = threadIdx.x % 64;
+  bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = static_cast<__bf16>(static_cast<float>((lane + e) % 7) * 0.125f);
+    b[e] = static_cast<__bf16>(static_cast<float>((lane * 3 + e) % 5) * 0.25f);
+  }
+  f32x16 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = zero16();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = mfma(a, b, acc[i]);
+  }
+  if (iters < 0) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s += acc[i][e];
+    sink[threadIdx.x] = s;
+  }
+}
+
 inline unsigned cdiv(int64_t a, int64_t b) { return static_cast<unsigned>((a + b - 1) / b); }
 
 }  // namespace
@@ -712,6 +740,35 @@ hipError_t bwd_pre(const AttnArgs& a, hipStream_t st) {
   if (a.d != DH) return hipErrorInvalidValue;
   hipLaunchKernelGGL(bwd_pre_kernel, dim3(cdiv(a.S, 16), a.nq), dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+hipError_t mfma_ceiling(int waves_per_simd, int iters, double* tflops, hipStream_t st) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  hipEvent_t t0, t1;
+  if ((e = hipEventCreate(&t0)) != hipSuccess) return e;
+  if ((e = hipEventCreate(&t1)) != hipSuccess) {
+    (void)hipEventDestroy(t0);
+    return e;
+  }
+  const unsigned grid = static_cast<unsigned>(cus * waves_per_simd);  // 4 waves per block = 1 per SIMD
+  hipLaunchKernelGGL(mfma_ceiling_kernel, dim3(grid), dim3(256), 0, st, nullptr, iters / 8);  // warm-up
+  e = hipEventRecord(t0, st);
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(mfma_ceiling_kernel, dim3(grid), dim3(256), 0, st, nullptr, iters);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) e = hipEventRecord(t1, st);
+  if (e == hipSuccess) e = hipEventSynchronize(t1);
+  float ms = 0.f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, t0, t1);
+  (void)hipEventDestroy(t0);
+  (void)hipEventDestroy(t1);
+  if (e == hipSuccess)
+    *tflops = static_cast<double>(grid) * 4 * iters * 4 * 32768.0 / (static_cast<double>(ms) * 1e-3) / 1e12;
+  return e;
 }
 
 hipError_t attn_dq(const AttnArgs& a, hipStream_t st) {

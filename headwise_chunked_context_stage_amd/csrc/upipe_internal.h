@@ -100,6 +100,8 @@ hipError_t attn_dkv(const AttnArgs& a, hipStream_t st);
 hipError_t attn_dq(const AttnArgs& a, hipStream_t st);
 hipError_t dw(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t, hipStream_t st);
 hipError_t dx(float* dX, int64_t S, int64_t D, int d, const ChunkTable& t, hipStream_t st);
+// dense MFMA stream on every CU; TFLOP/s (synchronous)
+hipError_t mfma_ceiling(int waves_per_simd, int iters, double* tflops, hipStream_t st);
 }  // namespace bf16
 namespace f32 {
 hipError_t proj(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t, hipStream_t st);

@@ -19,7 +19,7 @@ KERNEL_KINDS = ("proj", "attn_fwd", "bwd_pre", "attn_dkv", "attn_dq", "dw", "dx"
 
 EXPORTS = ("upipe_create", "upipe_destroy", "upipe_peak_bytes", "upipe_peak_bytes_phase",
            "upipe_fwd", "upipe_bwd", "upipe_strerror", "upipe_num_stages", "upipe_stage_info",
-           "upipe_timing_enable", "upipe_timing_read", "upipe_kernel_name")
+           "upipe_timing_enable", "upipe_timing_read", "upipe_kernel_name", "upipe_mfma_ceiling")
 
 _lib = None
 
@@ -64,6 +64,8 @@ def lib():
     L.upipe_timing_read.restype = i32
     L.upipe_kernel_name.argtypes = [i32]
     L.upipe_kernel_name.restype = ctypes.c_char_p
+    L.upipe_mfma_ceiling.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_double), vp]
+    L.upipe_mfma_ceiling.restype = i32
     _lib = L
     return L
 
@@ -181,6 +183,14 @@ def upipe_timing_read() -> dict:
 
 def upipe_kernel_name(kind: int) -> str:
     return lib().upipe_kernel_name(kind).decode()
+
+
+def upipe_mfma_ceiling(waves_per_simd: int = 2, iters: int = 1 << 14, stream=None) -> float:
+    """Measured dense bf16 MFMA TFLOP/s over every CU (synchronous)."""
+    out = ctypes.c_double(0.0)
+    _check(lib().upipe_mfma_ceiling(waves_per_simd, iters, ctypes.byref(out), _stream(stream)),
+           "upipe_mfma_ceiling")
+    return out.value
 
 
 class Plan:

@@ -129,6 +129,17 @@ int upipe_timing_enable(int on);
 int upipe_timing_read(double* ms, int64_t* launches, int n);
 const char* upipe_kernel_name(int kind);
 
+/* ---- measured matrix-core ceiling (for benchmarks) ----
+ * Runs a dense bf16 MFMA stream on every CU (v_mfma_f32_32x32x16_bf16, four
+ * independent accumulator chains per wave, operands in registers, no memory
+ * traffic) with `waves_per_simd` waves per SIMD (1..2), `iters` x 4 MFMAs per
+ * wave, on `stream` (a hipStream_t, may be null), waits for it, and writes
+ * the achieved TFLOP/s (2*32*32*16 flop per MFMA) to *tflops.  Allocates no
+ * device memory.  UPIPE_ERR_ARG for bad arguments, UPIPE_ERR_HIP on a HIP
+ * failure.  This is the practical ceiling the attention kernels are compared
+ * against next to the published dense peak. */
+int upipe_mfma_ceiling(int waves_per_simd, int iters, double* tflops, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

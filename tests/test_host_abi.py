@@ -35,6 +35,15 @@ def test_exports_every_declared_symbol():
         assert hasattr(L, name), name
 
 
+def test_mfma_ceiling_rejects_bad_arguments_before_any_device_call():
+    import ctypes
+    L = upipe.lib()
+    out = ctypes.c_double(0.0)
+    for w, it in ((0, 1024), (3, 1024), (1, 7), (-1, 1024)):
+        assert L.upipe_mfma_ceiling(w, it, ctypes.byref(out), None) == upipe.UPIPE_ERR_ARG
+    assert L.upipe_mfma_ceiling(2, 1024, None, None) == upipe.UPIPE_ERR_ARG
+
+
 def test_strerror():
     assert upipe.upipe_strerror(0) == "ok"
     for c in (1, 2, 3, 4):

@@ -141,6 +141,7 @@ BF16_CASES = [
     (2048, 1024, 4, 1),
     (768, 512, 8, 2),     # two groups of four
     (384, 256, 4, 4),     # MHA
+    (4096, 4096, 4, 1),   # one KV group of the Llama3-8B shape at full d_model
 ]
 
 

@@ -88,7 +88,7 @@ def source_sha():
 def traffic_for(kernel):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", "traffic.json")
+    p = os.path.join(ROOT, "profiles", "hbm_traffic_llama8b_s128k_U4.json")
     if not os.path.exists(p):
         return None
     try:

@@ -83,34 +83,81 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
   const int qt0 = a.causal ? static_cast<int>((static_cast<int64_t>(kt) * BN) / BM) : 0;
   const int per_head = nqt - qt0;
   const int niter = (h_hi - h_lo) * per_head;
-  auto tile_q0 = [&](int it) { return static_cast<int64_t>(qt0 + it % per_head) * BM; };
+  // Loop state, the same in every wave: tile t is query tile qt0 + t % per_head
+  // of head h_lo + t / per_head.  Cursors step through (head, query tile)
+  // without divisions; slot counters track t % NQ and t % NG.
+  struct Cur {
+    int h, qt;
+  };
+  auto adv = [&](Cur& x) {
+    if (++x.qt == nqt) {
+      x.qt = qt0;
+      ++x.h;
+    }
+  };
 
-  // Tile it + 1 is loaded from global memory during tile it - 1 and written
-  // to LDS during tile it: each load has a whole tile of time to arrive.
-  TileLoad<2, 512> lq, lo;
+  // Tile t + 1 is loaded from global memory during tile t - 1 and written to
+  // LDS during tile t: each load has a whole tile of time to arrive.  Thread
+  // tid stages rows srow and srow + 32, 16-byte chunk sc, of the Q and dO
+  // tiles; its offsets are fixed.
+  const int srow = tid >> 4, sc = tid & 15;
+  const int qoff = srow * DH + sc * 8;
+  const int goff = srow * static_cast<int>(ldo) + sc * 8;
+  const int loff0 = toff(srow, sc * 8), loff1 = toff(srow + 32, sc * 8);
+  u32x4 rq[2], rg[2];
   float rs = 0.f;  // raw LSE (threads 0..63) or D (64..127) of the staged tile
-  auto load = [&](int it) {
-    const int h = h_lo + it / per_head;
-    const int u = h - a.q_head0;
-    const int64_t q0 = tile_q0(it);
-    lq.load(static_cast<const u16*>(a.q) + static_cast<int64_t>(u) * S * DH, DH, q0, S, tid);
-    lo.load(static_cast<const u16*>(a.dO) + static_cast<int64_t>(h) * DH, ldo, q0, S, tid);
+  auto load = [&](const Cur& x) {
+    const int u = x.h - a.q_head0;
+    const int64_t q0 = static_cast<int64_t>(x.qt) * BM;
+    const u16* qb = static_cast<const u16*>(a.q) + (static_cast<int64_t>(u) * S + q0) * DH;
+    const u16* gb = static_cast<const u16*>(a.dO) + q0 * ldo + static_cast<int64_t>(x.h) * DH;
+    if (q0 + BM <= S) {  // whole tile inside the sequence (uniform)
+      rq[0] = ld16(qb + qoff);
+      rq[1] = ld16(qb + qoff + 32 * DH);
+      rg[0] = ld16(gb + goff);
+      rg[1] = ld16(gb + goff + 32 * ldo);
+    } else {  // last tile of a head: rows at or beyond S are zero
+      const int64_t left = S - q0 - srow;
+      rq[0] = 0 < left ? ld16(qb + qoff) : u32x4{0, 0, 0, 0};
+      rq[1] = 32 < left ? ld16(qb + qoff + 32 * DH) : u32x4{0, 0, 0, 0};
+      rg[0] = 0 < left ? ld16(gb + goff) : u32x4{0, 0, 0, 0};
+      rg[1] = 32 < left ? ld16(gb + goff + 32 * ldo) : u32x4{0, 0, 0, 0};
+    }
     if (tid < 2 * BM) {
       const int64_t q = min(q0 + (tid % BM), S - 1);
-      rs = tid < BM ? a.lse_in[static_cast<int64_t>(h) * S + q] : a.dd[static_cast<int64_t>(u) * S + q];
+      rs = tid < BM ? a.lse_in[static_cast<int64_t>(x.h) * S + q] : a.dd[static_cast<int64_t>(u) * S + q];
     }
   };
-  auto store = [&](int it) {
-    lq.store(qs + (it % NQ) * TILE, tid);
-    lo.store(gs + (it % NG) * TILE, tid);
+  auto store = [&](int slq, int slg, int qt) {
+    u16* qd = qs + slq * TILE;
+    u16* gd = gs + slg * TILE;
+    st16(qd + loff0, rq[0]);
+    st16(qd + loff1, rq[1]);
+    st16(gd + loff0, rg[0]);
+    st16(gd + loff1, rg[1]);
     if (tid < 2 * BM) {
-      const bool in = tile_q0(it) + (tid % BM) < S;
-      stat[it & 1][tid / BM][tid % BM] = tid < BM ? (in ? rs * kLog2e : INFINITY) : (in ? rs : 0.f);
+      const bool in = static_cast<int64_t>(qt) * BM + (tid % BM) < S;
+      stat[slg][tid / BM][tid % BM] = tid < BM ? (in ? rs * kLog2e : INFINITY) : (in ? rs : 0.f);
     }
   };
+  Cur cc{h_lo, qt0};  // tile it
+  Cur lc = cc;        // tile it + 2 (next to load)
+  adv(lc);
+  adv(lc);
+  int sq = 0, sg = 0;  // it % NQ, it % NG
   auto stage = [&](int it) {  // during tile it: tile it + 1 to LDS, tile it + 2 requested
-    if (it + 1 < niter) store(it + 1);
-    if (it + 2 < niter) load(it + 2);
+    if (it + 1 < niter) {
+      Cur n = cc;
+      adv(n);
+      store(sq + 1 == NQ ? 0 : sq + 1, sg ^ 1, n.qt);
+    }
+    if (it + 2 < niter) load(lc);
+  };
+  auto next_tile = [&]() {  // end of a round: tile it + 1 becomes current
+    adv(cc);
+    adv(lc);
+    sq = sq + 1 == NQ ? 0 : sq + 1;
+    sg ^= 1;
   };
 
   // 32x64 C blocks of one tile: rows (query) x keys of this wave, two chains
@@ -151,10 +198,14 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
   };
 
   if (niter > 0) {
-    load(0);
-    store(0);
+    load(cc);
+    store(0, 0, cc.qt);
   }
-  if (niter > 1) load(1);
+  if (niter > 1) {
+    Cur n = cc;
+    adv(n);
+    load(n);
+  }
   __syncthreads();
 
   // Both waves of a pair run niter + 1 rounds of two barriers each.
@@ -164,14 +215,14 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
       if (it < niter) {
         // S = Q K^T; P = exp(S - LSE), masked above the diagonal; fp32 P to the partner
         f32x16 sv[2];
-        row_pass(tile_addr(qs + (it % NQ) * TILE, lane), sv);
+        row_pass(tile_addr(qs + sq * TILE, lane), sv);
         stage(it);
-        const int64_t q0 = tile_q0(it);
+        const int64_t q0 = static_cast<int64_t>(cc.qt) * BM;
         const bool need_mask = a.causal && q0 < wk0 + 31;
         const int mlim = static_cast<int>(myk - q0);  // tile row r is masked when r < mlim
         f32x4 l4[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) l4[j] = *reinterpret_cast<const f32x4*>(&stat[it & 1][0][8 * j + 4 * hf]);
+        for (int j = 0; j < 8; ++j) l4[j] = *reinterpret_cast<const f32x4*>(&stat[sg][0][8 * j + 4 * hf]);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -190,25 +241,26 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
         for (int k4 = 0; k4 < 4; ++k4) op[k4] = pack8(sv[k4 / 2], k4 % 2);
       }
       __syncthreads();
-      if (it < niter) col_pass(tile_addr(gs + (it % NG) * TILE, lane), op);  // dV += P^T dO
+      if (it < niter) col_pass(tile_addr(gs + sg * TILE, lane), op);  // dV += P^T dO
       __syncthreads();
+      next_tile();
     }
   } else {
     bf16x8 op[4];  // dS of the previous tile, packed
     f32x16 sv[2];  // dP of the current tile
     for (int it = 0; it <= niter; ++it) {
       if (it < niter) {
-        row_pass(tile_addr(gs + (it % NG) * TILE, lane), sv);  // dP = dO V^T
+        row_pass(tile_addr(gs + sg * TILE, lane), sv);  // dP = dO V^T
         stage(it);
       }
-      if (it >= 1) col_pass(tile_addr(qs + ((it - 1) % NQ) * TILE, lane), op);  // dK += dS^T Q, tile it - 1
+      if (it >= 1) col_pass(tile_addr(qs + (sq == 0 ? NQ - 1 : sq - 1) * TILE, lane), op);  // dK += dS^T Q, tile it - 1
       __syncthreads();
       if (it < niter) {
         // dS = P (dP - D) with the partner's fp32 P
         f32x4 d4[8], p4[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          d4[j] = *reinterpret_cast<const f32x4*>(&stat[it & 1][1][8 * j + 4 * hf]);
+          d4[j] = *reinterpret_cast<const f32x4*>(&stat[sg][1][8 * j + 4 * hf]);
           p4[j] = pxch[kb][j][lane];
         }
 #pragma unroll
@@ -223,6 +275,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
         for (int k4 = 0; k4 < 4; ++k4) op[k4] = pack8(sv[k4 / 2], k4 % 2);
       }
       __syncthreads();
+      next_tile();
     }
   }
 

@@ -352,19 +352,20 @@ __global__ __launch_bounds__(256, 2) void dx_kernel(float* __restrict__ dX, int6
       }
 }
 
-// ---- forward.  Workgroup: 128 query rows of one head (4 waves x 32 rows);
-// key/value tiles of 64 rows, double-buffered.  Each wave computes
+// ---- forward.  Workgroup: 256 query rows of one head (8 waves x 32 rows);
+// key/value tiles of 64 rows, double-buffered, staged once for all 8 waves.  Each wave computes
 // S^T = K Q^T (lane = query row, registers = keys): row statistics are per
 // lane plus one exchange between the lane halves, and O^T = V^T P^T keeps the
 // query in the lane, so the online rescale is a per-lane scalar.
 namespace fw {
-constexpr int BM = 128, BN = 64;
+constexpr int BM = 256, BN = 64;
+constexpr int NT = 512;         // threads
 constexpr int TILE = BN * RS;   // elements of one 64-row tile
 constexpr int BUF = 2 * TILE;   // K and V
 constexpr float kLazy = 8.f;    // keep a stale running max while the new one exceeds it by <= 8 (log2)
 }  // namespace fw
 
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(fw::NT, 1) void attn_fwd_kernel(AttnArgs a) {
   using namespace fw;
   __shared__ __attribute__((aligned(16))) u16 lds[2 * BUF];
   const int64_t S = a.S;
@@ -391,7 +392,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   const int64_t kv_end = a.causal ? min(S, qfirst + BM) : S;
   const int ntiles = static_cast<int>((kv_end + BN - 1) / BN);
 
-  TileLoad<4> lk, lv;
+  TileLoad<BN * 16 / NT, NT> lk, lv;
   auto load = [&](int j) {
     lk.load(K, DH, static_cast<int64_t>(j) * BN, S, tid);
     lv.load(V, DH, static_cast<int64_t>(j) * BN, S, tid);
@@ -537,17 +538,18 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(AttnArgs a) {
   if (row < a.S && part == 0) a.dd[static_cast<int64_t>(u) * a.S + row] = acc;
 }
 
-// ---- dQ.  Workgroup: 128 query rows of one head (4 waves x 32 rows); key
-// tiles of 64 rows.  Orientation as in the forward (lane = query row): S^T
+// ---- dQ.  Workgroup: 256 query rows of one head (8 waves x 32 rows); key
+// tiles of 64 rows, staged once for all 8 waves.  Orientation as in the forward (lane = query row): S^T
 // and dP^T from registers Q, dO against K and V row operands, then
 // dQ^T += K^T dS^T with K read as a column operand of the same tile.
 namespace dqk {
-constexpr int BM = 128, BN = 64;
+constexpr int BM = 256, BN = 64;
+constexpr int NT = 512;  // threads
 constexpr int TILE = BN * RS;
 constexpr int BUF = 2 * TILE;  // K and V
 }  // namespace dqk
 
-__global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnArgs a) {
+__global__ __launch_bounds__(dqk::NT, 1) void attn_dq_kernel(AttnArgs a) {
   using namespace dqk;
   __shared__ __attribute__((aligned(16))) u16 lds[2 * BUF];
   const int64_t S = a.S;
@@ -582,7 +584,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnArgs a) {
   const int64_t kv_end = a.causal ? min(S, qfirst + BM) : S;
   const int ntiles = static_cast<int>((kv_end + BN - 1) / BN);
 
-  TileLoad<4> lk, lv;
+  TileLoad<BN * 16 / NT, NT> lk, lv;
   auto load = [&](int j) {
     lk.load(K, DH, static_cast<int64_t>(j) * BN, S, tid);
     lv.load(V, DH, static_cast<int64_t>(j) * BN, S, tid);
@@ -732,7 +734,7 @@ hipError_t dx(float* dX, int64_t S, int64_t D, int d, const ChunkTable& t, hipSt
 
 hipError_t attn_fwd(const AttnArgs& a, hipStream_t st) {
   if (a.d != DH) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3(cdiv(a.S, fw::BM) * a.nq), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(attn_fwd_kernel, dim3(cdiv(a.S, fw::BM) * a.nq), dim3(fw::NT), 0, st, a);
   return hipGetLastError();
 }
 
@@ -773,7 +775,7 @@ hipError_t mfma_ceiling(int waves_per_simd, int iters, double* tflops, hipStream
 
 hipError_t attn_dq(const AttnArgs& a, hipStream_t st) {
   if (a.d != DH) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_dq_kernel, dim3(cdiv(a.S, dqk::BM) * a.nq), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(attn_dq_kernel, dim3(cdiv(a.S, dqk::BM) * a.nq), dim3(dqk::NT), 0, st, a);
   return hipGetLastError();
 }
 

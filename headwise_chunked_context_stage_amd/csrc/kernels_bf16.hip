@@ -539,9 +539,11 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(AttnArgs a) {
 }
 
 // ---- dQ.  Workgroup: 256 query rows of one head (8 waves x 32 rows); key
-// tiles of 64 rows, staged once for all 8 waves.  Orientation as in the forward (lane = query row): S^T
-// and dP^T from registers Q, dO against K and V row operands, then
-// dQ^T += K^T dS^T with K read as a column operand of the same tile.
+// tiles of 64 rows, staged once for all 8 waves.  LDS holds two pairs of K/V
+// tiles: the waves run two tiles between barriers while the next pair is
+// copied in.  Orientation as in the forward (lane = query row): S^T and dP^T
+// from registers Q, dO against K and V row operands, then dQ^T += K^T dS^T
+// with K read as a column operand of the same tile.
 namespace dqk {
 constexpr int BM = 256, BN = 64;
 constexpr int NT = 512;  // threads
@@ -551,7 +553,7 @@ constexpr int BUF = 2 * TILE;  // K and V
 
 __global__ __launch_bounds__(dqk::NT, 1) void attn_dq_kernel(AttnArgs a) {
   using namespace dqk;
-  __shared__ __attribute__((aligned(16))) u16 lds[2 * BUF];
+  __shared__ __attribute__((aligned(16))) u16 lds[4 * BUF];
   const int64_t S = a.S;
   const int nqb = static_cast<int>((S + BM - 1) / BM);
   const int qb = nqb - 1 - static_cast<int>(blockIdx.x) / a.nq;
@@ -600,10 +602,12 @@ __global__ __launch_bounds__(dqk::NT, 1) void attn_dq_kernel(AttnArgs a) {
 
   load(0);
   store(0);
+  if (ntiles > 1) {
+    load(1);
+    store(1);
+  }
   __syncthreads();
-  for (int j = 0; j < ntiles; ++j) {
-    const int cur = j & 1;
-    if (j + 1 < ntiles) load(j + 1);
+  auto process = [&](int j, int cur) {
     const int64_t kv0 = static_cast<int64_t>(j) * BN;
     const bool active = !a.causal || kv0 <= wq0 + 31;
     if (active) {
@@ -657,7 +661,15 @@ __global__ __launch_bounds__(dqk::NT, 1) void attn_dq_kernel(AttnArgs a) {
         }
       }
     }
-    if (j + 1 < ntiles) store(cur ^ 1);
+  };
+  for (int j0 = 0; j0 < ntiles; j0 += 2) {
+    const int p = (j0 >> 1) & 1;  // pair slot of tiles j0, j0 + 1
+    if (j0 + 2 < ntiles) load(j0 + 2);
+    process(j0, 2 * p);
+    if (j0 + 2 < ntiles) store(2 * (p ^ 1));
+    if (j0 + 3 < ntiles) load(j0 + 3);
+    if (j0 + 1 < ntiles) process(j0 + 1, 2 * p + 1);
+    if (j0 + 3 < ntiles) store(2 * (p ^ 1) + 1);
     __syncthreads();
   }
 

@@ -12,6 +12,22 @@
 namespace upipe {
 namespace {
 
+// One 256-byte row from global memory straight into LDS (no registers): lane
+// l copies bytes 4l..4l+3 of the row at `src` to LDS byte address dst + 4l.
+// `src` and `dst` are wave-uniform.  The copy is counted by vmcnt only and is
+// not seen by the compiler's wait insertion: dma_wait() before the barrier
+// that publishes the rows.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_row(const void* src, unsigned dst, unsigned lane4) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(dst), "v"(lane4), "s"(src) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ unsigned lds_byte_addr(const void* p) {
+  return static_cast<unsigned>(reinterpret_cast<uintptr_t>((const lds_u16*)p));
+}
+
 // ---- dK, dV.  Workgroup: 128 key rows of one KV head, looping over the
 // stage's query heads of that group (ascending) and over 64-row query tiles.
 // Eight waves: each 32-key block has a pair of waves on one SIMD.  With the
@@ -36,7 +52,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
   using namespace kv;
   __shared__ __attribute__((aligned(16))) u16 qs[NQ * TILE];
   __shared__ __attribute__((aligned(16))) u16 gs[NG * TILE];
-  __shared__ __attribute__((aligned(16))) float stat[2][2][BM];  // [tile & 1][lse2, D][row]
+  __shared__ __attribute__((aligned(16))) float stat[2][2][BM];  // [tile & 1][LSE (natural log), D][row]
   __shared__ __attribute__((aligned(16))) f32x4 pxch[4][8][64];  // P of each key block: [block][reg/4][lane]
   const int64_t S = a.S;
   const int lid = xcd_snake(blockIdx.x, gridDim.x);
@@ -96,66 +112,58 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
     }
   };
 
-  // Tile t + 1 is loaded from global memory during tile t - 1 and written to
-  // LDS during tile t: each load has a whole tile of time to arrive.  Thread
-  // tid stages rows srow and srow + 32, 16-byte chunk sc, of the Q and dO
-  // tiles; its offsets are fixed.
+  // Tile t + 1 is copied into LDS during tile t.  Wave w copies logical rows
+  // 8w..8w+7 of the Q and dO tiles, one DMA row each; waves 0 and 4 copy the
+  // tile's LSE and D.  A tile that runs past S goes through registers
+  // instead, with zero rows (and LSE = +inf, D = 0) beyond S.
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const unsigned lane4 = 4u * lane;
+  const int pr0 = 16 * (wv >> 1) + (wv & 1);  // prow(8 wv + i) = pr0 + 4 (i % 4) + 2 (i / 4)
   const int srow = tid >> 4, sc = tid & 15;
-  const int qoff = srow * DH + sc * 8;
-  const int goff = srow * static_cast<int>(ldo) + sc * 8;
-  const int loff0 = toff(srow, sc * 8), loff1 = toff(srow + 32, sc * 8);
-  u32x4 rq[2], rg[2];
-  float rs = 0.f;  // raw LSE (threads 0..63) or D (64..127) of the staged tile
-  auto load = [&](const Cur& x) {
+  auto issue = [&](const Cur& x, int slq, int slg) {
     const int u = x.h - a.q_head0;
     const int64_t q0 = static_cast<int64_t>(x.qt) * BM;
     const u16* qb = static_cast<const u16*>(a.q) + (static_cast<int64_t>(u) * S + q0) * DH;
     const u16* gb = static_cast<const u16*>(a.dO) + q0 * ldo + static_cast<int64_t>(x.h) * DH;
-    if (q0 + BM <= S) {  // whole tile inside the sequence (uniform)
-      rq[0] = ld16(qb + qoff);
-      rq[1] = ld16(qb + qoff + 32 * DH);
-      rg[0] = ld16(gb + goff);
-      rg[1] = ld16(gb + goff + 32 * ldo);
-    } else {  // last tile of a head: rows at or beyond S are zero
-      const int64_t left = S - q0 - srow;
-      rq[0] = 0 < left ? ld16(qb + qoff) : u32x4{0, 0, 0, 0};
-      rq[1] = 32 < left ? ld16(qb + qoff + 32 * DH) : u32x4{0, 0, 0, 0};
-      rg[0] = 0 < left ? ld16(gb + goff) : u32x4{0, 0, 0, 0};
-      rg[1] = 32 < left ? ld16(gb + goff + 32 * ldo) : u32x4{0, 0, 0, 0};
-    }
-    if (tid < 2 * BM) {
-      const int64_t q = min(q0 + (tid % BM), S - 1);
-      rs = tid < BM ? a.lse_in[static_cast<int64_t>(x.h) * S + q] : a.dd[static_cast<int64_t>(u) * S + q];
-    }
-  };
-  auto store = [&](int slq, int slg, int qt) {
     u16* qd = qs + slq * TILE;
     u16* gd = gs + slg * TILE;
-    st16(qd + loff0, rq[0]);
-    st16(qd + loff1, rq[1]);
-    st16(gd + loff0, rg[0]);
-    st16(gd + loff1, rg[1]);
-    if (tid < 2 * BM) {
-      const bool in = static_cast<int64_t>(qt) * BM + (tid % BM) < S;
-      stat[slg][tid / BM][tid % BM] = tid < BM ? (in ? rs * kLog2e : INFINITY) : (in ? rs : 0.f);
+    if (q0 + BM <= S) {
+      const unsigned qa = lds_byte_addr(qd), ga = lds_byte_addr(gd);
+      const u16* qr = qb + 8 * wv * DH;
+      const u16* gr = gb + 8 * wv * ldo;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const unsigned off = static_cast<unsigned>((pr0 + 4 * (i & 3) + 2 * (i >> 2)) * RS * 2);
+        dma_row(qr + i * DH, qa + off, lane4);
+        dma_row(gr + i * ldo, ga + off, lane4);
+      }
+      if (wv == 0) dma_row(a.lse_in + static_cast<int64_t>(x.h) * S + q0, lds_byte_addr(&stat[slg][0][0]), lane4);
+      if (wv == 4) dma_row(a.dd + static_cast<int64_t>(u) * S + q0, lds_byte_addr(&stat[slg][1][0]), lane4);
+    } else {
+      const int64_t left = S - q0 - srow;
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const u32x4 vq = 32 * m < left ? ld16(qb + (srow + 32 * m) * DH + sc * 8) : u32x4{0, 0, 0, 0};
+        const u32x4 vg = 32 * m < left ? ld16(gb + (srow + 32 * m) * ldo + sc * 8) : u32x4{0, 0, 0, 0};
+        st16(qd + toff(srow + 32 * m, sc * 8), vq);
+        st16(gd + toff(srow + 32 * m, sc * 8), vg);
+      }
+      if (tid < 2 * BM) {
+        const int r = tid % BM;
+        const bool in = q0 + r < S;
+        const int64_t q = in ? q0 + r : S - 1;
+        stat[slg][tid / BM][r] = tid < BM ? (in ? a.lse_in[static_cast<int64_t>(x.h) * S + q] : INFINITY)
+                                          : (in ? a.dd[static_cast<int64_t>(u) * S + q] : 0.f);
+      }
     }
   };
   Cur cc{h_lo, qt0};  // tile it
-  Cur lc = cc;        // tile it + 2 (next to load)
-  adv(lc);
-  adv(lc);
+  Cur nc = cc;        // tile it + 1
+  adv(nc);
   int sq = 0, sg = 0;  // it % NQ, it % NG
-  auto stage = [&](int it) {  // during tile it: tile it + 1 to LDS, tile it + 2 requested
-    if (it + 1 < niter) {
-      Cur n = cc;
-      adv(n);
-      store(sq + 1 == NQ ? 0 : sq + 1, sg ^ 1, n.qt);
-    }
-    if (it + 2 < niter) load(lc);
-  };
   auto next_tile = [&]() {  // end of a round: tile it + 1 becomes current
     adv(cc);
-    adv(lc);
+    adv(nc);
     sq = sq + 1 == NQ ? 0 : sq + 1;
     sg ^= 1;
   };
@@ -197,26 +205,19 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
     }
   };
 
-  if (niter > 0) {
-    load(cc);
-    store(0, 0, cc.qt);
-  }
-  if (niter > 1) {
-    Cur n = cc;
-    adv(n);
-    load(n);
-  }
+  if (niter > 0) issue(cc, 0, 0);
+  dma_wait();
   __syncthreads();
 
   // Both waves of a pair run niter + 1 rounds of two barriers each.
   if (pwave) {
     for (int it = 0; it <= niter; ++it) {
       bf16x8 op[4];  // P of tile it, packed
+      if (it + 1 < niter) issue(nc, sq + 1 == NQ ? 0 : sq + 1, sg ^ 1);
       if (it < niter) {
         // S = Q K^T; P = exp(S - LSE), masked above the diagonal; fp32 P to the partner
         f32x16 sv[2];
         row_pass(tile_addr(qs + sq * TILE, lane), sv);
-        stage(it);
         const int64_t q0 = static_cast<int64_t>(cc.qt) * BM;
         const bool need_mask = a.causal && q0 < wk0 + 31;
         const int mlim = static_cast<int>(myk - q0);  // tile row r is masked when r < mlim
@@ -229,7 +230,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
           for (int g4 = 0; g4 < 4; ++g4) {
             const int j = 4 * qb + g4, r0 = 8 * j + 4 * hf;  // tile rows r0..r0+3 = registers 4*g4..4*g4+3
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sv[qb][4 * g4 + e] = ex2(__builtin_fmaf(sv[qb][4 * g4 + e], c, -l4[j][e]));
+            for (int e = 0; e < 4; ++e) sv[qb][4 * g4 + e] = ex2(__builtin_fmaf(sv[qb][4 * g4 + e], c, -kLog2e * l4[j][e]));
             if (need_mask) {
 #pragma unroll
               for (int e = 0; e < 4; ++e)
@@ -242,6 +243,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
       }
       __syncthreads();
       if (it < niter) col_pass(tile_addr(gs + sg * TILE, lane), op);  // dV += P^T dO
+      dma_wait();
       __syncthreads();
       next_tile();
     }
@@ -249,10 +251,8 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
     bf16x8 op[4];  // dS of the previous tile, packed
     f32x16 sv[2];  // dP of the current tile
     for (int it = 0; it <= niter; ++it) {
-      if (it < niter) {
-        row_pass(tile_addr(gs + sg * TILE, lane), sv);  // dP = dO V^T
-        stage(it);
-      }
+      if (it + 1 < niter) issue(nc, sq + 1 == NQ ? 0 : sq + 1, sg ^ 1);
+      if (it < niter) row_pass(tile_addr(gs + sg * TILE, lane), sv);  // dP = dO V^T
       if (it >= 1) col_pass(tile_addr(qs + (sq == 0 ? NQ - 1 : sq - 1) * TILE, lane), op);  // dK += dS^T Q, tile it - 1
       __syncthreads();
       if (it < niter) {
@@ -274,6 +274,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
 #pragma unroll
         for (int k4 = 0; k4 < 4; ++k4) op[k4] = pack8(sv[k4 / 2], k4 % 2);
       }
+      dma_wait();
       __syncthreads();
       next_tile();
     }

@@ -43,6 +43,9 @@ constexpr int GB = 128, GK = 64, GS = GK + 8;  // tile, k step, LDS row stride (
 constexpr int GBUF = 2 * GB * GS;             // elements per buffer (two operand tiles)
 
 // ---- projection: out[i][c] = sum_k X[i][k] W[c][k] for one head (d = 128).
+// X streams from HBM: global loads run NRR = 4 k-steps ahead of their LDS
+// store through a ring of register sets, so each has several steps of MFMA
+// time to arrive (one step ahead, the loop waited on HBM latency).
 __global__ __launch_bounds__(256, 2) void proj_kernel(const u16* __restrict__ X, int64_t S,
                                                       int64_t D, ChunkTable t, int nrb) {
   __shared__ __attribute__((aligned(16))) u16 lds[2 * GBUF];
@@ -55,24 +58,28 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(const u16* __restrict__ X,
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, col = lane % 32, hf = lane / 32;
   const int wm = wave / 2, wn = wave % 2;
 
-  u32x4 rx[4], rw[4];
-  auto load = [&](int64_t k0) {
+  constexpr int NRR = 4;
+  const int nk = static_cast<int>(D / GK);
+  u32x4 rx[NRR][4], rw[NRR][4];
+  auto load = [&](int set, int kb) {
+    if (kb >= nk) return;
+    const int64_t k0 = static_cast<int64_t>(kb) * GK;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int row = tid / 8 + 32 * m, chunk = tid % 8;
       const int64_t gi = i0 + row;
-      rx[m] = gi < S ? ld16(X + gi * D + k0 + chunk * 8) : u32x4{0, 0, 0, 0};
-      rw[m] = ld16(W + static_cast<int64_t>(row) * D + k0 + chunk * 8);
+      rx[set][m] = gi < S ? ld16(X + gi * D + k0 + chunk * 8) : u32x4{0, 0, 0, 0};
+      rw[set][m] = ld16(W + static_cast<int64_t>(row) * D + k0 + chunk * 8);
     }
   };
-  auto store = [&](int b) {
+  auto store = [&](int set, int b) {
     u16* xs = lds + b * GBUF;
     u16* ws = xs + GB * GS;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int row = tid / 8 + 32 * m, chunk = tid % 8;
-      st16(xs + row * GS + chunk * 8, rx[m]);
-      st16(ws + row * GS + chunk * 8, rw[m]);
+      st16(xs + row * GS + chunk * 8, rx[set][m]);
+      st16(ws + row * GS + chunk * 8, rw[set][m]);
     }
   };
 
@@ -82,13 +89,15 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(const u16* __restrict__ X,
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = zero16();
 
-  const int nk = static_cast<int>(D / GK);
-  load(0);
-  store(0);
+  // k-step kb's data sits in register set kb % NRR until its LDS store.
+#pragma unroll
+  for (int i = 0; i < NRR; ++i) load(i, i);
+  store(0, 0);
+  load(0, NRR);
   __syncthreads();
-  for (int kb = 0; kb < nk; ++kb) {
+  auto body = [&](int kb, auto setc) {  // setc = (kb + 1) % NRR, a compile-time constant
+    constexpr int SN = decltype(setc)::value;
     const int cur = kb & 1;
-    if (kb + 1 < nk) load(static_cast<int64_t>(kb + 1) * GK);
     const u16* xs = lds + cur * GBUF;
     const u16* ws = xs + GB * GS;
 #pragma unroll
@@ -103,9 +112,20 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(const u16* __restrict__ X,
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma(fa[mb], fb[nb], acc[mb][nb]);
     }
-    if (kb + 1 < nk) store(cur ^ 1);
+    if (kb + 1 < nk) store(SN, cur ^ 1);
+    load(SN, kb + 1 + NRR);  // the set just stored takes k-step kb + 1 + NRR
     __syncthreads();
+  };
+  int kb = 0;
+  for (; kb + NRR <= nk; kb += NRR) {
+    body(kb, std::integral_constant<int, 1 % NRR>{});
+    body(kb + 1, std::integral_constant<int, 2 % NRR>{});
+    body(kb + 2, std::integral_constant<int, 3 % NRR>{});
+    if constexpr (NRR > 3) body(kb + 3, std::integral_constant<int, 4 % NRR>{});
   }
+  if (kb < nk) body(kb, std::integral_constant<int, 1 % NRR>{});
+  if (kb + 1 < nk) body(kb + 1, std::integral_constant<int, 2 % NRR>{});
+  if (NRR > 3 && kb + 2 < nk) body(kb + 2, std::integral_constant<int, 3 % NRR>{});
   // Epilogue: C (bf16) -> LDS tile [128][136] -> coalesced 16-byte stores.
   constexpr int CS = GB + 8;
   u16* cs = lds;

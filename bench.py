@@ -233,9 +233,10 @@ def main():
                 "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic_for(dominant),
                 "work_per_launch": dwork, "avg_launch_ms": dk["avg_launch_ms"]}
 
-    # measured dense-MFMA ceiling of this chip (every CU, 2 waves per SIMD):
-    # context for frac, which stays against the published peak
-    ceiling = upipe.upipe_mfma_ceiling(2)
+    # measured dense-MFMA ceiling of this chip (every CU, 2 waves per SIMD,
+    # random bf16 operands, ~0.1 s per run so the clock has settled; best of
+    # two): context for frac, which stays against the published peak
+    ceiling = max(upipe.upipe_mfma_ceiling(2, 1 << 16) for _ in range(2))
     roof["measured_mfma_ceiling"] = ceiling
     if dunit == "flop":
         roof["frac_of_measured_ceiling"] = roof["achieved"] / ceiling

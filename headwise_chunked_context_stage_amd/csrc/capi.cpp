@@ -183,6 +183,11 @@ int upipe_create(upipe_plan** out, int64_t S, int64_t d_model, int H, int G, int
 
 void upipe_destroy(upipe_plan* p) { delete p; }
 
+int upipe_auto_u(int64_t S, int64_t d_model, int H, int G, int d_head, int causal, int dtype,
+                 size_t budget_bytes, int* U) {
+  return choose_u(S, d_model, H, G, d_head, causal, dtype, budget_bytes, U);
+}
+
 size_t upipe_peak_bytes(const upipe_plan* p) {
   if (!p) return 0;
   return std::max(p->p.ws.fwd_bytes, p->p.ws.bwd_bytes);

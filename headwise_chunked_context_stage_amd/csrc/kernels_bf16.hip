@@ -708,24 +708,44 @@ __global__ __launch_bounds__(dqk::NT, 1) void attn_dq_kernel(AttnArgs a) {
 }
 
 // ---- dense MFMA stream: four independent accumulator chains per wave,
-// operands in registers.  The result is stored only when iters < 0 (never),
-// which keeps the products live without any memory traffic.
-__global__ __launch_bounds__(256) void mfma_ceiling_kernel(float* sink, int iters) {
-  const unsigned lane = threadIdx.x % 64;
-  bf16x8 a, b;
+// operands in registers.  The operands are pseudo-random bf16 values in
+// [-2, 2) with random mantissas (four sets per wave, rotated): the matrix
+// core's power, and with it the clock it sustains, depends on how many bits
+// toggle, and attention data are dense random values, not constants.  The
+// result is stored only when iters < 0 (never), which keeps the products live
+// without any memory traffic.  `rounds` x 16 MFMAs per wave.
+__device__ __forceinline__ unsigned mix32(unsigned x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+__global__ __launch_bounds__(256) void mfma_ceiling_kernel(float* sink, int rounds) {
+  bf16x8 a[4], b[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    a[e] = static_cast<__bf16>(static_cast<float>((lane + e) % 7) * 0.125f);
-    b[e] = static_cast<__bf16>(static_cast<float>((lane * 3 + e) % 5) * 0.25f);
+  for (int v = 0; v < 4; ++v) {
+    u32x4 ra, rb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const unsigned h1 = mix32((blockIdx.x * 256u + threadIdx.x) * 16u + v * 4u + e), h2 = mix32(h1 ^ 0x9e3779b9u);
+      ra[e] = (h1 & 0x807f807fu) | 0x3f003f00u;  // sign, mantissa random; exponent 2^-1 or 2^0
+      rb[e] = (h2 & 0x807f807fu) | 0x3f003f00u;
+    }
+    a[v] = __builtin_bit_cast(bf16x8, ra);
+    b[v] = __builtin_bit_cast(bf16x8, rb);
   }
   f32x16 acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = zero16();
-  for (int it = 0; it < iters; ++it) {
+  for (int it = 0; it < rounds; ++it) {  // 16 MFMAs per round
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = mfma(a, b, acc[i]);
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = mfma(a[(r + i) & 3], b[(r + 2 * i) & 3], acc[i]);
   }
-  if (iters < 0) {
+  if (rounds < 0) {
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -788,10 +808,11 @@ hipError_t mfma_ceiling(int waves_per_simd, int iters, double* tflops, hipStream
     return e;
   }
   const unsigned grid = static_cast<unsigned>(cus * waves_per_simd);  // 4 waves per block = 1 per SIMD
-  hipLaunchKernelGGL(mfma_ceiling_kernel, dim3(grid), dim3(256), 0, st, nullptr, iters / 8);  // warm-up
+  const int rounds = iters / 4;  // iters x 4 MFMAs per wave, rounded down to whole rounds
+  hipLaunchKernelGGL(mfma_ceiling_kernel, dim3(grid), dim3(256), 0, st, nullptr, rounds / 8);  // warm-up
   e = hipEventRecord(t0, st);
   if (e == hipSuccess) {
-    hipLaunchKernelGGL(mfma_ceiling_kernel, dim3(grid), dim3(256), 0, st, nullptr, iters);
+    hipLaunchKernelGGL(mfma_ceiling_kernel, dim3(grid), dim3(256), 0, st, nullptr, rounds);
     e = hipGetLastError();
   }
   if (e == hipSuccess) e = hipEventRecord(t1, st);
@@ -801,7 +822,7 @@ hipError_t mfma_ceiling(int waves_per_simd, int iters, double* tflops, hipStream
   (void)hipEventDestroy(t0);
   (void)hipEventDestroy(t1);
   if (e == hipSuccess)
-    *tflops = static_cast<double>(grid) * 4 * iters * 4 * 32768.0 / (static_cast<double>(ms) * 1e-3) / 1e12;
+    *tflops = static_cast<double>(grid) * 4 * rounds * 16 * 32768.0 / (static_cast<double>(ms) * 1e-3) / 1e12;
   return e;
 }
 

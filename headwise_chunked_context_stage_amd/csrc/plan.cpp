@@ -93,4 +93,29 @@ int make_plan(Plan& p, int64_t S, int64_t D, int H, int G, int d, int U, int cau
   return UPIPE_OK;
 }
 
+// Chunk size from a memory budget.  The pages (paper.rainbus.top summary,
+// section 独立分析的弱点) suggest choosing U from the sequence length: large U
+// (few stages) for short sequences, small U (less memory) for long ones, and
+// section 实验结果 reports U as a memory/throughput trade-off.  With a fixed
+// budget this is the largest legal U whose workspace fits: the workspace
+// grows with S * U, so a longer sequence gets a smaller U.
+int choose_u(int64_t S, int64_t D, int H, int G, int d, int causal, int dtype, size_t budget,
+             int* U) {
+  if (!U) return UPIPE_ERR_ARG;
+  *U = 0;
+  if (H <= 0 || G <= 0 || H % G != 0) return UPIPE_ERR_ARG;
+  const int r = H / G;
+  for (int u = H; u >= 1; --u) {
+    if (H % u != 0 || !(r % u == 0 || u % r == 0)) continue;
+    Plan p;
+    const int rc = make_plan(p, S, D, H, G, d, u, causal, dtype);
+    if (rc != UPIPE_OK) return rc;  // shape errors do not depend on U
+    if (std::max(p.ws.fwd_bytes, p.ws.bwd_bytes) <= budget) {
+      *U = u;
+      return UPIPE_OK;
+    }
+  }
+  return UPIPE_ERR_WORKSPACE;
+}
+
 }  // namespace upipe

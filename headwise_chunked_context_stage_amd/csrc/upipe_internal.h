@@ -48,6 +48,8 @@ struct Plan {
 
 // Validates and builds; returns a UPIPE_* code.
 int make_plan(Plan& p, int64_t S, int64_t D, int H, int G, int d, int U, int causal, int dtype);
+int choose_u(int64_t S, int64_t D, int H, int G, int d, int causal, int dtype, size_t budget,
+             int* U);
 
 // ------------------------------------------------------------------ launch
 // A list of [S][d] operand buffers with matching weight row blocks.  Used for

@@ -19,7 +19,8 @@ KERNEL_KINDS = ("proj", "attn_fwd", "bwd_pre", "attn_dkv", "attn_dq", "dw", "dx"
 
 EXPORTS = ("upipe_create", "upipe_destroy", "upipe_peak_bytes", "upipe_peak_bytes_phase",
            "upipe_fwd", "upipe_bwd", "upipe_strerror", "upipe_num_stages", "upipe_stage_info",
-           "upipe_timing_enable", "upipe_timing_read", "upipe_kernel_name", "upipe_mfma_ceiling")
+           "upipe_timing_enable", "upipe_timing_read", "upipe_kernel_name", "upipe_mfma_ceiling",
+           "upipe_auto_u")
 
 _lib = None
 
@@ -66,6 +67,8 @@ def lib():
     L.upipe_kernel_name.restype = ctypes.c_char_p
     L.upipe_mfma_ceiling.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_double), vp]
     L.upipe_mfma_ceiling.restype = i32
+    L.upipe_auto_u.argtypes = [i64, i64, i32, i32, i32, i32, i32, sz, ctypes.POINTER(i32)]
+    L.upipe_auto_u.restype = i32
     _lib = L
     return L
 
@@ -190,6 +193,15 @@ def upipe_mfma_ceiling(waves_per_simd: int = 2, iters: int = 1 << 14, stream=Non
     out = ctypes.c_double(0.0)
     _check(lib().upipe_mfma_ceiling(waves_per_simd, iters, ctypes.byref(out), _stream(stream)),
            "upipe_mfma_ceiling")
+    return out.value
+
+
+def upipe_auto_u(S: int, d_model: int, H: int, G: int, d_head: int, budget_bytes: int,
+                 causal: bool = True, dtype="bf16") -> int:
+    """Largest legal U whose workspace fits budget_bytes (host only)."""
+    out = ctypes.c_int(0)
+    _check(lib().upipe_auto_u(S, d_model, H, G, d_head, int(bool(causal)), _dtype_code(dtype),
+                              budget_bytes, ctypes.byref(out)), "upipe_auto_u")
     return out.value
 
 

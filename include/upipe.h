@@ -70,6 +70,18 @@ enum {
 int upipe_create(upipe_plan** out, int64_t S, int64_t d_model, int H, int G, int d_head, int U,
                  int causal, int dtype);
 
+/* Chunk size from a memory budget (host only).  The pages (paper.rainbus.top
+ * summary of "Untied Ulysses", section 独立分析的弱点) propose choosing U from
+ * the sequence length, large for short sequences and small for long ones;
+ * section 实验结果 describes U as a memory/throughput trade-off.  Writes to *U
+ * the largest legal U (as for upipe_create) whose upipe_peak_bytes is at most
+ * budget_bytes, so for a fixed budget a longer S gets a smaller or equal U.
+ * Returns UPIPE_ERR_ARG (or UPIPE_ERR_UNSUPPORTED) for a shape upipe_create
+ * rejects for every U, UPIPE_ERR_WORKSPACE when not even U = 1 fits; *U is 0
+ * on failure.  U must not be NULL. */
+int upipe_auto_u(int64_t S, int64_t d_model, int H, int G, int d_head, int causal, int dtype,
+                 size_t budget_bytes, int* U);
+
 /* Release a plan (NULL is ignored). */
 void upipe_destroy(upipe_plan* p);
 
@@ -133,11 +145,14 @@ const char* upipe_kernel_name(int kind);
  * Runs a dense bf16 MFMA stream on every CU (v_mfma_f32_32x32x16_bf16, four
  * independent accumulator chains per wave, operands in registers, no memory
  * traffic) with `waves_per_simd` waves per SIMD (1..2), `iters` x 4 MFMAs per
- * wave, on `stream` (a hipStream_t, may be null), waits for it, and writes
- * the achieved TFLOP/s (2*32*32*16 flop per MFMA) to *tflops.  Allocates no
- * device memory.  UPIPE_ERR_ARG for bad arguments, UPIPE_ERR_HIP on a HIP
- * failure.  This is the practical ceiling the attention kernels are compared
- * against next to the published dense peak. */
+ * wave (iters rounded down to a multiple of 4), on `stream` (a hipStream_t,
+ * may be null), waits for it, and writes the achieved TFLOP/s (2*32*32*16
+ * flop per MFMA) to *tflops.  The operands are pseudo-random bf16 values with
+ * random mantissas: the power the matrix cores draw, and so the clock they
+ * sustain, depends on the data (constant operands run about 10% faster).
+ * Allocates no device memory.  UPIPE_ERR_ARG for bad arguments, UPIPE_ERR_HIP
+ * on a HIP failure.  This is the practical ceiling the attention kernels are
+ * compared against next to the published dense peak. */
 int upipe_mfma_ceiling(int waves_per_simd, int iters, double* tflops, void* stream);
 
 #ifdef __cplusplus

@@ -185,3 +185,50 @@ def test_stage_info_bad_index():
         p.stage_info(2)
     with pytest.raises(upipe.UpipeError):
         p.stage_info(-1)
+
+
+def test_auto_u_is_the_largest_legal_u_that_fits():
+    """upipe_auto_u: for every budget between consecutive plan sizes, the
+    chosen U is legal, its workspace fits, and no larger legal U fits."""
+    S, D, d = 4096, 1024, 128
+    for H, G in [(32, 8), (64, 8), (8, 8), (4, 1)]:
+        us = legal_us(H, G)
+        peak = {U: upipe.Plan(S, D, H, G, d, U).peak_bytes for U in us}
+        for budget in sorted(set(peak.values())) + [max(peak.values()) * 2]:
+            for b in (budget - 1, budget):
+                fits = [U for U in us if peak[U] <= b]
+                if not fits:
+                    with pytest.raises(upipe.UpipeError) as e:
+                        upipe.upipe_auto_u(S, D, H, G, d, b)
+                    assert e.value.code == upipe.UPIPE_ERR_WORKSPACE
+                    continue
+                U = upipe.upipe_auto_u(S, D, H, G, d, b)
+                assert U == max(fits) and peak[U] <= b
+
+
+def test_auto_u_longer_sequence_gets_smaller_u():
+    """The pages' dynamic-chunking reading: with a fixed memory budget, U
+    shrinks (never grows) as the sequence gets longer, down to no fit."""
+    H, G, D, d = 32, 8, 4096, 128
+    budget = upipe.Plan(262144, D, H, G, d, 16).peak_bytes
+    got = {}
+    for S in (16384, 65536, 131072, 262144, 524288, 1048576):
+        got[S] = upipe.upipe_auto_u(S, D, H, G, d, budget)
+        assert got[S] in legal_us(H, G)
+    seq = [got[S] for S in sorted(got)]
+    assert seq == sorted(seq, reverse=True)
+    assert got[16384] == H and got[262144] == 16 and got[524288] == 8 and got[1048576] == 4
+    with pytest.raises(upipe.UpipeError) as e:
+        upipe.upipe_auto_u(4194304, D, H, G, d, budget)
+    assert e.value.code == upipe.UPIPE_ERR_WORKSPACE
+
+
+def test_auto_u_rejects_bad_shapes_and_null_output():
+    with pytest.raises(upipe.UpipeError) as e:
+        upipe.upipe_auto_u(4096, 1024, 30, 8, 128, 1 << 40)  # G does not divide H
+    assert e.value.code == upipe.UPIPE_ERR_ARG
+    with pytest.raises(upipe.UpipeError) as e:
+        upipe.upipe_auto_u(4096, 1024, 32, 8, 64, 1 << 40)  # bf16 needs d_head = 128
+    assert e.value.code == upipe.UPIPE_ERR_UNSUPPORTED
+    L = upipe.lib()
+    assert L.upipe_auto_u(4096, 1024, 32, 8, 128, 1, 0, 1 << 40, None) == upipe.UPIPE_ERR_ARG

@@ -173,6 +173,25 @@ __device__ __forceinline__ bf16x8 col_frag(const TileAddr& ta, int r0, int n0) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
+// One 256-byte row from global memory straight into LDS (no registers): lane
+// l copies bytes 4l..4l+3 of the row at `src` to LDS byte address dst + 4l
+// (global_load_lds_dword; M0 holds the LDS address).  `src` and `dst` are
+// wave-uniform.  The copy is counted by vmcnt only and is not seen by the
+// compiler's wait insertion: dma_wait() before the barrier that publishes the
+// rows.  The kernels that use it issue no other global loads while copies are
+// in flight, apart from the register path for tiles that run past S, whose
+// compiler-inserted waits then cover the copies too.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_row(const void* src, unsigned dst, unsigned lane4) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(dst), "v"(lane4), "s"(src) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ unsigned lds_byte_addr(const void* p) {
+  return static_cast<unsigned>(reinterpret_cast<uintptr_t>((const lds_u16*)p));
+}
+
 // Copy rows [row0, row0 + nrows) of a [S][ld] bf16 matrix (128 columns from
 // `src`) into a tile; rows at or beyond S are zero.  NCH chunks of 16 bytes
 // per thread, thread t handling chunks t, t + 256, ...

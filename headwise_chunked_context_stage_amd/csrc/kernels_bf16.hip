@@ -373,21 +373,24 @@ __global__ __launch_bounds__(256, 2) void dx_kernel(float* __restrict__ dX, int6
 }
 
 // ---- forward.  Workgroup: 256 query rows of one head (8 waves x 32 rows);
-// key/value tiles of 64 rows, double-buffered, staged once for all 8 waves.  Each wave computes
-// S^T = K Q^T (lane = query row, registers = keys): row statistics are per
-// lane plus one exchange between the lane halves, and O^T = V^T P^T keeps the
-// query in the lane, so the online rescale is a per-lane scalar.
+// key/value tiles of 64 rows, double-buffered, copied once for all 8 waves.
+// Each wave computes S^T = K Q^T (lane = query row, registers = keys): row
+// statistics are per lane plus one exchange between the lane halves, and
+// O^T = V^T P^T keeps the query in the lane, so the online rescale is a
+// per-lane scalar.  Waves w and w + 4 share a SIMD and run "ping-pong": each
+// alternates a matrix phase and a softmax phase, one barrier phase apart, so
+// one wave's MFMAs meet the other's exponentials.
 namespace fw {
 constexpr int BM = 256, BN = 64;
 constexpr int NT = 512;         // threads
 constexpr int TILE = BN * RS;   // elements of one 64-row tile
-constexpr int BUF = 2 * TILE;   // K and V
 constexpr float kLazy = 8.f;    // keep a stale running max while the new one exceeds it by <= 8 (log2)
 }  // namespace fw
 
 __global__ __launch_bounds__(fw::NT, 1) void attn_fwd_kernel(AttnArgs a) {
   using namespace fw;
-  __shared__ __attribute__((aligned(16))) u16 lds[2 * BUF];
+  __shared__ __attribute__((aligned(16))) u16 kbuf[2 * TILE];
+  __shared__ __attribute__((aligned(16))) u16 vbuf[2 * TILE];
   const int64_t S = a.S;
   const int nqb = static_cast<int>((S + BM - 1) / BM);
   const int qb = nqb - 1 - static_cast<int>(blockIdx.x) / a.nq;  // longest rows first
@@ -399,6 +402,8 @@ __global__ __launch_bounds__(fw::NT, 1) void attn_fwd_kernel(AttnArgs a) {
   const u16* V = static_cast<const u16*>(a.v) + static_cast<int64_t>(gl) * S * DH;
 
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, col = lane % 32, hf = lane / 32;
+  const bool first = wave < 4;  // waves w and w + 4 share a SIMD; the second runs one phase later
+  const int st = tid & 255;     // copy index within the group: the first waves copy K tiles, the second V tiles
   const int64_t qfirst = static_cast<int64_t>(qb) * BM;
   const int64_t wq0 = qfirst + 32 * wave;
   const int64_t myq = wq0 + col;
@@ -411,36 +416,39 @@ __global__ __launch_bounds__(fw::NT, 1) void attn_fwd_kernel(AttnArgs a) {
 
   const int64_t kv_end = a.causal ? min(S, qfirst + BM) : S;
   const int ntiles = static_cast<int>((kv_end + BN - 1) / BN);
-
-  TileLoad<BN * 16 / NT, NT> lk, lv;
-  auto load = [&](int j) {
-    lk.load(K, DH, static_cast<int64_t>(j) * BN, S, tid);
-    lv.load(V, DH, static_cast<int64_t>(j) * BN, S, tid);
-  };
-  auto store = [&](int b) {
-    lk.store(lds + b * BUF, tid);
-    lv.store(lds + b * BUF + TILE, tid);
-  };
+  auto active = [&](int j) { return !a.causal || static_cast<int64_t>(j) * BN <= wq0 + 31; };
 
   f32x16 oacc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) oacc[i] = zero16();
   float m_run = -INFINITY, l_run = 0.f;
+  f32x16 s[2];   // S^T of the tile between its matrix phase and its softmax
+  bf16x8 pb[4];  // P^T of the tile between its softmax and the next matrix phase
 
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int j = 0; j < ntiles; ++j) {
-    const int cur = j & 1;
-    if (j + 1 < ntiles) load(j + 1);
-    const int64_t kv0 = static_cast<int64_t>(j) * BN;
-    const bool active = !a.causal || kv0 <= wq0 + 31;
-    if (active) {
-      const TileAddr ka = tile_addr(lds + cur * BUF, lane);
-      const TileAddr va = tile_addr(lds + cur * BUF + TILE, lane);
-      // S^T = K Q^T: two accumulator chains; the K operands of step t + 2 are
-      // requested before the MFMAs of step t are issued.
-      f32x16 s[2] = {zero16(), zero16()};
+  // Matrix phase of tile j: O^T += V^T P^T of tile j - 1, then S^T = K Q^T of tile j.
+  auto matrix_phase = [&](int j) {
+    if (j >= 1 && active(j - 1)) {
+      // step k4 outermost so the four accumulators alternate (each still
+      // sums k4 = 0..3 in order); V operands requested 3 groups ahead.
+      const TileAddr va = tile_addr(vbuf + ((j - 1) & 1) * TILE, lane);
+      bf16x8 fc[4];
+      auto load_c = [&](int gi) { return col_frag(va, 16 * (gi / 4), 32 * (gi % 4)); };
+      fc[0] = load_c(0);
+      fc[1] = load_c(1);
+      fc[2] = load_c(2);
+#pragma unroll
+      for (int gi = 0; gi < 16; ++gi) {
+        if (gi + 3 < 16) fc[(gi + 3) % 4] = load_c(gi + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        oacc[gi % 4] = mfma(fc[gi % 4], pb[gi / 4], oacc[gi % 4]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (j < ntiles && active(j)) {
+      // two accumulator chains; the K operands of step t + 2 are requested
+      // before the MFMAs of step t are issued
+      const TileAddr ka = tile_addr(kbuf + (j & 1) * TILE, lane);
+      s[0] = s[1] = zero16();
       bf16x8 fa[3][2];
       auto load_a = [&](int t, bf16x8 (&f)[2]) {
         f[0] = row_frag(ka, 0, t);
@@ -456,67 +464,104 @@ __global__ __launch_bounds__(fw::NT, 1) void attn_fwd_kernel(AttnArgs a) {
         s[1] = mfma(fa[t % 3][1], qf[t], s[1]);
         __builtin_amdgcn_sched_barrier(0);
       }
-      const bool need_mask = a.causal ? (kv0 + BN - 1 > wq0) : (kv0 + BN > S);
-      if (need_mask) {
-        // key kv0 + j is masked when j > myq - kv0 (causal) or j >= S - kv0
-        const int lim = static_cast<int>(a.causal ? min(myq - kv0, static_cast<int64_t>(BN)) :
-                                                    min(S - 1 - kv0, static_cast<int64_t>(BN)));
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int j = 32 * b + 8 * (i / 4) + 4 * hf + (i % 4);
-            if (j > lim) s[b][i] = -INFINITY;
-          }
-      }
-      float mt = s[0][0];
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[b][i]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32)) * c;
-      // Lazy running max: rescale only when the tile max exceeds it by more
-      // than kLazy (p <= 2^kLazy stays exact in fp32 and in bf16's exponent).
-      const float m_new = (mt > m_run + kLazy) ? mt : m_run;
-      if (__ballot(m_new != m_run)) {
-        const float alpha = ex2(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int d4 = 0; d4 < 4; ++d4)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[d4][i] *= alpha;
-        m_run = m_new;
-      }
-      float ls = 0.f;
+    }
+  };
+  // Softmax phase of tile j: mask, lazy running max, P = exp2(S c - m), row sums.
+  auto softmax_phase = [&](int j) {
+    if (j < 0 || j >= ntiles || !active(j)) return;
+    const int64_t kv0 = static_cast<int64_t>(j) * BN;
+    const bool need_mask = a.causal ? (kv0 + BN - 1 > wq0) : (kv0 + BN > S);
+    if (need_mask) {
+      // key kv0 + n is masked when n > myq - kv0 (causal) or n >= S - kv0
+      const int lim = static_cast<int>(a.causal ? min(myq - kv0, static_cast<int64_t>(BN)) :
+                                                  min(S - 1 - kv0, static_cast<int64_t>(BN)));
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = ex2(__builtin_fmaf(s[b][i], c, -m_run));
-          s[b][i] = p;
-          ls += p;
+          const int n = 32 * b + 8 * (i / 4) + 4 * hf + (i % 4);
+          if (n > lim) s[b][i] = -INFINITY;
         }
-      l_run += ls;
-      bf16x8 pb[4];
-#pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) pb[k4] = pack8(s[k4 / 2], k4 % 2);
-      // O^T += V^T P^T: step k4 outermost so the four accumulators alternate
-      // (each still sums k4 = 0..3 in order); V operands requested 3 groups ahead.
-      bf16x8 fc[4];
-      auto load_c = [&](int gi) { return col_frag(va, 16 * (gi / 4), 32 * (gi % 4)); };
-      fc[0] = load_c(0);
-      fc[1] = load_c(1);
-      fc[2] = load_c(2);
-#pragma unroll
-      for (int gi = 0; gi < 16; ++gi) {
-        if (gi + 3 < 16) fc[(gi + 3) % 4] = load_c(gi + 3);
-        __builtin_amdgcn_sched_barrier(0);
-        oacc[gi % 4] = mfma(fc[gi % 4], pb[gi / 4], oacc[gi % 4]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
     }
-    if (j + 1 < ntiles) store(cur ^ 1);
-    __syncthreads();
+    float mt = s[0][0];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[b][i]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32)) * c;
+    // Lazy running max: rescale only when the tile max exceeds it by more
+    // than kLazy (p <= 2^kLazy stays exact in fp32 and in bf16's exponent).
+    const float m_new = (mt > m_run + kLazy) ? mt : m_run;
+    if (__ballot(m_new != m_run)) {
+      const float alpha = ex2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[d4][i] *= alpha;
+      m_run = m_new;
+    }
+    float ls = 0.f;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = ex2(__builtin_fmaf(s[b][i], c, -m_run));
+        s[b][i] = p;
+        ls += p;
+      }
+    l_run += ls;
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) pb[k4] = pack8(s[k4 / 2], k4 % 2);
+  };
+
+  // Ping-pong: each wave alternates a matrix phase and a softmax phase, and
+  // the second wave of a SIMD runs one phase behind the first, so one wave's
+  // MFMAs overlap the other's exponentials.  Phases are separated by
+  // workgroup barriers.  K(j) is read in phases 2j (first waves) and 2j + 1
+  // (second waves); V(j) in phases 2j + 2 and 2j + 3.  Tile copies: the first
+  // waves copy K tiles, the second V tiles, 16 rows per wave, by direct
+  // global-to-LDS loads issued at the start of the wave's matrix phase (the
+  // softmax phase then carries no copy work).  K(j + 1) is issued in phase 2j
+  // and complete at the end of phase 2j + 1; V(j) is issued in phase 2j + 1
+  // and complete at its end.
+  const int wv = __builtin_amdgcn_readfirstlane(wave) & 3;
+  const unsigned lane4 = 4u * lane;
+  auto copy_tile = [&](const u16* src, int j, u16* dst) {
+    const int64_t r0 = static_cast<int64_t>(j) * BN;
+    if (r0 + BN <= S) {
+      const u16* g = src + (r0 + 16 * wv) * DH;
+      const unsigned d = lds_byte_addr(dst) + static_cast<unsigned>(16 * wv * RS * 2);
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        dma_row(g + i * DH, d + static_cast<unsigned>((((i & 3) << 2) | (((i >> 2) & 1) << 1) | ((i >> 3) & 1)) * RS * 2), lane4);
+    } else {
+      TileLoad<BN * 16 / 256, 256> tl;
+      tl.load(src, DH, r0, S, st);
+      tl.store(dst, st);
+    }
+  };
+  if (first) copy_tile(K, 0, kbuf);
+  dma_wait();
+  __syncthreads();
+  if (first) {
+    for (int j = 0; j <= ntiles; ++j) {
+      if (j + 1 < ntiles) copy_tile(K, j + 1, kbuf + ((j + 1) & 1) * TILE);
+      matrix_phase(j);
+      __syncthreads();
+      softmax_phase(j);
+      dma_wait();
+      __syncthreads();
+    }
+  } else {
+    for (int j = 0; j <= ntiles; ++j) {
+      softmax_phase(j - 1);
+      __syncthreads();
+      if (j < ntiles) copy_tile(V, j, vbuf + (j & 1) * TILE);
+      matrix_phase(j);
+      dma_wait();
+      __syncthreads();
+    }
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);

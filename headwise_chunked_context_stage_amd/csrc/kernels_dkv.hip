@@ -12,22 +12,6 @@
 namespace upipe {
 namespace {
 
-// One 256-byte row from global memory straight into LDS (no registers): lane
-// l copies bytes 4l..4l+3 of the row at `src` to LDS byte address dst + 4l.
-// `src` and `dst` are wave-uniform.  The copy is counted by vmcnt only and is
-// not seen by the compiler's wait insertion: dma_wait() before the barrier
-// that publishes the rows.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma_row(const void* src, unsigned dst, unsigned lane4) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(dst), "v"(lane4), "s"(src) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-__device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ unsigned lds_byte_addr(const void* p) {
-  return static_cast<unsigned>(reinterpret_cast<uintptr_t>((const lds_u16*)p));
-}
-
 // ---- dK, dV.  Workgroup: 128 key rows of one KV head, looping over the
 // stage's query heads of that group (ascending) and over 64-row query tiles.
 // Eight waves: each 32-key block has a pair of waves on one SIMD.  With the

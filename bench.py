@@ -68,7 +68,7 @@ def kernel_work(kind, S, D, d, U, r, causal=True):
     if kind == "dx":
         return 2.0 * S * D * d * (U + 2 * nkv), "flop"
     if kind == "bwd_pre":
-        return (2.0 * 2 * S * d + 4.0 * S) * U, "byte"  # read O, dO (bf16); write D (fp32)
+        return (2.0 * 2 * S * d + 12.0 * S) * U, "byte"  # read O, dO (bf16), LSE; write D, LSE*log2e (fp32)
     if kind == "fill":
         return 4.0 * S * D, "byte"
     return 0.0, "flop"

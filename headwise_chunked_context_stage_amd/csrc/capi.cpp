@@ -278,6 +278,7 @@ int upipe_bwd(const upipe_plan* h, const void* dO, const void* X, const void* Wq
     a.o_in = O;
     a.lse_in = LSE;
     a.dd = reinterpret_cast<float*>(at(ws, p.ws.dd));
+    a.lse2 = reinterpret_cast<float*>(at(ws, p.ws.lse2));
     a.dq = at(ws, p.ws.dq);
     a.dk = at(ws, p.ws.dk);
     a.dv = at(ws, p.ws.dv);

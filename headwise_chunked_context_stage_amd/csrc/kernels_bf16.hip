@@ -581,7 +581,9 @@ __global__ __launch_bounds__(fw::NT, 1) void attn_fwd_kernel(AttnArgs a) {
   }
 }
 
-// ---- D = rowsum(dO * O) for the stage's heads (fp32).  16 lanes per row.
+// ---- D = rowsum(dO * O) for the stage's heads (fp32), and the LSE in log2
+// units for the dK/dV pass, which copies both into LDS unchanged.  16 lanes
+// per row.
 __global__ __launch_bounds__(256) void bwd_pre_kernel(AttnArgs a) {
   const int u = blockIdx.y;
   const int h = a.q_head0 + u;
@@ -600,7 +602,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(AttnArgs a) {
   acc += __shfl_xor(acc, 4);
   acc += __shfl_xor(acc, 2);
   acc += __shfl_xor(acc, 1);
-  if (row < a.S && part == 0) a.dd[static_cast<int64_t>(u) * a.S + row] = acc;
+  if (row < a.S && part == 0) {
+    a.dd[static_cast<int64_t>(u) * a.S + row] = acc;
+    a.lse2[static_cast<int64_t>(u) * a.S + row] = a.lse_in[static_cast<int64_t>(h) * a.S + row] * kLog2e;
+  }
 }
 
 // ---- dQ.  Workgroup: 256 query rows of one head (8 waves x 32 rows); key

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
   using namespace kv;
   __shared__ __attribute__((aligned(16))) u16 qs[NQ * TILE];
   __shared__ __attribute__((aligned(16))) u16 gs[NG * TILE];
-  __shared__ __attribute__((aligned(16))) float stat[2][2][BM];  // [tile & 1][LSE (natural log), D][row]
+  __shared__ __attribute__((aligned(16))) float stat[2][2][BM];  // [tile & 1][LSE * log2(e), D][row]
   __shared__ __attribute__((aligned(16))) f32x4 pxch[4][8][64];  // P of each key block: [block][reg/4][lane]
   const int64_t S = a.S;
   const int lid = xcd_snake(blockIdx.x, gridDim.x);
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
         dma_row(qr + i * DH, qa + off, lane4);
         dma_row(gr + i * ldo, ga + off, lane4);
       }
-      if (wv == 0) dma_row(a.lse_in + static_cast<int64_t>(x.h) * S + q0, lds_byte_addr(&stat[slg][0][0]), lane4);
+      if (wv == 0) dma_row(a.lse2 + static_cast<int64_t>(u) * S + q0, lds_byte_addr(&stat[slg][0][0]), lane4);
       if (wv == 4) dma_row(a.dd + static_cast<int64_t>(u) * S + q0, lds_byte_addr(&stat[slg][1][0]), lane4);
     } else {
       const int64_t left = S - q0 - srow;
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
         const int r = tid % BM;
         const bool in = q0 + r < S;
         const int64_t q = in ? q0 + r : S - 1;
-        stat[slg][tid / BM][r] = tid < BM ? (in ? a.lse_in[static_cast<int64_t>(x.h) * S + q] : INFINITY)
+        stat[slg][tid / BM][r] = tid < BM ? (in ? a.lse2[static_cast<int64_t>(u) * S + q] : INFINITY)
                                           : (in ? a.dd[static_cast<int64_t>(u) * S + q] : 0.f);
       }
     }
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
           for (int g4 = 0; g4 < 4; ++g4) {
             const int j = 4 * qb + g4, r0 = 8 * j + 4 * hf;  // tile rows r0..r0+3 = registers 4*g4..4*g4+3
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sv[qb][4 * g4 + e] = ex2(__builtin_fmaf(sv[qb][4 * g4 + e], c, -kLog2e * l4[j][e]));
+            for (int e = 0; e < 4; ++e) sv[qb][4 * g4 + e] = ex2(__builtin_fmaf(sv[qb][4 * g4 + e], c, -l4[j][e]));
             if (need_mask) {
 #pragma unroll
               for (int e = 0; e < 4; ++e)

@@ -80,6 +80,7 @@ int make_plan(Plan& p, int64_t S, int64_t D, int H, int G, int d, int U, int cau
   w.v = take(nkv * Sd * e);
   w.fwd_bytes = off;
   w.dd = take(static_cast<size_t>(U) * S * 4);
+  w.lse2 = take(static_cast<size_t>(U) * S * 4);
   w.dq = take(U * Sd * e);
   w.dk = take(nkv * Sd * e);
   w.dv = take(nkv * Sd * e);

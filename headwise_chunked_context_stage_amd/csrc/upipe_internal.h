@@ -31,6 +31,7 @@ struct Stage {
 struct WsLayout {
   size_t q, k, v;              // Q [U][S][d], K [kv][S][d], V [kv][S][d]   (element type)
   size_t dd;                   // D = rowsum(dO*O) [U][S] fp32                 (backward)
+  size_t lse2;                 // LSE * log2(e) [U][S] fp32                    (backward)
   size_t dq;                   // dQ [U][S][d] (element type)                  (backward)
   size_t dk, dv;               // dK, dV [kv][S][d] (element type)             (backward)
   size_t dk_acc, dv_acc;       // fp32 carry of dK, dV across a group's stages (bf16 and U < r)
@@ -83,6 +84,7 @@ struct AttnArgs {
   const void* o_in;     // [S][H*d]
   const float* lse_in;  // [H][S]
   float* dd;            // D [nq][S]
+  float* lse2;          // LSE in log2 units [nq][S], written with D
   void* dq;             // dQ [nq][S][d]
   void* dk;             // dK [nkv][S][d], element type (written when the group is done)
   void* dv;

@@ -197,17 +197,18 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
   if (pwave) {
     for (int it = 0; it <= niter; ++it) {
       bf16x8 op[4];  // P of tile it, packed
+      __builtin_amdgcn_s_setprio(1);  // the first wave's S and exponentials are the round's critical path
       if (it + 1 < niter) issue(nc, sq + 1 == NQ ? 0 : sq + 1, sg ^ 1);
       if (it < niter) {
         // S = Q K^T; P = exp(S - LSE), masked above the diagonal; fp32 P to the partner
         f32x16 sv[2];
+        f32x4 l4[8];  // requested before the S MFMAs, so they are ready for the exponentials
+#pragma unroll
+        for (int j = 0; j < 8; ++j) l4[j] = *reinterpret_cast<const f32x4*>(&stat[sg][0][8 * j + 4 * hf]);
         row_pass(tile_addr(qs + sq * TILE, lane), sv);
         const int64_t q0 = static_cast<int64_t>(cc.qt) * BM;
         const bool need_mask = a.causal && q0 < wk0 + 31;
         const int mlim = static_cast<int>(myk - q0);  // tile row r is masked when r < mlim
-        f32x4 l4[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) l4[j] = *reinterpret_cast<const f32x4*>(&stat[sg][0][8 * j + 4 * hf]);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -226,6 +227,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
         for (int k4 = 0; k4 < 4; ++k4) op[k4] = pack8(sv[k4 / 2], k4 % 2);
       }
       __syncthreads();
+      __builtin_amdgcn_s_setprio(0);
       if (it < niter) col_pass(tile_addr(gs + sg * TILE, lane), op);  // dV += P^T dO
       dma_wait();
       __syncthreads();

@@ -96,13 +96,14 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
     }
   };
 
-  // Tile t + 1 is copied into LDS during tile t.  Wave w copies logical rows
-  // 8w..8w+7 of the Q and dO tiles, one DMA row each; waves 0 and 4 copy the
-  // tile's LSE and D.  A tile that runs past S goes through registers
-  // instead, with zero rows (and LSE = +inf, D = 0) beyond S.
+  // Tile t + 1 is copied into LDS during tile t, by the second waves of the
+  // pairs only (the first waves' S and exponentials are the round's critical
+  // path): wave 4 + w copies logical rows 16w..16w+15 of the Q and dO tiles,
+  // one direct row copy each; waves 4 and 5 copy the tile's LSE and D.  A
+  // tile that runs past S goes through registers instead, by every wave, with
+  // zero rows (and LSE = +inf, D = 0) beyond S.
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const unsigned lane4 = 4u * lane;
-  const int pr0 = 16 * (wv >> 1) + (wv & 1);  // prow(8 wv + i) = pr0 + 4 (i % 4) + 2 (i / 4)
   const int srow = tid >> 4, sc = tid & 15;
   auto issue = [&](const Cur& x, int slq, int slg) {
     const int u = x.h - a.q_head0;
@@ -112,17 +113,21 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
     u16* qd = qs + slq * TILE;
     u16* gd = gs + slg * TILE;
     if (q0 + BM <= S) {
-      const unsigned qa = lds_byte_addr(qd), ga = lds_byte_addr(gd);
-      const u16* qr = qb + 8 * wv * DH;
-      const u16* gr = gb + 8 * wv * ldo;
+      if (wv >= 4) {  // the second waves copy: rows 16 w'..16 w'+15, w' = wv - 4
+        const int w2 = wv - 4;
+        const unsigned qa = lds_byte_addr(qd) + static_cast<unsigned>(16 * w2 * RS * 2);
+        const unsigned ga = lds_byte_addr(gd) + static_cast<unsigned>(16 * w2 * RS * 2);
+        const u16* qr = qb + 16 * w2 * DH;
+        const u16* gr = gb + 16 * w2 * ldo;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const unsigned off = static_cast<unsigned>((pr0 + 4 * (i & 3) + 2 * (i >> 2)) * RS * 2);
-        dma_row(qr + i * DH, qa + off, lane4);
-        dma_row(gr + i * ldo, ga + off, lane4);
+        for (int i = 0; i < 16; ++i) {
+          const unsigned off = static_cast<unsigned>((((i & 3) << 2) | (((i >> 2) & 1) << 1) | ((i >> 3) & 1)) * RS * 2);
+          dma_row(qr + i * DH, qa + off, lane4);
+          dma_row(gr + i * ldo, ga + off, lane4);
+        }
+        if (wv == 4) dma_row(a.lse2 + static_cast<int64_t>(u) * S + q0, lds_byte_addr(&stat[slg][0][0]), lane4);
+        if (wv == 5) dma_row(a.dd + static_cast<int64_t>(u) * S + q0, lds_byte_addr(&stat[slg][1][0]), lane4);
       }
-      if (wv == 0) dma_row(a.lse2 + static_cast<int64_t>(u) * S + q0, lds_byte_addr(&stat[slg][0][0]), lane4);
-      if (wv == 4) dma_row(a.dd + static_cast<int64_t>(u) * S + q0, lds_byte_addr(&stat[slg][1][0]), lane4);
     } else {
       const int64_t left = S - q0 - srow;
 #pragma unroll

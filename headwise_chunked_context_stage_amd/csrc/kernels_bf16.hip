@@ -521,43 +521,51 @@ __global__ __launch_bounds__(fw::NT, 1) void attn_fwd_kernel(AttnArgs a) {
   // workgroup barriers.  K(j) is read in phases 2j (first waves) and 2j + 1
   // (second waves); V(j) in phases 2j + 2 and 2j + 3.  Tile copies: the first
   // waves copy K tiles, the second V tiles, 16 rows per wave, by direct
-  // global-to-LDS loads issued at the start of the wave's matrix phase (the
-  // softmax phase then carries no copy work).  K(j + 1) is issued in phase 2j
-  // and complete at the end of phase 2j + 1; V(j) is issued in phase 2j + 1
-  // and complete at its end.
+  // global-to-LDS loads, half at the start of each of the wave's two phases
+  // (issuing a row copy costs a wave tens of cycles, so neither phase takes
+  // all of them).  K(j + 1) is issued in phases 2j and 2j + 1 and complete at
+  // the end of 2j + 1; V(j) is issued in phases 2j and 2j + 1 and complete at
+  // the end of 2j + 1.
   const int wv = __builtin_amdgcn_readfirstlane(wave) & 3;
   const unsigned lane4 = 4u * lane;
-  auto copy_tile = [&](const u16* src, int j, u16* dst) {
+  // half `part` (rows 8 part .. 8 part + 7 of the wave's 16); a tile that
+  // runs past S is copied whole, through registers, with part 0
+  auto copy_tile = [&](const u16* src, int j, u16* dst, int part) {
     const int64_t r0 = static_cast<int64_t>(j) * BN;
     if (r0 + BN <= S) {
       const u16* g = src + (r0 + 16 * wv) * DH;
       const unsigned d = lds_byte_addr(dst) + static_cast<unsigned>(16 * wv * RS * 2);
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
+      for (int i = 8 * part; i < 8 * part + 8; ++i)
         dma_row(g + i * DH, d + static_cast<unsigned>((((i & 3) << 2) | (((i >> 2) & 1) << 1) | ((i >> 3) & 1)) * RS * 2), lane4);
-    } else {
+    } else if (part == 0) {
       TileLoad<BN * 16 / 256, 256> tl;
       tl.load(src, DH, r0, S, st);
       tl.store(dst, st);
     }
   };
-  if (first) copy_tile(K, 0, kbuf);
+  if (first) {
+    copy_tile(K, 0, kbuf, 0);
+    copy_tile(K, 0, kbuf, 1);
+  }
   dma_wait();
   __syncthreads();
   if (first) {
     for (int j = 0; j <= ntiles; ++j) {
-      if (j + 1 < ntiles) copy_tile(K, j + 1, kbuf + ((j + 1) & 1) * TILE);
+      if (j + 1 < ntiles) copy_tile(K, j + 1, kbuf + ((j + 1) & 1) * TILE, 0);
       matrix_phase(j);
       __syncthreads();
+      if (j + 1 < ntiles) copy_tile(K, j + 1, kbuf + ((j + 1) & 1) * TILE, 1);
       softmax_phase(j);
       dma_wait();
       __syncthreads();
     }
   } else {
     for (int j = 0; j <= ntiles; ++j) {
+      if (j < ntiles) copy_tile(V, j, vbuf + (j & 1) * TILE, 0);
       softmax_phase(j - 1);
       __syncthreads();
-      if (j < ntiles) copy_tile(V, j, vbuf + (j & 1) * TILE);
+      if (j < ntiles) copy_tile(V, j, vbuf + (j & 1) * TILE, 1);
       matrix_phase(j);
       dma_wait();
       __syncthreads();

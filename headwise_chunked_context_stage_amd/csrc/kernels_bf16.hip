@@ -149,14 +149,25 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(const u16* __restrict__ X,
 }
 
 // ---- weight gradient: dW[c][k] = sum_i A[i][c] X[i][k] (one chunk, K = S).
-// Both operands are read with i along the k-slots, so both tiles are staged
-// transposed (identity slot order).  A launch has few output tiles and a long
-// contraction, so each workgroup splits K: two groups of four waves sum the
-// first and the second half of the k-steps (the split point depends on S
-// only), and the halves are added in that order through LDS.
+// Both operands have the contraction index i along the rows of their source
+// ([S][128] activation-gradient chunk, [S][D] input), so both are copied
+// row-major into LDS in the attention tile layout (64 rows of 128 columns,
+// 16-byte chunks, no transposes) and read as column operands with the
+// transposing LDS reads; A and B then present the same k-slot order.  A launch
+// has few output tiles and a long contraction, so each workgroup splits K: two
+// groups of four waves sum the first and the second half of the k-steps (the
+// split point depends on S only), and the halves are added in that order
+// through LDS.
+namespace dwk {
+constexpr int ROWS = 64;            // contraction rows per k-step
+constexpr int TILE = ROWS * RS;     // one operand tile
+constexpr int NRR = 3;              // k-steps of global loads in flight
+}  // namespace dwk
+
 __global__ __launch_bounds__(512, 1) void dw_kernel(const u16* __restrict__ X, int64_t S, int64_t D,
                                                     ChunkTable t, int ncb) {
-  __shared__ __attribute__((aligned(16))) u16 lds[2][2 * GBUF];  // [group][buffer]
+  using namespace dwk;
+  __shared__ __attribute__((aligned(16))) u16 lds[2][2][2 * TILE];  // [group][buffer][A tile, X tile]
   const int total = ncb * t.n;
   const int lid = xcd_remap(blockIdx.x, total);
   const int cb = lid / t.n, ch = lid % t.n;
@@ -166,45 +177,40 @@ __global__ __launch_bounds__(512, 1) void dw_kernel(const u16* __restrict__ X, i
   const int grp = threadIdx.x / 256, tid = threadIdx.x % 256;
   const int wave = tid / 64, lane = tid % 64, col = lane % 32, hf = lane / 32;
   const int wm = wave / 2, wn = wave % 2;
-  // staging role: threads 0..127 of a group stage A (rows of S x 128 head
-  // columns), 128..255 stage X (rows of S x 128 columns of D); each one 8x8 block.
-  const int st = tid % 128, rg = st / 16, cc = st % 16;
-  const bool isA = tid < 128;
-  u16* gl = lds[grp];
+  // staging: thread tid moves rows tid/16 + 16 m (m < 4), 16-byte chunk tid % 16,
+  // of the A tile and of the X tile
+  const int srow = tid >> 4, sc = tid & 15;
 
-  // Global loads run three k-steps ahead through a ring of register sets;
-  // LDS is double-buffered.
-  constexpr int NRR = 3;
   u32x4 rr[NRR][8];
-  const int nk_all = static_cast<int>((S + GK - 1) / GK);
+  const int nk_all = static_cast<int>((S + ROWS - 1) / ROWS);
   const int half = (nk_all + 1) / 2;
-  const int kfirst = grp ? half : 0;                  // first k-step of this group
-  const int nk = grp ? nk_all - half : half;          // k-steps of this group
-  const int nk_max = half;                            // rounds run by both groups
+  const int kfirst = grp ? half : 0;          // first k-step of this group
+  const int nk = grp ? nk_all - half : half;  // k-steps of this group
+  const int nk_max = half;                    // rounds run by both groups
   auto load = [&](int set, int kb) {
-    const int64_t s0 = static_cast<int64_t>(kfirst + kb) * GK;
+    const int64_t s0 = static_cast<int64_t>(kfirst + kb) * ROWS;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int64_t gi = s0 + rg * 8 + m;
-      if (kb < nk && gi < S)
-        rr[set][m] = isA ? ld16(A + gi * DH + cc * 8) : ld16(X + gi * D + k0 + cc * 8);
-      else
-        rr[set][m] = u32x4{0, 0, 0, 0};
+    for (int m = 0; m < 4; ++m) {
+      const int64_t gi = s0 + srow + 16 * m;
+      const bool in = kb < nk && gi < S;
+      rr[set][m] = in ? ld16(A + gi * DH + sc * 8) : u32x4{0, 0, 0, 0};
+      rr[set][4 + m] = in ? ld16(X + gi * D + k0 + sc * 8) : u32x4{0, 0, 0, 0};
     }
   };
   auto store = [&](int set, int b) {
-    u16* base = gl + b * GBUF + (isA ? 0 : GB * GS);
-    u32x4 tc[8];
-    transpose8(rr[set], tc);
+    u16* at = lds[grp][b];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) st16(base + (cc * 8 + c) * GS + rg * 8, tc[c]);
+    for (int m = 0; m < 4; ++m) {
+      st16(at + toff(srow + 16 * m, sc * 8), rr[set][m]);
+      st16(at + TILE + toff(srow + 16 * m, sc * 8), rr[set][4 + m]);
+    }
   };
 
   f32x16 acc[2][2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a2 = 0; a2 < 2; ++a2)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = zero16();
+    for (int b2 = 0; b2 < 2; ++b2) acc[a2][b2] = zero16();
 
   // k-step kb's data sits in register set kb % NRR until its LDS store.
   // Steps beyond a group's range load zeros and are not accumulated.
@@ -218,15 +224,15 @@ __global__ __launch_bounds__(512, 1) void dw_kernel(const u16* __restrict__ X, i
     constexpr int SN = decltype(setc)::value;
     const int cur = kb & 1;
     if (kb < nk) {
-      const u16* as = gl + cur * GBUF;
-      const u16* xs = as + GB * GS;
+      const TileAddr ta = tile_addr(lds[grp][cur], lane);
+      const TileAddr tx = tile_addr(lds[grp][cur] + TILE, lane);
 #pragma unroll
-      for (int t4 = 0; t4 < GK / 16; ++t4) {
+      for (int t4 = 0; t4 < ROWS / 16; ++t4) {
         bf16x8 fa[2], fb[2];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) fa[mb] = frag(as + (64 * wm + 32 * mb + col) * GS + 16 * t4 + 8 * hf);
+        for (int mb = 0; mb < 2; ++mb) fa[mb] = col_frag(ta, 16 * t4, 64 * wm + 32 * mb);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) fb[nb] = frag(xs + (64 * wn + 32 * nb + col) * GS + 16 * t4 + 8 * hf);
+        for (int nb = 0; nb < 2; ++nb) fb[nb] = col_frag(tx, 16 * t4, 64 * wn + 32 * nb);
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -248,7 +254,7 @@ __global__ __launch_bounds__(512, 1) void dw_kernel(const u16* __restrict__ X, i
   if (kb + 1 < nk_max) body(kb + 1, std::integral_constant<int, 2>{});
 
   // second half to LDS (fp32, C layout per lane), then first + second in that order
-  float* red = reinterpret_cast<float*>(lds[1]);  // 64 KB of the second group's buffers
+  float* red = reinterpret_cast<float*>(lds[1]);  // the second group's buffers
   if (grp == 1) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)

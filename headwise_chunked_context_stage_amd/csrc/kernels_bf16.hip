@@ -287,47 +287,61 @@ __global__ __launch_bounds__(512, 1) void dw_kernel(const u16* __restrict__ X, i
 
 // ---- input gradient: dX[i][k] += sum over chunks (table order) of
 // sum_c A[i][c] W[c][k].  dX itself is the fp32 running sum (the MFMA C input).
+// The W tile (64 rows c x 128 columns k) is copied row-major in the attention
+// tile layout and read as column operands with the transposing LDS reads,
+// which present c in "slot order" (lane half h: c = 4h..4h+3, 8+4h..8+4h+3 of
+// each 16); the A tile (128 rows i x 64 columns c) is stored with the middle
+// 8-byte blocks of every 16-column group swapped, so that its plain row reads
+// present c in the same order.  No in-register transposes.
+namespace dxk {
+constexpr int WT = 64 * RS;  // W tile (64 rows of 128 columns)
+constexpr int AT = GB * GS;  // A tile (128 rows of 64 columns, row stride GS)
+}  // namespace dxk
+
 __global__ __launch_bounds__(256, 2) void dx_kernel(float* __restrict__ dX, int64_t S, int64_t D,
                                                     ChunkTable t, int nrb, int ncb) {
-  __shared__ __attribute__((aligned(16))) u16 lds[2 * GBUF];
+  using namespace dxk;
+  __shared__ __attribute__((aligned(16))) u16 lds[2 * (AT + WT)];
   const int lid = xcd_remap(blockIdx.x, nrb * ncb);
   const int rb = lid / ncb, cb = lid % ncb;
   const int64_t i0 = static_cast<int64_t>(rb) * GB;
   const int64_t k0 = static_cast<int64_t>(cb) * GB;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, col = lane % 32, hf = lane / 32;
   const int wm = wave / 2, wn = wave % 2;
-  const int rg = (tid % 128) / 16, cc = tid % 16;  // W staging block (threads 0..127)
 
-  u32x4 ra[4], rw[8];
+  // A: thread tid moves 16-column groups (row tid / 4 + 64 m, group tid % 4), m < 2;
+  // W: rows tid / 16 + 16 m (m < 4), 16-byte chunk tid % 16.
+  const int arow = tid >> 2, agrp = tid & 3;
+  const int wrow = tid >> 4, wc = tid & 15;
+  u32x4 ra[2][2], rw[4];
   auto load = [&](int step) {
     const int ch = step / (DH / GK), c0 = (step % (DH / GK)) * GK;
-    const u16* A = static_cast<const u16*>(t.a[ch]);
-    const u16* W = static_cast<const u16*>(t.w[ch]);
+    const u16* Ap = static_cast<const u16*>(t.a[ch]);
+    const u16* Wp = static_cast<const u16*>(t.w[ch]);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int row = tid / 8 + 32 * m, chunk = tid % 8;
-      const int64_t gi = i0 + row;
-      ra[m] = gi < S ? ld16(A + gi * DH + c0 + chunk * 8) : u32x4{0, 0, 0, 0};
+    for (int m = 0; m < 2; ++m) {
+      const int64_t gi = i0 + arow + 64 * m;
+      const u16* src = Ap + gi * DH + c0 + 16 * agrp;
+      ra[m][0] = gi < S ? ld16(src) : u32x4{0, 0, 0, 0};
+      ra[m][1] = gi < S ? ld16(src + 8) : u32x4{0, 0, 0, 0};
     }
-    if (tid < 128) {
 #pragma unroll
-      for (int m = 0; m < 8; ++m) rw[m] = ld16(W + static_cast<int64_t>(c0 + rg * 8 + m) * D + k0 + cc * 8);
-    }
+    for (int m = 0; m < 4; ++m) rw[m] = ld16(Wp + static_cast<int64_t>(c0 + wrow + 16 * m) * D + k0 + wc * 8);
   };
   auto store = [&](int b) {
-    u16* as = lds + b * GBUF;
-    u16* wt = as + GB * GS;
+    u16* as = lds + b * (AT + WT);
+    u16* wt = as + AT;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int row = tid / 8 + 32 * m, chunk = tid % 8;
-      st16(as + row * GS + chunk * 8, ra[m]);
+    for (int m = 0; m < 2; ++m) {
+      // logical columns [0-3 | 4-7] [8-11 | 12-15] -> physical [0-3 | 8-11] [4-7 | 12-15]
+      const u32x4 lo = {ra[m][0][0], ra[m][0][1], ra[m][1][0], ra[m][1][1]};
+      const u32x4 hi = {ra[m][0][2], ra[m][0][3], ra[m][1][2], ra[m][1][3]};
+      u16* dst = as + (arow + 64 * m) * GS + 16 * agrp;
+      st16(dst, lo);
+      st16(dst + 8, hi);
     }
-    if (tid < 128) {
-      u32x4 tc[8];
-      transpose8(rw, tc);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) st16(wt + (cc * 8 + c) * GS + rg * 8, tc[c]);
-    }
+    for (int m = 0; m < 4; ++m) st16(wt + toff(wrow + 16 * m, wc * 8), rw[m]);
   };
 
   f32x16 acc[2][2];
@@ -349,15 +363,15 @@ __global__ __launch_bounds__(256, 2) void dx_kernel(float* __restrict__ dX, int6
   for (int sidx = 0; sidx < nsteps; ++sidx) {
     const int cur = sidx & 1;
     if (sidx + 1 < nsteps) load(sidx + 1);
-    const u16* as = lds + cur * GBUF;
-    const u16* wt = as + GB * GS;
+    const u16* as = lds + cur * (AT + WT);
+    const TileAddr tw = tile_addr(lds + cur * (AT + WT) + AT, lane);
 #pragma unroll
     for (int t4 = 0; t4 < GK / 16; ++t4) {
       bf16x8 fa[2], fb[2];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) fa[mb] = frag(as + (64 * wm + 32 * mb + col) * GS + 16 * t4 + 8 * hf);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) fb[nb] = frag(wt + (64 * wn + 32 * nb + col) * GS + 16 * t4 + 8 * hf);
+      for (int nb = 0; nb < 2; ++nb) fb[nb] = col_frag(tw, 16 * t4, 64 * wn + 32 * nb);
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll

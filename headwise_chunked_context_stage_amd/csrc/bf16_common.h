@@ -60,21 +60,6 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& c, int t) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// 8x8 bf16 transpose: in[j] = row j (8 elements), out[c] = column c.
-__device__ __forceinline__ void transpose8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int k = c / 2;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const unsigned a = in[2 * m][k], b = in[2 * m + 1][k];
-      out[c][m] = (c & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-    }
-  }
-}
-
-// Row (within a 16-row group) of slot m of the 8-slot half `hh`.
-__device__ __forceinline__ int slot_row(int hh, int m) { return m < 4 ? 4 * hh + m : 8 + 4 * hh + (m - 4); }
 
 // Map a workgroup id so that each XCD (ids are dealt round-robin over 8 XCDs)
 // runs one contiguous range of logical ids.

@@ -11,10 +11,12 @@
 // indices in any fixed order.  This is what lets an fp32 C result feed the
 // next product straight from registers: the 8 registers 8t..8t+7 of a C block
 // in lane half h hold the rows 16t + {4h..4h+3, 8+4h..8+4h+3}, and an operand
-// read from LDS must present the same rows in its slots 8h..8h+7.  Tiles that
-// are read "transposed" (k along a row of the source) are therefore staged
-// into LDS with that row order inside every 16-row group ("slot order"), by an
-// in-register 8x8 transpose during the global->LDS copy.
+// read from LDS must present the same rows in its slots 8h..8h+7 ("slot
+// order").  Operands whose contraction index runs down the rows of their
+// source tile are read with the transposing LDS reads (ds_read_b64_tr_b16),
+// which deliver exactly that order; an operand read along rows is stored with
+// its columns permuted to match (the dX GEMM's A tile).  No kernel transposes
+// in registers.
 //
 // Attention (flash formulation; the per-stage attention of the pages,
 // paper.rainbus.top summary of "Untied Ulysses", section 方法步骤详情 step (3)):

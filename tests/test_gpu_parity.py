@@ -180,6 +180,25 @@ def test_bf16_short_sequences(S):
             assert np.max(np.abs(host(out["O"])[0, h * 128:(h + 1) * 128] - v0[0, g * 128:(g + 1) * 128])) < 2e-2
 
 
+def test_auto_u_runs_bit_identical_to_u1():
+    """upipe_auto_u picks a legal U under a workspace budget; the layer run
+    with that U and a workspace of exactly its size equals the U = 1 run bit
+    for bit (chunking never changes results)."""
+    shape = LayerShape(S=768, D=512, H=8, G=2, d=128)
+    inp = {k: v.cuda() for k, v in make_inputs(shape, "bf16", seed=5, device="cpu").items()}
+    budget = upipe.Plan(shape.S, shape.D, shape.H, shape.G, shape.d, 4).peak_bytes + 1000
+    U = upipe.upipe_auto_u(shape.S, shape.D, shape.H, shape.G, shape.d, budget)
+    say("auto U=%d for a budget of %d bytes" % (U, budget))
+    assert U == 4
+    plan = upipe.Plan(shape.S, shape.D, shape.H, shape.G, shape.d, U)
+    assert plan.peak_bytes <= budget
+    out = run(plan, inp)
+    torch.cuda.synchronize()
+    assert out["ws"].numel() == plan.peak_bytes
+    out.pop("ws")
+    assert_same_bits(run_layer(shape, "bf16", 1, inp), out, "auto U")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_non_causal(dtype):
     shape = LayerShape(S=320, D=256, H=4, G=2, d=128 if dtype == "bf16" else 64)

@@ -177,6 +177,54 @@ __device__ __forceinline__ unsigned lds_byte_addr(const void* p) {
   return static_cast<unsigned>(reinterpret_cast<uintptr_t>((const lds_u16*)p));
 }
 
+// ---- Swizzled attention tiles: 64 rows of 128 bf16 columns, 256-byte rows
+// without padding; the 16-byte chunk c of row r sits at position c ^ swz(r),
+// swz(r) = 4 (r % 4) + (r / 4) % 4.  Sixteen consecutive rows read at one
+// chunk (row operands) and the transposing reads of four rows by 64 bytes
+// (column operands) both touch every bank once per 256 bytes.  A tile can be
+// filled by 4-row direct copies (global_load_lds_dwordx4: 1 KB of LDS per wave
+// instruction), the lanes fetching their chunks from the permuted positions.
+__device__ __forceinline__ int swz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+struct SwzAddr {
+  unsigned row;  // row operand, rows lane % 32 (+ 32 blk), chunk 2t + lane / 32: ^ 32t
+  unsigned col;  // column operand, rows r0 + 4 (lane / 32) + (lane % 16) / 4, columns n0 + ...: ^ 64 (n0 / 32)
+};
+__device__ __forceinline__ SwzAddr swz_addr(const u16* tile, int lane) {
+  const unsigned base = lds_byte_addr(tile);  // 256-byte aligned
+  const int hf = lane >> 5, g16 = (lane >> 4) & 1, i16 = lane & 15, k = i16 >> 2, cp = i16 & 3;
+  const int r0 = lane & 31;
+  unsigned rw = base + r0 * 256u + 16u * (hf ^ swz(r0));
+  unsigned cl = base + (4 * hf + k) * 256u + 64u * k + 16u * ((2 * g16 + (cp >> 1)) ^ hf) + 8u * (cp & 1);
+  asm volatile("" : "+v"(rw), "+v"(cl));
+  return SwzAddr{rw, cl};
+}
+__device__ __forceinline__ bf16x8 swz_row_frag(const SwzAddr& a, int blk, int t) {
+  const unsigned p = (a.row ^ (32u * t)) + 8192u * blk;
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const lds_u32x4*>(static_cast<uintptr_t>(p)));
+}
+// Column operand: column n0 + lane % 32 of rows r0 .. r0 + 15 (r0 % 16 == 0,
+// n0 % 32 == 0) in the slot order of a C block.
+__device__ __forceinline__ bf16x8 swz_col_frag(const SwzAddr& a, int r0, int n0) {
+  const unsigned lo = (a.col ^ (2u * n0)) + 256u * r0;
+  const unsigned hi = (a.col ^ (2u * n0 + 32u)) + 256u * (r0 + 8);
+  const v4i16 l4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_v4i16*>(static_cast<uintptr_t>(lo)));
+  const v4i16 h4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_v4i16*>(static_cast<uintptr_t>(hi)));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, l4), h2 = __builtin_bit_cast(u32x2, h4);
+  return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+}
+// Element offset of (row r, 16-byte chunk c) in a swizzled tile.
+__device__ __forceinline__ int swz_off(int r, int c) { return r * 128 + 8 * (c ^ swz(r)); }
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// Rows 4q .. 4q + 3 (q < 4) of a 16-row block: src and dst are the block's
+// first row (wave-uniform); voff = (lane / 16) * 256 + 16 ((lane % 16) ^ (4 (lane / 16) + q)).
+__device__ __forceinline__ void dma_rows4(const void* src, unsigned dst, unsigned voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(dst), "v"(voff), "s"(src) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // Copy rows [row0, row0 + nrows) of a [S][ld] bf16 matrix (128 columns from
 // `src`) into a tile; rows at or beyond S are zero.  NCH chunks of 16 bytes
 // per thread, thread t handling chunks t, t + 256, ...

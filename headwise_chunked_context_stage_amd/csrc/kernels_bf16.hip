@@ -639,21 +639,24 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(AttnArgs a) {
 }
 
 // ---- dQ.  Workgroup: 256 query rows of one head (8 waves x 32 rows); key
-// tiles of 64 rows, staged once for all 8 waves.  LDS holds two pairs of K/V
+// tiles of 64 rows, copied once for all 8 waves.  LDS holds two pairs of K/V
 // tiles: the waves run two tiles between barriers while the next pair is
 // copied in.  Orientation as in the forward (lane = query row): S^T and dP^T
 // from registers Q, dO against K and V row operands, then dQ^T += K^T dS^T
-// with K read as a column operand of the same tile.
+// with K read as a column operand of the same tile.  The tiles are swizzled
+// and filled by 4-row direct copies issued by the first wave of each SIMD:
+// with two waves per SIMD the first (older) wave finishes its tiles well
+// ahead of the second, so it has the time to issue them.
 namespace dqk {
 constexpr int BM = 256, BN = 64;
 constexpr int NT = 512;  // threads
-constexpr int TILE = BN * RS;
-constexpr int BUF = 2 * TILE;  // K and V
+constexpr int TILE = BN * 128;  // swizzled 64-row tile (elements)
+constexpr int BUF = 2 * TILE;   // K and V
 }  // namespace dqk
 
 __global__ __launch_bounds__(dqk::NT, 1) void attn_dq_kernel(AttnArgs a) {
   using namespace dqk;
-  __shared__ __attribute__((aligned(16))) u16 lds[4 * BUF];
+  __shared__ __attribute__((aligned(256))) u16 lds[4 * BUF];
   const int64_t S = a.S;
   const int nqb = static_cast<int>((S + BM - 1) / BM);
   const int qb = nqb - 1 - static_cast<int>(blockIdx.x) / a.nq;
@@ -663,6 +666,7 @@ __global__ __launch_bounds__(dqk::NT, 1) void attn_dq_kernel(AttnArgs a) {
   const u16* K = static_cast<const u16*>(a.k) + static_cast<int64_t>(gl) * S * DH;
   const u16* V = static_cast<const u16*>(a.v) + static_cast<int64_t>(gl) * S * DH;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, col = lane % 32, hf = lane / 32;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int64_t qfirst = static_cast<int64_t>(qb) * BM;
   const int64_t wq0 = qfirst + 32 * wave;
   const int64_t myq = wq0 + col;
@@ -686,33 +690,65 @@ __global__ __launch_bounds__(dqk::NT, 1) void attn_dq_kernel(AttnArgs a) {
   const int64_t kv_end = a.causal ? min(S, qfirst + BM) : S;
   const int ntiles = static_cast<int>((kv_end + BN - 1) / BN);
 
-  TileLoad<BN * 16 / NT, NT> lk, lv;
-  auto load = [&](int j) {
-    lk.load(K, DH, static_cast<int64_t>(j) * BN, S, tid);
-    lv.load(V, DH, static_cast<int64_t>(j) * BN, S, tid);
+  // Copies: waves 0..3 each move rows 16 w .. 16 w + 15 of the K and V tiles,
+  // four 4-row copies per tile.  A tile that runs past S is staged through
+  // registers by every thread (rows beyond S are zero).
+  unsigned voff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) voff[q] = (lane >> 4) * 256u + 16u * ((lane & 15) ^ (4 * (lane >> 4) + q));
+  auto copy_tile = [&](const u16* src, int j, u16* dst) {  // waves 0..3, whole tiles only
+    const int64_t r0 = static_cast<int64_t>(j) * BN + 16 * wv;
+    const unsigned d = lds_byte_addr(dst) + static_cast<unsigned>(16 * wv * 256);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dma_rows4(src + (r0 + 4 * q) * DH, d + 1024u * q, voff[q]);
   };
-  auto store = [&](int b) {
-    lk.store(lds + b * BUF, tid);
-    lv.store(lds + b * BUF + TILE, tid);
+  auto stage_regs = [&](const u16* src, int j, u16* dst) {  // every thread, synchronous
+    const int64_t r0 = static_cast<int64_t>(j) * BN;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int e = tid + NT * m, row = e >> 4, ck = e & 15;
+      const u32x4 v = r0 + row < S ? ld16(src + (r0 + row) * DH + 8 * ck) : u32x4{0, 0, 0, 0};
+      st16(dst + swz_off(row, ck), v);
+    }
+  };
+  auto whole = [&](int j) { return static_cast<int64_t>(j) * BN + BN <= S; };
+  // tiles j and j + 1 (when they exist) into pair slot p
+  auto issue_pair = [&](int j, int p) {
+    const bool w0 = j < ntiles && whole(j), w1 = j + 1 >= ntiles || whole(j + 1);
+    if (w0 && w1) {
+      if (wv < 4) {
+        copy_tile(K, j, lds + 2 * p * BUF);
+        copy_tile(V, j, lds + 2 * p * BUF + TILE);
+        if (j + 1 < ntiles) {
+          copy_tile(K, j + 1, lds + (2 * p + 1) * BUF);
+          copy_tile(V, j + 1, lds + (2 * p + 1) * BUF + TILE);
+        }
+      }
+    } else {
+      if (j < ntiles) {
+        stage_regs(K, j, lds + 2 * p * BUF);
+        stage_regs(V, j, lds + 2 * p * BUF + TILE);
+      }
+      if (j + 1 < ntiles) {
+        stage_regs(K, j + 1, lds + (2 * p + 1) * BUF);
+        stage_regs(V, j + 1, lds + (2 * p + 1) * BUF + TILE);
+      }
+    }
   };
 
   f32x16 dq[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) dq[i] = zero16();
 
-  load(0);
-  store(0);
-  if (ntiles > 1) {
-    load(1);
-    store(1);
-  }
+  issue_pair(0, 0);
+  dma_wait();
   __syncthreads();
   auto process = [&](int j, int cur) {
     const int64_t kv0 = static_cast<int64_t>(j) * BN;
     const bool active = !a.causal || kv0 <= wq0 + 31;
     if (active) {
-      const TileAddr ks = tile_addr(lds + cur * BUF, lane);
-      const TileAddr vs = tile_addr(lds + cur * BUF + TILE, lane);
+      const SwzAddr ks = swz_addr(lds + cur * BUF, lane);
+      const SwzAddr vs = swz_addr(lds + cur * BUF + TILE, lane);
       const bool need_mask = a.causal ? (kv0 + BN - 1 > wq0) : (kv0 + BN > S);
       // key kv0 + j is masked when j > lim
       const int lim = static_cast<int>(a.causal ? min(myq - kv0, static_cast<int64_t>(BN)) :
@@ -724,8 +760,8 @@ __global__ __launch_bounds__(dqk::NT, 1) void attn_dq_kernel(AttnArgs a) {
         f32x16 s = zero16(), dp = zero16();
         bf16x8 fa[2][2];
         auto load_a = [&](int t, bf16x8 (&f)[2]) {
-          f[0] = row_frag(ks, b, t);
-          f[1] = row_frag(vs, b, t);
+          f[0] = swz_row_frag(ks, b, t);
+          f[1] = swz_row_frag(vs, b, t);
         };
         load_a(0, fa[0]);
 #pragma unroll
@@ -749,7 +785,7 @@ __global__ __launch_bounds__(dqk::NT, 1) void attn_dq_kernel(AttnArgs a) {
         // step outermost: four alternating accumulators, each summing its
         // 16-key steps in order; K operands requested 2 groups ahead
         bf16x8 fc[3];
-        auto load_c = [&](int gi) { return col_frag(ks, 32 * b + 16 * (gi / 4), 32 * (gi % 4)); };
+        auto load_c = [&](int gi) { return swz_col_frag(ks, 32 * b + 16 * (gi / 4), 32 * (gi % 4)); };
         fc[0] = load_c(0);
         fc[1] = load_c(1);
 #pragma unroll
@@ -764,12 +800,10 @@ __global__ __launch_bounds__(dqk::NT, 1) void attn_dq_kernel(AttnArgs a) {
   };
   for (int j0 = 0; j0 < ntiles; j0 += 2) {
     const int p = (j0 >> 1) & 1;  // pair slot of tiles j0, j0 + 1
-    if (j0 + 2 < ntiles) load(j0 + 2);
+    if (j0 + 2 < ntiles) issue_pair(j0 + 2, p ^ 1);
     process(j0, 2 * p);
-    if (j0 + 2 < ntiles) store(2 * (p ^ 1));
-    if (j0 + 3 < ntiles) load(j0 + 3);
     if (j0 + 1 < ntiles) process(j0 + 1, 2 * p + 1);
-    if (j0 + 3 < ntiles) store(2 * (p ^ 1) + 1);
+    dma_wait();
     __syncthreads();
   }
 

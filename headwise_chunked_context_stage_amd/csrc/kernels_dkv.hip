@@ -27,15 +27,15 @@ namespace {
 // registers, and across the stages of a group in the fp32 carry buffers.
 namespace kv {
 constexpr int BN = 128, BM = 64;
-constexpr int TILE = BM * RS;  // one 64-row tile
+constexpr int TILE = BM * 128;  // one swizzled 64-row tile
 constexpr int NQ = 3;          // Q tiles it - 1 (dK), it (S), it + 1 (being filled)
 constexpr int NG = 2;          // dO tiles it (dP, dV), it + 1 (being filled)
 }  // namespace kv
 
 __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
   using namespace kv;
-  __shared__ __attribute__((aligned(16))) u16 qs[NQ * TILE];
-  __shared__ __attribute__((aligned(16))) u16 gs[NG * TILE];
+  __shared__ __attribute__((aligned(256))) u16 qs[NQ * TILE];
+  __shared__ __attribute__((aligned(256))) u16 gs[NG * TILE];
   __shared__ __attribute__((aligned(16))) float stat[2][2][BM];  // [tile & 1][LSE * log2(e), D][row]
   __shared__ __attribute__((aligned(16))) f32x4 pxch[4][8][64];  // P of each key block: [block][reg/4][lane]
   const int64_t S = a.S;
@@ -105,6 +105,10 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const unsigned lane4 = 4u * lane;
   const int srow = tid >> 4, sc = tid & 15;
+  // per-lane parts of the 4-row copies: row lane / 16 of the four, chunk
+  // (lane % 16) ^ (4 (lane / 16) + q) of it (the swizzle of the tile)
+  const unsigned swx = 16u * ((lane & 15) ^ (4 * (lane >> 4)));
+  const unsigned rq = (lane >> 4) * 256u, rg = (lane >> 4) * static_cast<unsigned>(ldo * 2);
   auto issue = [&](const Cur& x, int slq, int slg) {
     const int u = x.h - a.q_head0;
     const int64_t q0 = static_cast<int64_t>(x.qt) * BM;
@@ -113,17 +117,17 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
     u16* qd = qs + slq * TILE;
     u16* gd = gs + slg * TILE;
     if (q0 + BM <= S) {
-      if (wv >= 4) {  // the second waves copy: rows 16 w'..16 w'+15, w' = wv - 4
+      if (wv >= 4) {  // the second waves copy: rows 16 w'..16 w'+15, w' = wv - 4, four rows per copy
         const int w2 = wv - 4;
-        const unsigned qa = lds_byte_addr(qd) + static_cast<unsigned>(16 * w2 * RS * 2);
-        const unsigned ga = lds_byte_addr(gd) + static_cast<unsigned>(16 * w2 * RS * 2);
+        const unsigned qa = lds_byte_addr(qd) + static_cast<unsigned>(16 * w2 * 256);
+        const unsigned ga = lds_byte_addr(gd) + static_cast<unsigned>(16 * w2 * 256);
         const u16* qr = qb + 16 * w2 * DH;
         const u16* gr = gb + 16 * w2 * ldo;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const unsigned off = static_cast<unsigned>((((i & 3) << 2) | (((i >> 2) & 1) << 1) | ((i >> 3) & 1)) * RS * 2);
-          dma_row(qr + i * DH, qa + off, lane4);
-          dma_row(gr + i * ldo, ga + off, lane4);
+        for (int q = 0; q < 4; ++q) {
+          const unsigned sw = swx ^ (16u * q);  // 16 ((lane % 16) ^ (4 (lane / 16) + q))
+          dma_rows4(qr + 4 * q * DH, qa + 1024u * q, rq + sw);
+          dma_rows4(gr + 4 * q * ldo, ga + 1024u * q, rg + sw);
         }
         if (wv == 4) dma_row(a.lse2 + static_cast<int64_t>(u) * S + q0, lds_byte_addr(&stat[slg][0][0]), lane4);
         if (wv == 5) dma_row(a.dd + static_cast<int64_t>(u) * S + q0, lds_byte_addr(&stat[slg][1][0]), lane4);
@@ -134,8 +138,8 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
       for (int m = 0; m < 2; ++m) {
         const u32x4 vq = 32 * m < left ? ld16(qb + (srow + 32 * m) * DH + sc * 8) : u32x4{0, 0, 0, 0};
         const u32x4 vg = 32 * m < left ? ld16(gb + (srow + 32 * m) * ldo + sc * 8) : u32x4{0, 0, 0, 0};
-        st16(qd + toff(srow + 32 * m, sc * 8), vq);
-        st16(gd + toff(srow + 32 * m, sc * 8), vg);
+        st16(qd + swz_off(srow + 32 * m, sc), vq);
+        st16(gd + swz_off(srow + 32 * m, sc), vg);
       }
       if (tid < 2 * BM) {
         const int r = tid % BM;
@@ -159,12 +163,12 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
 
   // 32x64 C blocks of one tile: rows (query) x keys of this wave, two chains
   // over the 128 head columns; row operands from LDS two steps ahead.
-  auto row_pass = [&](const TileAddr& xa, f32x16 (&sv)[2]) {
+  auto row_pass = [&](const SwzAddr& xa, f32x16 (&sv)[2]) {
     sv[0] = sv[1] = zero16();
     bf16x8 fa[3][2];
     auto row_ops = [&](int t, bf16x8 (&f)[2]) {
-      f[0] = row_frag(xa, 0, t);
-      f[1] = row_frag(xa, 1, t);
+      f[0] = swz_row_frag(xa, 0, t);
+      f[1] = swz_row_frag(xa, 1, t);
     };
     row_ops(0, fa[0]);
     row_ops(1, fa[1]);
@@ -180,9 +184,9 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
   // acc += op^T Y over the 64 rows of a tile: Y read as column operands,
   // step k4 outermost so the four accumulators alternate (each sums
   // k4 = 0..3 in order); operands requested two groups ahead.
-  auto col_pass = [&](const TileAddr& ya, const bf16x8 (&op)[4]) {
+  auto col_pass = [&](const SwzAddr& ya, const bf16x8 (&op)[4]) {
     bf16x8 fc[3];
-    auto col_op = [&](int gi) { return col_frag(ya, 16 * (gi / 4), 32 * (gi % 4)); };
+    auto col_op = [&](int gi) { return swz_col_frag(ya, 16 * (gi / 4), 32 * (gi % 4)); };
     fc[0] = col_op(0);
     fc[1] = col_op(1);
 #pragma unroll
@@ -210,7 +214,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
         f32x4 l4[8];  // requested before the S MFMAs, so they are ready for the exponentials
 #pragma unroll
         for (int j = 0; j < 8; ++j) l4[j] = *reinterpret_cast<const f32x4*>(&stat[sg][0][8 * j + 4 * hf]);
-        row_pass(tile_addr(qs + sq * TILE, lane), sv);
+        row_pass(swz_addr(qs + sq * TILE, lane), sv);
         const int64_t q0 = static_cast<int64_t>(cc.qt) * BM;
         const bool need_mask = a.causal && q0 < wk0 + 31;
         const int mlim = static_cast<int>(myk - q0);  // tile row r is masked when r < mlim
@@ -233,7 +237,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
       }
       __syncthreads();
       __builtin_amdgcn_s_setprio(0);
-      if (it < niter) col_pass(tile_addr(gs + sg * TILE, lane), op);  // dV += P^T dO
+      if (it < niter) col_pass(swz_addr(gs + sg * TILE, lane), op);  // dV += P^T dO
       dma_wait();
       __syncthreads();
       next_tile();
@@ -243,8 +247,8 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
     f32x16 sv[2];  // dP of the current tile
     for (int it = 0; it <= niter; ++it) {
       if (it + 1 < niter) issue(nc, sq + 1 == NQ ? 0 : sq + 1, sg ^ 1);
-      if (it < niter) row_pass(tile_addr(gs + sg * TILE, lane), sv);  // dP = dO V^T
-      if (it >= 1) col_pass(tile_addr(qs + (sq == 0 ? NQ - 1 : sq - 1) * TILE, lane), op);  // dK += dS^T Q, tile it - 1
+      if (it < niter) row_pass(swz_addr(gs + sg * TILE, lane), sv);  // dP = dO V^T
+      if (it >= 1) col_pass(swz_addr(qs + (sq == 0 ? NQ - 1 : sq - 1) * TILE, lane), op);  // dK += dS^T Q, tile it - 1
       __syncthreads();
       if (it < niter) {
         // dS = P (dP - D) with the partner's fp32 P

@@ -98,10 +98,10 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
 
   // Tile t + 1 is copied into LDS during tile t, by the second waves of the
   // pairs only (the first waves' S and exponentials are the round's critical
-  // path): wave 4 + w copies logical rows 16w..16w+15 of the Q and dO tiles,
-  // one direct row copy each; waves 4 and 5 copy the tile's LSE and D.  A
-  // tile that runs past S goes through registers instead, by every wave, with
-  // zero rows (and LSE = +inf, D = 0) beyond S.
+  // path): wave 4 + w copies rows 16w..16w+15 of the swizzled Q and dO tiles,
+  // four rows per direct copy; waves 4 and 5 copy the tile's LSE and D (one
+  // 256-byte row each).  A tile that runs past S goes through registers
+  // instead, by every wave, with zero rows (and LSE = +inf, D = 0) beyond S.
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const unsigned lane4 = 4u * lane;
   const int srow = tid >> 4, sc = tid & 15;

@@ -405,14 +405,14 @@ __global__ __launch_bounds__(256, 2) void dx_kernel(float* __restrict__ dX, int6
 namespace fw {
 constexpr int BM = 256, BN = 64;
 constexpr int NT = 512;         // threads
-constexpr int TILE = BN * RS;   // elements of one 64-row tile
+constexpr int TILE = BN * 128;  // elements of one swizzled 64-row tile
 constexpr float kLazy = 8.f;    // keep a stale running max while the new one exceeds it by <= 8 (log2)
 }  // namespace fw
 
 __global__ __launch_bounds__(fw::NT, 1) void attn_fwd_kernel(AttnArgs a) {
   using namespace fw;
-  __shared__ __attribute__((aligned(16))) u16 kbuf[2 * TILE];
-  __shared__ __attribute__((aligned(16))) u16 vbuf[2 * TILE];
+  __shared__ __attribute__((aligned(256))) u16 kbuf[2 * TILE];
+  __shared__ __attribute__((aligned(256))) u16 vbuf[2 * TILE];
   const int64_t S = a.S;
   const int nqb = static_cast<int>((S + BM - 1) / BM);
   const int qb = nqb - 1 - static_cast<int>(blockIdx.x) / a.nq;  // longest rows first
@@ -452,9 +452,9 @@ __global__ __launch_bounds__(fw::NT, 1) void attn_fwd_kernel(AttnArgs a) {
     if (j >= 1 && active(j - 1)) {
       // step k4 outermost so the four accumulators alternate (each still
       // sums k4 = 0..3 in order); V operands requested 3 groups ahead.
-      const TileAddr va = tile_addr(vbuf + ((j - 1) & 1) * TILE, lane);
+      const SwzAddr va = swz_addr(vbuf + ((j - 1) & 1) * TILE, lane);
       bf16x8 fc[4];
-      auto load_c = [&](int gi) { return col_frag(va, 16 * (gi / 4), 32 * (gi % 4)); };
+      auto load_c = [&](int gi) { return swz_col_frag(va, 16 * (gi / 4), 32 * (gi % 4)); };
       fc[0] = load_c(0);
       fc[1] = load_c(1);
       fc[2] = load_c(2);
@@ -469,12 +469,12 @@ __global__ __launch_bounds__(fw::NT, 1) void attn_fwd_kernel(AttnArgs a) {
     if (j < ntiles && active(j)) {
       // two accumulator chains; the K operands of step t + 2 are requested
       // before the MFMAs of step t are issued
-      const TileAddr ka = tile_addr(kbuf + (j & 1) * TILE, lane);
+      const SwzAddr ka = swz_addr(kbuf + (j & 1) * TILE, lane);
       s[0] = s[1] = zero16();
       bf16x8 fa[3][2];
       auto load_a = [&](int t, bf16x8 (&f)[2]) {
-        f[0] = row_frag(ka, 0, t);
-        f[1] = row_frag(ka, 1, t);
+        f[0] = swz_row_frag(ka, 0, t);
+        f[1] = swz_row_frag(ka, 1, t);
       };
       load_a(0, fa[0]);
       load_a(1, fa[1]);
@@ -542,28 +542,30 @@ __global__ __launch_bounds__(fw::NT, 1) void attn_fwd_kernel(AttnArgs a) {
   // MFMAs overlap the other's exponentials.  Phases are separated by
   // workgroup barriers.  K(j) is read in phases 2j (first waves) and 2j + 1
   // (second waves); V(j) in phases 2j + 2 and 2j + 3.  Tile copies: the first
-  // waves copy K tiles, the second V tiles, 16 rows per wave, by direct
-  // global-to-LDS loads, half at the start of each of the wave's two phases
+  // waves copy K tiles, the second V tiles (swizzled), 16 rows per wave, by
+  // 4-row direct global-to-LDS copies, half at the start of each of the wave's two phases
   // (issuing a row copy costs a wave tens of cycles, so neither phase takes
   // all of them).  K(j + 1) is issued in phases 2j and 2j + 1 and complete at
   // the end of 2j + 1; V(j) is issued in phases 2j and 2j + 1 and complete at
   // the end of 2j + 1.
   const int wv = __builtin_amdgcn_readfirstlane(wave) & 3;
-  const unsigned lane4 = 4u * lane;
-  // half `part` (rows 8 part .. 8 part + 7 of the wave's 16); a tile that
-  // runs past S is copied whole, through registers, with part 0
+  // per-lane parts of the 4-row copies into the swizzled tiles: row lane / 16
+  // of the four, chunk (lane % 16) ^ (4 (lane / 16) + q)
+  const unsigned swx = 16u * ((lane & 15) ^ (4 * (lane >> 4))), rq = (lane >> 4) * 256u;
+  // half `part` (rows 8 part .. 8 part + 7 of the wave's 16, two 4-row
+  // copies); a tile that runs past S is copied whole, through registers, with part 0
   auto copy_tile = [&](const u16* src, int j, u16* dst, int part) {
     const int64_t r0 = static_cast<int64_t>(j) * BN;
     if (r0 + BN <= S) {
       const u16* g = src + (r0 + 16 * wv) * DH;
-      const unsigned d = lds_byte_addr(dst) + static_cast<unsigned>(16 * wv * RS * 2);
+      const unsigned d = lds_byte_addr(dst) + static_cast<unsigned>(16 * wv * 256);
 #pragma unroll
-      for (int i = 8 * part; i < 8 * part + 8; ++i)
-        dma_row(g + i * DH, d + static_cast<unsigned>((((i & 3) << 2) | (((i >> 2) & 1) << 1) | ((i >> 3) & 1)) * RS * 2), lane4);
+      for (int q = 2 * part; q < 2 * part + 2; ++q) dma_rows4(g + 4 * q * DH, d + 1024u * q, rq + (swx ^ (16u * q)));
     } else if (part == 0) {
       TileLoad<BN * 16 / 256, 256> tl;
       tl.load(src, DH, r0, S, st);
-      tl.store(dst, st);
+#pragma unroll
+      for (int m = 0; m < BN * 16 / 256; ++m) st16(dst + swz_off((st >> 4) + 16 * m, st & 15), tl.r[m]);
     }
   };
   if (first) {

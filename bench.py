@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="llama8b_s128k")
     ap.add_argument("--U", type=int, default=None)
+    ap.add_argument("--pipeline", action="store_true",
+                    help="stage pipelining: the GEMMs of neighbouring stages on a second stream")
     ap.add_argument("--skip-cpu-baseline", action="store_true",
                     help="omit the oracle timing (profiling runs only)")
     ap.add_argument("--cpu-baseline-S", type=int, default=8192)
@@ -156,7 +158,8 @@ def main():
     S, D, H, G, d = shape.S, shape.D, shape.H, shape.G, shape.d
     r = H // G
     dev = torch.device("cuda:0")
-    print("bench: %s S=%d D=%d H=%d G=%d d=%d U=%d" % (args.config, S, D, H, G, d, U),
+    print("bench: %s S=%d D=%d H=%d G=%d d=%d U=%d%s" % (args.config, S, D, H, G, d, U,
+                                                       " pipelined" if args.pipeline else ""),
           file=sys.stderr, flush=True)
 
     if args.copy_calibration_mib > 0:
@@ -169,7 +172,7 @@ def main():
         print("bench: calibration copy of %d bytes" % n, file=sys.stderr, flush=True)
         del src, dst
     inp = make_inputs(shape, cfg["dtype"], seed=0, device="cuda")
-    plan = upipe.Plan(S, D, H, G, d, U, causal=True, dtype=cfg["dtype"])
+    plan = upipe.Plan(S, D, H, G, d, U, causal=True, dtype=cfg["dtype"], pipeline=args.pipeline)
     out = alloc_outputs(plan, dev)
     torch.cuda.synchronize()
     mem_before = torch.cuda.memory_allocated()
@@ -269,7 +272,7 @@ def main():
         "config": {"workload": "causal GQA attention layer fwd+bwd, one GPU, Llama3-8B attention "
                                "shape" if args.config.startswith("llama") else args.config,
                    "name": args.config, "S": S, "d_model": D, "H": H, "G": G, "d_head": d,
-                   "U": U, "causal": True, "seed": 0},
+                   "U": U, "pipeline": args.pipeline, "causal": True, "seed": 0},
         "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "attn_kernels_tflops": aflops / (attn_ms * 1e-3) / 1e12 if attn_ms > 0 else None,
         "attn_kernels_pct_peak": (100.0 * aflops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS

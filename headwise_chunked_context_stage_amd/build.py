@@ -22,8 +22,7 @@ COMMON = [
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # MFMA results in arch VGPRs: the softmax reads S/dP straight from the
-    # accumulators instead of copying them out of AGPRs (the dK/dV kernel
-    # pins its long-lived sums to AGPRs explicitly)
+    # accumulators instead of copying them out of AGPRs
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument",
 ]

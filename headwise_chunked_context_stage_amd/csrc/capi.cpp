@@ -13,8 +13,12 @@
 //                       dX += (gradients) x (weights) with dX itself as the
 //                       running fp32 sum.
 // All work is enqueued on the caller's stream; nothing here synchronises.
+// A pipelined plan also uses one helper stream per device: the projections
+// of the next stage and the gradient GEMMs of the current one run there,
+// ordered against the attention kernels on the caller's stream by events.
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -100,11 +104,11 @@ hipError_t stage_projection(const Plan& p, const Stage& st, const Kernels& K, co
   const size_t hbuf = static_cast<size_t>(p.S) * p.d * e;   // bytes of one head's [S][d] buffer
   std::vector<std::pair<const void*, void*>> jobs;
   for (int h = 0; h < st.nq; ++h)
-    jobs.push_back({at(Wq, (st.q0 + h) * wrows), at(ws, p.ws.q + h * hbuf)});
+    jobs.push_back({at(Wq, (st.q0 + h) * wrows), at(ws, p.ws.q[st.slot] + h * hbuf)});
   if (st.load) {
     for (int g = 0; g < st.nkv; ++g) {
-      jobs.push_back({at(Wk, (st.kv0 + g) * wrows), at(ws, p.ws.k + g * hbuf)});
-      jobs.push_back({at(Wv, (st.kv0 + g) * wrows), at(ws, p.ws.v + g * hbuf)});
+      jobs.push_back({at(Wk, (st.kv0 + g) * wrows), at(ws, p.ws.k[st.kvslot] + g * hbuf)});
+      jobs.push_back({at(Wv, (st.kv0 + g) * wrows), at(ws, p.ws.v[st.kvslot] + g * hbuf)});
     }
   }
   for (size_t b = 0; b < jobs.size(); b += kMaxChunks) {
@@ -132,12 +136,216 @@ AttnArgs attn_args(const Plan& p, const Stage& st, void* ws) {
   a.q_head0 = st.q0;
   a.r = p.r;
   a.kv_head0 = st.kv0;
-  a.q = at(ws, p.ws.q);
-  a.k = at(ws, p.ws.k);
-  a.v = at(ws, p.ws.v);
+  a.q = at(ws, p.ws.q[st.slot]);
+  a.k = at(ws, p.ws.k[st.kvslot]);
+  a.v = at(ws, p.ws.v[st.kvslot]);
   a.first_of_group = st.load ? 1 : 0;
   a.last_of_group = st.done ? 1 : 0;
   return a;
+}
+
+// Backward attention of one stage: D pre-pass, dK/dV, dQ.
+struct BwdIn {
+  const void *dO, *X, *Wq, *Wk, *Wv, *O;
+  const float* LSE;
+  float *dX, *dWq, *dWk, *dWv;
+  void* ws;
+};
+
+AttnArgs bwd_args(const Plan& p, const Stage& st, const BwdIn& in) {
+  AttnArgs a = attn_args(p, st, in.ws);
+  a.dO = in.dO;
+  a.o_in = in.O;
+  a.lse_in = in.LSE;
+  a.dd = reinterpret_cast<float*>(at(in.ws, p.ws.dd));
+  a.lse2 = reinterpret_cast<float*>(at(in.ws, p.ws.lse2));
+  a.dq = at(in.ws, p.ws.dq[st.slot]);
+  // dK/dV belong to the KV group: the fp32 variant carries them across the
+  // group's stages in these buffers, so they follow the K/V copy
+  a.dk = at(in.ws, p.ws.dk[st.kvslot]);
+  a.dv = at(in.ws, p.ws.dv[st.kvslot]);
+  if (p.ws.dk_acc) {
+    a.dk_acc = reinterpret_cast<float*>(at(in.ws, p.ws.dk_acc));
+    a.dv_acc = reinterpret_cast<float*>(at(in.ws, p.ws.dv_acc));
+  }
+  return a;
+}
+
+// Weight and input gradients of one stage, in the one global order used for
+// dX: inside each KV group, its query heads ascending, then the group's dK,
+// then its dV.  Every U walks this same sequence, so dX is summed in the same
+// order.
+hipError_t stage_gradients(const Plan& p, const Stage& st, const Kernels& K, const BwdIn& in,
+                           hipStream_t s) {
+  const size_t e = p.elem();
+  const size_t wrows = static_cast<size_t>(p.d) * p.D * e;
+  const size_t dwrows = static_cast<size_t>(p.d) * p.D;  // fp32 elements of one head's dW rows
+  const size_t hbuf = static_cast<size_t>(p.S) * p.d * e;
+  char* dq = at(in.ws, p.ws.dq[st.slot]);
+  char* dk = at(in.ws, p.ws.dk[st.kvslot]);
+  char* dv = at(in.ws, p.ws.dv[st.kvslot]);
+  struct Chunk {
+    void* a;
+    const void* w;
+    float* dw;
+  };
+  std::vector<Chunk> chunks;
+  auto add_q = [&](int hq) {
+    chunks.push_back({dq + (hq - st.q0) * hbuf, at(in.Wq, hq * wrows), in.dWq + hq * dwrows});
+  };
+  auto add_kv = [&](int g) {
+    chunks.push_back({dk + (g - st.kv0) * hbuf, at(in.Wk, g * wrows), in.dWk + g * dwrows});
+    chunks.push_back({dv + (g - st.kv0) * hbuf, at(in.Wv, g * wrows), in.dWv + g * dwrows});
+  };
+  for (int hq = st.q0; hq < st.q0 + st.nq; ++hq) {
+    add_q(hq);
+    const bool group_end = ((hq + 1) % p.r) == 0;
+    if (group_end && st.done) add_kv(hq / p.r);
+  }
+  for (size_t b = 0; b < chunks.size(); b += kMaxChunks) {
+    ChunkTable t;
+    std::memset(&t, 0, sizeof(t));
+    t.n = static_cast<int>(std::min<size_t>(kMaxChunks, chunks.size() - b));
+    for (int i = 0; i < t.n; ++i) {
+      t.a[i] = chunks[b + i].a;
+      t.w[i] = chunks[b + i].w;
+      t.dw[i] = chunks[b + i].dw;
+    }
+    hipError_t err = timed(UPIPE_K_DW, s, [&] { return K.dw(in.X, p.S, p.D, p.d, t, s); });
+    if (err != hipSuccess) return err;
+    err = timed(UPIPE_K_DX, s, [&] { return K.dx(in.dX, p.S, p.D, p.d, t, s); });
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+// ------------------------------------------------------------ pipelining
+// One helper stream per device, created on first use and kept.
+std::mutex g_smu;
+std::map<int, hipStream_t> g_helper;
+
+hipError_t helper_stream(hipStream_t* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> g(g_smu);
+  auto it = g_helper.find(dev);
+  if (it != g_helper.end()) {
+    *out = it->second;
+    return hipSuccess;
+  }
+  hipStream_t h = nullptr;
+  e = hipStreamCreateWithFlags(&h, hipStreamNonBlocking);
+  if (e != hipSuccess) return e;
+  g_helper[dev] = h;
+  *out = h;
+  return hipSuccess;
+}
+
+// Ordering events.  A call takes a set, records and waits on them while it
+// enqueues, and gives them back before it returns: a wait binds to the record
+// that precedes it on the host, so a later call may record the same events
+// again while earlier work is still in flight.
+constexpr int kSyncEvents = 7;
+std::mutex g_emu;
+std::vector<hipEvent_t> g_sync_pool;
+
+struct SyncEvents {
+  hipEvent_t ev[kSyncEvents] = {};
+  int n = 0;
+  hipError_t take() {
+    std::lock_guard<std::mutex> g(g_emu);
+    while (n < kSyncEvents) {
+      if (!g_sync_pool.empty()) {
+        ev[n++] = g_sync_pool.back();
+        g_sync_pool.pop_back();
+        continue;
+      }
+      hipError_t e = hipEventCreateWithFlags(&ev[n], hipEventDisableTiming);
+      if (e != hipSuccess) return e;
+      ++n;
+    }
+    return hipSuccess;
+  }
+  ~SyncEvents() {
+    std::lock_guard<std::mutex> g(g_emu);
+    for (int i = 0; i < n; ++i) g_sync_pool.push_back(ev[i]);
+  }
+};
+
+// `waiter` waits for the work enqueued on `signaller` so far.
+hipError_t order(hipEvent_t ev, hipStream_t signaller, hipStream_t waiter) {
+  hipError_t e = hipEventRecord(ev, signaller);
+  if (e != hipSuccess) return e;
+  return hipStreamWaitEvent(waiter, ev, 0);
+}
+
+// Forward, pipelined: stage s + 1's projection (helper stream) runs while
+// stage s's attention (caller's stream) does.  Stage s uses buffer copy
+// s mod 2, so the projection of s + 1 waits only for the attention of s - 1.
+hipError_t fwd_pipelined(const Plan& p, const Kernels& K, const void* X, const void* Wq,
+                         const void* Wk, const void* Wv, void* O, float* LSE, void* ws,
+                         hipStream_t s, hipStream_t h, SyncEvents& E) {
+  hipEvent_t start = E.ev[0], proj_done[2] = {E.ev[1], E.ev[2]}, attn_done[2] = {E.ev[3], E.ev[4]};
+  const int n = static_cast<int>(p.stages.size());
+  hipError_t e = order(start, s, h);  // inputs written on the caller's stream
+  if (e != hipSuccess) return e;
+  e = stage_projection(p, p.stages[0], K, X, Wq, Wk, Wv, ws, h);
+  if (e == hipSuccess) e = hipEventRecord(proj_done[0], h);
+  for (int i = 0; i < n && e == hipSuccess; ++i) {
+    const Stage& st = p.stages[i];
+    e = hipStreamWaitEvent(s, proj_done[i % 2], 0);
+    if (e != hipSuccess) break;
+    AttnArgs a = attn_args(p, st, ws);
+    a.o = O;
+    a.lse = LSE;
+    e = timed(UPIPE_K_ATTN_FWD, s, [&] { return K.attn_fwd(a, s); });
+    if (e == hipSuccess) e = hipEventRecord(attn_done[i % 2], s);
+    if (e != hipSuccess || i + 1 == n) break;
+    // copy (i + 1) mod 2 was last read by the attention of stage i - 1
+    if (i >= 1) e = hipStreamWaitEvent(h, attn_done[(i - 1) % 2], 0);
+    if (e == hipSuccess) e = stage_projection(p, p.stages[i + 1], K, X, Wq, Wk, Wv, ws, h);
+    if (e == hipSuccess) e = hipEventRecord(proj_done[(i + 1) % 2], h);
+  }
+  return e;
+}
+
+// Backward, pipelined.  Caller's stream: D pre-pass, dK/dV and dQ of each
+// stage.  Helper stream: the projection of stage s + 1, then the dW and dX
+// GEMMs of stage s, in stage order (dX keeps its one summation order).
+// Copy s mod 2 of Q/K/V is free again once dQ of stage s - 1 has run; copy
+// s mod 2 of dQ once dX of stage s - 2 has.  dK/dV use the K/V copy of their
+// group; the group two loads back finished its dX by stage s - 2 as well.
+hipError_t bwd_pipelined(const Plan& p, const Kernels& K, const BwdIn& in, hipStream_t s,
+                         hipStream_t h, SyncEvents& E) {
+  hipEvent_t start = E.ev[0], proj_done[2] = {E.ev[1], E.ev[2]}, dq_done[2] = {E.ev[3], E.ev[4]},
+             dx_done[2] = {E.ev[5], E.ev[6]};
+  const int n = static_cast<int>(p.stages.size());
+  hipError_t e = order(start, s, h);  // dX cleared and inputs written on the caller's stream
+  if (e != hipSuccess) return e;
+  e = stage_projection(p, p.stages[0], K, in.X, in.Wq, in.Wk, in.Wv, in.ws, h);
+  if (e == hipSuccess) e = hipEventRecord(proj_done[0], h);
+  for (int i = 0; i < n && e == hipSuccess; ++i) {
+    const Stage& st = p.stages[i];
+    const AttnArgs a = bwd_args(p, st, in);
+    e = timed(UPIPE_K_BWD_PRE, s, [&] { return K.bwd_pre(a, s); });
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, proj_done[i % 2], 0);
+    if (e == hipSuccess && i >= 2) e = hipStreamWaitEvent(s, dx_done[i % 2], 0);
+    if (e == hipSuccess) e = timed(UPIPE_K_ATTN_DKV, s, [&] { return K.attn_dkv(a, s); });
+    if (e == hipSuccess) e = timed(UPIPE_K_ATTN_DQ, s, [&] { return K.attn_dq(a, s); });
+    if (e == hipSuccess) e = hipEventRecord(dq_done[i % 2], s);
+    if (e == hipSuccess && i + 1 < n) {
+      if (i >= 1) e = hipStreamWaitEvent(h, dq_done[(i - 1) % 2], 0);
+      if (e == hipSuccess)
+        e = stage_projection(p, p.stages[i + 1], K, in.X, in.Wq, in.Wk, in.Wv, in.ws, h);
+      if (e == hipSuccess) e = hipEventRecord(proj_done[(i + 1) % 2], h);
+    }
+    if (e == hipSuccess) e = hipStreamWaitEvent(h, dq_done[i % 2], 0);
+    if (e == hipSuccess) e = stage_gradients(p, st, K, in, h);
+    if (e == hipSuccess) e = hipEventRecord(dx_done[i % 2], h);
+  }
+  if (e == hipSuccess) e = hipStreamWaitEvent(s, dx_done[(n - 1) % 2], 0);  // join
+  return e;
 }
 
 }  // namespace
@@ -168,11 +376,16 @@ extern "C" {
 
 int upipe_create(upipe_plan** out, int64_t S, int64_t d_model, int H, int G, int d_head, int U,
                  int causal, int dtype) {
+  return upipe_create_ex(out, S, d_model, H, G, d_head, U, causal, dtype, 0);
+}
+
+int upipe_create_ex(upipe_plan** out, int64_t S, int64_t d_model, int H, int G, int d_head, int U,
+                    int causal, int dtype, int flags) {
   if (!out) return UPIPE_ERR_ARG;
   *out = nullptr;
   upipe_plan* h = new (std::nothrow) upipe_plan;
   if (!h) return UPIPE_ERR_ARG;
-  int rc = make_plan(h->p, S, d_model, H, G, d_head, U, causal, dtype);
+  int rc = make_plan(h->p, S, d_model, H, G, d_head, U, causal, dtype, flags);
   if (rc != UPIPE_OK) {
     delete h;
     return rc;
@@ -234,6 +447,14 @@ int upipe_fwd(const upipe_plan* h, const void* X, const void* Wq, const void* Wk
   if (!ws || !aligned(ws, kAlign) || ws_bytes < p.ws.fwd_bytes) return UPIPE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Kernels K = kernels_for(p.dtype);
+  if (p.pipeline) {
+    hipStream_t hs = nullptr;
+    SyncEvents E;
+    UPIPE_TRY(helper_stream(&hs));
+    UPIPE_TRY(E.take());
+    UPIPE_TRY(fwd_pipelined(p, K, X, Wq, Wk, Wv, O, LSE, ws, s, hs, E));
+    return UPIPE_OK;
+  }
   for (const Stage& st : p.stages) {
     UPIPE_TRY(stage_projection(p, st, K, X, Wq, Wk, Wv, ws, s));
     AttnArgs a = attn_args(p, st, ws);
@@ -264,65 +485,27 @@ int upipe_bwd(const upipe_plan* h, const void* dO, const void* X, const void* Wq
     return UPIPE_ERR_ARG;
   if (!ws || !aligned(ws, kAlign) || ws_bytes < p.ws.bwd_bytes) return UPIPE_ERR_WORKSPACE;
   const Kernels K = kernels_for(p.dtype);
-  const size_t e = p.elem();
-  const size_t wrows = static_cast<size_t>(p.d) * p.D * e;
-  const size_t dwrows = static_cast<size_t>(p.d) * p.D;  // fp32 elements of one head's dW rows
-  const size_t hbuf = static_cast<size_t>(p.S) * p.d * e;
+  const BwdIn in{dO, X, Wq, Wk, Wv, O, LSE, dX, dWq, dWk, dWv, ws};
+  hipStream_t hs = nullptr;
+  SyncEvents E;
+  if (p.pipeline) {  // before anything is enqueued
+    UPIPE_TRY(helper_stream(&hs));
+    UPIPE_TRY(E.take());
+  }
 
   UPIPE_TRY(timed(UPIPE_K_FILL, s,
                   [&] { return fill_zero(dX, static_cast<size_t>(p.S) * p.D * 4, s); }));
+  if (p.pipeline) {
+    UPIPE_TRY(bwd_pipelined(p, K, in, s, hs, E));
+    return UPIPE_OK;
+  }
   for (const Stage& st : p.stages) {
     UPIPE_TRY(stage_projection(p, st, K, X, Wq, Wk, Wv, ws, s));
-    AttnArgs a = attn_args(p, st, ws);
-    a.dO = dO;
-    a.o_in = O;
-    a.lse_in = LSE;
-    a.dd = reinterpret_cast<float*>(at(ws, p.ws.dd));
-    a.lse2 = reinterpret_cast<float*>(at(ws, p.ws.lse2));
-    a.dq = at(ws, p.ws.dq);
-    a.dk = at(ws, p.ws.dk);
-    a.dv = at(ws, p.ws.dv);
-    if (p.ws.dk_acc) {
-      a.dk_acc = reinterpret_cast<float*>(at(ws, p.ws.dk_acc));
-      a.dv_acc = reinterpret_cast<float*>(at(ws, p.ws.dv_acc));
-    }
+    const AttnArgs a = bwd_args(p, st, in);
     UPIPE_TRY(timed(UPIPE_K_BWD_PRE, s, [&] { return K.bwd_pre(a, s); }));
     UPIPE_TRY(timed(UPIPE_K_ATTN_DKV, s, [&] { return K.attn_dkv(a, s); }));
     UPIPE_TRY(timed(UPIPE_K_ATTN_DQ, s, [&] { return K.attn_dq(a, s); }));
-
-    // Gradient chunks in the one global order used for dX: inside each KV
-    // group, its query heads ascending, then the group's dK, then its dV.
-    // Every U walks this same sequence, so dX is summed in the same order.
-    struct Chunk {
-      void* a;
-      const void* w;
-      float* dw;
-    };
-    std::vector<Chunk> chunks;
-    auto add_q = [&](int hq) {
-      chunks.push_back({at(a.dq, (hq - st.q0) * hbuf), at(Wq, hq * wrows), dWq + hq * dwrows});
-    };
-    auto add_kv = [&](int g) {
-      chunks.push_back({at(a.dk, (g - st.kv0) * hbuf), at(Wk, g * wrows), dWk + g * dwrows});
-      chunks.push_back({at(a.dv, (g - st.kv0) * hbuf), at(Wv, g * wrows), dWv + g * dwrows});
-    };
-    for (int hq = st.q0; hq < st.q0 + st.nq; ++hq) {
-      add_q(hq);
-      const bool group_end = ((hq + 1) % p.r) == 0;
-      if (group_end && st.done) add_kv(hq / p.r);
-    }
-    for (size_t b = 0; b < chunks.size(); b += kMaxChunks) {
-      ChunkTable t;
-      std::memset(&t, 0, sizeof(t));
-      t.n = static_cast<int>(std::min<size_t>(kMaxChunks, chunks.size() - b));
-      for (int i = 0; i < t.n; ++i) {
-        t.a[i] = chunks[b + i].a;
-        t.w[i] = chunks[b + i].w;
-        t.dw[i] = chunks[b + i].dw;
-      }
-      UPIPE_TRY(timed(UPIPE_K_DW, s, [&] { return K.dw(X, p.S, p.D, p.d, t, s); }));
-      UPIPE_TRY(timed(UPIPE_K_DX, s, [&] { return K.dx(dX, p.S, p.D, p.d, t, s); }));
-    }
+    UPIPE_TRY(stage_gradients(p, st, K, in, s));
   }
   return UPIPE_OK;
 }

@@ -18,7 +18,9 @@
 
 namespace upipe {
 
-int make_plan(Plan& p, int64_t S, int64_t D, int H, int G, int d, int U, int causal, int dtype) {
+int make_plan(Plan& p, int64_t S, int64_t D, int H, int G, int d, int U, int causal, int dtype,
+              int flags) {
+  if ((flags & ~UPIPE_PIPELINE) != 0) return UPIPE_ERR_ARG;
   if (S < 0 || D <= 0 || H <= 0 || G <= 0 || d <= 0 || U <= 0) return UPIPE_ERR_ARG;
   if (causal != 0 && causal != 1) return UPIPE_ERR_ARG;
   if (dtype != UPIPE_BF16 && dtype != UPIPE_F32) return UPIPE_ERR_ARG;
@@ -47,8 +49,10 @@ int make_plan(Plan& p, int64_t S, int64_t D, int H, int G, int d, int U, int cau
   p.causal = causal;
   p.dtype = dtype;
   p.kv_per_stage = std::max(1, U / r);
+  p.pipeline = (flags & UPIPE_PIPELINE) ? 1 : 0;
 
   p.stages.clear();
+  int loads = 0;  // stages so far that project K and V
   for (int s = 0; s < H / U; ++s) {
     Stage st;
     st.q0 = s * U;
@@ -61,10 +65,16 @@ int make_plan(Plan& p, int64_t S, int64_t D, int H, int G, int d, int U, int cau
       st.load = (st.q0 % r) == 0;
       st.done = ((st.q0 + U) % r) == 0;
     }
+    if (st.load) ++loads;
+    // Pipelined: consecutive stages alternate between two copies of the
+    // stage buffers, and consecutive K/V loads between two copies of K/V.
+    st.slot = p.pipeline ? s % 2 : 0;
+    st.kvslot = p.pipeline ? (loads - 1) % 2 : 0;
     p.stages.push_back(st);
   }
 
-  // Stage buffers: one region each, reused by every stage.
+  // Stage buffers: one region each, reused by every stage (two copies of
+  // the per-stage regions when pipelined).
   const size_t e = p.elem();
   const size_t Sd = static_cast<size_t>(S) * d;
   const size_t nkv = p.kv_per_stage;
@@ -75,15 +85,20 @@ int make_plan(Plan& p, int64_t S, int64_t D, int H, int G, int d, int U, int cau
     off = align_up(off + bytes);
     return at;
   };
-  w.q = take(U * Sd * e);
-  w.k = take(nkv * Sd * e);
-  w.v = take(nkv * Sd * e);
+  const int copies = p.pipeline ? 2 : 1;
+  auto take2 = [&](size_t (&at)[2], size_t bytes) {
+    at[0] = take(bytes);
+    at[1] = copies == 2 ? take(bytes) : at[0];
+  };
+  take2(w.q, U * Sd * e);
+  take2(w.k, nkv * Sd * e);
+  take2(w.v, nkv * Sd * e);
   w.fwd_bytes = off;
   w.dd = take(static_cast<size_t>(U) * S * 4);
   w.lse2 = take(static_cast<size_t>(U) * S * 4);
-  w.dq = take(U * Sd * e);
-  w.dk = take(nkv * Sd * e);
-  w.dv = take(nkv * Sd * e);
+  take2(w.dq, U * Sd * e);
+  take2(w.dk, nkv * Sd * e);
+  take2(w.dv, nkv * Sd * e);
   if (dtype == UPIPE_BF16 && U < r) {
     w.dk_acc = take(Sd * 4);
     w.dv_acc = take(Sd * 4);

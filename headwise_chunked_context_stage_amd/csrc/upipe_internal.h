@@ -20,20 +20,25 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // [kv0, kv0+nkv) they read.  `load`: the stage is the first of those KV heads'
 // group, so it projects K and V; `done`: it is the last, so it finishes their
 // gradients.  Stages run in ascending head order; with groups contiguous this
-// projects every KV head exactly once per group.
+// projects every KV head exactly once per group.  `slot` selects the copy of
+// the per-stage buffers (Q, dQ) and `kvslot` the copy of the per-group ones
+// (K, V, dK, dV); both are 0 unless the plan is pipelined (two copies of each).
 struct Stage {
   int q0, nq;
   int kv0, nkv;
   bool load, done;
+  int slot, kvslot;
 };
 
 // Byte offsets of the stage buffers inside the caller's workspace.
+// The regions indexed [2] have two copies in a pipelined plan (index = the
+// stage's slot or kvslot) and one otherwise ([1] == [0]).
 struct WsLayout {
-  size_t q, k, v;              // Q [U][S][d], K [kv][S][d], V [kv][S][d]   (element type)
+  size_t q[2], k[2], v[2];     // Q [U][S][d], K [kv][S][d], V [kv][S][d]   (element type)
   size_t dd;                   // D = rowsum(dO*O) [U][S] fp32                 (backward)
   size_t lse2;                 // LSE * log2(e) [U][S] fp32                    (backward)
-  size_t dq;                   // dQ [U][S][d] (element type)                  (backward)
-  size_t dk, dv;               // dK, dV [kv][S][d] (element type)             (backward)
+  size_t dq[2];                // dQ [U][S][d] (element type)                  (backward)
+  size_t dk[2], dv[2];         // dK, dV [kv][S][d] (element type)             (backward)
   size_t dk_acc, dv_acc;       // fp32 carry of dK, dV across a group's stages (bf16 and U < r)
   size_t fwd_bytes, bwd_bytes;
 };
@@ -42,13 +47,15 @@ struct Plan {
   int64_t S, D;
   int H, G, d, U, r, causal, dtype;
   int kv_per_stage;  // max(1, U / r)
+  int pipeline;      // stage s + 1's projection overlaps stage s's attention
   std::vector<Stage> stages;
   WsLayout ws;
   size_t elem() const { return dtype == UPIPE_BF16 ? 2 : 4; }
 };
 
 // Validates and builds; returns a UPIPE_* code.
-int make_plan(Plan& p, int64_t S, int64_t D, int H, int G, int d, int U, int causal, int dtype);
+int make_plan(Plan& p, int64_t S, int64_t D, int H, int G, int d, int U, int causal, int dtype,
+              int flags = 0);
 int choose_u(int64_t S, int64_t D, int H, int G, int d, int causal, int dtype, size_t budget,
              int* U);
 

@@ -15,9 +15,10 @@ LIB_PATH = os.path.join(_HERE, "libupipe.so")
 
 UPIPE_BF16, UPIPE_F32 = 0, 1
 UPIPE_OK, UPIPE_ERR_ARG, UPIPE_ERR_UNSUPPORTED, UPIPE_ERR_WORKSPACE, UPIPE_ERR_HIP = 0, 1, 2, 3, 4
+UPIPE_PIPELINE = 1  # plan flag: stage pipelining on a second stream
 KERNEL_KINDS = ("proj", "attn_fwd", "bwd_pre", "attn_dkv", "attn_dq", "dw", "dx", "fill")
 
-EXPORTS = ("upipe_create", "upipe_destroy", "upipe_peak_bytes", "upipe_peak_bytes_phase",
+EXPORTS = ("upipe_create", "upipe_create_ex", "upipe_destroy", "upipe_peak_bytes", "upipe_peak_bytes_phase",
            "upipe_fwd", "upipe_bwd", "upipe_strerror", "upipe_num_stages", "upipe_stage_info",
            "upipe_timing_enable", "upipe_timing_read", "upipe_kernel_name", "upipe_mfma_ceiling",
            "upipe_auto_u")
@@ -43,6 +44,8 @@ def lib():
     vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     L.upipe_create.argtypes = [ctypes.POINTER(vp), i64, i64, i32, i32, i32, i32, i32, i32]
     L.upipe_create.restype = i32
+    L.upipe_create_ex.argtypes = [ctypes.POINTER(vp), i64, i64, i32, i32, i32, i32, i32, i32, i32]
+    L.upipe_create_ex.restype = i32
     L.upipe_destroy.argtypes = [vp]
     L.upipe_destroy.restype = None
     L.upipe_peak_bytes.argtypes = [vp]
@@ -128,6 +131,13 @@ def upipe_create(S, d_model, H, G, d_head, U, causal=1, dtype="bf16") -> int:
     return h.value
 
 
+def upipe_create_ex(S, d_model, H, G, d_head, U, causal=1, dtype="bf16", flags=0) -> int:
+    h = ctypes.c_void_p()
+    _check(lib().upipe_create_ex(ctypes.byref(h), S, d_model, H, G, d_head, U, int(causal),
+                                 _dtype_code(dtype), int(flags)), "upipe_create_ex")
+    return h.value
+
+
 def upipe_destroy(plan) -> None:
     lib().upipe_destroy(plan)
 
@@ -208,11 +218,16 @@ def upipe_auto_u(S: int, d_model: int, H: int, G: int, d_head: int, budget_bytes
 class Plan:
     """Owns a plan handle; the layer's shape and stage size U are fixed here."""
 
-    def __init__(self, S, d_model, H, G, d_head, U, causal=True, dtype="bf16"):
+    def __init__(self, S, d_model, H, G, d_head, U, causal=True, dtype="bf16", pipeline=False):
         self.S, self.D, self.H, self.G, self.d, self.U = S, d_model, H, G, d_head, U
         self.causal = bool(causal)
+        self.pipeline = bool(pipeline)
         self.dtype = "bf16" if _dtype_code(dtype) == UPIPE_BF16 else "f32"
-        self.handle = upipe_create(S, d_model, H, G, d_head, U, int(self.causal), dtype)
+        if self.pipeline:
+            self.handle = upipe_create_ex(S, d_model, H, G, d_head, U, int(self.causal), dtype,
+                                          UPIPE_PIPELINE)
+        else:
+            self.handle = upipe_create(S, d_model, H, G, d_head, U, int(self.causal), dtype)
 
     def __del__(self):
         h = getattr(self, "handle", None)

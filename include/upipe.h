@@ -70,12 +70,36 @@ enum {
 int upipe_create(upipe_plan** out, int64_t S, int64_t d_model, int H, int G, int d_head, int U,
                  int causal, int dtype);
 
+/* Plan flags for upipe_create_ex. */
+enum {
+  /* Stage pipelining (the pages' suggested improvement of overlapping the
+   * stages; paper.rainbus.top summary, sections 局限与改进 and 独立分析的弱点).
+   * The stage buffers get two copies, and each call runs the projection
+   * GEMMs of stage s + 1 and, in the backward, the weight- and
+   * input-gradient GEMMs of stage s on a second stream while stage s + 1's
+   * attention kernels run on the caller's stream.  Every kernel, its inputs
+   * and the order of every accumulation are those of the plain plan, so the
+   * results are bit-identical; upipe_peak_bytes grows by one more copy of
+   * the Q, K, V (and dQ, dK, dV) stage buffers.  The second stream (default
+   * priority, one per device, created on the first pipelined call on the
+   * current device, which must be the device of `stream`) and a pool of
+   * events are kept until the process ends; the calls allocate no device
+   * memory. */
+  UPIPE_PIPELINE = 1
+};
+
+/* upipe_create with flags (a combination of the values above; 0 gives the
+ * same plan as upipe_create).  Unknown flag bits return UPIPE_ERR_ARG. */
+int upipe_create_ex(upipe_plan** out, int64_t S, int64_t d_model, int H, int G, int d_head, int U,
+                    int causal, int dtype, int flags);
+
 /* Chunk size from a memory budget (host only).  The pages (paper.rainbus.top
  * summary of "Untied Ulysses", section 独立分析的弱点) propose choosing U from
  * the sequence length, large for short sequences and small for long ones;
  * section 实验结果 describes U as a memory/throughput trade-off.  Writes to *U
- * the largest legal U (as for upipe_create) whose upipe_peak_bytes is at most
- * budget_bytes, so for a fixed budget a longer S gets a smaller or equal U.
+ * the largest legal U (as for upipe_create) whose upipe_peak_bytes (plan
+ * without flags) is at most budget_bytes, so for a fixed budget a longer S
+ * gets a smaller or equal U.
  * Returns UPIPE_ERR_ARG (or UPIPE_ERR_UNSUPPORTED) for a shape upipe_create
  * rejects for every U, UPIPE_ERR_WORKSPACE when not even U = 1 fits; *U is 0
  * on failure.  U must not be NULL. */

@@ -58,8 +58,9 @@ def host(t):
     return t.detach().double().cpu().numpy()
 
 
-def run_layer(shape, dtype, U, inp, causal=True, backward=True):
-    plan = upipe.Plan(shape.S, shape.D, shape.H, shape.G, shape.d, U, causal=causal, dtype=dtype)
+def run_layer(shape, dtype, U, inp, causal=True, backward=True, pipeline=False):
+    plan = upipe.Plan(shape.S, shape.D, shape.H, shape.G, shape.d, U, causal=causal, dtype=dtype,
+                      pipeline=pipeline)
     out = run(plan, inp, backward_pass=backward)
     torch.cuda.synchronize()
     out.pop("ws")
@@ -199,6 +200,35 @@ def test_auto_u_runs_bit_identical_to_u1():
     assert_same_bits(run_layer(shape, "bf16", 1, inp), out, "auto U")
 
 
+@pytest.mark.parametrize("S,D,H,G,d,dtype", [(768, 512, 8, 2, 128, "bf16"),
+                                              (1000, 1024, 4, 1, 128, "bf16"),
+                                              (320, 256, 4, 2, 64, "f32")])
+def test_pipelined_plan_bit_identical(S, D, H, G, d, dtype):
+    """Stage pipelining (pages' overlap suggestion; paper.rainbus.top summary,
+    section 局限与改进) only moves GEMMs to a second stream with event ordering
+    and alternates two copies of the stage buffers: for every legal U the
+    pipelined layer equals the plain U = 1 layer bit for bit, on the default
+    stream and on a side stream, and again on a later call (events reused)."""
+    shape = LayerShape(S=S, D=D, H=H, G=G, d=d)
+    inp = {k: v.cuda() for k, v in make_inputs(shape, dtype, seed=11, device="cpu").items()}
+    ref = run_layer(shape, dtype, 1, inp)
+    for U in legal_us(H, G):
+        say("pipelined %s S=%d H=%d G=%d U=%d" % (dtype, S, H, G, U))
+        assert_same_bits(ref, run_layer(shape, dtype, U, inp, pipeline=True), "pipelined U=%d" % U)
+    say("pipelined U=1 on a side stream")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    plan = upipe.Plan(S, D, H, G, d, 1, dtype=dtype, pipeline=True)
+    with torch.cuda.stream(side):
+        out = run(plan, inp)
+        out2 = run(plan, inp)
+    torch.cuda.synchronize()
+    out.pop("ws")
+    out2.pop("ws")
+    assert_same_bits(ref, out, "side stream")
+    assert_same_bits(ref, out2, "side stream, second call")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_non_causal(dtype):
     shape = LayerShape(S=320, D=256, H=4, G=2, d=128 if dtype == "bf16" else 64)
@@ -333,6 +363,9 @@ def test_full_size_llama8b_s128k_bench_config():
     inp = make_inputs(shape, "bf16", seed=0, device="cuda")
     say("llama8b S=131072 U=4")
     out = run_layer(shape, "bf16", 4, inp)
+    say("llama8b S=131072 U=4 pipelined")
+    assert_same_bits(out, run_layer(shape, "bf16", 4, inp, pipeline=True), "pipelined")
+    torch.cuda.empty_cache()
     S = shape.S
     sampled_rows_check(shape, inp, out, [0, 1, 100, 1023, 1024, 2047],
                        [S - 1, S - 2, S - 129, S - 4096], (0, 4))

@@ -145,8 +145,9 @@ def test_qwen3_32b_reduction_matches_pages():
 FAKE = 1 << 20  # a 256-aligned non-null address; never dereferenced (validation fails first)
 
 
-def test_fwd_bwd_reject_before_launch():
-    p = upipe.Plan(512, 256, 4, 2, 64, 2, dtype="f32")
+@pytest.mark.parametrize("pipeline", [False, True])
+def test_fwd_bwd_reject_before_launch(pipeline):
+    p = upipe.Plan(512, 256, 4, 2, 64, 2, dtype="f32", pipeline=pipeline)
     need = p.peak_bytes
     ok = [FAKE] * 6
     with pytest.raises(upipe.UpipeError) as e:
@@ -232,3 +233,43 @@ def test_auto_u_rejects_bad_shapes_and_null_output():
     assert e.value.code == upipe.UPIPE_ERR_UNSUPPORTED
     L = upipe.lib()
     assert L.upipe_auto_u(4096, 1024, 32, 8, 128, 1, 0, 1 << 40, None) == upipe.UPIPE_ERR_ARG
+
+
+def test_pipelined_plan_doubles_the_per_stage_buffers():
+    """Stage pipelining (the pages' overlap suggestion, paper.rainbus.top summary,
+    sections 局限与改进 and 独立分析的弱点) keeps two copies of the Q/K/V stage
+    buffers and of the dQ/dK/dV buffers; the D, LSE*log2(e) and fp32 dK/dV carry
+    regions stay single.  Closed forms in element counts, every region a multiple
+    of 256 bytes at these sizes."""
+    S, d = 4096, 128
+    for H, G in [(32, 8), (8, 2), (8, 8)]:
+        r = H // G
+        for U in legal_us(H, G):
+            kv_s = max(1, U // r)
+            plain = upipe.Plan(S, 1024, H, G, d, U)
+            pipe = upipe.Plan(S, 1024, H, G, d, U, pipeline=True)
+            qkv = 2 * S * d * (U + 2 * kv_s)
+            single = 2 * 4 * S * U + (2 * 4 * S * d if U < r else 0)  # D, LSE*log2 e, carry
+            assert plain.peak_bytes_phase(0) == qkv
+            assert pipe.peak_bytes_phase(0) == 2 * qkv
+            assert plain.peak_bytes_phase(1) == 2 * qkv + single
+            assert pipe.peak_bytes_phase(1) == 4 * qkv + single
+            assert pipe.num_stages == plain.num_stages
+            for s in range(plain.num_stages):
+                assert pipe.stage_info(s) == plain.stage_info(s)
+
+
+def test_create_ex_flags():
+    h = upipe.upipe_create_ex(4096, 1024, 8, 2, 128, 2, 1, "bf16", 0)
+    try:
+        assert upipe.upipe_peak_bytes(h) == upipe.Plan(4096, 1024, 8, 2, 128, 2).peak_bytes
+    finally:
+        upipe.upipe_destroy(h)
+    for bad in (2, 4, -1, 1 << 30):
+        with pytest.raises(upipe.UpipeError) as e:
+            upipe.upipe_create_ex(4096, 1024, 8, 2, 128, 2, 1, "bf16", bad)
+        assert e.value.code == upipe.UPIPE_ERR_ARG
+    # shape errors are reported as for upipe_create
+    with pytest.raises(upipe.UpipeError) as e:
+        upipe.upipe_create_ex(4096, 1024, 8, 2, 128, 3, 1, "bf16", upipe.UPIPE_PIPELINE)
+    assert e.value.code == upipe.UPIPE_ERR_ARG

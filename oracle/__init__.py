@@ -44,12 +44,14 @@ def _load():
             build()
         lib = ctypes.CDLL(_LIB)
         i64, i32, vp, dp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p
-        lib.oracle_forward.argtypes = [i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, dp, dp, i32]
+        f64 = ctypes.c_double
+        lib.oracle_forward.argtypes = [i64, i64, i32, i32, i32, i32, f64, i32, vp, vp, vp, vp, dp,
+                                       dp, i32]
         lib.oracle_forward.restype = i32
-        lib.oracle_forward_rows.argtypes = [i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp,
+        lib.oracle_forward_rows.argtypes = [i64, i64, i32, i32, i32, i32, f64, i32, vp, vp, vp, vp,
                                             vp, i64, i32, i32, dp, dp, i32]
         lib.oracle_forward_rows.restype = i32
-        lib.oracle_backward.argtypes = [i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+        lib.oracle_backward.argtypes = [i64, i64, i32, i32, i32, i32, f64, i32, vp, vp, vp, vp, vp,
                                         dp, dp, dp, dp, dp, dp, i32]
         lib.oracle_backward.restype = i32
         _lib = lib
@@ -85,14 +87,17 @@ def _ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
-def forward(X, Wq, Wk, Wv, H: int, G: int, d: int, causal: bool = True, nthreads: int | None = None):
-    """Return (O [S][H*d], LSE [H][S]) in fp64."""
+def forward(X, Wq, Wk, Wv, H: int, G: int, d: int, causal: bool = True, nthreads: int | None = None,
+            rope_theta: float = 0.0):
+    """Return (O [S][H*d], LSE [H][S]) in fp64.  rope_theta > 0 applies the
+    rotary embedding to queries and keys (see the C++ header)."""
     (X, Wq, Wk, Wv), enc = _prep([X, Wq, Wk, Wv])
     S, D = X.shape
     _check_shapes(S, D, H, G, d, Wq, Wk, Wv)
     O = np.empty((S, H * d), np.float64)
     LSE = np.empty((H, S), np.float64)
-    rc = _load().oracle_forward(S, D, H, G, d, int(bool(causal)), enc, _ptr(X), _ptr(Wq), _ptr(Wk),
+    rc = _load().oracle_forward(S, D, H, G, d, int(bool(causal)), float(rope_theta), enc, _ptr(X),
+                                _ptr(Wq), _ptr(Wk),
                                 _ptr(Wv), _ptr(O), _ptr(LSE), nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle_forward rejected the shape")
@@ -100,7 +105,7 @@ def forward(X, Wq, Wk, Wv, H: int, G: int, d: int, causal: bool = True, nthreads
 
 
 def forward_rows(X, Wq, Wk, Wv, H: int, G: int, d: int, rows, causal: bool = True,
-                 heads=None, nthreads: int | None = None):
+                 heads=None, nthreads: int | None = None, rope_theta: float = 0.0):
     """Forward at the token rows `rows` only, for query heads range(*heads)
     (default: all): (O_rows [n][H*d], LSE_rows [H][n]) in fp64; entries of
     heads outside the range are NaN."""
@@ -112,7 +117,8 @@ def forward_rows(X, Wq, Wk, Wv, H: int, G: int, d: int, rows, causal: bool = Tru
     h0, h1 = heads if heads is not None else (0, H)
     O = np.full((n, H * d), np.nan, np.float64)
     LSE = np.full((H, n), np.nan, np.float64)
-    rc = _load().oracle_forward_rows(S, D, H, G, d, int(bool(causal)), enc, _ptr(X), _ptr(Wq),
+    rc = _load().oracle_forward_rows(S, D, H, G, d, int(bool(causal)), float(rope_theta), enc,
+                                     _ptr(X), _ptr(Wq),
                                      _ptr(Wk), _ptr(Wv), _ptr(rows), n, int(h0), int(h1), _ptr(O),
                                      _ptr(LSE), nthreads or default_threads())
     if rc != 0:
@@ -121,7 +127,7 @@ def forward_rows(X, Wq, Wk, Wv, H: int, G: int, d: int, rows, causal: bool = Tru
 
 
 def backward(X, Wq, Wk, Wv, dO, H: int, G: int, d: int, causal: bool = True,
-             nthreads: int | None = None):
+             nthreads: int | None = None, rope_theta: float = 0.0):
     """Forward + backward of L = sum(O * dO).
 
     Returns a dict of fp64 arrays: O, LSE, dX, dWq, dWk, dWv.
@@ -139,7 +145,8 @@ def backward(X, Wq, Wk, Wv, dO, H: int, G: int, d: int, causal: bool = True,
         "dWk": np.empty((G * d, D), np.float64),
         "dWv": np.empty((G * d, D), np.float64),
     }
-    rc = _load().oracle_backward(S, D, H, G, d, int(bool(causal)), enc, _ptr(X), _ptr(Wq), _ptr(Wk),
+    rc = _load().oracle_backward(S, D, H, G, d, int(bool(causal)), float(rope_theta), enc, _ptr(X),
+                                 _ptr(Wq), _ptr(Wk),
                                  _ptr(Wv), _ptr(dO), _ptr(out["O"]), _ptr(out["LSE"]),
                                  _ptr(out["dX"]), _ptr(out["dWq"]), _ptr(out["dWk"]),
                                  _ptr(out["dWv"]), nthreads or default_threads())

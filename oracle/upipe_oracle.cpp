@@ -22,10 +22,20 @@
 //
 // Readings where the pages are silent (each one listed in the design notes):
 //  softmax scale tau = 1/sqrt(d_head); causal mask j <= i (diagonal kept);
-//  no RoPE, bias, dropout or output projection; batch 1; query head h uses KV
+//  no bias, dropout or output projection; batch 1; query head h uses KV
 //  head floor(h / (H/G)); LSE is the natural log of sum_j exp(tau q_i.k_j);
 //  the backward is that of L = sum(O * dO) (dO given), with gradients for
 //  X, Wq, Wk, Wv.
+//
+// Rotary position embedding (optional, rope_theta > 0; not on the pages, it
+// belongs to the Llama and Qwen model families that run this layer): the
+// rotate-half form.  For frequency c < d/2, w_c = theta^(-2c/d), and at token
+// position i the pair (c, c + d/2) of every query and key row is rotated by
+// the angle i*w_c:
+//   y[c]       = x[c] cos(i w_c) - x[c + d/2] sin(i w_c)
+//   y[c + d/2] = x[c + d/2] cos(i w_c) + x[c] sin(i w_c)
+// Values are not rotated.  The backward applies the transposed rotation to
+// the gradients of the rotated rows.
 //
 // Arithmetic: every input element is decoded exactly into an fp64 value
 // (bf16 bits, fp32 or fp64 storage) and everything after that is fp64, in
@@ -91,6 +101,7 @@ double dot(const double* a, const double* b, int64_t n) {
 struct Shape {
   int64_t S, D;
   int H, G, d, causal;
+  double rope_theta;  // 0: no rotary embedding
   int r() const { return H / G; }
   int kv(int h) const { return h / r(); }
   double tau() const { return 1.0 / std::sqrt(static_cast<double>(d)); }
@@ -99,7 +110,27 @@ struct Shape {
 };
 
 bool shape_ok(const Shape& s) {
-  return s.S >= 1 && s.D >= 1 && s.H >= 1 && s.G >= 1 && s.d >= 1 && (s.H % s.G) == 0;
+  return s.S >= 1 && s.D >= 1 && s.H >= 1 && s.G >= 1 && s.d >= 1 && (s.H % s.G) == 0 &&
+         s.rope_theta >= 0.0 && (s.rope_theta == 0.0 || s.d % 2 == 0);
+}
+
+// Rotary embedding of rows [0, nrows) of a [nrows][d] block whose row t sits at
+// token position pos[t] (pos = null: position t).  sign = +1 rotates by +angle
+// (forward), -1 by -angle (the transpose, for gradients).
+void rotate_rows(double* x, int64_t nrows, const int64_t* pos, const Shape& s, int sign) {
+  if (s.rope_theta == 0.0) return;
+  const int half = s.d / 2;
+  for (int64_t t = 0; t < nrows; ++t) {
+    const double i = static_cast<double>(pos ? pos[t] : t);
+    double* row = x + t * s.d;
+    for (int c = 0; c < half; ++c) {
+      const double w = std::pow(s.rope_theta, -2.0 * c / s.d);
+      const double cs = std::cos(i * w), sn = sign * std::sin(i * w);
+      const double a = row[c], b = row[c + half];
+      row[c] = a * cs - b * sn;
+      row[c + half] = b * cs + a * sn;
+    }
+  }
 }
 
 // Project rows [0, nrows) of X ([S][D]) through the rows of W that belong to
@@ -146,10 +177,10 @@ extern "C" {
 // Forward.  X [S][D], Wq [H*d][D], Wk/Wv [G*d][D] in encoding `enc`.
 // Outputs (fp64, caller-owned): O [S][H*d] (column h*d+c), LSE [H][S].
 // Returns 0, or 1 on an invalid shape.
-int oracle_forward(int64_t S, int64_t D, int H, int G, int d, int causal, int enc,
-                   const void* Xp, const void* Wqp, const void* Wkp, const void* Wvp,
+int oracle_forward(int64_t S, int64_t D, int H, int G, int d, int causal, double rope_theta,
+                   int enc, const void* Xp, const void* Wqp, const void* Wkp, const void* Wvp,
                    double* O, double* LSE, int nthreads) {
-  Shape s{S, D, H, G, d, causal};
+  Shape s{S, D, H, G, d, causal, rope_theta};
   if (!shape_ok(s)) return 1;
   std::vector<double> X = decode(Xp, enc, S * D);
   std::vector<double> Wq = decode(Wqp, enc, static_cast<int64_t>(H) * d * D);
@@ -160,8 +191,10 @@ int oracle_forward(int64_t S, int64_t D, int H, int G, int d, int causal, int en
   for (int g = 0; g < G; ++g) {
     project_head(X, Wk, s, g, S, nullptr, K.data(), nthreads);
     project_head(X, Wv, s, g, S, nullptr, V.data(), nthreads);
+    rotate_rows(K.data(), S, nullptr, s, +1);
     for (int h = g * s.r(); h < (g + 1) * s.r(); ++h) {
       project_head(X, Wq, s, h, S, nullptr, Q.data(), nthreads);
+      rotate_rows(Q.data(), S, nullptr, s, +1);
       parallel_for(S, nthreads, [&](int64_t i) {
         std::vector<double> scores;
         std::vector<double> o(static_cast<size_t>(d));
@@ -178,11 +211,11 @@ int oracle_forward(int64_t S, int64_t D, int H, int G, int d, int causal, int en
 // are token indices; keys/values are projected only for the KV heads of those
 // query heads and the positions those rows see.  Outputs: Orows [nrows][H*d],
 // LSErows [H][nrows] (fp64); entries of other heads are left untouched.
-int oracle_forward_rows(int64_t S, int64_t D, int H, int G, int d, int causal, int enc,
-                        const void* Xp, const void* Wqp, const void* Wkp, const void* Wvp,
-                        const int64_t* rows, int64_t nrows, int h0, int h1, double* Orows,
-                        double* LSErows, int nthreads) {
-  Shape s{S, D, H, G, d, causal};
+int oracle_forward_rows(int64_t S, int64_t D, int H, int G, int d, int causal,
+                        double rope_theta, int enc, const void* Xp, const void* Wqp,
+                        const void* Wkp, const void* Wvp, const int64_t* rows, int64_t nrows,
+                        int h0, int h1, double* Orows, double* LSErows, int nthreads) {
+  Shape s{S, D, H, G, d, causal, rope_theta};
   if (!shape_ok(s) || nrows < 0 || h0 < 0 || h1 > H || h0 >= h1) return 1;
   int64_t need = 0;  // keys needed: [0, need)
   for (int64_t t = 0; t < nrows; ++t) {
@@ -207,8 +240,10 @@ int oracle_forward_rows(int64_t S, int64_t D, int H, int G, int d, int causal, i
   for (int g = s.kv(h0); g <= s.kv(h1 - 1); ++g) {
     project_head(X, Wk, sk, g, need, nullptr, K.data(), nthreads);
     project_head(X, Wv, sk, g, need, nullptr, V.data(), nthreads);
+    rotate_rows(K.data(), need, nullptr, s, +1);
     for (int h = std::max(h0, g * s.r()); h < std::min(h1, (g + 1) * s.r()); ++h) {
       project_head(Xq, Wq, sq, h, nrows, nullptr, Q.data(), nthreads);
+      rotate_rows(Q.data(), nrows, rows, s, +1);
       parallel_for(nrows, nthreads, [&](int64_t t) {
         std::vector<double> scores;
         std::vector<double> o(static_cast<size_t>(d));
@@ -234,11 +269,11 @@ int oracle_forward_rows(int64_t S, int64_t D, int H, int G, int d, int causal, i
 // Row quantities (dQ) are computed by a pass over query rows, column
 // quantities (dK, dV) by a pass over key rows; each recomputes P and dP from
 // Q, K, V, LSE and dO, so no two threads ever write the same element.
-int oracle_backward(int64_t S, int64_t D, int H, int G, int d, int causal, int enc,
-                    const void* Xp, const void* Wqp, const void* Wkp, const void* Wvp,
+int oracle_backward(int64_t S, int64_t D, int H, int G, int d, int causal, double rope_theta,
+                    int enc, const void* Xp, const void* Wqp, const void* Wkp, const void* Wvp,
                     const void* dOp, double* O, double* LSE, double* dX, double* dWq,
                     double* dWk, double* dWv, int nthreads) {
-  Shape s{S, D, H, G, d, causal};
+  Shape s{S, D, H, G, d, causal, rope_theta};
   if (!shape_ok(s)) return 1;
   const int64_t Hd = static_cast<int64_t>(H) * d;
   const int r = s.r();
@@ -251,10 +286,15 @@ int oracle_backward(int64_t S, int64_t D, int H, int G, int d, int causal, int e
   // Projections for every head (the oracle is not memory-frugal).
   std::vector<double> Q(static_cast<size_t>(H * S * d)), K(static_cast<size_t>(G * S * d)),
       V(static_cast<size_t>(G * S * d));
-  for (int h = 0; h < H; ++h) project_head(X, Wq, s, h, S, nullptr, &Q[h * S * d], nthreads);
+  // Q and K are kept rotated (when rope_theta > 0): the attention sees them so.
+  for (int h = 0; h < H; ++h) {
+    project_head(X, Wq, s, h, S, nullptr, &Q[h * S * d], nthreads);
+    rotate_rows(&Q[h * S * d], S, nullptr, s, +1);
+  }
   for (int g = 0; g < G; ++g) {
     project_head(X, Wk, s, g, S, nullptr, &K[g * S * d], nthreads);
     project_head(X, Wv, s, g, S, nullptr, &V[g * S * d], nthreads);
+    rotate_rows(&K[g * S * d], S, nullptr, s, +1);
   }
 
   // Forward (O, LSE) and D.
@@ -318,6 +358,11 @@ int oracle_backward(int64_t S, int64_t D, int H, int G, int d, int causal, int e
       }
     });
   }
+
+  // dQ and dK so far are gradients of the rotated rows; the projections see
+  // them through the transposed rotation.
+  for (int h = 0; h < H; ++h) rotate_rows(&dQ[h * S * d], S, nullptr, s, -1);
+  for (int g = 0; g < G; ++g) rotate_rows(&dK[g * S * d], S, nullptr, s, -1);
 
   // Weight gradients: dW[row][k] = sum_i grad[i][row] * X[i][k].
   auto weight_grad = [&](const std::vector<double>& grad, int nheads, double* dW) {

@@ -263,3 +263,135 @@ def test_sampled_rows_head_subset(oracle_mod):
     np.testing.assert_array_equal(Or[:, d:4 * d], O[rows][:, d:4 * d])
     np.testing.assert_array_equal(Lr[1:4], LSE[1:4][:, rows])
     assert np.all(np.isnan(Or[:, :d])) and np.all(np.isnan(Lr[4:]))
+
+
+# ------------------------------------------------------------ rotary embedding
+# Rotate-half rotary position embedding (an option of the layer, from the model
+# families that run it, not from the pages): the pair (c, c + d/2) of a query
+# or key row at position i turns by i * theta^(-2c/d).
+
+def torch_layer_rope(X, Wq, Wk, Wv, dO, H, G, d, causal, theta):
+    """torch fp64 reference with the rotation written as a complex product
+    (z_c = x_c + i x_{c+d/2} times exp(i * angle)), autograd backward."""
+    t = {k: torch.tensor(v, dtype=torch.float64, requires_grad=(k != "dO"))
+         for k, v in dict(X=X, Wq=Wq, Wk=Wk, Wv=Wv, dO=dO).items()}
+    S = X.shape[0]
+    half = d // 2
+    freq = theta ** (-2.0 * torch.arange(half, dtype=torch.float64) / d)
+    ang = torch.arange(S, dtype=torch.float64)[:, None] * freq[None, :]
+    rot = torch.polar(torch.ones_like(ang), ang)  # [S][half] complex
+
+    def rope(x):  # x [heads][S][d]
+        z = torch.complex(x[..., :half], x[..., half:]) * rot
+        return torch.cat([z.real, z.imag], dim=-1)
+
+    q = rope((t["X"] @ t["Wq"].T).reshape(S, H, d).transpose(0, 1))
+    k = rope((t["X"] @ t["Wk"].T).reshape(S, G, d).transpose(0, 1))
+    v = (t["X"] @ t["Wv"].T).reshape(S, G, d).transpose(0, 1)
+    k = k.repeat_interleave(H // G, dim=0)
+    v = v.repeat_interleave(H // G, dim=0)
+    o = torch.nn.functional.scaled_dot_product_attention(q[None], k[None], v[None],
+                                                         is_causal=causal)[0]
+    O = o.transpose(0, 1).reshape(S, H * d)
+    (O * t["dO"]).sum().backward()
+    scores = (q @ k.transpose(1, 2)) / math.sqrt(d)
+    if causal:
+        mask = torch.ones(S, S, dtype=torch.bool).tril()
+        scores = scores.masked_fill(~mask, float("-inf"))
+    lse = torch.logsumexp(scores, dim=-1)
+    return dict(O=O.detach().numpy(), LSE=lse.detach().numpy(), dX=t["X"].grad.numpy(),
+                dWq=t["Wq"].grad.numpy(), dWk=t["Wk"].grad.numpy(), dWv=t["Wv"].grad.numpy())
+
+
+@pytest.mark.parametrize("shape", [(37, 24, 4, 2, 8), (29, 16, 3, 3, 8), (50, 24, 8, 1, 8)])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("theta", [10000.0, 3.0])
+def test_rope_against_torch_complex_rotation(oracle_mod, shape, causal, theta):
+    S, D, H, G, d = shape
+    X, Wq, Wk, Wv, dO = draw(S, D, H, G, d, seed=S + 1)
+    got = oracle_mod.backward(X, Wq, Wk, Wv, dO, H, G, d, causal=causal, rope_theta=theta)
+    ref = torch_layer_rope(X, Wq, Wk, Wv, dO, H, G, d, causal, theta)
+    for name in ("O", "LSE", "dX", "dWq", "dWk", "dWv"):
+        close(got[name], ref[name])
+    O, LSE = oracle_mod.forward(X, Wq, Wk, Wv, H, G, d, causal=causal, rope_theta=theta)
+    np.testing.assert_array_equal(O, got["O"])
+    np.testing.assert_array_equal(LSE, got["LSE"])
+    rows = [0, 5, S - 1]
+    Or, Lr = oracle_mod.forward_rows(X, Wq, Wk, Wv, H, G, d, rows, causal=causal, rope_theta=theta)
+    close(Or, O[rows])
+    close(Lr, LSE[:, rows])
+
+
+def test_rope_two_tokens_by_hand(oracle_mod):
+    """S = 2, d = 2 (one frequency, w_0 = 1), Q = K = V = X = identity rows.
+    Position 0 is not rotated; position 1 turns (0, 1) by one radian to
+    (-sin 1, cos 1).  Row 1: scores tau*(-sin 1) against key 0 and tau*1
+    against itself."""
+    X = np.eye(2)
+    W = np.eye(2)
+    O, LSE = oracle_mod.forward(X, W, W, W, 1, 1, 2, rope_theta=500000.0)
+    tau = 1.0 / math.sqrt(2.0)
+    s0, s1 = -tau * math.sin(1.0), tau
+    l1 = math.log(math.exp(s0) + math.exp(s1))
+    assert abs(LSE[0, 0] - tau) <= 1e-15
+    assert abs(LSE[0, 1] - l1) <= 1e-15
+    np.testing.assert_allclose(O[0], [1.0, 0.0], atol=1e-15)
+    np.testing.assert_allclose(O[1], [math.exp(s0 - l1), math.exp(s1 - l1)], atol=1e-15)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_rope_finite_differences(oracle_mod, causal):
+    S, D, H, G, d = 21, 12, 4, 2, 6
+    X, Wq, Wk, Wv, dO = draw(S, D, H, G, d, seed=9)
+    theta = 7.0
+    g = oracle_mod.backward(X, Wq, Wk, Wv, dO, H, G, d, causal=causal, rope_theta=theta)
+    params = dict(X=X, Wq=Wq, Wk=Wk, Wv=Wv)
+    rng = np.random.default_rng(4)
+
+    def loss(p):
+        O, _ = oracle_mod.forward(p["X"], p["Wq"], p["Wk"], p["Wv"], H, G, d, causal=causal,
+                                  nthreads=1, rope_theta=theta)
+        return float(np.sum(O * dO))
+
+    for name, grad in (("X", "dX"), ("Wq", "dWq"), ("Wk", "dWk"), ("Wv", "dWv")):
+        for _ in range(20):
+            idx = tuple(int(rng.integers(0, n)) for n in params[name].shape)
+            base = params[name][idx]
+            eps = 1e-6 * max(1.0, abs(base))
+            plus = {k: v.copy() for k, v in params.items()}
+            minus = {k: v.copy() for k, v in params.items()}
+            plus[name][idx] = base + eps
+            minus[name][idx] = base - eps
+            fd = (loss(plus) - loss(minus)) / (2 * eps)
+            an = g[grad][idx]
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, idx, fd, an)
+
+
+def test_rope_leaves_position_zero_and_values_alone(oracle_mod):
+    """Position 0 turns by angle 0: with causal masking, row 0 of O and LSE is
+    the same with or without the rotation.  With Wq = 0 every score is 0 and
+    the rotation of a zero query changes nothing: O is the prefix mean of V."""
+    S, D, H, G, d = 17, 12, 4, 2, 6
+    X, Wq, Wk, Wv, _ = draw(S, D, H, G, d, seed=2)
+    O0, L0 = oracle_mod.forward(X, Wq, Wk, Wv, H, G, d)
+    O1, L1 = oracle_mod.forward(X, Wq, Wk, Wv, H, G, d, rope_theta=10000.0)
+    np.testing.assert_array_equal(O0[0], O1[0])
+    np.testing.assert_array_equal(L0[:, 0], L1[:, 0])
+    assert np.max(np.abs(O0[1:] - O1[1:])) > 1e-3  # it does act on later rows
+    Wq0 = np.zeros_like(Wq)
+    O2, L2 = oracle_mod.forward(X, Wq0, Wk, Wv, H, G, d, rope_theta=10000.0)
+    r = H // G
+    for h in range(H):
+        g = h // r
+        v = X @ Wv[g * d:(g + 1) * d].T
+        pref = np.cumsum(v, axis=0) / np.arange(1, S + 1)[:, None]
+        close(O2[:, h * d:(h + 1) * d], pref, 1e-13)
+        close(L2[h], np.log(np.arange(1, S + 1)), 1e-13)
+
+
+def test_rope_rejects_odd_head_dim(oracle_mod):
+    X, Wq, Wk, Wv, _ = draw(8, 6, 2, 1, 3)
+    with pytest.raises(ValueError):
+        oracle_mod.forward(X, Wq, Wk, Wv, 2, 1, 3, rope_theta=10000.0)
+    with pytest.raises(ValueError):
+        oracle_mod.forward(X, Wq, Wk, Wv, 2, 1, 3, rope_theta=-1.0)

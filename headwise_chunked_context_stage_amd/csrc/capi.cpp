@@ -87,11 +87,37 @@ struct Kernels {
   decltype(&bf16::dx) dx;
 };
 
+// fp32 variant: the rotary embedding runs as in-place passes right after the
+// producing kernel (the bf16 kernels apply it in their epilogues, before
+// rounding).  fp32 storage is exact, so both orders give the same values.
+hipError_t f32_proj(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t,
+                    const Rope& rope, hipStream_t st) {
+  hipError_t e = f32::proj(X, S, D, d, t, st);
+  for (int i = 0; i < t.n && e == hipSuccess; ++i)
+    if ((t.rot >> i) & 1) e = f32::rope(static_cast<float*>(t.a[i]), 1, S, d, rope, +1, st);
+  return e;
+}
+
+hipError_t f32_attn_dq(const AttnArgs& a, hipStream_t st) {
+  hipError_t e = f32::attn_dq(a, st);
+  if (e == hipSuccess && a.rope.on)
+    e = f32::rope(static_cast<float*>(a.dq), a.nq, a.S, a.d, a.rope, -1, st);
+  return e;
+}
+
+hipError_t f32_attn_dkv(const AttnArgs& a, hipStream_t st) {
+  hipError_t e = f32::attn_dkv(a, st);
+  const int nkv = a.nq >= a.r ? a.nq / a.r : 1;
+  if (e == hipSuccess && a.rope.on && a.last_of_group)
+    e = f32::rope(static_cast<float*>(a.dk), nkv, a.S, a.d, a.rope, -1, st);
+  return e;
+}
+
 Kernels kernels_for(int dtype) {
   if (dtype == UPIPE_BF16)
     return {bf16::proj, bf16::attn_fwd, bf16::bwd_pre, bf16::attn_dkv, bf16::attn_dq, bf16::dw,
             bf16::dx};
-  return {f32::proj, f32::attn_fwd, f32::bwd_pre, f32::attn_dkv, f32::attn_dq, f32::dw, f32::dx};
+  return {f32_proj, f32::attn_fwd, f32::bwd_pre, f32_attn_dkv, f32_attn_dq, f32::dw, f32::dx};
 }
 
 // Project the stage's query heads (and its KV heads when it opens their group)
@@ -102,13 +128,19 @@ hipError_t stage_projection(const Plan& p, const Stage& st, const Kernels& K, co
   const size_t e = p.elem();
   const size_t wrows = static_cast<size_t>(p.d) * p.D * e;  // bytes of one head's weight rows
   const size_t hbuf = static_cast<size_t>(p.S) * p.d * e;   // bytes of one head's [S][d] buffer
-  std::vector<std::pair<const void*, void*>> jobs;
+  struct Job {
+    const void* w;
+    void* a;
+    bool rotate;  // queries and keys take the rotary embedding, values do not
+  };
+  const bool rope = p.rope.on != 0;
+  std::vector<Job> jobs;
   for (int h = 0; h < st.nq; ++h)
-    jobs.push_back({at(Wq, (st.q0 + h) * wrows), at(ws, p.ws.q[st.slot] + h * hbuf)});
+    jobs.push_back({at(Wq, (st.q0 + h) * wrows), at(ws, p.ws.q[st.slot] + h * hbuf), rope});
   if (st.load) {
     for (int g = 0; g < st.nkv; ++g) {
-      jobs.push_back({at(Wk, (st.kv0 + g) * wrows), at(ws, p.ws.k[st.kvslot] + g * hbuf)});
-      jobs.push_back({at(Wv, (st.kv0 + g) * wrows), at(ws, p.ws.v[st.kvslot] + g * hbuf)});
+      jobs.push_back({at(Wk, (st.kv0 + g) * wrows), at(ws, p.ws.k[st.kvslot] + g * hbuf), rope});
+      jobs.push_back({at(Wv, (st.kv0 + g) * wrows), at(ws, p.ws.v[st.kvslot] + g * hbuf), false});
     }
   }
   for (size_t b = 0; b < jobs.size(); b += kMaxChunks) {
@@ -116,10 +148,12 @@ hipError_t stage_projection(const Plan& p, const Stage& st, const Kernels& K, co
     std::memset(&t, 0, sizeof(t));
     t.n = static_cast<int>(std::min<size_t>(kMaxChunks, jobs.size() - b));
     for (int i = 0; i < t.n; ++i) {
-      t.w[i] = jobs[b + i].first;
-      t.a[i] = jobs[b + i].second;
+      t.w[i] = jobs[b + i].w;
+      t.a[i] = jobs[b + i].a;
+      if (jobs[b + i].rotate) t.rot |= uint64_t(1) << i;
     }
-    hipError_t err = timed(UPIPE_K_PROJ, s, [&] { return K.proj(X, p.S, p.D, p.d, t, s); });
+    hipError_t err =
+        timed(UPIPE_K_PROJ, s, [&] { return K.proj(X, p.S, p.D, p.d, t, p.rope, s); });
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
@@ -141,6 +175,7 @@ AttnArgs attn_args(const Plan& p, const Stage& st, void* ws) {
   a.v = at(ws, p.ws.v[st.kvslot]);
   a.first_of_group = st.load ? 1 : 0;
   a.last_of_group = st.done ? 1 : 0;
+  a.rope = p.rope;
   return a;
 }
 
@@ -381,11 +416,16 @@ int upipe_create(upipe_plan** out, int64_t S, int64_t d_model, int H, int G, int
 
 int upipe_create_ex(upipe_plan** out, int64_t S, int64_t d_model, int H, int G, int d_head, int U,
                     int causal, int dtype, int flags) {
+  return upipe_create_rope(out, S, d_model, H, G, d_head, U, causal, dtype, flags, 0.0);
+}
+
+int upipe_create_rope(upipe_plan** out, int64_t S, int64_t d_model, int H, int G, int d_head, int U,
+                      int causal, int dtype, int flags, double rope_theta) {
   if (!out) return UPIPE_ERR_ARG;
   *out = nullptr;
   upipe_plan* h = new (std::nothrow) upipe_plan;
   if (!h) return UPIPE_ERR_ARG;
-  int rc = make_plan(h->p, S, d_model, H, G, d_head, U, causal, dtype, flags);
+  int rc = make_plan(h->p, S, d_model, H, G, d_head, U, causal, dtype, flags, rope_theta);
   if (rc != UPIPE_OK) {
     delete h;
     return rc;

@@ -34,6 +34,7 @@
 
 #include "upipe_internal.h"
 #include "bf16_common.h"
+#include "rope_device.h"
 
 namespace upipe {
 namespace {
@@ -48,8 +49,10 @@ constexpr int GBUF = 2 * GB * GS;             // elements per buffer (two operan
 // X streams from HBM: global loads run NRR = 4 k-steps ahead of their LDS
 // store through a ring of register sets, so each has several steps of MFMA
 // time to arrive (one step ahead, the loop waited on HBM latency).
+// Chunks marked in t.rot (queries and keys under a rotary embedding) are
+// rotated in fp32 before their single rounding to bf16.
 __global__ __launch_bounds__(256, 2) void proj_kernel(const u16* __restrict__ X, int64_t S,
-                                                      int64_t D, ChunkTable t, int nrb) {
+                                                      int64_t D, ChunkTable t, int nrb, Rope rope) {
   __shared__ __attribute__((aligned(16))) u16 lds[2 * GBUF];
   const int total = nrb * t.n;
   const int lid = xcd_remap(blockIdx.x, total);
@@ -128,6 +131,51 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(const u16* __restrict__ X,
   if (kb < nk) body(kb, std::integral_constant<int, 1 % NRR>{});
   if (kb + 1 < nk) body(kb + 1, std::integral_constant<int, 2 % NRR>{});
   if (NRR > 3 && kb + 2 < nk) body(kb + 2, std::integral_constant<int, 3 % NRR>{});
+  if ((t.rot >> ch) & 1) {
+    // Rotated chunk: C (fp32) -> LDS tile [128][132]; each thread then reads
+    // 8 consecutive columns of a row and the 8 columns d/2 away, rotates the
+    // pairs and stores 8 bf16 (16 bytes).  The column group is fixed per
+    // thread, so its 8 frequencies are read once.
+    constexpr int CF = GB + 4;
+    float* cf = reinterpret_cast<float*>(lds);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = 64 * wm + 32 * mb + 8 * (i / 4) + 4 * hf + (i % 4);
+          cf[row * CF + 64 * wn + 32 * nb + col] = acc[mb][nb][i];
+        }
+    __syncthreads();
+    const int chunk = tid % 16, c0 = 8 * chunk;
+    const bool upper = chunk >= 8;  // columns d/2 .. d-1
+    double fw[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) fw[k] = rope.fw[(c0 % 64) + k];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int row = tid / 16 + 16 * m;
+      const int64_t gi = i0 + row;
+      if (gi >= S) continue;
+      const float* own = cf + row * CF + c0;
+      const float* other = cf + row * CF + (c0 ^ 64);
+      float y[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        float cs, sn;
+        rope_cs(gi, fw[k], cs, sn);
+        float lo = upper ? other[k] : own[k], hi = upper ? own[k] : other[k];
+        rope_fwd(lo, hi, cs, sn);
+        y[k] = upper ? hi : lo;
+      }
+      u32x4 v;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = pack2(y[2 * k], y[2 * k + 1]);
+      st16(out + gi * DH + c0, v);
+    }
+    return;
+  }
   // Epilogue: C (bf16) -> LDS tile [128][136] -> coalesced 16-byte stores.
   constexpr int CS = GB + 8;
   u16* cs = lds;
@@ -814,10 +862,29 @@ __global__ __launch_bounds__(dqk::NT, 1) void attn_dq_kernel(AttnArgs a) {
 #pragma unroll
     for (int d4 = 0; d4 < 4; ++d4)
 #pragma unroll
+      for (int i = 0; i < 16; ++i) dq[d4][i] *= tau;
+    if (a.rope.on) {
+      // gradient of the unrotated query: the transposed rotation, applied to
+      // the pairs (c, c + 64) = blocks d4 and d4 + 2 at the same register
+#pragma unroll
+      for (int d4 = 0; d4 < 2; ++d4)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float cs, sn;
+          rope_cs(myq, a.rope.fw[32 * d4 + 8 * (i / 4) + 4 * hf + (i % 4)], cs, sn);
+          float lo = dq[d4][i], hi = dq[d4 + 2][i];
+          rope_bwd(lo, hi, cs, sn);
+          dq[d4][i] = lo;
+          dq[d4 + 2][i] = hi;
+        }
+    }
+#pragma unroll
+    for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         u32x2 v;
-        v[0] = pack2(dq[d4][4 * g4 + 0] * tau, dq[d4][4 * g4 + 1] * tau);
-        v[1] = pack2(dq[d4][4 * g4 + 2] * tau, dq[d4][4 * g4 + 3] * tau);
+        v[0] = pack2(dq[d4][4 * g4 + 0], dq[d4][4 * g4 + 1]);
+        v[1] = pack2(dq[d4][4 * g4 + 2], dq[d4][4 * g4 + 3]);
         *reinterpret_cast<u32x2*>(out + 32 * d4 + 8 * g4 + 4 * hf) = v;
       }
   }
@@ -877,11 +944,13 @@ inline unsigned cdiv(int64_t a, int64_t b) { return static_cast<unsigned>((a + b
 
 namespace bf16 {
 
-hipError_t proj(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t, hipStream_t st) {
+hipError_t proj(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t, const Rope& rope,
+                hipStream_t st) {
   if (d != DH || D % GK != 0) return hipErrorInvalidValue;
+  if (t.rot != 0 && !rope.on) return hipErrorInvalidValue;
   const int nrb = static_cast<int>(cdiv(S, GB));
   hipLaunchKernelGGL(proj_kernel, dim3(nrb * t.n), dim3(256), 0, st, static_cast<const u16*>(X), S,
-                     D, t, nrb);
+                     D, t, nrb, rope);
   return hipGetLastError();
 }
 

@@ -8,6 +8,7 @@
 
 #include "upipe_internal.h"
 #include "bf16_common.h"
+#include "rope_device.h"
 
 namespace upipe {
 namespace {
@@ -279,6 +280,29 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
     float* carry = pwave ? a.dv_acc : a.dk_acc;
     u16* out = static_cast<u16*>(pwave ? a.dv : a.dk);
     const float scale = pwave ? 1.f : tau;
+    if (a.last_of_group) {
+#pragma unroll
+      for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[d4][i] *= scale;
+      if (!pwave && a.rope.on) {
+        // gradient of the unrotated key (the group's finished sum): the
+        // transposed rotation of the pairs (c, c + 64) = blocks d4, d4 + 2
+#pragma unroll
+        for (int d4 = 0; d4 < 2; ++d4) {
+          const double fw = a.rope.fw[32 * d4 + col];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float cs, sn;
+            rope_cs(wk0 + 8 * (i / 4) + 4 * hf + (i % 4), fw, cs, sn);
+            float lo = acc[d4][i], hi = acc[d4 + 2][i];
+            rope_bwd(lo, hi, cs, sn);
+            acc[d4][i] = lo;
+            acc[d4 + 2][i] = hi;
+          }
+        }
+      }
+    }
 #pragma unroll
     for (int d4 = 0; d4 < 4; ++d4)
 #pragma unroll
@@ -287,7 +311,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
         if (kr >= S) continue;
         const int64_t off = (static_cast<int64_t>(gl) * S + kr) * DH + 32 * d4 + col;
         if (a.last_of_group)
-          out[off] = __builtin_bit_cast(u16, static_cast<__bf16>(acc[d4][i] * scale));
+          out[off] = __builtin_bit_cast(u16, static_cast<__bf16>(acc[d4][i]));
         else
           carry[off] = acc[d4][i];
       }

@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 
 #include "upipe_internal.h"
+#include "rope_device.h"
 
 namespace upipe {
 namespace {
@@ -232,6 +233,26 @@ __global__ __launch_bounds__(128) void attn_dkv_kernel(AttnArgs a) {
   }
 }
 
+// Rotary embedding in place: one thread per (buffer, row, pair c < d/2).
+// sign +1 rotates, -1 applies the transposed rotation (gradients).  fp32
+// storage holds the kernels' results exactly, so rotating after the producer
+// gives the same values as rotating in its epilogue.
+__global__ __launch_bounds__(256) void rope_kernel(float* __restrict__ buf, int64_t S, int d,
+                                                   Rope r, int sign) {
+  const int half = d / 2;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= S * half) return;
+  const int64_t i = e / half;
+  const int c = static_cast<int>(e % half);
+  float* row = buf + static_cast<int64_t>(blockIdx.y) * S * d + i * d;
+  float cs, sn;
+  rope_cs(i, r.fw[c], cs, sn);
+  if (sign > 0)
+    rope_fwd(row[c], row[c + half], cs, sn);
+  else
+    rope_bwd(row[c], row[c + half], cs, sn);
+}
+
 inline unsigned cdiv(int64_t a, int64_t b) { return static_cast<unsigned>((a + b - 1) / b); }
 
 }  // namespace
@@ -265,6 +286,14 @@ hipError_t dw(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t, h
 hipError_t dx(float* dX, int64_t S, int64_t D, int d, const ChunkTable& t, hipStream_t st) {
   hipLaunchKernelGGL(dx_kernel, dim3(cdiv(D, 256), static_cast<unsigned>(S)), dim3(256), 0, st, dX,
                      S, D, d, t);
+  return hipGetLastError();
+}
+
+hipError_t rope(float* buf, int n, int64_t S, int d, const Rope& r, int sign, hipStream_t st) {
+  if (n <= 0 || S <= 0) return hipSuccess;
+  if (!r.on || d % 2 != 0 || d / 2 > kMaxRopePairs) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rope_kernel, dim3(cdiv(S * (d / 2), 256), n), dim3(256), 0, st, buf, S, d, r,
+                     sign);
   return hipGetLastError();
 }
 

@@ -12,15 +12,23 @@
 // section 局限与改进, concerns several devices): U divides H, and either U
 // divides the group size r = H/G (a stage lies inside one group) or r divides
 // U (a stage holds whole groups).  No stage ever cuts a group unevenly.
+//
+// Optional rotary position embedding of queries and keys (not on the pages;
+// the Llama and Qwen model families that run this layer use it): rotate-half
+// form with base theta.  It changes no buffer size.
 #include <algorithm>
+#include <cmath>
+#include <cstring>
 
 #include "upipe_internal.h"
 
 namespace upipe {
 
 int make_plan(Plan& p, int64_t S, int64_t D, int H, int G, int d, int U, int causal, int dtype,
-              int flags) {
+              int flags, double rope_theta) {
   if ((flags & ~UPIPE_PIPELINE) != 0) return UPIPE_ERR_ARG;
+  // rope_theta: 0 (no rotary embedding) or a finite positive base
+  if (!(rope_theta >= 0.0) || !std::isfinite(rope_theta)) return UPIPE_ERR_ARG;
   if (S < 0 || D <= 0 || H <= 0 || G <= 0 || d <= 0 || U <= 0) return UPIPE_ERR_ARG;
   if (causal != 0 && causal != 1) return UPIPE_ERR_ARG;
   if (dtype != UPIPE_BF16 && dtype != UPIPE_F32) return UPIPE_ERR_ARG;
@@ -50,6 +58,15 @@ int make_plan(Plan& p, int64_t S, int64_t D, int H, int G, int d, int U, int cau
   p.dtype = dtype;
   p.kv_per_stage = std::max(1, U / r);
   p.pipeline = (flags & UPIPE_PIPELINE) ? 1 : 0;
+  // Rotary embedding: w_c = theta^(-2c/d) for c < d/2, kept as turns per
+  // position (w_c / 2 pi) in fp64.
+  p.rope_theta = rope_theta;
+  std::memset(&p.rope, 0, sizeof(p.rope));
+  if (rope_theta > 0.0) {
+    p.rope.on = 1;
+    for (int c = 0; c < d / 2; ++c)
+      p.rope.fw[c] = std::pow(rope_theta, -2.0 * c / d) / (2.0 * 3.14159265358979323846);
+  }
 
   p.stages.clear();
   int loads = 0;  // stages so far that project K and V

@@ -43,11 +43,24 @@ struct WsLayout {
   size_t fwd_bytes, bwd_bytes;
 };
 
+// Rotary position embedding of queries and keys (rotate-half form): the pair
+// (c, c + d/2) of a row at token position i turns by the angle i * w_c with
+// w_c = theta^(-2c/d).  fw[c] = w_c / (2 pi) in fp64 (turns per position), so
+// a kernel takes the fractional part of i * fw[c] in fp64 and evaluates the
+// sine and cosine of that fraction of a turn in fp32.
+constexpr int kMaxRopePairs = 64;  // d / 2 for d <= 128
+struct Rope {
+  int on;
+  double fw[kMaxRopePairs];
+};
+
 struct Plan {
   int64_t S, D;
   int H, G, d, U, r, causal, dtype;
   int kv_per_stage;  // max(1, U / r)
   int pipeline;      // stage s + 1's projection overlaps stage s's attention
+  double rope_theta; // 0: no rotary embedding
+  Rope rope;         // frequencies derived from rope_theta and d
   std::vector<Stage> stages;
   WsLayout ws;
   size_t elem() const { return dtype == UPIPE_BF16 ? 2 : 4; }
@@ -55,7 +68,7 @@ struct Plan {
 
 // Validates and builds; returns a UPIPE_* code.
 int make_plan(Plan& p, int64_t S, int64_t D, int H, int G, int d, int U, int causal, int dtype,
-              int flags = 0);
+              int flags = 0, double rope_theta = 0.0);
 int choose_u(int64_t S, int64_t D, int H, int G, int d, int causal, int dtype, size_t budget,
              int* U);
 
@@ -66,6 +79,7 @@ int choose_u(int64_t S, int64_t D, int H, int G, int d, int causal, int dtype, s
 constexpr int kMaxChunks = 64;
 struct ChunkTable {
   int n;
+  uint64_t rot;               // projection: bit i set = rotate chunk i's rows (queries, keys)
   const void* w[kMaxChunks];  // weight rows [d][D] of this chunk
   void* a[kMaxChunks];        // [S][d] activation / gradient buffer of this chunk
   float* dw[kMaxChunks];      // [d][D] fp32 weight-gradient rows (dW launches only)
@@ -99,12 +113,18 @@ struct AttnArgs {
   float* dv_acc;
   int first_of_group;   // this launch starts the group's dK/dV accumulation
   int last_of_group;    // this launch completes it
+  // rotary embedding: the bf16 kernels map the gradients of the rotated
+  // queries and keys back through the transposed rotation as they write
+  // dQ and the finished dK
+  Rope rope;
 };
 
 // Kernel launchers (one set per element type).  Return hipSuccess or the
 // launch error.  `S` is the number of tokens; X is [S][D].
 namespace bf16 {
-hipError_t proj(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t, hipStream_t st);
+// Chunks with their bit set in t.rot are rotated (rope) before rounding.
+hipError_t proj(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t, const Rope& rope,
+                hipStream_t st);
 hipError_t attn_fwd(const AttnArgs& a, hipStream_t st);
 hipError_t bwd_pre(const AttnArgs& a, hipStream_t st);
 hipError_t attn_dkv(const AttnArgs& a, hipStream_t st);
@@ -122,6 +142,9 @@ hipError_t attn_dkv(const AttnArgs& a, hipStream_t st);
 hipError_t attn_dq(const AttnArgs& a, hipStream_t st);
 hipError_t dw(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t, hipStream_t st);
 hipError_t dx(float* dX, int64_t S, int64_t D, int d, const ChunkTable& t, hipStream_t st);
+// In-place rotation of n [S][d] fp32 buffers at `buf` (consecutive): sign +1
+// rotates queries/keys, -1 applies the transposed rotation to gradients.
+hipError_t rope(float* buf, int n, int64_t S, int d, const Rope& r, int sign, hipStream_t st);
 }  // namespace f32
 hipError_t fill_zero(void* p, size_t bytes, hipStream_t st);
 

@@ -18,7 +18,7 @@ UPIPE_OK, UPIPE_ERR_ARG, UPIPE_ERR_UNSUPPORTED, UPIPE_ERR_WORKSPACE, UPIPE_ERR_H
 UPIPE_PIPELINE = 1  # plan flag: stage pipelining on a second stream
 KERNEL_KINDS = ("proj", "attn_fwd", "bwd_pre", "attn_dkv", "attn_dq", "dw", "dx", "fill")
 
-EXPORTS = ("upipe_create", "upipe_create_ex", "upipe_destroy", "upipe_peak_bytes", "upipe_peak_bytes_phase",
+EXPORTS = ("upipe_create", "upipe_create_ex", "upipe_create_rope", "upipe_destroy", "upipe_peak_bytes", "upipe_peak_bytes_phase",
            "upipe_fwd", "upipe_bwd", "upipe_strerror", "upipe_num_stages", "upipe_stage_info",
            "upipe_timing_enable", "upipe_timing_read", "upipe_kernel_name", "upipe_mfma_ceiling",
            "upipe_auto_u")
@@ -46,6 +46,9 @@ def lib():
     L.upipe_create.restype = i32
     L.upipe_create_ex.argtypes = [ctypes.POINTER(vp), i64, i64, i32, i32, i32, i32, i32, i32, i32]
     L.upipe_create_ex.restype = i32
+    L.upipe_create_rope.argtypes = [ctypes.POINTER(vp), i64, i64, i32, i32, i32, i32, i32, i32, i32,
+                                    ctypes.c_double]
+    L.upipe_create_rope.restype = i32
     L.upipe_destroy.argtypes = [vp]
     L.upipe_destroy.restype = None
     L.upipe_peak_bytes.argtypes = [vp]
@@ -138,6 +141,15 @@ def upipe_create_ex(S, d_model, H, G, d_head, U, causal=1, dtype="bf16", flags=0
     return h.value
 
 
+def upipe_create_rope(S, d_model, H, G, d_head, U, causal=1, dtype="bf16", flags=0,
+                      rope_theta=0.0) -> int:
+    h = ctypes.c_void_p()
+    _check(lib().upipe_create_rope(ctypes.byref(h), S, d_model, H, G, d_head, U, int(causal),
+                                   _dtype_code(dtype), int(flags), float(rope_theta)),
+           "upipe_create_rope")
+    return h.value
+
+
 def upipe_destroy(plan) -> None:
     lib().upipe_destroy(plan)
 
@@ -218,12 +230,18 @@ def upipe_auto_u(S: int, d_model: int, H: int, G: int, d_head: int, budget_bytes
 class Plan:
     """Owns a plan handle; the layer's shape and stage size U are fixed here."""
 
-    def __init__(self, S, d_model, H, G, d_head, U, causal=True, dtype="bf16", pipeline=False):
+    def __init__(self, S, d_model, H, G, d_head, U, causal=True, dtype="bf16", pipeline=False,
+                 rope_theta=0.0):
         self.S, self.D, self.H, self.G, self.d, self.U = S, d_model, H, G, d_head, U
         self.causal = bool(causal)
         self.pipeline = bool(pipeline)
+        self.rope_theta = float(rope_theta)
         self.dtype = "bf16" if _dtype_code(dtype) == UPIPE_BF16 else "f32"
-        if self.pipeline:
+        if self.rope_theta != 0.0:
+            self.handle = upipe_create_rope(S, d_model, H, G, d_head, U, int(self.causal), dtype,
+                                            UPIPE_PIPELINE if self.pipeline else 0,
+                                            self.rope_theta)
+        elif self.pipeline:
             self.handle = upipe_create_ex(S, d_model, H, G, d_head, U, int(self.causal), dtype,
                                           UPIPE_PIPELINE)
         else:

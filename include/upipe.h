@@ -20,8 +20,10 @@
  *  - the all-to-all exchanges of steps (2) and (4) are between devices and are
  *    not part of one GPU's share.
  * Readings where the pages are silent: softmax scale 1/sqrt(d_head), causal
- * mask j <= i, no RoPE / bias / output projection, batch 1, natural-log LSE,
+ * mask j <= i, no bias / output projection, batch 1, natural-log LSE,
  * backward of L = sum(O * dO) with recomputation of each stage's Q, K, V.
+ * A rotary position embedding of queries and keys is optional
+ * (upipe_create_rope); it is off unless asked for.
  *
  * Layouts (row-major, batch 1, all tensor pointers are DEVICE pointers owned
  * by the caller; element type `dtype` unless stated):
@@ -92,6 +94,23 @@ enum {
  * same plan as upipe_create).  Unknown flag bits return UPIPE_ERR_ARG. */
 int upipe_create_ex(upipe_plan** out, int64_t S, int64_t d_model, int H, int G, int d_head, int U,
                     int causal, int dtype, int flags);
+
+/* upipe_create_ex with a rotary position embedding of queries and keys.  Not
+ * on the pages: the Llama and Qwen model families that run this layer rotate
+ * each projected query and key row before the attention (rotate-half form).
+ * For c < d_head/2 and w_c = rope_theta^(-2c/d_head), the pair (c, c+d_head/2)
+ * of the row at token position i (0 .. S-1) turns by the angle i*w_c:
+ *   y[c]          = x[c] cos(i w_c) - x[c + d_head/2] sin(i w_c)
+ *   y[c+d_head/2] = x[c + d_head/2] cos(i w_c) + x[c] sin(i w_c)
+ * Values are not rotated; the backward returns the gradients of the
+ * unrotated projections (the transposed rotation).  In bf16 the rotation
+ * happens in fp32 before the stage buffers' single rounding.  The angle's
+ * turn fraction is taken in fp64, its sine and cosine in fp32.
+ * rope_theta = 0 turns the embedding off (the plain upipe_create_ex plan);
+ * a negative, NaN or infinite rope_theta returns UPIPE_ERR_ARG.  The
+ * workspace does not change. */
+int upipe_create_rope(upipe_plan** out, int64_t S, int64_t d_model, int H, int G, int d_head,
+                      int U, int causal, int dtype, int flags, double rope_theta);
 
 /* Chunk size from a memory budget (host only).  The pages (paper.rainbus.top
  * summary of "Untied Ulysses", section 独立分析的弱点) propose choosing U from

@@ -16,14 +16,39 @@ import math
 import torch
 
 
-def bf16_path_emulation(inp, H: int, G: int, d: int, causal: bool = True) -> dict:
+def _rotation(S: int, d: int, theta: float):
+    """cos and sin [S][d/2] of the rotary angles i * theta^(-2c/d), from fp64."""
+    half = d // 2
+    w = theta ** (-2.0 * torch.arange(half, dtype=torch.float64) / d)
+    ang = torch.arange(S, dtype=torch.float64)[:, None] * w[None, :]
+    return torch.cos(ang).float(), torch.sin(ang).float()
+
+
+def _rotate(x, cs, sn, sign):
+    """Rotate-half rotation of the last dim of x [heads][S][d]; sign -1 is the
+    transpose (for gradients)."""
+    half = x.shape[-1] // 2
+    a, b = x[..., :half], x[..., half:]
+    sn = sn * sign
+    return torch.cat([a * cs - b * sn, b * cs + a * sn], dim=-1)
+
+
+def bf16_path_emulation(inp, H: int, G: int, d: int, causal: bool = True,
+                        rope_theta: float = 0.0) -> dict:
+    """With rope_theta > 0, queries and keys are rotated in fp32 before their
+    rounding, and dQ, dK take the transposed rotation before theirs."""
     bf = lambda t: t.to(torch.bfloat16).float()
     X, Wq, Wk, Wv, dO = [inp[k].detach().cpu().float() for k in ("X", "Wq", "Wk", "Wv", "dO")]
     S = X.shape[0]
     r = H // G
     tau = 1.0 / math.sqrt(d)
-    Q = bf(X @ Wq.T).reshape(S, H, d).transpose(0, 1)
-    K = bf(X @ Wk.T).reshape(S, G, d).transpose(0, 1).repeat_interleave(r, 0)
+    if rope_theta > 0:
+        cs, sn = _rotation(S, d, rope_theta)
+        rot = lambda t, sign: _rotate(t, cs, sn, sign)
+    else:
+        rot = lambda t, sign: t
+    Q = bf(rot((X @ Wq.T).reshape(S, H, d).transpose(0, 1), 1))
+    K = bf(rot((X @ Wk.T).reshape(S, G, d).transpose(0, 1), 1)).repeat_interleave(r, 0)
     V = bf(X @ Wv.T).reshape(S, G, d).transpose(0, 1).repeat_interleave(r, 0)
     s = (Q @ K.transpose(1, 2).contiguous()) * tau
     if causal:
@@ -39,10 +64,10 @@ def bf16_path_emulation(inp, H: int, G: int, d: int, causal: bool = True) -> dic
     P = torch.exp(s - lse[..., None])
     dP = go @ V.transpose(1, 2).contiguous()
     dS = P * (dP - Dd)
-    dQ = bf(tau * (bf(dS) @ K))
+    dQ = bf(rot(tau * (bf(dS) @ K), -1))
     dKh = bf(dS).transpose(1, 2).contiguous() @ Q
     dVh = bf(P).transpose(1, 2).contiguous() @ go
-    dK = bf(tau * dKh.reshape(G, r, S, d).sum(1))
+    dK = bf(rot(tau * dKh.reshape(G, r, S, d).sum(1), -1))
     dV = bf(dVh.reshape(G, r, S, d).sum(1))
     dQf = dQ.transpose(0, 1).reshape(S, H * d)
     dKf = dK.transpose(0, 1).reshape(S, G * d)

@@ -58,18 +58,18 @@ def host(t):
     return t.detach().double().cpu().numpy()
 
 
-def run_layer(shape, dtype, U, inp, causal=True, backward=True, pipeline=False):
+def run_layer(shape, dtype, U, inp, causal=True, backward=True, pipeline=False, rope_theta=0.0):
     plan = upipe.Plan(shape.S, shape.D, shape.H, shape.G, shape.d, U, causal=causal, dtype=dtype,
-                      pipeline=pipeline)
+                      pipeline=pipeline, rope_theta=rope_theta)
     out = run(plan, inp, backward_pass=backward)
     torch.cuda.synchronize()
     out.pop("ws")
     return out
 
 
-def oracle_full(shape, inp, causal=True):
+def oracle_full(shape, inp, causal=True, rope_theta=0.0):
     np_in = [to_numpy_exact(inp[k]) for k in ("X", "Wq", "Wk", "Wv", "dO")]
-    return oracle.backward(*np_in, shape.H, shape.G, shape.d, causal=causal)
+    return oracle.backward(*np_in, shape.H, shape.G, shape.d, causal=causal, rope_theta=rope_theta)
 
 
 def compare(name, got, ref, max_abs, mean_abs):
@@ -83,14 +83,14 @@ def rel_frob(got, ref):
     return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
 
 
-def check_against_oracle(out, ref, dtype, inp=None, shape=None, causal=True):
+def check_against_oracle(out, ref, dtype, inp=None, shape=None, causal=True, rope_theta=0.0):
     if dtype == "f32":
         for k in OUTS:
             compare(k, host(out[k]), ref[k], 2e-2, 2e-3)
         return
     for k in ("O", "LSE"):
         compare(k, host(out[k]), ref[k], 2e-2, 2e-3)
-    emu = bf16_path_emulation(inp, shape.H, shape.G, shape.d, causal=causal)
+    emu = bf16_path_emulation(inp, shape.H, shape.G, shape.d, causal=causal, rope_theta=rope_theta)
     for k in ("O", "LSE", "dX", "dWq", "dWk", "dWv"):
         got = host(out[k])
         floor = np.abs(emu[k].double().numpy() - ref[k])
@@ -246,6 +246,60 @@ def test_non_causal(dtype):
             assert_same_bits(first, out, "U=%d" % U)
 
 
+# ---------------------------------------------------------------- rotary embedding
+# Optional rotate-half rotary embedding of queries and keys (the Llama and Qwen
+# families' attention; not on the pages): the projection rotates Q and K before
+# rounding, dQ and the finished dK take the transposed rotation.
+ROPE_CASES = [
+    # S, D, H, G, d, dtype, theta
+    (1000, 1024, 4, 1, 128, "bf16", 10000.0),   # ragged
+    (768, 512, 8, 2, 128, "bf16", 500000.0),    # two groups, Llama3's base
+    (2048, 1024, 4, 2, 128, "bf16", 1000000.0),  # Qwen3's base; U = 1 carries dK over stages
+    (320, 256, 4, 2, 64, "f32", 10000.0),
+]
+
+
+@pytest.mark.parametrize("S,D,H,G,d,dtype,theta", ROPE_CASES)
+def test_rope_matches_oracle_and_is_U_invariant(S, D, H, G, d, dtype, theta):
+    shape = LayerShape(S=S, D=D, H=H, G=G, d=d)
+    cpu_inp = make_inputs(shape, dtype, seed=13, device="cpu")
+    ref = oracle_full(shape, cpu_inp, rope_theta=theta)
+    inp = {k: v.cuda() for k, v in cpu_inp.items()}
+    first = None
+    for U in legal_us(H, G):
+        say("rope %s theta=%g S=%d D=%d H=%d G=%d U=%d" % (dtype, theta, S, D, H, G, U))
+        out = run_layer(shape, dtype, U, inp, rope_theta=theta)
+        if first is None:
+            check_against_oracle(out, ref, dtype, cpu_inp, shape, rope_theta=theta)
+            first = out
+        else:
+            assert_same_bits(first, out, "U=%d" % U)
+    say("rope pipelined U=%d" % legal_us(H, G)[-1])
+    assert_same_bits(first, run_layer(shape, dtype, legal_us(H, G)[-1], inp, pipeline=True,
+                                      rope_theta=theta), "pipelined")
+    plain = run_layer(shape, dtype, 1, inp)
+    assert not torch.equal(plain["O"][1:], first["O"][1:])  # the embedding is applied
+
+
+def test_rope_long_positions():
+    """Rotary angles at token positions up to 2^20 (one turn fraction per
+    position in fp64): forward rows near the end of a 1M-token sequence
+    against the oracle.  A narrow d_model keeps the oracle's key projection
+    over all positions short; the scaling identities cover the backward."""
+    shape = LayerShape(S=1 << 20, D=128, H=2, G=1, d=128)
+    inp = make_inputs(shape, "bf16", seed=17, device="cuda")
+    say("rope S=1048576 D=128 H=2 G=1 U=2 theta=10000")
+    out = run_layer(shape, "bf16", 2, inp, rope_theta=10000.0)
+    S = shape.S
+    sampled_rows_check(shape, inp, out, [0, 1, 4095],
+                       [S - 1, S - 2, S - 1000, (1 << 19) + 3], (0, 2), rope_theta=10000.0)
+    e = identities(out, inp)
+    say("  identities %.2e %.2e %.2e" % e)
+    assert max(e) < 1e-4
+    for k in OUTS:
+        assert torch.isfinite(out[k]).all(), k
+
+
 def test_empty_sequence_zero_weight_gradients():
     shape = LayerShape(S=0, D=256, H=4, G=2, d=128)
     plan = upipe.Plan(0, 256, 4, 2, 128, 2)
@@ -298,7 +352,7 @@ def identities(out, inp):
     return e1, e2, e3
 
 
-def sampled_rows_check(shape, inp, out, rows_all, rows_late, late_heads):
+def sampled_rows_check(shape, inp, out, rows_all, rows_late, late_heads, rope_theta=0.0):
     """Forward rows against the oracle.  With causal masking row i depends only
     on X rows 0..i, so the oracle gets X[:max_row + 1] (a shorter sequence)."""
     n = max(rows_all + rows_late) + 1
@@ -309,7 +363,8 @@ def sampled_rows_check(shape, inp, out, rows_all, rows_late, late_heads):
         if not rows:
             continue
         say("  oracle rows %s heads %s" % (rows[:4], heads))
-        Or, Lr = oracle.forward_rows(*np_in, shape.H, shape.G, shape.d, rows, heads=heads)
+        Or, Lr = oracle.forward_rows(*np_in, shape.H, shape.G, shape.d, rows, heads=heads,
+                                     rope_theta=rope_theta)
         c0, c1 = heads[0] * shape.d, heads[1] * shape.d
         got_o = host(O[rows])[:, c0:c1]
         got_l = host(LSE[heads[0]:heads[1]][:, rows])

@@ -76,6 +76,41 @@ def test_create_validation(args, code):
         assert e.value.code == code
 
 
+@pytest.mark.parametrize("theta,code", [
+    (0.0, upipe.UPIPE_OK), (10000.0, upipe.UPIPE_OK), (500000.0, upipe.UPIPE_OK),
+    (0.5, upipe.UPIPE_OK), (-1.0, upipe.UPIPE_ERR_ARG), (float("nan"), upipe.UPIPE_ERR_ARG),
+    (float("inf"), upipe.UPIPE_ERR_ARG), (-0.0, upipe.UPIPE_OK),
+])
+def test_create_rope_validation(theta, code):
+    """The rotary embedding's base must be 0 (off) or finite and positive."""
+    if code == upipe.UPIPE_OK:
+        p = upipe.upipe_create_rope(256, 256, 4, 2, 128, 2, 1, "bf16", 0, theta)
+        upipe.upipe_destroy(p)
+    else:
+        with pytest.raises(upipe.UpipeError) as e:
+            upipe.upipe_create_rope(256, 256, 4, 2, 128, 2, 1, "bf16", 0, theta)
+        assert e.value.code == code
+
+
+def test_rope_leaves_schedule_and_workspace_unchanged():
+    for flags in (0, upipe.UPIPE_PIPELINE):
+        a = upipe.upipe_create_ex(4096, 1024, 32, 8, 128, 4, 1, "bf16", flags)
+        b = upipe.upipe_create_rope(4096, 1024, 32, 8, 128, 4, 1, "bf16", flags, 500000.0)
+        try:
+            for ph in (0, 1):
+                assert upipe.upipe_peak_bytes_phase(a, ph) == upipe.upipe_peak_bytes_phase(b, ph)
+            assert upipe.upipe_num_stages(a) == upipe.upipe_num_stages(b)
+            for s in range(upipe.upipe_num_stages(a)):
+                assert upipe.upipe_stage_info(a, s) == upipe.upipe_stage_info(b, s)
+        finally:
+            upipe.upipe_destroy(a)
+            upipe.upipe_destroy(b)
+    with pytest.raises(upipe.UpipeError):  # shape checks still apply
+        upipe.upipe_create_rope(128, 256, 4, 2, 64, 1, 1, "bf16", 0, 10000.0)
+    with pytest.raises(upipe.UpipeError):  # and flag checks
+        upipe.upipe_create_rope(128, 256, 4, 2, 128, 1, 1, "bf16", 8, 10000.0)
+
+
 @pytest.mark.parametrize("H,G", [(32, 8), (64, 8), (4, 2), (4, 1), (8, 8), (24, 4)])
 def test_schedule_covers_heads_and_loads_kv_once(H, G):
     r = H // G

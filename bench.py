@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--U", type=int, default=None)
     ap.add_argument("--pipeline", action="store_true",
                     help="stage pipelining: the GEMMs of neighbouring stages on a second stream")
+    ap.add_argument("--rope-theta", type=float, default=0.0,
+                    help="rotary embedding of queries and keys with this base (0: none)")
     ap.add_argument("--skip-cpu-baseline", action="store_true",
                     help="omit the oracle timing (profiling runs only)")
     ap.add_argument("--cpu-baseline-S", type=int, default=8192)
@@ -76,7 +78,7 @@ def kernel_work(kind, S, D, d, U, r, causal=True):
     return 0.0, "flop"
 
 
-KERNEL_SOURCES = ("bf16_common.h", "kernels_bf16.hip", "kernels_dkv.hip")
+KERNEL_SOURCES = ("bf16_common.h", "kernels_bf16.hip", "kernels_dkv.hip", "rope_device.h")
 
 
 def source_sha():
@@ -172,7 +174,8 @@ def main():
         print("bench: calibration copy of %d bytes" % n, file=sys.stderr, flush=True)
         del src, dst
     inp = make_inputs(shape, cfg["dtype"], seed=0, device="cuda")
-    plan = upipe.Plan(S, D, H, G, d, U, causal=True, dtype=cfg["dtype"], pipeline=args.pipeline)
+    plan = upipe.Plan(S, D, H, G, d, U, causal=True, dtype=cfg["dtype"], pipeline=args.pipeline,
+                      rope_theta=args.rope_theta)
     out = alloc_outputs(plan, dev)
     torch.cuda.synchronize()
     mem_before = torch.cuda.memory_allocated()
@@ -272,7 +275,8 @@ def main():
         "config": {"workload": "causal GQA attention layer fwd+bwd, one GPU, Llama3-8B attention "
                                "shape" if args.config.startswith("llama") else args.config,
                    "name": args.config, "S": S, "d_model": D, "H": H, "G": G, "d_head": d,
-                   "U": U, "pipeline": args.pipeline, "causal": True, "seed": 0},
+                   "U": U, "pipeline": args.pipeline, "rope_theta": args.rope_theta, "causal": True,
+                   "seed": 0},
         "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "attn_kernels_tflops": aflops / (attn_ms * 1e-3) / 1e12 if attn_ms > 0 else None,
         "attn_kernels_pct_peak": (100.0 * aflops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS

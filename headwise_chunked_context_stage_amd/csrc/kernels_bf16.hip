@@ -352,8 +352,23 @@ __global__ __launch_bounds__(256, 2) void dx_kernel(float* __restrict__ dX, int6
                                                     ChunkTable t, int nrb, int ncb) {
   using namespace dxk;
   __shared__ __attribute__((aligned(16))) u16 lds[2 * (AT + WT)];
+  // Each XCD takes a contiguous range of tiles and walks it in panels of
+  // 8 row blocks x 8 column blocks: the ~64 workgroups in flight on one XCD
+  // then share 8 A row panels and 8 W column panels (about 3 MB, within its
+  // L2) instead of touching every W column panel for 2 row blocks.  Rows
+  // past the last whole panel keep the row-major order.
+  constexpr int PR = 8, PC = 8;
   const int lid = xcd_remap(blockIdx.x, nrb * ncb);
-  const int rb = lid / ncb, cb = lid % ncb;
+  int rb, cb;
+  if (ncb % PC == 0 && lid < (nrb / PR) * PR * ncb) {
+    const int p = lid / (PR * ncb), q = lid % (PR * ncb);
+    const int w = q % (PR * PC);
+    rb = p * PR + w % PR;
+    cb = (q / (PR * PC)) * PC + w / PR;
+  } else {
+    rb = lid / ncb;
+    cb = lid % ncb;
+  }
   const int64_t i0 = static_cast<int64_t>(rb) * GB;
   const int64_t k0 = static_cast<int64_t>(cb) * GB;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, col = lane % 32, hf = lane / 32;

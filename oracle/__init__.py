@@ -54,6 +54,8 @@ def _load():
         lib.oracle_backward.argtypes = [i64, i64, i32, i32, i32, i32, f64, i32, vp, vp, vp, vp, vp,
                                         dp, dp, dp, dp, dp, dp, i32]
         lib.oracle_backward.restype = i32
+        lib.oracle_out_proj.argtypes = [i64, i64, i64, i32, dp, vp, vp, dp, dp, dp, i32]
+        lib.oracle_out_proj.restype = i32
         _lib = lib
     return _lib
 
@@ -152,6 +154,59 @@ def backward(X, Wq, Wk, Wv, dO, H: int, G: int, d: int, causal: bool = True,
                                  _ptr(out["dWv"]), nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle_backward rejected the shape")
+    return out
+
+
+def out_proj(O, Wo, dY=None, nthreads: int | None = None):
+    """Output projection by definition (fp64): returns (Y, dO, dWo) with
+    Y = O Wo^T, dO = dY Wo, dWo = dY^T O (dO and dWo are None without dY).
+    O is fp64 [S][H*d]; Wo [D][H*d] and dY [S][D] share one encoding."""
+    O = np.ascontiguousarray(O, dtype=np.float64)
+    S, Hd = O.shape
+    arrs, enc = _prep([Wo] + ([dY] if dY is not None else []))
+    Wo = arrs[0]
+    D = Wo.shape[0]
+    if Wo.shape != (D, Hd):
+        raise ValueError("Wo must be [D][H*d]")
+    if dY is not None and arrs[1].shape != (S, D):
+        raise ValueError("dY must be [S][D]")
+    Y = np.empty((S, D), np.float64)
+    dO = np.empty((S, Hd), np.float64) if dY is not None else None
+    dWo = np.empty((D, Hd), np.float64) if dY is not None else None
+    nul = ctypes.c_void_p(0)
+    rc = _load().oracle_out_proj(S, D, Hd, enc, _ptr(O), _ptr(Wo),
+                                 _ptr(arrs[1]) if dY is not None else nul, _ptr(Y),
+                                 _ptr(dO) if dO is not None else nul,
+                                 _ptr(dWo) if dWo is not None else nul, nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_out_proj rejected the shape")
+    return Y, dO, dWo
+
+
+def decode_exact(a) -> np.ndarray:
+    """fp64 copy of an oracle input (bf16 bit patterns, fp32 or fp64), exact."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if a.dtype in (np.float32, np.float64):
+        return a.astype(np.float64)
+    raise TypeError("unsupported oracle input dtype %s" % a.dtype)
+
+
+def backward_out(X, Wq, Wk, Wv, Wo, dY, H: int, G: int, d: int, causal: bool = True,
+                 nthreads: int | None = None, rope_theta: float = 0.0):
+    """The layer followed by its output projection, forward + backward of
+    L = sum(Y * dY) with Y = O Wo^T.  Composes the definitions: attention
+    forward, Y = O Wo^T, dO = dY Wo, then the attention backward with that dO
+    (every input decoded exactly to fp64 first), and dWo = dY^T O.
+    Returns a dict of fp64 arrays: O, LSE, Y, dX, dWq, dWk, dWv, dWo."""
+    O, LSE = forward(X, Wq, Wk, Wv, H, G, d, causal=causal, nthreads=nthreads,
+                     rope_theta=rope_theta)
+    Y, dO, dWo = out_proj(O, Wo, dY, nthreads=nthreads)
+    ex = [decode_exact(a) for a in (X, Wq, Wk, Wv)]
+    out = backward(*ex, dO, H, G, d, causal=causal, nthreads=nthreads, rope_theta=rope_theta)
+    out["Y"] = Y
+    out["dWo"] = dWo
     return out
 
 

@@ -22,7 +22,7 @@
 //
 // Readings where the pages are silent (each one listed in the design notes):
 //  softmax scale tau = 1/sqrt(d_head); causal mask j <= i (diagonal kept);
-//  no bias, dropout or output projection; batch 1; query head h uses KV
+//  no bias or dropout; batch 1; query head h uses KV
 //  head floor(h / (H/G)); LSE is the natural log of sum_j exp(tau q_i.k_j);
 //  the backward is that of L = sum(O * dO) (dO given), with gradients for
 //  X, Wq, Wk, Wv.
@@ -36,6 +36,11 @@
 //   y[c + d/2] = x[c + d/2] cos(i w_c) + x[c] sin(i w_c)
 // Values are not rotated.  The backward applies the transposed rotation to
 // the gradients of the rotated rows.
+//
+// Output projection (optional, oracle_out_proj; not on the pages' step list,
+// it is the linear map that follows attention in the Llama and Qwen blocks):
+// Y = O Wo^T with Wo [d_model][H*d]; for L = sum(Y * dY) the attention output
+// receives dO = dY Wo and the weight dWo = dY^T O.
 //
 // Arithmetic: every input element is decoded exactly into an fp64 value
 // (bf16 bits, fp32 or fp64 storage) and everything after that is fp64, in
@@ -392,6 +397,42 @@ int oracle_backward(int64_t S, int64_t D, int H, int G, int d, int causal, doubl
       dX[i * D + k] = acc;
     }
   });
+  return 0;
+}
+
+// Output projection and its backward, by definition.  O [S][Hd] fp64 (the
+// attention output), Wo [D][Hd] and dY [S][D] in encoding `enc` (dY may be
+// null: forward only).  Outputs (fp64, caller-owned, any may be null):
+//   Y[i][k]   = sum_c O[i][c] Wo[k][c]
+//   dO[i][c]  = sum_k dY[i][k] Wo[k][c]
+//   dWo[k][c] = sum_i dY[i][k] O[i][c]
+// Returns 0, or 1 on an invalid shape.
+int oracle_out_proj(int64_t S, int64_t D, int64_t Hd, int enc, const double* O, const void* Wop,
+                    const void* dYp, double* Y, double* dO, double* dWo, int nthreads) {
+  if (S < 0 || D < 1 || Hd < 1) return 1;
+  std::vector<double> Wo = decode(Wop, enc, D * Hd);
+  if (Y)
+    parallel_for(S, nthreads, [&](int64_t i) {
+      for (int64_t k = 0; k < D; ++k) Y[i * D + k] = dot(&O[i * Hd], &Wo[k * Hd], Hd);
+    });
+  if (!dYp) return 0;
+  std::vector<double> dY = decode(dYp, enc, S * D);
+  if (dO)
+    parallel_for(S, nthreads, [&](int64_t i) {
+      for (int64_t c = 0; c < Hd; ++c) {
+        double acc = 0.0;
+        for (int64_t k = 0; k < D; ++k) acc += dY[i * D + k] * Wo[k * Hd + c];
+        dO[i * Hd + c] = acc;
+      }
+    });
+  if (dWo)
+    parallel_for(D, nthreads, [&](int64_t k) {
+      for (int64_t c = 0; c < Hd; ++c) {
+        double acc = 0.0;
+        for (int64_t i = 0; i < S; ++i) acc += dY[i * D + k] * O[i * Hd + c];
+        dWo[k * Hd + c] = acc;
+      }
+    });
   return 0;
 }
 

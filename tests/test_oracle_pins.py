@@ -395,3 +395,100 @@ def test_rope_rejects_odd_head_dim(oracle_mod):
         oracle_mod.forward(X, Wq, Wk, Wv, 2, 1, 3, rope_theta=10000.0)
     with pytest.raises(ValueError):
         oracle_mod.forward(X, Wq, Wk, Wv, 2, 1, 3, rope_theta=-1.0)
+
+
+# ------------------------------------------------------------ output projection
+# Y = O Wo^T after the attention (the linear map that follows attention in the
+# Llama and Qwen blocks; not on the pages' step list).  Loss L = sum(Y * dY).
+
+def torch_layer_out(X, Wq, Wk, Wv, Wo, dY, H, G, d, causal, theta=0.0):
+    """torch fp64 library layer with the output projection as a Linear map,
+    autograd backward (rotary embedding as a complex product when theta > 0)."""
+    t = {k: torch.tensor(v, dtype=torch.float64, requires_grad=(k != "dY"))
+         for k, v in dict(X=X, Wq=Wq, Wk=Wk, Wv=Wv, Wo=Wo, dY=dY).items()}
+    S = X.shape[0]
+    half = d // 2
+
+    def rope(x):
+        if theta <= 0:
+            return x
+        freq = theta ** (-2.0 * torch.arange(half, dtype=torch.float64) / d)
+        ang = torch.arange(S, dtype=torch.float64)[:, None] * freq[None, :]
+        z = torch.complex(x[..., :half], x[..., half:]) * torch.polar(torch.ones_like(ang), ang)
+        return torch.cat([z.real, z.imag], dim=-1)
+
+    q = rope((t["X"] @ t["Wq"].T).reshape(S, H, d).transpose(0, 1))
+    k = rope((t["X"] @ t["Wk"].T).reshape(S, G, d).transpose(0, 1)).repeat_interleave(H // G, 0)
+    v = (t["X"] @ t["Wv"].T).reshape(S, G, d).transpose(0, 1).repeat_interleave(H // G, 0)
+    o = torch.nn.functional.scaled_dot_product_attention(q[None], k[None], v[None],
+                                                         is_causal=causal)[0]
+    O = o.transpose(0, 1).reshape(S, H * d)
+    Y = torch.nn.functional.linear(O, t["Wo"])
+    (Y * t["dY"]).sum().backward()
+    return dict(O=O.detach().numpy(), Y=Y.detach().numpy(), dX=t["X"].grad.numpy(),
+                dWq=t["Wq"].grad.numpy(), dWk=t["Wk"].grad.numpy(), dWv=t["Wv"].grad.numpy(),
+                dWo=t["Wo"].grad.numpy())
+
+
+def draw_out(S, D, H, G, d, seed):
+    X, Wq, Wk, Wv, _ = draw(S, D, H, G, d, seed=seed)
+    rng = np.random.default_rng(seed + 100)
+    Wo = rng.standard_normal((D, H * d)) / math.sqrt(H * d)
+    dY = rng.standard_normal((S, D))
+    return X, Wq, Wk, Wv, Wo, dY
+
+
+@pytest.mark.parametrize("shape", SHAPES[:3])
+@pytest.mark.parametrize("causal,theta", [(True, 0.0), (False, 0.0), (True, 10000.0)])
+def test_out_proj_against_torch_library(oracle_mod, shape, causal, theta):
+    S, D, H, G, d = shape
+    X, Wq, Wk, Wv, Wo, dY = draw_out(S, D, H, G, d, seed=S + 1)
+    got = oracle_mod.backward_out(X, Wq, Wk, Wv, Wo, dY, H, G, d, causal=causal, rope_theta=theta)
+    ref = torch_layer_out(X, Wq, Wk, Wv, Wo, dY, H, G, d, causal, theta)
+    for name in ("O", "Y", "dX", "dWq", "dWk", "dWv", "dWo"):
+        close(got[name], ref[name])
+
+
+def test_out_proj_finite_differences(oracle_mod):
+    S, D, H, G, d = 17, 10, 2, 1, 6
+    X, Wq, Wk, Wv, Wo, dY = draw_out(S, D, H, G, d, seed=21)
+    g = oracle_mod.backward_out(X, Wq, Wk, Wv, Wo, dY, H, G, d)
+    rng = np.random.default_rng(5)
+
+    def loss(p):
+        O, _ = oracle_mod.forward(p["X"], Wq, Wk, Wv, H, G, d, nthreads=1)
+        Y, _, _ = oracle_mod.out_proj(O, p["Wo"], nthreads=1)
+        return float(np.sum(Y * dY))
+
+    params = dict(X=X, Wo=Wo)
+    for name, grad in (("Wo", "dWo"), ("X", "dX")):
+        for _ in range(20):
+            idx = tuple(int(rng.integers(0, n)) for n in params[name].shape)
+            base = params[name][idx]
+            eps = 1e-6 * max(1.0, abs(base))
+            plus = {k: v.copy() for k, v in params.items()}
+            minus = {k: v.copy() for k, v in params.items()}
+            plus[name][idx] = base + eps
+            minus[name][idx] = base - eps
+            fd = (loss(plus) - loss(minus)) / (2 * eps)
+            an = g[grad][idx]
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, idx, fd, an)
+
+
+def test_out_proj_identity_weight_and_scaling(oracle_mod):
+    """Wo = I (d_model = H*d): Y = O, and the layer's gradients equal those of
+    the plain layer with dO = dY; dWo = dY^T O.  For any Wo, <dWo, Wo> =
+    <dY, Y> (Y is linear in Wo)."""
+    S, D, H, G, d = 26, 16, 4, 2, 4
+    X, Wq, Wk, Wv, _, dY = draw_out(S, D, H, G, d, seed=23)
+    eye = np.eye(D)
+    got = oracle_mod.backward_out(X, Wq, Wk, Wv, eye, dY, H, G, d)
+    plain = oracle_mod.backward(X, Wq, Wk, Wv, dY, H, G, d)
+    np.testing.assert_array_equal(got["Y"], got["O"])
+    for name in ("O", "LSE", "dX", "dWq", "dWk", "dWv"):
+        np.testing.assert_array_equal(got[name], plain[name])
+    close(got["dWo"], dY.T @ got["O"], 1e-14)
+    _, _, _, _, Wo, _ = draw_out(S, D, H, G, d, seed=24)
+    r = oracle_mod.backward_out(X, Wq, Wk, Wv, Wo, dY, H, G, d)
+    lhs, rhs = float(np.sum(r["dWo"] * Wo)), float(np.sum(dY * r["Y"]))
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(rhs))

@@ -85,6 +85,9 @@ struct Kernels {
   decltype(&bf16::attn_dq) attn_dq;
   decltype(&bf16::dw) dw;
   decltype(&bf16::dx) dx;
+  decltype(&bf16::oproj) oproj;
+  decltype(&bf16::dout) dout;
+  decltype(&bf16::dwo) dwo;
 };
 
 // fp32 variant: the rotary embedding runs as in-place passes right after the
@@ -116,8 +119,9 @@ hipError_t f32_attn_dkv(const AttnArgs& a, hipStream_t st) {
 Kernels kernels_for(int dtype) {
   if (dtype == UPIPE_BF16)
     return {bf16::proj, bf16::attn_fwd, bf16::bwd_pre, bf16::attn_dkv, bf16::attn_dq, bf16::dw,
-            bf16::dx};
-  return {f32_proj, f32::attn_fwd, f32::bwd_pre, f32_attn_dkv, f32_attn_dq, f32::dw, f32::dx};
+            bf16::dx, bf16::oproj, bf16::dout, bf16::dwo};
+  return {f32_proj, f32::attn_fwd, f32::bwd_pre, f32_attn_dkv, f32_attn_dq, f32::dw, f32::dx,
+          f32::oproj, f32::dout, f32::dwo};
 }
 
 // Project the stage's query heads (and its KV heads when it opens their group)
@@ -189,7 +193,10 @@ struct BwdIn {
 
 AttnArgs bwd_args(const Plan& p, const Stage& st, const BwdIn& in) {
   AttnArgs a = attn_args(p, st, in.ws);
-  a.dO = in.dO;
+  a.dO = in.dO;  // the caller's [S][H*d]
+  a.ldo = static_cast<int64_t>(p.H) * p.d;
+  a.do_hs = p.d;
+  a.do_h0 = 0;
   a.o_in = in.O;
   a.lse_in = in.LSE;
   a.dd = reinterpret_cast<float*>(at(in.ws, p.ws.dd));
@@ -252,6 +259,74 @@ hipError_t stage_gradients(const Plan& p, const Stage& st, const Kernels& K, con
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
+}
+
+// ------------------------------------------------------- output projection
+// The output projection's operands for one call (null members: not used).
+struct OutProj {
+  const void* Wo;  // [D][H*d]
+  float* Y;        // forward: [S][D] fp32 running sum
+  const void* dY;  // backward: [S][D]
+  const void* O;   // backward: the forward's O [S][H*d]
+  float* dWo;      // backward: [D][H*d] fp32
+};
+
+// The stage's heads as chunks: a = the head's columns of A (row stride H*d),
+// w = the same columns of Wo, dw = the same columns of dWo; `out` (if set)
+// replaces a by the head's [S][d] slice of the stage dO buffer.
+template <typename F>
+hipError_t per_head_chunks(const Plan& p, const Stage& st, const void* A, const void* Wo,
+                           float* dWo, char* out, F&& launch) {
+  const size_t e = p.elem();
+  for (int b = 0; b < st.nq; b += kMaxChunks) {
+    ChunkTable t;
+    std::memset(&t, 0, sizeof(t));
+    t.n = std::min(kMaxChunks, st.nq - b);
+    for (int i = 0; i < t.n; ++i) {
+      const int u = b + i, h = st.q0 + u;
+      const size_t col = static_cast<size_t>(h) * p.d;
+      t.w[i] = at(Wo, col * e);
+      t.a[i] = out ? static_cast<void*>(out + static_cast<size_t>(u) * p.S * p.d * e)
+                   : const_cast<char*>(at(A, col * e));
+      t.dw[i] = dWo ? dWo + col : nullptr;
+    }
+    hipError_t err = launch(t);
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+// Forward: Y += O_s Wo_s^T for the stage's heads, after its attention.
+hipError_t stage_oproj(const Plan& p, const Stage& st, const Kernels& K, const void* O,
+                       const OutProj& op, hipStream_t s) {
+  const int64_t ld = static_cast<int64_t>(p.H) * p.d;
+  return per_head_chunks(p, st, O, op.Wo, nullptr, nullptr, [&](const ChunkTable& t) {
+    return timed(UPIPE_K_OPROJ, s, [&] { return K.oproj(op.Y, p.S, p.D, p.d, t, ld, s); });
+  });
+}
+
+// Backward, before the stage's attention backward: dO of its heads into the
+// stage buffer, and the heads' columns of dWo.
+hipError_t stage_out_grads(const Plan& p, const Stage& st, const Kernels& K, void* ws,
+                           const OutProj& op, hipStream_t s) {
+  const int64_t ld = static_cast<int64_t>(p.H) * p.d;
+  hipError_t e = per_head_chunks(p, st, nullptr, op.Wo, nullptr, at(ws, p.ws.dob),
+                                 [&](const ChunkTable& t) {
+    return timed(UPIPE_K_DOUT, s, [&] { return K.dout(op.dY, p.S, p.D, p.d, t, ld, s); });
+  });
+  if (e != hipSuccess) return e;
+  return per_head_chunks(p, st, op.O, op.Wo, op.dWo, nullptr, [&](const ChunkTable& t) {
+    return timed(UPIPE_K_DWO, s, [&] { return K.dwo(op.dY, p.S, p.D, p.d, t, ld, s); });
+  });
+}
+
+// The attention backward of a stage reads dO from the stage buffer.
+AttnArgs with_stage_do(const Plan& p, const Stage& st, void* ws, AttnArgs a) {
+  a.dO = at(ws, p.ws.dob);
+  a.ldo = p.d;
+  a.do_hs = static_cast<int64_t>(p.S) * p.d;
+  a.do_h0 = st.q0;
+  return a;
 }
 
 // ------------------------------------------------------------ pipelining
@@ -320,7 +395,7 @@ hipError_t order(hipEvent_t ev, hipStream_t signaller, hipStream_t waiter) {
 // s mod 2, so the projection of s + 1 waits only for the attention of s - 1.
 hipError_t fwd_pipelined(const Plan& p, const Kernels& K, const void* X, const void* Wq,
                          const void* Wk, const void* Wv, void* O, float* LSE, void* ws,
-                         hipStream_t s, hipStream_t h, SyncEvents& E) {
+                         hipStream_t s, hipStream_t h, SyncEvents& E, const OutProj* op) {
   hipEvent_t start = E.ev[0], proj_done[2] = {E.ev[1], E.ev[2]}, attn_done[2] = {E.ev[3], E.ev[4]};
   const int n = static_cast<int>(p.stages.size());
   hipError_t e = order(start, s, h);  // inputs written on the caller's stream
@@ -336,6 +411,7 @@ hipError_t fwd_pipelined(const Plan& p, const Kernels& K, const void* X, const v
     a.lse = LSE;
     e = timed(UPIPE_K_ATTN_FWD, s, [&] { return K.attn_fwd(a, s); });
     if (e == hipSuccess) e = hipEventRecord(attn_done[i % 2], s);
+    if (e == hipSuccess && op) e = stage_oproj(p, st, K, O, *op, s);
     if (e != hipSuccess || i + 1 == n) break;
     // copy (i + 1) mod 2 was last read by the attention of stage i - 1
     if (i >= 1) e = hipStreamWaitEvent(h, attn_done[(i - 1) % 2], 0);
@@ -352,7 +428,7 @@ hipError_t fwd_pipelined(const Plan& p, const Kernels& K, const void* X, const v
 // s mod 2 of dQ once dX of stage s - 2 has.  dK/dV use the K/V copy of their
 // group; the group two loads back finished its dX by stage s - 2 as well.
 hipError_t bwd_pipelined(const Plan& p, const Kernels& K, const BwdIn& in, hipStream_t s,
-                         hipStream_t h, SyncEvents& E) {
+                         hipStream_t h, SyncEvents& E, const OutProj* op) {
   hipEvent_t start = E.ev[0], proj_done[2] = {E.ev[1], E.ev[2]}, dq_done[2] = {E.ev[3], E.ev[4]},
              dx_done[2] = {E.ev[5], E.ev[6]};
   const int n = static_cast<int>(p.stages.size());
@@ -362,8 +438,11 @@ hipError_t bwd_pipelined(const Plan& p, const Kernels& K, const BwdIn& in, hipSt
   if (e == hipSuccess) e = hipEventRecord(proj_done[0], h);
   for (int i = 0; i < n && e == hipSuccess; ++i) {
     const Stage& st = p.stages[i];
-    const AttnArgs a = bwd_args(p, st, in);
-    e = timed(UPIPE_K_BWD_PRE, s, [&] { return K.bwd_pre(a, s); });
+    // the stage dO buffer is single: its GEMMs run on this stream, after
+    // dQ of the previous stage has read it
+    if (op) e = stage_out_grads(p, st, K, in.ws, *op, s);
+    const AttnArgs a = op ? with_stage_do(p, st, in.ws, bwd_args(p, st, in)) : bwd_args(p, st, in);
+    if (e == hipSuccess) e = timed(UPIPE_K_BWD_PRE, s, [&] { return K.bwd_pre(a, s); });
     if (e == hipSuccess) e = hipStreamWaitEvent(s, proj_done[i % 2], 0);
     if (e == hipSuccess && i >= 2) e = hipStreamWaitEvent(s, dx_done[i % 2], 0);
     if (e == hipSuccess) e = timed(UPIPE_K_ATTN_DKV, s, [&] { return K.attn_dkv(a, s); });
@@ -477,6 +556,85 @@ const char* upipe_strerror(int code) {
   }
 }
 
+}  // extern "C"
+
+namespace {
+
+// Forward of every stage; `op` adds the output projection.  Arguments are
+// validated by the callers.
+int run_fwd(const Plan& p, const void* X, const void* Wq, const void* Wk, const void* Wv,
+            void* O, float* LSE, void* ws, hipStream_t s, const OutProj* op) {
+  const Kernels K = kernels_for(p.dtype);
+  if (p.pipeline) {
+    hipStream_t hs = nullptr;
+    SyncEvents E;
+    UPIPE_TRY(helper_stream(&hs));
+    UPIPE_TRY(E.take());
+    if (op)
+      UPIPE_TRY(timed(UPIPE_K_FILL, s, [&] {
+        return fill_zero(op->Y, static_cast<size_t>(p.S) * p.D * 4, s);
+      }));
+    UPIPE_TRY(fwd_pipelined(p, K, X, Wq, Wk, Wv, O, LSE, ws, s, hs, E, op));
+    return UPIPE_OK;
+  }
+  if (op)
+    UPIPE_TRY(timed(UPIPE_K_FILL, s,
+                    [&] { return fill_zero(op->Y, static_cast<size_t>(p.S) * p.D * 4, s); }));
+  for (const Stage& st : p.stages) {
+    UPIPE_TRY(stage_projection(p, st, K, X, Wq, Wk, Wv, ws, s));
+    AttnArgs a = attn_args(p, st, ws);
+    a.o = O;
+    a.lse = LSE;
+    UPIPE_TRY(timed(UPIPE_K_ATTN_FWD, s, [&] { return K.attn_fwd(a, s); }));
+    if (op) UPIPE_TRY(stage_oproj(p, st, K, O, *op, s));
+  }
+  return UPIPE_OK;
+}
+
+// Backward of every stage; `op` adds the output projection (dO of each stage
+// from dY; in.dO unused).  Arguments are validated by the callers.
+int run_bwd(const Plan& p, const BwdIn& in, hipStream_t s, const OutProj* op) {
+  const Kernels K = kernels_for(p.dtype);
+  hipStream_t hs = nullptr;
+  SyncEvents E;
+  if (p.pipeline) {  // before anything is enqueued
+    UPIPE_TRY(helper_stream(&hs));
+    UPIPE_TRY(E.take());
+  }
+  UPIPE_TRY(timed(UPIPE_K_FILL, s,
+                  [&] { return fill_zero(in.dX, static_cast<size_t>(p.S) * p.D * 4, s); }));
+  if (p.pipeline) {
+    UPIPE_TRY(bwd_pipelined(p, K, in, s, hs, E, op));
+    return UPIPE_OK;
+  }
+  for (const Stage& st : p.stages) {
+    UPIPE_TRY(stage_projection(p, st, K, in.X, in.Wq, in.Wk, in.Wv, in.ws, s));
+    if (op) UPIPE_TRY(stage_out_grads(p, st, K, in.ws, *op, s));
+    const AttnArgs a = op ? with_stage_do(p, st, in.ws, bwd_args(p, st, in)) : bwd_args(p, st, in);
+    UPIPE_TRY(timed(UPIPE_K_BWD_PRE, s, [&] { return K.bwd_pre(a, s); }));
+    UPIPE_TRY(timed(UPIPE_K_ATTN_DKV, s, [&] { return K.attn_dkv(a, s); }));
+    UPIPE_TRY(timed(UPIPE_K_ATTN_DQ, s, [&] { return K.attn_dq(a, s); }));
+    UPIPE_TRY(stage_gradients(p, st, K, in, s));
+  }
+  return UPIPE_OK;
+}
+
+// Empty sequence: every weight gradient is an empty sum.
+int zero_weight_grads(const Plan& p, float* dWq, float* dWk, float* dWv, float* dWo,
+                      hipStream_t s) {
+  const size_t wq_bytes = static_cast<size_t>(p.H) * p.d * p.D * 4;
+  const size_t wkv_bytes = static_cast<size_t>(p.G) * p.d * p.D * 4;
+  UPIPE_TRY(timed(UPIPE_K_FILL, s, [&] { return fill_zero(dWq, wq_bytes, s); }));
+  UPIPE_TRY(timed(UPIPE_K_FILL, s, [&] { return fill_zero(dWk, wkv_bytes, s); }));
+  UPIPE_TRY(timed(UPIPE_K_FILL, s, [&] { return fill_zero(dWv, wkv_bytes, s); }));
+  if (dWo) UPIPE_TRY(timed(UPIPE_K_FILL, s, [&] { return fill_zero(dWo, wq_bytes, s); }));
+  return UPIPE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int upipe_fwd(const upipe_plan* h, const void* X, const void* Wq, const void* Wk, const void* Wv,
               void* O, float* LSE, void* ws, size_t ws_bytes, void* stream) {
   if (!h) return UPIPE_ERR_ARG;
@@ -485,24 +643,21 @@ int upipe_fwd(const upipe_plan* h, const void* X, const void* Wq, const void* Wk
   if (!ptr_ok(X) || !ptr_ok(Wq) || !ptr_ok(Wk) || !ptr_ok(Wv) || !ptr_ok(O) || !ptr_ok(LSE))
     return UPIPE_ERR_ARG;
   if (!ws || !aligned(ws, kAlign) || ws_bytes < p.ws.fwd_bytes) return UPIPE_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const Kernels K = kernels_for(p.dtype);
-  if (p.pipeline) {
-    hipStream_t hs = nullptr;
-    SyncEvents E;
-    UPIPE_TRY(helper_stream(&hs));
-    UPIPE_TRY(E.take());
-    UPIPE_TRY(fwd_pipelined(p, K, X, Wq, Wk, Wv, O, LSE, ws, s, hs, E));
-    return UPIPE_OK;
-  }
-  for (const Stage& st : p.stages) {
-    UPIPE_TRY(stage_projection(p, st, K, X, Wq, Wk, Wv, ws, s));
-    AttnArgs a = attn_args(p, st, ws);
-    a.o = O;
-    a.lse = LSE;
-    UPIPE_TRY(timed(UPIPE_K_ATTN_FWD, s, [&] { return K.attn_fwd(a, s); }));
-  }
-  return UPIPE_OK;
+  return run_fwd(p, X, Wq, Wk, Wv, O, LSE, ws, static_cast<hipStream_t>(stream), nullptr);
+}
+
+int upipe_fwd_out(const upipe_plan* h, const void* X, const void* Wq, const void* Wk,
+                  const void* Wv, const void* Wo, void* O, float* LSE, float* Y, void* ws,
+                  size_t ws_bytes, void* stream) {
+  if (!h || !h->p.out_proj) return UPIPE_ERR_ARG;
+  const Plan& p = h->p;
+  if (p.S == 0) return UPIPE_OK;
+  if (!ptr_ok(X) || !ptr_ok(Wq) || !ptr_ok(Wk) || !ptr_ok(Wv) || !ptr_ok(Wo) || !ptr_ok(O) ||
+      !ptr_ok(LSE) || !ptr_ok(Y))
+    return UPIPE_ERR_ARG;
+  if (!ws || !aligned(ws, kAlign) || ws_bytes < p.ws.fwd_bytes) return UPIPE_ERR_WORKSPACE;
+  const OutProj op{Wo, Y, nullptr, nullptr, nullptr};
+  return run_fwd(p, X, Wq, Wk, Wv, O, LSE, ws, static_cast<hipStream_t>(stream), &op);
 }
 
 int upipe_bwd(const upipe_plan* h, const void* dO, const void* X, const void* Wq, const void* Wk,
@@ -512,42 +667,31 @@ int upipe_bwd(const upipe_plan* h, const void* dO, const void* X, const void* Wq
   const Plan& p = h->p;
   if (!ptr_ok(dWq) || !ptr_ok(dWk) || !ptr_ok(dWv)) return UPIPE_ERR_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const size_t wq_bytes = static_cast<size_t>(p.H) * p.d * p.D * 4;
-  const size_t wkv_bytes = static_cast<size_t>(p.G) * p.d * p.D * 4;
-  if (p.S == 0) {  // empty sequence: every weight gradient is an empty sum
-    UPIPE_TRY(timed(UPIPE_K_FILL, s, [&] { return fill_zero(dWq, wq_bytes, s); }));
-    UPIPE_TRY(timed(UPIPE_K_FILL, s, [&] { return fill_zero(dWk, wkv_bytes, s); }));
-    UPIPE_TRY(timed(UPIPE_K_FILL, s, [&] { return fill_zero(dWv, wkv_bytes, s); }));
-    return UPIPE_OK;
-  }
+  if (p.S == 0) return zero_weight_grads(p, dWq, dWk, dWv, nullptr, s);
   if (!ptr_ok(dO) || !ptr_ok(X) || !ptr_ok(Wq) || !ptr_ok(Wk) || !ptr_ok(Wv) || !ptr_ok(O) ||
       !ptr_ok(LSE) || !ptr_ok(dX))
     return UPIPE_ERR_ARG;
   if (!ws || !aligned(ws, kAlign) || ws_bytes < p.ws.bwd_bytes) return UPIPE_ERR_WORKSPACE;
-  const Kernels K = kernels_for(p.dtype);
   const BwdIn in{dO, X, Wq, Wk, Wv, O, LSE, dX, dWq, dWk, dWv, ws};
-  hipStream_t hs = nullptr;
-  SyncEvents E;
-  if (p.pipeline) {  // before anything is enqueued
-    UPIPE_TRY(helper_stream(&hs));
-    UPIPE_TRY(E.take());
-  }
+  return run_bwd(p, in, s, nullptr);
+}
 
-  UPIPE_TRY(timed(UPIPE_K_FILL, s,
-                  [&] { return fill_zero(dX, static_cast<size_t>(p.S) * p.D * 4, s); }));
-  if (p.pipeline) {
-    UPIPE_TRY(bwd_pipelined(p, K, in, s, hs, E));
-    return UPIPE_OK;
-  }
-  for (const Stage& st : p.stages) {
-    UPIPE_TRY(stage_projection(p, st, K, X, Wq, Wk, Wv, ws, s));
-    const AttnArgs a = bwd_args(p, st, in);
-    UPIPE_TRY(timed(UPIPE_K_BWD_PRE, s, [&] { return K.bwd_pre(a, s); }));
-    UPIPE_TRY(timed(UPIPE_K_ATTN_DKV, s, [&] { return K.attn_dkv(a, s); }));
-    UPIPE_TRY(timed(UPIPE_K_ATTN_DQ, s, [&] { return K.attn_dq(a, s); }));
-    UPIPE_TRY(stage_gradients(p, st, K, in, s));
-  }
-  return UPIPE_OK;
+int upipe_bwd_out(const upipe_plan* h, const void* dY, const void* X, const void* Wq,
+                  const void* Wk, const void* Wv, const void* Wo, const void* O, const float* LSE,
+                  float* dX, float* dWq, float* dWk, float* dWv, float* dWo, void* ws,
+                  size_t ws_bytes, void* stream) {
+  if (!h || !h->p.out_proj) return UPIPE_ERR_ARG;
+  const Plan& p = h->p;
+  if (!ptr_ok(dWq) || !ptr_ok(dWk) || !ptr_ok(dWv) || !ptr_ok(dWo)) return UPIPE_ERR_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.S == 0) return zero_weight_grads(p, dWq, dWk, dWv, dWo, s);
+  if (!ptr_ok(dY) || !ptr_ok(X) || !ptr_ok(Wq) || !ptr_ok(Wk) || !ptr_ok(Wv) || !ptr_ok(Wo) ||
+      !ptr_ok(O) || !ptr_ok(LSE) || !ptr_ok(dX))
+    return UPIPE_ERR_ARG;
+  if (!ws || !aligned(ws, kAlign) || ws_bytes < p.ws.bwd_bytes) return UPIPE_ERR_WORKSPACE;
+  const BwdIn in{nullptr, X, Wq, Wk, Wv, O, LSE, dX, dWq, dWk, dWv, ws};
+  const OutProj op{Wo, nullptr, dY, O, dWo};
+  return run_bwd(p, in, s, &op);
 }
 
 int upipe_timing_enable(int on) {
@@ -583,7 +727,8 @@ int upipe_mfma_ceiling(int waves_per_simd, int iters, double* tflops, void* stre
 
 const char* upipe_kernel_name(int kind) {
   static const char* names[UPIPE_K_COUNT] = {"proj", "attn_fwd", "bwd_pre", "attn_dkv",
-                                             "attn_dq", "dw", "dx", "fill"};
+                                             "attn_dq", "dw", "dx", "fill",
+                                             "oproj", "dout", "dwo"};
   if (kind < 0 || kind >= UPIPE_K_COUNT) return "unknown";
   return names[kind];
 }

@@ -214,8 +214,12 @@ constexpr int TILE = ROWS * RS;     // one operand tile
 constexpr int NRR = 3;              // k-steps of global loads in flight
 }  // namespace dwk
 
+// TR (the output projection's weight gradient): A has row stride `ld`
+// (a head's columns of O [S][H*d]) and the result is stored transposed,
+// dW[k][c] at t.dw[ch] + k * ld + c (dWo [d_model][H*d]).
+template <bool TR>
 __global__ __launch_bounds__(512, 1) void dw_kernel(const u16* __restrict__ X, int64_t S, int64_t D,
-                                                    ChunkTable t, int ncb) {
+                                                    ChunkTable t, int ncb, int64_t ld) {
   using namespace dwk;
   __shared__ __attribute__((aligned(16))) u16 lds[2][2][2 * TILE];  // [group][buffer][A tile, X tile]
   const int total = ncb * t.n;
@@ -243,7 +247,7 @@ __global__ __launch_bounds__(512, 1) void dw_kernel(const u16* __restrict__ X, i
     for (int m = 0; m < 4; ++m) {
       const int64_t gi = s0 + srow + 16 * m;
       const bool in = kb < nk && gi < S;
-      rr[set][m] = in ? ld16(A + gi * DH + sc * 8) : u32x4{0, 0, 0, 0};
+      rr[set][m] = in ? ld16(A + gi * (TR ? ld : DH) + sc * 8) : u32x4{0, 0, 0, 0};
       rr[set][4 + m] = in ? ld16(X + gi * D + k0 + sc * 8) : u32x4{0, 0, 0, 0};
     }
   };
@@ -324,12 +328,20 @@ __global__ __launch_bounds__(512, 1) void dw_kernel(const u16* __restrict__ X, i
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const f32x4 o = *reinterpret_cast<const f32x4*>(red + (((wave * 4 + mb * 2 + nb) * 4 + i4) * 64 + lane) * 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * i4 + e;
-            const int c = 64 * wm + 32 * mb + 8 * (i / 4) + 4 * hf + (i % 4);
+          if constexpr (TR) {  // registers 4 i4 .. 4 i4 + 3 hold four consecutive c
+            const int c = 64 * wm + 32 * mb + 8 * i4 + 4 * hf;
             const int64_t k = k0 + 64 * wn + 32 * nb + col;
-            dW[static_cast<int64_t>(c) * D + k] = acc[mb][nb][i] + o[e];
+            *reinterpret_cast<f32x4*>(dW + k * ld + c) =
+                f32x4{acc[mb][nb][4 * i4] + o[0], acc[mb][nb][4 * i4 + 1] + o[1],
+                      acc[mb][nb][4 * i4 + 2] + o[2], acc[mb][nb][4 * i4 + 3] + o[3]};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int i = 4 * i4 + e;
+              const int c = 64 * wm + 32 * mb + 8 * (i / 4) + 4 * hf + (i % 4);
+              const int64_t k = k0 + 64 * wn + 32 * nb + col;
+              dW[static_cast<int64_t>(c) * D + k] = acc[mb][nb][i] + o[e];
+            }
           }
         }
   }
@@ -455,6 +467,211 @@ __global__ __launch_bounds__(256, 2) void dx_kernel(float* __restrict__ dX, int6
         const int64_t k = k0 + 64 * wn + 32 * nb + col;
         if (gi < S) dX[gi * D + k] = acc[mb][nb][i];
       }
+}
+
+// ---- output projection: Y[i][k] += sum over chunks (heads ascending) of
+// sum_c A[i][c] B[k][c], A = a head's columns of O [S][H*d], B = the same
+// columns of Wo [d_model][H*d] (both with row stride ld).  Both operands run
+// along the contraction in memory, so both tiles (128 rows x 64 columns) are
+// staged row-major and read with plain row reads, as in the projection; Y is
+// the fp32 running sum across stages (the MFMA C input), as dX is, so every
+// U sums in the same order.  Tiles in panels per XCD as in dx_kernel.
+__global__ __launch_bounds__(256, 2) void oproj_kernel(float* __restrict__ Y, int64_t S, int64_t D,
+                                                       ChunkTable t, int nrb, int ncb, int64_t ld) {
+  __shared__ __attribute__((aligned(16))) u16 lds[2 * GBUF];
+  constexpr int PR = 8, PC = 8;
+  const int lid = xcd_remap(blockIdx.x, nrb * ncb);
+  int rb, cb;
+  if (ncb % PC == 0 && lid < (nrb / PR) * PR * ncb) {
+    const int p = lid / (PR * ncb), q = lid % (PR * ncb);
+    const int w = q % (PR * PC);
+    rb = p * PR + w % PR;
+    cb = (q / (PR * PC)) * PC + w / PR;
+  } else {
+    rb = lid / ncb;
+    cb = lid % ncb;
+  }
+  const int64_t i0 = static_cast<int64_t>(rb) * GB;
+  const int64_t k0 = static_cast<int64_t>(cb) * GB;
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, col = lane % 32, hf = lane / 32;
+  const int wm = wave / 2, wn = wave % 2;
+  // thread tid moves 16-column groups (row tid / 4 + 64 m, group tid % 4), m < 2, of both tiles
+  const int arow = tid >> 2, agrp = tid & 3;
+  u32x4 ra[2][2], rb2[2][2];
+  auto load = [&](int step) {
+    const int ch = step / (DH / GK), c0 = (step % (DH / GK)) * GK;
+    const u16* Ap = static_cast<const u16*>(t.a[ch]);
+    const u16* Bp = static_cast<const u16*>(t.w[ch]);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int64_t gi = i0 + arow + 64 * m;
+      const u16* src = Ap + gi * ld + c0 + 16 * agrp;
+      ra[m][0] = gi < S ? ld16(src) : u32x4{0, 0, 0, 0};
+      ra[m][1] = gi < S ? ld16(src + 8) : u32x4{0, 0, 0, 0};
+      const u16* wsrc = Bp + (k0 + arow + 64 * m) * ld + c0 + 16 * agrp;
+      rb2[m][0] = ld16(wsrc);
+      rb2[m][1] = ld16(wsrc + 8);
+    }
+  };
+  auto store = [&](int b) {
+    u16* as = lds + b * GBUF;
+    u16* bs = as + GB * GS;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      st16(as + (arow + 64 * m) * GS + 16 * agrp, ra[m][0]);
+      st16(as + (arow + 64 * m) * GS + 16 * agrp + 8, ra[m][1]);
+      st16(bs + (arow + 64 * m) * GS + 16 * agrp, rb2[m][0]);
+      st16(bs + (arow + 64 * m) * GS + 16 * agrp + 8, rb2[m][1]);
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t gi = i0 + 64 * wm + 32 * mb + 8 * (i / 4) + 4 * hf + (i % 4);
+        const int64_t k = k0 + 64 * wn + 32 * nb + col;
+        acc[mb][nb][i] = gi < S ? Y[gi * D + k] : 0.f;
+      }
+
+  const int nsteps = t.n * (DH / GK);
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int sidx = 0; sidx < nsteps; ++sidx) {
+    const int cur = sidx & 1;
+    if (sidx + 1 < nsteps) load(sidx + 1);
+    const u16* as = lds + cur * GBUF;
+    const u16* bs = as + GB * GS;
+#pragma unroll
+    for (int t4 = 0; t4 < GK / 16; ++t4) {
+      bf16x8 fa[2], fb[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) fa[mb] = frag(as + (64 * wm + 32 * mb + col) * GS + 16 * t4 + 8 * hf);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) fb[nb] = frag(bs + (64 * wn + 32 * nb + col) * GS + 16 * t4 + 8 * hf);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma(fa[mb], fb[nb], acc[mb][nb]);
+    }
+    if (sidx + 1 < nsteps) store(cur ^ 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t gi = i0 + 64 * wm + 32 * mb + 8 * (i / 4) + 4 * hf + (i % 4);
+        const int64_t k = k0 + 64 * wn + 32 * nb + col;
+        if (gi < S) Y[gi * D + k] = acc[mb][nb][i];
+      }
+}
+
+// ---- gradient of the attention output through the output projection:
+// out[i][c] = sum_k dY[i][k] B[k][c] for one head (chunk), B = the head's
+// columns of Wo [d_model][H*d] (row stride ld), K = d_model.  B's
+// contraction index runs down its rows, so its tile (64 rows k x 128 columns
+// c) is staged row-major and read with the transposing LDS reads, and the dY
+// tile is stored with the middle 8-byte blocks of every 16-column group
+// swapped to present the same k-slot order, as in dx_kernel.  The result is
+// rounded to bf16 once, through LDS, into the stage buffer [S][d].
+__global__ __launch_bounds__(256, 2) void dout_kernel(const u16* __restrict__ dY, int64_t S,
+                                                      int64_t D, ChunkTable t, int nrb, int64_t ld) {
+  using namespace dxk;
+  __shared__ __attribute__((aligned(16))) u16 lds[2 * (AT + WT)];
+  const int total = nrb * t.n;
+  const int lid = xcd_remap(blockIdx.x, total);
+  const int rb = lid / t.n, ch = lid % t.n;
+  const u16* Bp = static_cast<const u16*>(t.w[ch]);
+  u16* out = static_cast<u16*>(t.a[ch]);
+  const int64_t i0 = static_cast<int64_t>(rb) * GB;
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, col = lane % 32, hf = lane / 32;
+  const int wm = wave / 2, wn = wave % 2;
+  const int arow = tid >> 2, agrp = tid & 3;
+  const int wrow = tid >> 4, wc = tid & 15;
+  u32x4 ra[2][2], rw[4];
+  auto load = [&](int step) {
+    const int64_t kk = static_cast<int64_t>(step) * GK;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int64_t gi = i0 + arow + 64 * m;
+      const u16* src = dY + gi * D + kk + 16 * agrp;
+      ra[m][0] = gi < S ? ld16(src) : u32x4{0, 0, 0, 0};
+      ra[m][1] = gi < S ? ld16(src + 8) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) rw[m] = ld16(Bp + (kk + wrow + 16 * m) * ld + wc * 8);
+  };
+  auto store = [&](int b) {
+    u16* as = lds + b * (AT + WT);
+    u16* wt = as + AT;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const u32x4 lo = {ra[m][0][0], ra[m][0][1], ra[m][1][0], ra[m][1][1]};
+      const u32x4 hi = {ra[m][0][2], ra[m][0][3], ra[m][1][2], ra[m][1][3]};
+      u16* dst = as + (arow + 64 * m) * GS + 16 * agrp;
+      st16(dst, lo);
+      st16(dst + 8, hi);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) st16(wt + toff(wrow + 16 * m, wc * 8), rw[m]);
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = zero16();
+  const int nsteps = static_cast<int>(D / GK);
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int sidx = 0; sidx < nsteps; ++sidx) {
+    const int cur = sidx & 1;
+    if (sidx + 1 < nsteps) load(sidx + 1);
+    const u16* as = lds + cur * (AT + WT);
+    const TileAddr tw = tile_addr(lds + cur * (AT + WT) + AT, lane);
+#pragma unroll
+    for (int t4 = 0; t4 < GK / 16; ++t4) {
+      bf16x8 fa[2], fb[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) fa[mb] = frag(as + (64 * wm + 32 * mb + col) * GS + 16 * t4 + 8 * hf);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) fb[nb] = col_frag(tw, 16 * t4, 64 * wn + 32 * nb);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma(fa[mb], fb[nb], acc[mb][nb]);
+    }
+    if (sidx + 1 < nsteps) store(cur ^ 1);
+    __syncthreads();
+  }
+  // C (bf16) -> LDS tile [128][136] -> coalesced 16-byte stores
+  constexpr int CS = GB + 8;
+  u16* cs = lds;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 64 * wm + 32 * mb + 8 * (i / 4) + 4 * hf + (i % 4);
+        const int c = 64 * wn + 32 * nb + col;
+        cs[row * CS + c] = __builtin_bit_cast(u16, static_cast<__bf16>(acc[mb][nb][i]));
+      }
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const int e = tid + 256 * m, row = e / 16, chunk = e % 16;
+    const int64_t gi = i0 + row;
+    if (gi < S) st16(out + gi * DH + chunk * 8, ld16(cs + row * CS + chunk * 8));
+  }
 }
 
 // ---- forward.  Workgroup: 256 query rows of one head (8 waves x 32 rows);
@@ -687,7 +904,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(AttnArgs a) {
   float acc = 0.f;
   if (row < a.S) {
     const int64_t off = row * static_cast<int64_t>(a.H) * DH + static_cast<int64_t>(h) * DH + part * 8;
-    const u32x4 g = ld16(static_cast<const u16*>(a.dO) + off);
+    const int64_t goff = (h - a.do_h0) * a.do_hs + row * a.ldo + part * 8;
+    const u32x4 g = ld16(static_cast<const u16*>(a.dO) + goff);
     const u32x4 o = ld16(static_cast<const u16*>(a.o_in) + off);
     const bf16x8 gb = __builtin_bit_cast(bf16x8, g), ob = __builtin_bit_cast(bf16x8, o);
 #pragma unroll
@@ -741,8 +959,8 @@ __global__ __launch_bounds__(dqk::NT, 1) void attn_dq_kernel(AttnArgs a) {
   bf16x8 qf[8], gf[8];
   {
     const u16* Q = static_cast<const u16*>(a.q) + static_cast<int64_t>(u) * S * DH;
-    const u16* dO = static_cast<const u16*>(a.dO) + static_cast<int64_t>(h) * DH;
-    const int64_t ldo = static_cast<int64_t>(a.H) * DH;
+    const u16* dO = static_cast<const u16*>(a.dO) + (h - a.do_h0) * a.do_hs;
+    const int64_t ldo = a.ldo;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       qf[t] = __builtin_bit_cast(bf16x8, myq < S ? ld16(Q + myq * DH + 16 * t + 8 * hf) : u32x4{0, 0, 0, 0});
@@ -972,8 +1190,17 @@ hipError_t proj(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t,
 hipError_t dw(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t, hipStream_t st) {
   if (d != DH || D % GB != 0) return hipErrorInvalidValue;
   const int ncb = static_cast<int>(D / GB);
-  hipLaunchKernelGGL(dw_kernel, dim3(ncb * t.n), dim3(512), 0, st, static_cast<const u16*>(X), S, D,
-                     t, ncb);
+  hipLaunchKernelGGL(dw_kernel<false>, dim3(ncb * t.n), dim3(512), 0, st, static_cast<const u16*>(X),
+                     S, D, t, ncb, int64_t(DH));
+  return hipGetLastError();
+}
+
+hipError_t dwo(const void* dY, int64_t S, int64_t D, int d, const ChunkTable& t, int64_t ld,
+               hipStream_t st) {
+  if (d != DH || D % GB != 0 || ld % 4 != 0) return hipErrorInvalidValue;
+  const int ncb = static_cast<int>(D / GB);
+  hipLaunchKernelGGL(dw_kernel<true>, dim3(ncb * t.n), dim3(512), 0, st, static_cast<const u16*>(dY),
+                     S, D, t, ncb, ld);
   return hipGetLastError();
 }
 
@@ -981,6 +1208,23 @@ hipError_t dx(float* dX, int64_t S, int64_t D, int d, const ChunkTable& t, hipSt
   if (d != DH || D % GB != 0) return hipErrorInvalidValue;
   const int nrb = static_cast<int>(cdiv(S, GB)), ncb = static_cast<int>(D / GB);
   hipLaunchKernelGGL(dx_kernel, dim3(nrb * ncb), dim3(256), 0, st, dX, S, D, t, nrb, ncb);
+  return hipGetLastError();
+}
+
+hipError_t oproj(float* Y, int64_t S, int64_t D, int d, const ChunkTable& t, int64_t ld,
+                 hipStream_t st) {
+  if (d != DH || D % GB != 0 || ld % 8 != 0) return hipErrorInvalidValue;
+  const int nrb = static_cast<int>(cdiv(S, GB)), ncb = static_cast<int>(D / GB);
+  hipLaunchKernelGGL(oproj_kernel, dim3(nrb * ncb), dim3(256), 0, st, Y, S, D, t, nrb, ncb, ld);
+  return hipGetLastError();
+}
+
+hipError_t dout(const void* dY, int64_t S, int64_t D, int d, const ChunkTable& t, int64_t ld,
+                hipStream_t st) {
+  if (d != DH || D % GK != 0 || ld % 8 != 0) return hipErrorInvalidValue;
+  const int nrb = static_cast<int>(cdiv(S, GB));
+  hipLaunchKernelGGL(dout_kernel, dim3(nrb * t.n), dim3(256), 0, st, static_cast<const u16*>(dY), S,
+                     D, t, nrb, ld);
   return hipGetLastError();
 }
 

@@ -50,7 +50,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
   const int64_t myk = wk0 + col;
   const float tau = 1.f / sqrtf(static_cast<float>(DH));
   const float c = kLog2e * tau;
-  const int64_t ldo = static_cast<int64_t>(a.H) * DH;
+  const int64_t ldo = a.ldo;
 
   // K rows (first wave of a pair) or V rows (second) of this key block, as B operands.
   bf16x8 kvf[8];
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
     const int u = x.h - a.q_head0;
     const int64_t q0 = static_cast<int64_t>(x.qt) * BM;
     const u16* qb = static_cast<const u16*>(a.q) + (static_cast<int64_t>(u) * S + q0) * DH;
-    const u16* gb = static_cast<const u16*>(a.dO) + q0 * ldo + static_cast<int64_t>(x.h) * DH;
+    const u16* gb = static_cast<const u16*>(a.dO) + (x.h - a.do_h0) * a.do_hs + q0 * ldo;
     u16* qd = qs + slq * TILE;
     u16* gd = gs + slg * TILE;
     if (q0 + BM <= S) {

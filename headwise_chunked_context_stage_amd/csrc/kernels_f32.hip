@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(AttnArgs a) {
   if (i >= a.S) return;
   const int h = a.q_head0 + u;
   const int64_t off = i * static_cast<int64_t>(a.H) * DH + static_cast<int64_t>(h) * DH;
-  const float* dO = static_cast<const float*>(a.dO) + off;
+  const float* dO = static_cast<const float*>(a.dO) + (h - a.do_h0) * a.do_hs + i * a.ldo;
   const float* O = static_cast<const float*>(a.o_in) + off;
   float acc = 0.f;
   for (int e = 0; e < DH; ++e) acc += dO[e] * O[e];
@@ -156,8 +156,7 @@ __global__ __launch_bounds__(128) void attn_dq_kernel(AttnArgs a) {
   const float* Q = static_cast<const float*>(a.q) + (static_cast<int64_t>(u) * a.S + i) * DH;
   const float* K = static_cast<const float*>(a.k) + static_cast<int64_t>(g) * a.S * DH;
   const float* V = static_cast<const float*>(a.v) + static_cast<int64_t>(g) * a.S * DH;
-  const float* dO = static_cast<const float*>(a.dO) + i * static_cast<int64_t>(a.H) * DH +
-                    static_cast<int64_t>(h) * DH;
+  const float* dO = static_cast<const float*>(a.dO) + (h - a.do_h0) * a.do_hs + i * a.ldo;
   const float tau = 1.f / sqrtf(static_cast<float>(DH));
   const float c = kLog2e * tau;
   const float lse2 = a.lse_in[static_cast<int64_t>(h) * a.S + i] * kLog2e;
@@ -211,8 +210,8 @@ __global__ __launch_bounds__(128) void attn_dkv_kernel(AttnArgs a) {
   for (int h = h_lo; h < h_hi; ++h) {
     const int u = h - a.q_head0;
     const float* Q = static_cast<const float*>(a.q) + static_cast<int64_t>(u) * a.S * DH;
-    const float* dO = static_cast<const float*>(a.dO) + static_cast<int64_t>(h) * DH;
-    const int64_t ldo = static_cast<int64_t>(a.H) * DH;
+    const float* dO = static_cast<const float*>(a.dO) + (h - a.do_h0) * a.do_hs;
+    const int64_t ldo = a.ldo;
     for (int64_t i = a.causal ? j : 0; i < a.S; ++i) {
       float s = 0.f, dp = 0.f;
       for (int e = 0; e < DH; ++e) {
@@ -251,6 +250,48 @@ __global__ __launch_bounds__(256) void rope_kernel(float* __restrict__ buf, int6
     rope_fwd(row[c], row[c + half], cs, sn);
   else
     rope_bwd(row[c], row[c + half], cs, sn);
+}
+
+// Output projection, one thread per output element with fixed loop orders.
+// Y[i][k] += sum over chunks (heads ascending), then c ascending, of
+// O[i][c] Wo[k][c]; Y is the running sum across stages, so every U adds the
+// same terms in the same order.
+__global__ __launch_bounds__(256) void oproj_kernel(float* __restrict__ Y, int64_t S, int64_t D,
+                                                    int d, ChunkTable t, int64_t ld) {
+  const int64_t k = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t i = blockIdx.y;
+  if (k >= D) return;
+  float acc = Y[i * D + k];
+  for (int ch = 0; ch < t.n; ++ch) {
+    const float* o = static_cast<const float*>(t.a[ch]) + i * ld;
+    const float* w = static_cast<const float*>(t.w[ch]) + k * ld;
+    for (int c = 0; c < d; ++c) acc += o[c] * w[c];
+  }
+  Y[i * D + k] = acc;
+}
+
+// out[i][c] = sum_k dY[i][k] Wo[k][c] (k ascending), for chunk blockIdx.z.
+__global__ __launch_bounds__(256) void dout_kernel(const float* __restrict__ dY, int64_t S,
+                                                   int64_t D, int d, ChunkTable t, int64_t ld) {
+  const int c = threadIdx.x % 64 + 64 * blockIdx.y;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / 64;
+  if (i >= S || c >= d) return;
+  const float* w = static_cast<const float*>(t.w[blockIdx.z]) + c;
+  float acc = 0.f;
+  for (int64_t k = 0; k < D; ++k) acc += dY[i * D + k] * w[k * ld];
+  static_cast<float*>(t.a[blockIdx.z])[i * d + c] = acc;
+}
+
+// dWo[k][c] = sum_i dY[i][k] O[i][c] (i ascending), for chunk blockIdx.z.
+__global__ __launch_bounds__(256) void dwo_kernel(const float* __restrict__ dY, int64_t S,
+                                                  int64_t D, int d, ChunkTable t, int64_t ld) {
+  const int c = threadIdx.x % 64 + 64 * blockIdx.y;
+  const int64_t k = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / 64;
+  if (k >= D || c >= d) return;
+  const float* o = static_cast<const float*>(t.a[blockIdx.z]) + c;
+  float acc = 0.f;
+  for (int64_t i = 0; i < S; ++i) acc += dY[i * D + k] * o[i * ld];
+  t.dw[blockIdx.z][k * ld + c] = acc;
 }
 
 inline unsigned cdiv(int64_t a, int64_t b) { return static_cast<unsigned>((a + b - 1) / b); }
@@ -294,6 +335,29 @@ hipError_t rope(float* buf, int n, int64_t S, int d, const Rope& r, int sign, hi
   if (!r.on || d % 2 != 0 || d / 2 > kMaxRopePairs) return hipErrorInvalidValue;
   hipLaunchKernelGGL(rope_kernel, dim3(cdiv(S * (d / 2), 256), n), dim3(256), 0, st, buf, S, d, r,
                      sign);
+  return hipGetLastError();
+}
+
+hipError_t oproj(float* Y, int64_t S, int64_t D, int d, const ChunkTable& t, int64_t ld,
+                 hipStream_t st) {
+  if (S <= 0) return hipSuccess;
+  hipLaunchKernelGGL(oproj_kernel, dim3(cdiv(D, 256), static_cast<unsigned>(S)), dim3(256), 0, st,
+                     Y, S, D, d, t, ld);
+  return hipGetLastError();
+}
+
+hipError_t dout(const void* dY, int64_t S, int64_t D, int d, const ChunkTable& t, int64_t ld,
+                hipStream_t st) {
+  if (S <= 0) return hipSuccess;
+  hipLaunchKernelGGL(dout_kernel, dim3(cdiv(S, 4), cdiv(d, 64), t.n), dim3(256), 0, st,
+                     static_cast<const float*>(dY), S, D, d, t, ld);
+  return hipGetLastError();
+}
+
+hipError_t dwo(const void* dY, int64_t S, int64_t D, int d, const ChunkTable& t, int64_t ld,
+               hipStream_t st) {
+  hipLaunchKernelGGL(dwo_kernel, dim3(cdiv(D, 4), cdiv(d, 64), t.n), dim3(256), 0, st,
+                     static_cast<const float*>(dY), S, D, d, t, ld);
   return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ namespace upipe {
 
 int make_plan(Plan& p, int64_t S, int64_t D, int H, int G, int d, int U, int causal, int dtype,
               int flags, double rope_theta) {
-  if ((flags & ~UPIPE_PIPELINE) != 0) return UPIPE_ERR_ARG;
+  if ((flags & ~(UPIPE_PIPELINE | UPIPE_OUT_PROJ)) != 0) return UPIPE_ERR_ARG;
   // rope_theta: 0 (no rotary embedding) or a finite positive base
   if (!(rope_theta >= 0.0) || !std::isfinite(rope_theta)) return UPIPE_ERR_ARG;
   if (S < 0 || D <= 0 || H <= 0 || G <= 0 || d <= 0 || U <= 0) return UPIPE_ERR_ARG;
@@ -58,6 +58,7 @@ int make_plan(Plan& p, int64_t S, int64_t D, int H, int G, int d, int U, int cau
   p.dtype = dtype;
   p.kv_per_stage = std::max(1, U / r);
   p.pipeline = (flags & UPIPE_PIPELINE) ? 1 : 0;
+  p.out_proj = (flags & UPIPE_OUT_PROJ) ? 1 : 0;
   // Rotary embedding: w_c = theta^(-2c/d) for c < d/2, kept as turns per
   // position (w_c / 2 pi) in fp64.
   p.rope_theta = rope_theta;
@@ -122,6 +123,8 @@ int make_plan(Plan& p, int64_t S, int64_t D, int H, int G, int d, int U, int cau
   } else {
     w.dk_acc = w.dv_acc = 0;
   }
+  // With the output projection the backward forms each stage's dO from dY.
+  w.dob = p.out_proj ? take(U * Sd * e) : 0;
   w.bwd_bytes = off;
   return UPIPE_OK;
 }

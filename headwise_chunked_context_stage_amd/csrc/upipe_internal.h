@@ -40,6 +40,8 @@ struct WsLayout {
   size_t dq[2];                // dQ [U][S][d] (element type)                  (backward)
   size_t dk[2], dv[2];         // dK, dV [kv][S][d] (element type)             (backward)
   size_t dk_acc, dv_acc;       // fp32 carry of dK, dV across a group's stages (bf16 and U < r)
+  size_t dob;                  // dO of the stage's heads [U][S][d] (element type), from dY through
+                               // the output projection (plans with UPIPE_OUT_PROJ; else 0)
   size_t fwd_bytes, bwd_bytes;
 };
 
@@ -59,6 +61,7 @@ struct Plan {
   int H, G, d, U, r, causal, dtype;
   int kv_per_stage;  // max(1, U / r)
   int pipeline;      // stage s + 1's projection overlaps stage s's attention
+  int out_proj;      // the workspace holds the stage dO buffer of upipe_bwd_out
   double rope_theta; // 0: no rotary embedding
   Rope rope;         // frequencies derived from rope_theta and d
   std::vector<Stage> stages;
@@ -101,7 +104,10 @@ struct AttnArgs {
   void* o;        // O [S][H*d]
   float* lse;     // LSE [H][S]
   // backward
-  const void* dO;       // [S][H*d]
+  const void* dO;       // row i of head h at dO + (h - do_h0) * do_hs + i * ldo (elements):
+  int64_t ldo;          //   the caller's [S][H*d]: ldo = H*d, do_hs = d, do_h0 = 0;
+  int64_t do_hs;        //   a stage buffer [U][S][d]: ldo = d, do_hs = S*d, do_h0 = the
+  int do_h0;            //   stage's first query head
   const void* o_in;     // [S][H*d]
   const float* lse_in;  // [H][S]
   float* dd;            // D [nq][S]
@@ -131,6 +137,17 @@ hipError_t attn_dkv(const AttnArgs& a, hipStream_t st);
 hipError_t attn_dq(const AttnArgs& a, hipStream_t st);
 hipError_t dw(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t, hipStream_t st);
 hipError_t dx(float* dX, int64_t S, int64_t D, int d, const ChunkTable& t, hipStream_t st);
+// Output projection (chunks = heads ascending; a[ch] / w[ch] point at the
+// head's columns of O and Wo, row stride ld = H*d):
+//   oproj: Y [S][D] fp32 += sum_ch O_ch Wo_ch^T   (Y is the running sum)
+//   dout:  a[ch] ([S][d], element type) = dY Wo_ch, dY [S][D]
+//   dwo:   dw[ch] (head's columns of dWo, row stride ld) = dY^T O_ch
+hipError_t oproj(float* Y, int64_t S, int64_t D, int d, const ChunkTable& t, int64_t ld,
+                 hipStream_t st);
+hipError_t dout(const void* dY, int64_t S, int64_t D, int d, const ChunkTable& t, int64_t ld,
+                hipStream_t st);
+hipError_t dwo(const void* dY, int64_t S, int64_t D, int d, const ChunkTable& t, int64_t ld,
+               hipStream_t st);
 // dense MFMA stream on every CU; TFLOP/s (synchronous)
 hipError_t mfma_ceiling(int waves_per_simd, int iters, double* tflops, hipStream_t st);
 }  // namespace bf16
@@ -145,6 +162,12 @@ hipError_t dx(float* dX, int64_t S, int64_t D, int d, const ChunkTable& t, hipSt
 // In-place rotation of n [S][d] fp32 buffers at `buf` (consecutive): sign +1
 // rotates queries/keys, -1 applies the transposed rotation to gradients.
 hipError_t rope(float* buf, int n, int64_t S, int d, const Rope& r, int sign, hipStream_t st);
+hipError_t oproj(float* Y, int64_t S, int64_t D, int d, const ChunkTable& t, int64_t ld,
+                 hipStream_t st);
+hipError_t dout(const void* dY, int64_t S, int64_t D, int d, const ChunkTable& t, int64_t ld,
+                hipStream_t st);
+hipError_t dwo(const void* dY, int64_t S, int64_t D, int d, const ChunkTable& t, int64_t ld,
+               hipStream_t st);
 }  // namespace f32
 hipError_t fill_zero(void* p, size_t bytes, hipStream_t st);
 

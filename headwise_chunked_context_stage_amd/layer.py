@@ -44,3 +44,20 @@ def run(plan, inp, backward_pass: bool = True, stream=None):
     if backward_pass:
         backward(plan, inp, out, stream)
     return out
+
+
+def run_out(plan, inp, backward_pass: bool = True, stream=None):
+    """The layer with its output projection (plan created with out_proj=True;
+    inputs also hold Wo [D][H*d] and dY [S][D]): forward into O, LSE and
+    Y (fp32 [S][D]), and the backward into dX, dWq, dWk, dWv, dWo (fp32)."""
+    dev = inp["X"].device
+    out = alloc_outputs(plan, dev, backward=backward_pass)
+    out["Y"] = torch.empty((plan.S, plan.D), dtype=torch.float32, device=dev)
+    plan.fwd_out(inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], out["O"], out["LSE"],
+                 out["Y"], out["ws"], stream=stream)
+    if backward_pass:
+        out["dWo"] = torch.empty((plan.D, plan.H * plan.d), dtype=torch.float32, device=dev)
+        plan.bwd_out(inp["dY"], inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], out["O"],
+                     out["LSE"], out["dX"], out["dWq"], out["dWk"], out["dWv"], out["dWo"],
+                     out["ws"], stream=stream)
+    return out

@@ -16,12 +16,14 @@ LIB_PATH = os.path.join(_HERE, "libupipe.so")
 UPIPE_BF16, UPIPE_F32 = 0, 1
 UPIPE_OK, UPIPE_ERR_ARG, UPIPE_ERR_UNSUPPORTED, UPIPE_ERR_WORKSPACE, UPIPE_ERR_HIP = 0, 1, 2, 3, 4
 UPIPE_PIPELINE = 1  # plan flag: stage pipelining on a second stream
-KERNEL_KINDS = ("proj", "attn_fwd", "bwd_pre", "attn_dkv", "attn_dq", "dw", "dx", "fill")
+UPIPE_OUT_PROJ = 2  # plan flag: workspace for upipe_bwd_out (output projection)
+KERNEL_KINDS = ("proj", "attn_fwd", "bwd_pre", "attn_dkv", "attn_dq", "dw", "dx", "fill",
+                "oproj", "dout", "dwo")
 
 EXPORTS = ("upipe_create", "upipe_create_ex", "upipe_create_rope", "upipe_destroy", "upipe_peak_bytes", "upipe_peak_bytes_phase",
            "upipe_fwd", "upipe_bwd", "upipe_strerror", "upipe_num_stages", "upipe_stage_info",
            "upipe_timing_enable", "upipe_timing_read", "upipe_kernel_name", "upipe_mfma_ceiling",
-           "upipe_auto_u")
+           "upipe_auto_u", "upipe_fwd_out", "upipe_bwd_out")
 
 _lib = None
 
@@ -59,6 +61,10 @@ def lib():
     L.upipe_fwd.restype = i32
     L.upipe_bwd.argtypes = [vp] * 13 + [sz, vp]
     L.upipe_bwd.restype = i32
+    L.upipe_fwd_out.argtypes = [vp] * 10 + [sz, vp]
+    L.upipe_fwd_out.restype = i32
+    L.upipe_bwd_out.argtypes = [vp] * 15 + [sz, vp]
+    L.upipe_bwd_out.restype = i32
     L.upipe_strerror.argtypes = [i32]
     L.upipe_strerror.restype = ctypes.c_char_p
     L.upipe_num_stages.argtypes = [vp]
@@ -178,6 +184,24 @@ def upipe_bwd(plan, dO, X, Wq, Wk, Wv, O, LSE, dX, dWq, dWk, dWv, ws, ws_bytes=N
                            ws_bytes, _stream(stream, dX, dWq)), "upipe_bwd")
 
 
+def upipe_fwd_out(plan, X, Wq, Wk, Wv, Wo, O, LSE, Y, ws, ws_bytes=None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if hasattr(ws, "numel") else 0
+    _check(lib().upipe_fwd_out(plan, _addr(X), _addr(Wq), _addr(Wk), _addr(Wv), _addr(Wo), _addr(O),
+                               _addr(LSE), _addr(Y), _addr(ws), ws_bytes, _stream(stream, X, Y)),
+           "upipe_fwd_out")
+
+
+def upipe_bwd_out(plan, dY, X, Wq, Wk, Wv, Wo, O, LSE, dX, dWq, dWk, dWv, dWo, ws, ws_bytes=None,
+                  stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if hasattr(ws, "numel") else 0
+    _check(lib().upipe_bwd_out(plan, _addr(dY), _addr(X), _addr(Wq), _addr(Wk), _addr(Wv),
+                               _addr(Wo), _addr(O), _addr(LSE), _addr(dX), _addr(dWq), _addr(dWk),
+                               _addr(dWv), _addr(dWo), _addr(ws), ws_bytes,
+                               _stream(stream, dX, dWq)), "upipe_bwd_out")
+
+
 def upipe_strerror(code: int) -> str:
     return lib().upipe_strerror(code).decode()
 
@@ -231,16 +255,17 @@ class Plan:
     """Owns a plan handle; the layer's shape and stage size U are fixed here."""
 
     def __init__(self, S, d_model, H, G, d_head, U, causal=True, dtype="bf16", pipeline=False,
-                 rope_theta=0.0):
+                 rope_theta=0.0, out_proj=False):
         self.S, self.D, self.H, self.G, self.d, self.U = S, d_model, H, G, d_head, U
         self.causal = bool(causal)
         self.pipeline = bool(pipeline)
+        self.out_proj = bool(out_proj)
         self.rope_theta = float(rope_theta)
         self.dtype = "bf16" if _dtype_code(dtype) == UPIPE_BF16 else "f32"
-        if self.rope_theta != 0.0:
+        flags = (UPIPE_PIPELINE if self.pipeline else 0) | (UPIPE_OUT_PROJ if self.out_proj else 0)
+        if self.rope_theta != 0.0 or self.out_proj:
             self.handle = upipe_create_rope(S, d_model, H, G, d_head, U, int(self.causal), dtype,
-                                            UPIPE_PIPELINE if self.pipeline else 0,
-                                            self.rope_theta)
+                                            flags, self.rope_theta)
         elif self.pipeline:
             self.handle = upipe_create_ex(S, d_model, H, G, d_head, U, int(self.causal), dtype,
                                           UPIPE_PIPELINE)
@@ -275,3 +300,11 @@ class Plan:
 
     def bwd(self, dO, X, Wq, Wk, Wv, O, LSE, dX, dWq, dWk, dWv, ws, ws_bytes=None, stream=None):
         upipe_bwd(self.handle, dO, X, Wq, Wk, Wv, O, LSE, dX, dWq, dWk, dWv, ws, ws_bytes, stream)
+
+    def fwd_out(self, X, Wq, Wk, Wv, Wo, O, LSE, Y, ws, ws_bytes=None, stream=None):
+        upipe_fwd_out(self.handle, X, Wq, Wk, Wv, Wo, O, LSE, Y, ws, ws_bytes, stream)
+
+    def bwd_out(self, dY, X, Wq, Wk, Wv, Wo, O, LSE, dX, dWq, dWk, dWv, dWo, ws, ws_bytes=None,
+                stream=None):
+        upipe_bwd_out(self.handle, dY, X, Wq, Wk, Wv, Wo, O, LSE, dX, dWq, dWk, dWv, dWo, ws,
+                      ws_bytes, stream)

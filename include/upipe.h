@@ -87,7 +87,13 @@ enum {
    * current device, which must be the device of `stream`) and a pool of
    * events are kept until the process ends; the calls allocate no device
    * memory. */
-  UPIPE_PIPELINE = 1
+  UPIPE_PIPELINE = 1,
+  /* Output projection (upipe_fwd_out / upipe_bwd_out).  Not on the pages'
+   * step list: the linear map Y = O Wo^T that follows attention in the Llama
+   * and Qwen blocks, which a drop-in attention module has to include.  The
+   * workspace of the backward grows by the stage's dO buffer
+   * (U * S * d_head elements); upipe_fwd and upipe_bwd work as before. */
+  UPIPE_OUT_PROJ = 2
 };
 
 /* upipe_create with flags (a combination of the values above; 0 gives the
@@ -149,6 +155,26 @@ int upipe_bwd(const upipe_plan* p, const void* dO, const void* X, const void* Wq
               const void* Wv, const void* O, const float* LSE, float* dX, float* dWq, float* dWk,
               float* dWv, void* ws, size_t ws_bytes, void* stream);
 
+/* The layer followed by its output projection (plan created with
+ * UPIPE_OUT_PROJ, else UPIPE_ERR_ARG).  Wo is [d_model][H*d] (nn.Linear
+ * "out x in", element type `dtype`).  upipe_fwd_out writes O and LSE as
+ * upipe_fwd does and overwrites Y [S][d_model] (fp32) with O Wo^T, which it
+ * accumulates stage by stage in Y itself (heads ascending), so every U gives
+ * the same bits.  O is still the caller's buffer: the backward reads it. */
+int upipe_fwd_out(const upipe_plan* p, const void* X, const void* Wq, const void* Wk,
+                  const void* Wv, const void* Wo, void* O, float* LSE, float* Y, void* ws,
+                  size_t ws_bytes, void* stream);
+
+/* Backward of L = sum(Y * dY), dY [S][d_model] in element type `dtype`, given
+ * the forward's O and LSE.  Each stage forms its heads' dO = dY Wo (rounded
+ * to the element type once, in the workspace) and runs the attention
+ * backward with it; overwrites dX, dWq, dWk, dWv as upipe_bwd does and
+ * dWo [d_model][H*d] (fp32) with dY^T O. */
+int upipe_bwd_out(const upipe_plan* p, const void* dY, const void* X, const void* Wq,
+                  const void* Wk, const void* Wv, const void* Wo, const void* O, const float* LSE,
+                  float* dX, float* dWq, float* dWk, float* dWv, float* dWo, void* ws,
+                  size_t ws_bytes, void* stream);
+
 /* Text for an error code (static storage). */
 const char* upipe_strerror(int code);
 
@@ -178,7 +204,10 @@ enum {
   UPIPE_K_DW = 5,       /* weight-gradient GEMM */
   UPIPE_K_DX = 6,       /* input-gradient GEMM */
   UPIPE_K_FILL = 7,     /* zero fill */
-  UPIPE_K_COUNT = 8
+  UPIPE_K_OPROJ = 8,    /* output projection Y += O Wo^T */
+  UPIPE_K_DOUT = 9,     /* dO = dY Wo */
+  UPIPE_K_DWO = 10,     /* dWo = dY^T O */
+  UPIPE_K_COUNT = 11
 };
 int upipe_timing_enable(int on);
 int upipe_timing_read(double* ms, int64_t* launches, int n);

@@ -34,11 +34,18 @@ def _rotate(x, cs, sn, sign):
 
 
 def bf16_path_emulation(inp, H: int, G: int, d: int, causal: bool = True,
-                        rope_theta: float = 0.0) -> dict:
+                        rope_theta: float = 0.0, out_proj: bool = False) -> dict:
     """With rope_theta > 0, queries and keys are rotated in fp32 before their
-    rounding, and dQ, dK take the transposed rotation before theirs."""
+    rounding, and dQ, dK take the transposed rotation before theirs.  With
+    out_proj, Y = O Wo^T and dWo = dY^T O in fp32 from the stored O, and the
+    attention backward runs with dO = dY Wo rounded to bf16 once."""
     bf = lambda t: t.to(torch.bfloat16).float()
-    X, Wq, Wk, Wv, dO = [inp[k].detach().cpu().float() for k in ("X", "Wq", "Wk", "Wv", "dO")]
+    X, Wq, Wk, Wv = [inp[k].detach().cpu().float() for k in ("X", "Wq", "Wk", "Wv")]
+    if out_proj:
+        Wo, dY = inp["Wo"].detach().cpu().float(), inp["dY"].detach().cpu().float()
+        dO = bf(dY @ Wo)
+    else:
+        dO = inp["dO"].detach().cpu().float()
     S = X.shape[0]
     r = H // G
     tau = 1.0 / math.sqrt(d)
@@ -72,7 +79,12 @@ def bf16_path_emulation(inp, H: int, G: int, d: int, causal: bool = True,
     dQf = dQ.transpose(0, 1).reshape(S, H * d)
     dKf = dK.transpose(0, 1).reshape(S, G * d)
     dVf = dV.transpose(0, 1).reshape(S, G * d)
+    extra = {}
+    if out_proj:
+        Of = O.transpose(0, 1).reshape(S, H * d)
+        extra = {"Y": Of @ Wo.T, "dWo": dY.T @ Of}
     return {
+        **extra,
         "O": O.transpose(0, 1).reshape(S, H * d),
         "LSE": lse,
         "dX": dQf @ Wq + dKf @ Wk + dVf @ Wv,

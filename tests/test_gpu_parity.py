@@ -27,7 +27,7 @@ import torch
 
 import oracle
 from headwise_chunked_context_stage_amd import upipe
-from headwise_chunked_context_stage_amd.layer import alloc_outputs, backward, forward, run
+from headwise_chunked_context_stage_amd.layer import alloc_outputs, backward, forward, run, run_out
 from headwise_chunked_context_stage_amd.synth import CONFIGS, LayerShape, make_inputs, to_numpy_exact
 
 from bf16_floor import bf16_path_emulation
@@ -298,6 +298,72 @@ def test_rope_long_positions():
     assert max(e) < 1e-4
     for k in OUTS:
         assert torch.isfinite(out[k]).all(), k
+
+
+# ---------------------------------------------------------------- output projection
+# Y = O Wo^T after the attention (the Llama / Qwen attention block's output map;
+# not on the pages' step list): forward into Y (fp32, summed stage by stage),
+# backward from dY with each stage's dO = dY Wo formed in the workspace.
+OUT_KEYS = ("O", "LSE", "Y", "dX", "dWq", "dWk", "dWv", "dWo")
+OUT_CASES = [
+    # S, D, H, G, d, dtype, theta
+    (1000, 1024, 4, 1, 128, "bf16", 0.0),       # ragged
+    (768, 512, 8, 2, 128, "bf16", 500000.0),    # two groups, with the rotary embedding
+    (512, 1536, 8, 8, 128, "bf16", 0.0),        # MHA, d_model (1536) wider than H*d (1024)
+    (320, 256, 4, 2, 64, "f32", 10000.0),
+]
+
+
+def run_layer_out(shape, dtype, U, inp, pipeline=False, rope_theta=0.0):
+    plan = upipe.Plan(shape.S, shape.D, shape.H, shape.G, shape.d, U, dtype=dtype,
+                      pipeline=pipeline, rope_theta=rope_theta, out_proj=True)
+    out = run_out(plan, inp)
+    torch.cuda.synchronize()
+    out.pop("ws")
+    return out
+
+
+@pytest.mark.parametrize("S,D,H,G,d,dtype,theta", OUT_CASES)
+def test_out_proj_matches_oracle_and_is_U_invariant(S, D, H, G, d, dtype, theta):
+    shape = LayerShape(S=S, D=D, H=H, G=G, d=d)
+    cpu_inp = make_inputs(shape, dtype, seed=19, device="cpu", out_proj=True)
+    ref = oracle.backward_out(*[to_numpy_exact(cpu_inp[k]) for k in
+                                ("X", "Wq", "Wk", "Wv", "Wo", "dY")],
+                              H, G, d, rope_theta=theta)
+    inp = {k: v.cuda() for k, v in cpu_inp.items()}
+    first = None
+    for U in legal_us(H, G):
+        say("out-proj %s theta=%g S=%d D=%d H=%d G=%d U=%d" % (dtype, theta, S, D, H, G, U))
+        out = run_layer_out(shape, dtype, U, inp, rope_theta=theta)
+        if first is None:
+            first = out
+            if dtype == "f32":
+                for k in OUT_KEYS:
+                    compare(k, host(out[k]), ref[k], 2e-2, 2e-3)
+            else:
+                emu = bf16_path_emulation(cpu_inp, H, G, d, rope_theta=theta, out_proj=True)
+                for k in OUT_KEYS:
+                    got = host(out[k])
+                    err = np.abs(got - ref[k])
+                    floor = np.abs(emu[k].double().numpy() - ref[k])
+                    fr = rel_frob(got, ref[k])
+                    say("  %-4s max %.3e mean %.3e relfrob %.3e | floor max %.3e mean %.3e"
+                        % (k, err.max(), err.mean(), fr, floor.max(), floor.mean()))
+                    assert err.max() <= 1.25 * floor.max() + 1e-3, (k, "max above the bf16 floor")
+                    assert err.mean() <= 1.25 * floor.mean() + 1e-5, (k, "mean above the floor")
+                    assert fr <= 1e-2, (k, fr)
+                for k in ("O", "LSE", "Y"):
+                    compare(k, host(out[k]), ref[k], 2e-2, 2e-3)
+        else:
+            assert_same_bits(first, out, "U=%d" % U)
+    say("out-proj pipelined U=%d" % legal_us(H, G)[-1])
+    assert_same_bits(first, run_layer_out(shape, dtype, legal_us(H, G)[-1], inp, pipeline=True,
+                                          rope_theta=theta), "pipelined")
+    # the plain entry points on the same plan still give the plain layer
+    plan = upipe.Plan(S, D, H, G, d, 1, dtype=dtype, rope_theta=theta, out_proj=True)
+    plain = run(plan, inp, backward_pass=False)
+    torch.cuda.synchronize()
+    assert torch.equal(plain["O"], first["O"]) and torch.equal(plain["LSE"], first["LSE"])
 
 
 def test_empty_sequence_zero_weight_gradients():

@@ -300,7 +300,7 @@ def test_create_ex_flags():
         assert upipe.upipe_peak_bytes(h) == upipe.Plan(4096, 1024, 8, 2, 128, 2).peak_bytes
     finally:
         upipe.upipe_destroy(h)
-    for bad in (2, 4, -1, 1 << 30):
+    for bad in (4, 8, -1, 1 << 30):
         with pytest.raises(upipe.UpipeError) as e:
             upipe.upipe_create_ex(4096, 1024, 8, 2, 128, 2, 1, "bf16", bad)
         assert e.value.code == upipe.UPIPE_ERR_ARG
@@ -308,3 +308,41 @@ def test_create_ex_flags():
     with pytest.raises(upipe.UpipeError) as e:
         upipe.upipe_create_ex(4096, 1024, 8, 2, 128, 3, 1, "bf16", upipe.UPIPE_PIPELINE)
     assert e.value.code == upipe.UPIPE_ERR_ARG
+
+
+def test_out_proj_plan_workspace_and_validation():
+    """UPIPE_OUT_PROJ adds the stage dO buffer (U*S*d elements) to the
+    backward workspace only; the output-projection entry points refuse a plan
+    without the flag and bad pointers, before any launch."""
+    import ctypes
+    S, D, H, G, d = 4096, 1024, 32, 8, 128
+    for U in legal_us(H, G):
+        for dtype, e in (("bf16", 2),):
+            a = upipe.upipe_create_ex(S, D, H, G, d, U, 1, dtype, 0)
+            b = upipe.upipe_create_ex(S, D, H, G, d, U, 1, dtype, upipe.UPIPE_OUT_PROJ)
+            try:
+                assert upipe.upipe_peak_bytes_phase(b, 0) == upipe.upipe_peak_bytes_phase(a, 0)
+                extra = upipe.upipe_peak_bytes_phase(b, 1) - upipe.upipe_peak_bytes_phase(a, 1)
+                assert U * S * d * e <= extra < U * S * d * e + 256
+            finally:
+                upipe.upipe_destroy(a)
+                upipe.upipe_destroy(b)
+    L = upipe.lib()
+    plain = upipe.Plan(256, 256, 4, 2, 128, 2)
+    outp = upipe.Plan(256, 256, 4, 2, 128, 2, out_proj=True)
+    fake = [ctypes.c_void_p(1 << 20) for _ in range(16)]  # aligned, never dereferenced
+    ws = 1 << 20
+    # a plan without the flag
+    assert L.upipe_fwd_out(plain.handle, *fake[:8], ws, outp.peak_bytes, None) == upipe.UPIPE_ERR_ARG
+    assert L.upipe_bwd_out(plain.handle, *fake[:13], ws, outp.peak_bytes, None) == upipe.UPIPE_ERR_ARG
+    # null or misaligned pointers, small workspace
+    assert L.upipe_fwd_out(outp.handle, *fake[:4], None, *fake[5:8], ws, outp.peak_bytes,
+                           None) == upipe.UPIPE_ERR_ARG
+    assert L.upipe_fwd_out(outp.handle, *fake[:7], ctypes.c_void_p((1 << 20) + 4), ws,
+                           outp.peak_bytes, None) == upipe.UPIPE_ERR_ARG
+    assert L.upipe_bwd_out(outp.handle, *fake[:12], None, ws, outp.peak_bytes,
+                           None) == upipe.UPIPE_ERR_ARG
+    assert L.upipe_bwd_out(outp.handle, *fake[:13], ws, outp.peak_bytes - 1,
+                           None) == upipe.UPIPE_ERR_WORKSPACE
+    assert L.upipe_bwd_out(outp.handle, *fake[:13], ws + 8, outp.peak_bytes,
+                           None) == upipe.UPIPE_ERR_WORKSPACE

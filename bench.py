@@ -41,6 +41,8 @@ def parse():
                     help="stage pipelining: the GEMMs of neighbouring stages on a second stream")
     ap.add_argument("--rope-theta", type=float, default=0.0,
                     help="rotary embedding of queries and keys with this base (0: none)")
+    ap.add_argument("--out-proj", action="store_true",
+                    help="the layer with its output projection (upipe_fwd_out / upipe_bwd_out)")
     ap.add_argument("--skip-cpu-baseline", action="store_true",
                     help="omit the oracle timing (profiling runs only)")
     ap.add_argument("--cpu-baseline-S", type=int, default=8192)
@@ -75,6 +77,8 @@ def kernel_work(kind, S, D, d, U, r, causal=True):
         return (2.0 * 2 * S * d + 12.0 * S) * U, "byte"  # read O, dO (bf16), LSE; write D, LSE*log2e (fp32)
     if kind == "fill":
         return 4.0 * S * D, "byte"
+    if kind in ("oproj", "dout", "dwo"):  # output projection: Y += O Wo^T, dO = dY Wo, dWo = dY^T O
+        return 2.0 * S * D * d * U, "flop"
     return 0.0, "flop"
 
 
@@ -173,16 +177,26 @@ def main():
         torch.cuda.synchronize()
         print("bench: calibration copy of %d bytes" % n, file=sys.stderr, flush=True)
         del src, dst
-    inp = make_inputs(shape, cfg["dtype"], seed=0, device="cuda")
+    inp = make_inputs(shape, cfg["dtype"], seed=0, device="cuda", out_proj=args.out_proj)
     plan = upipe.Plan(S, D, H, G, d, U, causal=True, dtype=cfg["dtype"], pipeline=args.pipeline,
-                      rope_theta=args.rope_theta)
+                      rope_theta=args.rope_theta, out_proj=args.out_proj)
     out = alloc_outputs(plan, dev)
+    if args.out_proj:
+        out["Y"] = torch.empty((S, D), dtype=torch.float32, device=dev)
+        out["dWo"] = torch.empty((D, H * d), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     mem_before = torch.cuda.memory_allocated()
 
     def step():
-        forward(plan, inp, out)
-        backward(plan, inp, out)
+        if args.out_proj:
+            plan.fwd_out(inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], out["O"],
+                         out["LSE"], out["Y"], out["ws"])
+            plan.bwd_out(inp["dY"], inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"],
+                         out["O"], out["LSE"], out["dX"], out["dWq"], out["dWk"], out["dWv"],
+                         out["dWo"], out["ws"])
+        else:
+            forward(plan, inp, out)
+            backward(plan, inp, out)
 
     for _ in range(args.warmup):
         step()
@@ -206,7 +220,7 @@ def main():
     ms_per_step = 1e3 * elapsed / args.steps
     aflops = attn_flops(S, H, d)
     value = aflops / (ms_per_step * 1e-3) / 1e12
-    proj_flops = 8.0 * S * D * (H + 2 * G) * d
+    proj_flops = 8.0 * S * D * (H + 2 * G) * d + (6.0 * S * D * H * d if args.out_proj else 0.0)
 
     kernels = {}
     for kind, rec in ktimes.items():
@@ -217,7 +231,8 @@ def main():
         work, unit = kernel_work(kind, S, D, d, min(U, H), r)
         ent = {"ms_per_step": rec["ms"] / args.steps, "launches_per_step": n_per_step,
                "avg_launch_ms": avg_ms}
-        if kind in ("attn_fwd", "attn_dkv", "attn_dq", "proj", "dw", "dx") and U >= r:
+        if kind in ("attn_fwd", "attn_dkv", "attn_dq", "proj", "dw", "dx", "oproj", "dout",
+                    "dwo") and U >= r:
             ent["tflops"] = work / (avg_ms * 1e-3) / 1e12
         elif kind in ("bwd_pre",):
             ent["gbps"] = work / (avg_ms * 1e-3) / 1e9
@@ -275,7 +290,8 @@ def main():
         "config": {"workload": "causal GQA attention layer fwd+bwd, one GPU, Llama3-8B attention "
                                "shape" if args.config.startswith("llama") else args.config,
                    "name": args.config, "S": S, "d_model": D, "H": H, "G": G, "d_head": d,
-                   "U": U, "pipeline": args.pipeline, "rope_theta": args.rope_theta, "causal": True,
+                   "U": U, "pipeline": args.pipeline, "rope_theta": args.rope_theta,
+                   "out_proj": args.out_proj, "causal": True,
                    "seed": 0},
         "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "attn_kernels_tflops": aflops / (attn_ms * 1e-3) / 1e12 if attn_ms > 0 else None,

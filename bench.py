@@ -56,6 +56,9 @@ def attn_flops(S, H, d, causal=True):
     return 14.0 * d * pairs * H  # 2 fwd + 5 bwd matmuls, 2*d flops each per pair
 
 
+H_ALL = 32  # query heads of the layer (set from the workload in main)
+
+
 def kernel_work(kind, S, D, d, U, r, causal=True):
     """Algorithmic work of one launch of `kind` in a stage of U query heads
     (U >= r: whole groups).  Returns (amount, unit)."""
@@ -77,8 +80,10 @@ def kernel_work(kind, S, D, d, U, r, causal=True):
         return (2.0 * 2 * S * d + 12.0 * S) * U, "byte"  # read O, dO (bf16), LSE; write D, LSE*log2e (fp32)
     if kind == "fill":
         return 4.0 * S * D, "byte"
-    if kind in ("oproj", "dout", "dwo"):  # output projection: Y += O Wo^T, dO = dY Wo, dWo = dY^T O
+    if kind == "dout":  # output projection's dO = dY Wo for a stage's heads
         return 2.0 * S * D * d * U, "flop"
+    if kind in ("oproj", "dwo"):  # Y = O Wo^T and dWo = dY^T O, one launch for all heads (H <= 64)
+        return 2.0 * S * D * d * H_ALL, "flop"
     return 0.0, "flop"
 
 
@@ -163,6 +168,8 @@ def main():
     U = args.U or cfg["U"][0]
     S, D, H, G, d = shape.S, shape.D, shape.H, shape.G, shape.d
     r = H // G
+    global H_ALL
+    H_ALL = min(H, 64)
     dev = torch.device("cuda:0")
     print("bench: %s S=%d D=%d H=%d G=%d d=%d U=%d%s" % (args.config, S, D, H, G, d, U,
                                                        " pipelined" if args.pipeline else ""),

@@ -296,26 +296,45 @@ hipError_t per_head_chunks(const Plan& p, const Stage& st, const void* A, const 
   return hipSuccess;
 }
 
-// Forward: Y += O_s Wo_s^T for the stage's heads, after its attention.
-hipError_t stage_oproj(const Plan& p, const Stage& st, const Kernels& K, const void* O,
-                       const OutProj& op, hipStream_t s) {
+// Every head at once (the projections below need only the finished O, or
+// the inputs dY and O).
+Stage all_heads(const Plan& p) {
+  Stage st{};
+  st.q0 = 0;
+  st.nq = p.H;
+  return st;
+}
+
+// Forward, after the last stage: Y = O Wo^T over all heads, ascending, with
+// Y (zeroed first) as the fp32 running sum.  Summing the stages' O_s Wo_s^T
+// into Y one stage at a time gives the same bits (the sum runs through Y in
+// fp32 in the same head order), at 8 x the read-modify-write of Y.
+hipError_t layer_oproj(const Plan& p, const Kernels& K, const void* O, const OutProj& op,
+                       hipStream_t s) {
   const int64_t ld = static_cast<int64_t>(p.H) * p.d;
-  return per_head_chunks(p, st, O, op.Wo, nullptr, nullptr, [&](const ChunkTable& t) {
+  hipError_t e = timed(UPIPE_K_FILL, s,
+                       [&] { return fill_zero(op.Y, static_cast<size_t>(p.S) * p.D * 4, s); });
+  if (e != hipSuccess) return e;
+  return per_head_chunks(p, all_heads(p), O, op.Wo, nullptr, nullptr, [&](const ChunkTable& t) {
     return timed(UPIPE_K_OPROJ, s, [&] { return K.oproj(op.Y, p.S, p.D, p.d, t, ld, s); });
   });
 }
 
 // Backward, before the stage's attention backward: dO of its heads into the
-// stage buffer, and the heads' columns of dWo.
-hipError_t stage_out_grads(const Plan& p, const Stage& st, const Kernels& K, void* ws,
-                           const OutProj& op, hipStream_t s) {
+// stage buffer.
+hipError_t stage_dout(const Plan& p, const Stage& st, const Kernels& K, void* ws,
+                      const OutProj& op, hipStream_t s) {
   const int64_t ld = static_cast<int64_t>(p.H) * p.d;
-  hipError_t e = per_head_chunks(p, st, nullptr, op.Wo, nullptr, at(ws, p.ws.dob),
-                                 [&](const ChunkTable& t) {
+  return per_head_chunks(p, st, nullptr, op.Wo, nullptr, at(ws, p.ws.dob), [&](const ChunkTable& t) {
     return timed(UPIPE_K_DOUT, s, [&] { return K.dout(op.dY, p.S, p.D, p.d, t, ld, s); });
   });
-  if (e != hipSuccess) return e;
-  return per_head_chunks(p, st, op.O, op.Wo, op.dWo, nullptr, [&](const ChunkTable& t) {
+}
+
+// Backward: dWo = dY^T O for every head (one launch fills the chip; a
+// stage's heads alone would leave it half idle).
+hipError_t layer_dwo(const Plan& p, const Kernels& K, const OutProj& op, hipStream_t s) {
+  const int64_t ld = static_cast<int64_t>(p.H) * p.d;
+  return per_head_chunks(p, all_heads(p), op.O, op.Wo, op.dWo, nullptr, [&](const ChunkTable& t) {
     return timed(UPIPE_K_DWO, s, [&] { return K.dwo(op.dY, p.S, p.D, p.d, t, ld, s); });
   });
 }
@@ -395,7 +414,7 @@ hipError_t order(hipEvent_t ev, hipStream_t signaller, hipStream_t waiter) {
 // s mod 2, so the projection of s + 1 waits only for the attention of s - 1.
 hipError_t fwd_pipelined(const Plan& p, const Kernels& K, const void* X, const void* Wq,
                          const void* Wk, const void* Wv, void* O, float* LSE, void* ws,
-                         hipStream_t s, hipStream_t h, SyncEvents& E, const OutProj* op) {
+                         hipStream_t s, hipStream_t h, SyncEvents& E) {
   hipEvent_t start = E.ev[0], proj_done[2] = {E.ev[1], E.ev[2]}, attn_done[2] = {E.ev[3], E.ev[4]};
   const int n = static_cast<int>(p.stages.size());
   hipError_t e = order(start, s, h);  // inputs written on the caller's stream
@@ -411,7 +430,6 @@ hipError_t fwd_pipelined(const Plan& p, const Kernels& K, const void* X, const v
     a.lse = LSE;
     e = timed(UPIPE_K_ATTN_FWD, s, [&] { return K.attn_fwd(a, s); });
     if (e == hipSuccess) e = hipEventRecord(attn_done[i % 2], s);
-    if (e == hipSuccess && op) e = stage_oproj(p, st, K, O, *op, s);
     if (e != hipSuccess || i + 1 == n) break;
     // copy (i + 1) mod 2 was last read by the attention of stage i - 1
     if (i >= 1) e = hipStreamWaitEvent(h, attn_done[(i - 1) % 2], 0);
@@ -440,7 +458,7 @@ hipError_t bwd_pipelined(const Plan& p, const Kernels& K, const BwdIn& in, hipSt
     const Stage& st = p.stages[i];
     // the stage dO buffer is single: its GEMMs run on this stream, after
     // dQ of the previous stage has read it
-    if (op) e = stage_out_grads(p, st, K, in.ws, *op, s);
+    if (op) e = stage_dout(p, st, K, in.ws, *op, s);
     const AttnArgs a = op ? with_stage_do(p, st, in.ws, bwd_args(p, st, in)) : bwd_args(p, st, in);
     if (e == hipSuccess) e = timed(UPIPE_K_BWD_PRE, s, [&] { return K.bwd_pre(a, s); });
     if (e == hipSuccess) e = hipStreamWaitEvent(s, proj_done[i % 2], 0);
@@ -570,24 +588,17 @@ int run_fwd(const Plan& p, const void* X, const void* Wq, const void* Wk, const 
     SyncEvents E;
     UPIPE_TRY(helper_stream(&hs));
     UPIPE_TRY(E.take());
-    if (op)
-      UPIPE_TRY(timed(UPIPE_K_FILL, s, [&] {
-        return fill_zero(op->Y, static_cast<size_t>(p.S) * p.D * 4, s);
-      }));
-    UPIPE_TRY(fwd_pipelined(p, K, X, Wq, Wk, Wv, O, LSE, ws, s, hs, E, op));
-    return UPIPE_OK;
+    UPIPE_TRY(fwd_pipelined(p, K, X, Wq, Wk, Wv, O, LSE, ws, s, hs, E));
+  } else {
+    for (const Stage& st : p.stages) {
+      UPIPE_TRY(stage_projection(p, st, K, X, Wq, Wk, Wv, ws, s));
+      AttnArgs a = attn_args(p, st, ws);
+      a.o = O;
+      a.lse = LSE;
+      UPIPE_TRY(timed(UPIPE_K_ATTN_FWD, s, [&] { return K.attn_fwd(a, s); }));
+    }
   }
-  if (op)
-    UPIPE_TRY(timed(UPIPE_K_FILL, s,
-                    [&] { return fill_zero(op->Y, static_cast<size_t>(p.S) * p.D * 4, s); }));
-  for (const Stage& st : p.stages) {
-    UPIPE_TRY(stage_projection(p, st, K, X, Wq, Wk, Wv, ws, s));
-    AttnArgs a = attn_args(p, st, ws);
-    a.o = O;
-    a.lse = LSE;
-    UPIPE_TRY(timed(UPIPE_K_ATTN_FWD, s, [&] { return K.attn_fwd(a, s); }));
-    if (op) UPIPE_TRY(stage_oproj(p, st, K, O, *op, s));
-  }
+  if (op) UPIPE_TRY(layer_oproj(p, K, O, *op, s));  // on the caller's stream, after every stage
   return UPIPE_OK;
 }
 
@@ -603,13 +614,14 @@ int run_bwd(const Plan& p, const BwdIn& in, hipStream_t s, const OutProj* op) {
   }
   UPIPE_TRY(timed(UPIPE_K_FILL, s,
                   [&] { return fill_zero(in.dX, static_cast<size_t>(p.S) * p.D * 4, s); }));
+  if (op) UPIPE_TRY(layer_dwo(p, K, *op, s));  // reads only the inputs dY and O
   if (p.pipeline) {
     UPIPE_TRY(bwd_pipelined(p, K, in, s, hs, E, op));
     return UPIPE_OK;
   }
   for (const Stage& st : p.stages) {
     UPIPE_TRY(stage_projection(p, st, K, in.X, in.Wq, in.Wk, in.Wv, in.ws, s));
-    if (op) UPIPE_TRY(stage_out_grads(p, st, K, in.ws, *op, s));
+    if (op) UPIPE_TRY(stage_dout(p, st, K, in.ws, *op, s));
     const AttnArgs a = op ? with_stage_do(p, st, in.ws, bwd_args(p, st, in)) : bwd_args(p, st, in);
     UPIPE_TRY(timed(UPIPE_K_BWD_PRE, s, [&] { return K.bwd_pre(a, s); }));
     UPIPE_TRY(timed(UPIPE_K_ATTN_DKV, s, [&] { return K.attn_dkv(a, s); }));

@@ -158,9 +158,10 @@ int upipe_bwd(const upipe_plan* p, const void* dO, const void* X, const void* Wq
 /* The layer followed by its output projection (plan created with
  * UPIPE_OUT_PROJ, else UPIPE_ERR_ARG).  Wo is [d_model][H*d] (nn.Linear
  * "out x in", element type `dtype`).  upipe_fwd_out writes O and LSE as
- * upipe_fwd does and overwrites Y [S][d_model] (fp32) with O Wo^T, which it
- * accumulates stage by stage in Y itself (heads ascending), so every U gives
- * the same bits.  O is still the caller's buffer: the backward reads it. */
+ * upipe_fwd does and overwrites Y [S][d_model] (fp32) with O Wo^T, computed
+ * after the last stage over all heads in ascending order with Y itself as
+ * the fp32 running sum, so every U gives the same bits.  O is still the
+ * caller's buffer: the backward reads it. */
 int upipe_fwd_out(const upipe_plan* p, const void* X, const void* Wq, const void* Wk,
                   const void* Wv, const void* Wo, void* O, float* LSE, float* Y, void* ws,
                   size_t ws_bytes, void* stream);
@@ -169,7 +170,8 @@ int upipe_fwd_out(const upipe_plan* p, const void* X, const void* Wq, const void
  * the forward's O and LSE.  Each stage forms its heads' dO = dY Wo (rounded
  * to the element type once, in the workspace) and runs the attention
  * backward with it; overwrites dX, dWq, dWk, dWv as upipe_bwd does and
- * dWo [d_model][H*d] (fp32) with dY^T O. */
+ * dWo [d_model][H*d] (fp32) with dY^T O (one pass over all heads, since it
+ * needs only the inputs dY and O). */
 int upipe_bwd_out(const upipe_plan* p, const void* dY, const void* X, const void* Wq,
                   const void* Wk, const void* Wv, const void* Wo, const void* O, const float* LSE,
                   float* dX, float* dWq, float* dWk, float* dWv, float* dWo, void* ws,

@@ -54,6 +54,9 @@ def _load():
         lib.oracle_backward.argtypes = [i64, i64, i32, i32, i32, i32, f64, i32, vp, vp, vp, vp, vp,
                                         dp, dp, dp, dp, dp, dp, i32]
         lib.oracle_backward.restype = i32
+        lib.oracle_dx_tail.argtypes = [i64, i64, i32, i32, i32, f64, i32, vp, vp, vp, vp, vp, i64,
+                                       dp, i32]
+        lib.oracle_dx_tail.restype = i32
         lib.oracle_out_proj.argtypes = [i64, i64, i64, i32, dp, vp, vp, dp, dp, dp, i32]
         lib.oracle_out_proj.restype = i32
         _lib = lib
@@ -154,6 +157,22 @@ def backward(X, Wq, Wk, Wv, dO, H: int, G: int, d: int, causal: bool = True,
                                  _ptr(out["dWv"]), nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle_backward rejected the shape")
+    return out
+
+
+def dx_tail(X, Wq, Wk, Wv, dO, H: int, G: int, d: int, t0: int, nthreads: int | None = None,
+            rope_theta: float = 0.0):
+    """Input gradient dX at rows t0 .. S-1 of the causal layer (fp64
+    [S - t0][D]), exactly as oracle_backward defines it, at O((S - t0) S)
+    attention cost (see the C++ source)."""
+    (X, Wq, Wk, Wv, dO), enc = _prep([X, Wq, Wk, Wv, dO])
+    S, D = X.shape
+    _check_shapes(S, D, H, G, d, Wq, Wk, Wv)
+    out = np.empty((S - t0, D), np.float64)
+    rc = _load().oracle_dx_tail(S, D, H, G, d, float(rope_theta), enc, _ptr(X), _ptr(Wq), _ptr(Wk),
+                                _ptr(Wv), _ptr(dO), int(t0), _ptr(out), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_dx_tail rejected the arguments")
     return out
 
 

@@ -400,6 +400,106 @@ int oracle_backward(int64_t S, int64_t D, int H, int G, int d, int causal, doubl
   return 0;
 }
 
+// Input gradient at the last rows [t0, S) of a causal layer, from the same
+// definition as oracle_backward but without the O(S^2) passes: row t of dX
+// needs dQ_h[t] (query row t against keys <= t), and dK_g[t], dV_g[t], which
+// gather over query rows i >= t only, so every attention row involved lies in
+// [t0, S).  K and V are projected for all positions; Q, O, LSE and D only for
+// rows [t0, S).  Output dXt [(S - t0)][D] (fp64).  Returns 0, or 1 on an
+// invalid shape, t0 outside [0, S) or a non-causal layer.
+int oracle_dx_tail(int64_t S, int64_t D, int H, int G, int d, double rope_theta, int enc,
+                   const void* Xp, const void* Wqp, const void* Wkp, const void* Wvp,
+                   const void* dOp, int64_t t0, double* dXt, int nthreads) {
+  Shape s{S, D, H, G, d, 1, rope_theta};
+  if (!shape_ok(s) || t0 < 0 || t0 >= S) return 1;
+  const int64_t Hd = static_cast<int64_t>(H) * d, n = S - t0;
+  const int r = s.r();
+  std::vector<double> X = decode(Xp, enc, S * D);
+  std::vector<double> Wq = decode(Wqp, enc, Hd * D);
+  std::vector<double> Wk = decode(Wkp, enc, static_cast<int64_t>(G) * d * D);
+  std::vector<double> Wv = decode(Wvp, enc, static_cast<int64_t>(G) * d * D);
+  std::vector<double> dO = decode(dOp, enc, S * Hd);
+  std::vector<int64_t> rows(static_cast<size_t>(n));
+  for (int64_t t = 0; t < n; ++t) rows[t] = t0 + t;
+
+  std::vector<double> K(static_cast<size_t>(G * S * d)), V(static_cast<size_t>(G * S * d));
+  for (int g = 0; g < G; ++g) {
+    project_head(X, Wk, s, g, S, nullptr, &K[g * S * d], nthreads);
+    project_head(X, Wv, s, g, S, nullptr, &V[g * S * d], nthreads);
+    rotate_rows(&K[g * S * d], S, nullptr, s, +1);
+  }
+  // Q, LSE and D of query rows [t0, S) (index t = i - t0).
+  std::vector<double> Q(static_cast<size_t>(H * n * d)), LSE(static_cast<size_t>(H * n)),
+      Dv(static_cast<size_t>(H * n));
+  for (int h = 0; h < H; ++h) {
+    project_head(X, Wq, s, h, n, rows.data(), &Q[h * n * d], nthreads);
+    rotate_rows(&Q[h * n * d], n, rows.data(), s, +1);
+    const int g = s.kv(h);
+    parallel_for(n, nthreads, [&](int64_t t) {
+      std::vector<double> scores;
+      std::vector<double> o(static_cast<size_t>(d));
+      const int64_t i = t0 + t;
+      LSE[h * n + t] = attend_row(&Q[(h * n + t) * d], &K[g * S * d], &V[g * S * d], s, i,
+                                  o.data(), scores);
+      Dv[h * n + t] = dot(&dO[i * Hd + h * d], o.data(), d);
+    });
+  }
+  auto prob = [&](int h, int64_t t, int64_t j) {  // P of query row t0 + t, key j
+    const int g = s.kv(h);
+    return std::exp(s.tau() * dot(&Q[(h * n + t) * d], &K[(g * S + j) * d], d) - LSE[h * n + t]);
+  };
+  auto dprob = [&](int h, int64_t t, int64_t j) {
+    const int g = s.kv(h);
+    return dot(&dO[(t0 + t) * Hd + h * d], &V[(g * S + j) * d], d);
+  };
+  // dQ of rows [t0, S): keys 0 .. i.
+  std::vector<double> dQ(static_cast<size_t>(H * n * d), 0.0);
+  for (int h = 0; h < H; ++h) {
+    const int g = s.kv(h);
+    parallel_for(n, nthreads, [&](int64_t t) {
+      double* dq = &dQ[(h * n + t) * d];
+      for (int64_t j = 0; j <= t0 + t; ++j) {
+        const double ds = prob(h, t, j) * (dprob(h, t, j) - Dv[h * n + t]);
+        for (int c = 0; c < d; ++c) dq[c] += s.tau() * ds * K[(g * S + j) * d + c];
+      }
+    });
+  }
+  // dK, dV of key rows [t0, S): query rows i >= key, heads of the group ascending.
+  std::vector<double> dK(static_cast<size_t>(G * n * d), 0.0), dV(static_cast<size_t>(G * n * d), 0.0);
+  for (int g = 0; g < G; ++g) {
+    parallel_for(n, nthreads, [&](int64_t tj) {
+      const int64_t j = t0 + tj;
+      double* dk = &dK[(g * n + tj) * d];
+      double* dv = &dV[(g * n + tj) * d];
+      for (int h = g * r; h < (g + 1) * r; ++h) {
+        for (int64_t t = tj; t < n; ++t) {
+          const double p = prob(h, t, j);
+          const double ds = p * (dprob(h, t, j) - Dv[h * n + t]);
+          for (int c = 0; c < d; ++c) {
+            dk[c] += s.tau() * ds * Q[(h * n + t) * d + c];
+            dv[c] += p * dO[(t0 + t) * Hd + h * d + c];
+          }
+        }
+      }
+    });
+  }
+  for (int h = 0; h < H; ++h) rotate_rows(&dQ[h * n * d], n, rows.data(), s, -1);
+  for (int g = 0; g < G; ++g) rotate_rows(&dK[g * n * d], n, rows.data(), s, -1);
+  parallel_for(n, nthreads, [&](int64_t t) {
+    for (int64_t k = 0; k < D; ++k) {
+      double acc = 0.0;
+      for (int h = 0; h < H; ++h)
+        for (int c = 0; c < d; ++c) acc += dQ[(h * n + t) * d + c] * Wq[(h * d + c) * D + k];
+      for (int g = 0; g < G; ++g)
+        for (int c = 0; c < d; ++c)
+          acc += dK[(g * n + t) * d + c] * Wk[(g * d + c) * D + k] +
+                 dV[(g * n + t) * d + c] * Wv[(g * d + c) * D + k];
+      dXt[t * D + k] = acc;
+    }
+  });
+  return 0;
+}
+
 // Output projection and its backward, by definition.  O [S][Hd] fp64 (the
 // attention output), Wo [D][Hd] and dY [S][D] in encoding `enc` (dY may be
 // null: forward only).  Outputs (fp64, caller-owned, any may be null):

@@ -293,6 +293,7 @@ def test_rope_long_positions():
     S = shape.S
     sampled_rows_check(shape, inp, out, [0, 1, 4095],
                        [S - 1, S - 2, S - 1000, (1 << 19) + 3], (0, 2), rope_theta=10000.0)
+    dx_tail_check(shape, inp, out, 8, rope_theta=10000.0)
     e = identities(out, inp)
     say("  identities %.2e %.2e %.2e" % e)
     assert max(e) < 1e-4
@@ -439,6 +440,24 @@ def sampled_rows_check(shape, inp, out, rows_all, rows_late, late_heads, rope_th
         compare("LSE", got_l, Lr[heads[0]:heads[1]], 2e-2, 2e-3)
 
 
+def dx_tail_check(shape, inp, out, n_rows, rope_theta=0.0):
+    """Backward rows against the oracle at full size: dX of the last n_rows
+    tokens is cheap to compute exactly (only the last query rows see the last
+    keys).  Gated on mean-abs <= 2e-3 and relative Frobenius error <= 1e-2,
+    with a gross max-abs bound; the bf16 floor emulation is out of reach at
+    these sizes."""
+    S = shape.S
+    t0 = S - n_rows
+    say("  oracle dX rows %d .. %d" % (t0, S - 1))
+    ref = oracle.dx_tail(*[to_numpy_exact(inp[k]) for k in ("X", "Wq", "Wk", "Wv", "dO")],
+                         shape.H, shape.G, shape.d, t0, rope_theta=rope_theta)
+    got = host(out["dX"][t0:])
+    err = np.abs(got - ref)
+    fr = rel_frob(got, ref)
+    say("  dX   max %.3e mean %.3e relfrob %.3e" % (err.max(), err.mean(), fr))
+    assert err.mean() <= 2e-3 and fr <= 1e-2 and err.max() <= 5e-2, (err.max(), err.mean(), fr)
+
+
 def run_measured(shape, U, inp):
     """fwd + bwd with the device high-water mark taken around the calls: the
     library allocates nothing, so the only intermediate memory is the
@@ -469,6 +488,7 @@ def test_full_size_llama8b_s32k_U_invariant():
             first = out
             sampled_rows_check(shape, inp, out, [0, 1, 2, 63, 64, 127, 128, 129, 1000, 2047],
                                [], None)
+            dx_tail_check(shape, inp, out, 16)
             e = identities(out, inp)
             say("  identities %.2e %.2e %.2e" % e)
             assert max(e) < 1e-4

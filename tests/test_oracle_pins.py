@@ -492,3 +492,28 @@ def test_out_proj_identity_weight_and_scaling(oracle_mod):
     r = oracle_mod.backward_out(X, Wq, Wk, Wv, Wo, dY, H, G, d)
     lhs, rhs = float(np.sum(r["dWo"] * Wo)), float(np.sum(dY * r["Y"]))
     assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(rhs))
+
+
+# ------------------------------------------------------------ dX at the last rows
+@pytest.mark.parametrize("shape", [(37, 24, 4, 2, 8), (50, 24, 8, 1, 8), (29, 16, 3, 3, 8)])
+@pytest.mark.parametrize("theta", [0.0, 10000.0])
+def test_dx_tail_matches_full_backward(oracle_mod, shape, theta):
+    """The tail routine (only query rows >= t0 attend) reproduces the full
+    backward's dX rows t0 .. S-1, and torch's, for several t0 including 0."""
+    S, D, H, G, d = shape
+    X, Wq, Wk, Wv, dO = draw(S, D, H, G, d, seed=31)
+    full = oracle_mod.backward(X, Wq, Wk, Wv, dO, H, G, d, rope_theta=theta)
+    ref = (torch_layer_rope(X, Wq, Wk, Wv, dO, H, G, d, True, theta) if theta > 0
+           else torch_layer(X, Wq, Wk, Wv, dO, H, G, d, True))
+    for t0 in (0, 1, S // 2, S - 3, S - 1):
+        tail = oracle_mod.dx_tail(X, Wq, Wk, Wv, dO, H, G, d, t0, rope_theta=theta)
+        assert tail.shape == (S - t0, D)
+        close(tail, full["dX"][t0:], 1e-12)
+        close(tail, ref["dX"][t0:])
+
+
+def test_dx_tail_rejects_bad_rows(oracle_mod):
+    X, Wq, Wk, Wv, dO = draw(8, 8, 2, 1, 4, seed=1)
+    for t0 in (-1, 8):
+        with pytest.raises(ValueError):
+            oracle_mod.dx_tail(X, Wq, Wk, Wv, dO, 2, 1, 4, t0)

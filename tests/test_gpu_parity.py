@@ -510,6 +510,7 @@ def test_full_size_llama8b_s128k_bench_config():
     S = shape.S
     sampled_rows_check(shape, inp, out, [0, 1, 100, 1023, 1024, 2047],
                        [S - 1, S - 2, S - 129, S - 4096], (0, 4))
+    dx_tail_check(shape, inp, out, 8)
     e = identities(out, inp)
     say("  identities %.2e %.2e %.2e" % e)
     assert max(e) < 1e-4
@@ -537,6 +538,7 @@ def test_full_size_qwen32b_s64k_U_invariant_and_peak_bytes():
             first = out
             sampled_rows_check(shape, inp, out, [0, 1, 100, 1023, 1024, 4095],
                                [S - 1, S - 2, S - 1000], (0, r))
+            dx_tail_check(shape, inp, out, 8)
             e = identities(out, inp)
             say("  identities %.2e %.2e %.2e" % e)
             assert max(e) < 1e-4

@@ -213,11 +213,18 @@ def main():
     upipe.upipe_timing_enable(True)
     upipe.upipe_timing_read()  # drop anything pending
     torch.cuda.synchronize()
+    # step boundaries as events on the stream every call is enqueued on (the
+    # current stream: the library runs there unless pipelined, and a
+    # pipelined call joins its helper stream back before returning)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
+    marks[0].record()
     for i in range(args.steps):
         step()
+        marks[i + 1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     upipe.upipe_timing_enable(False)
     ktimes = upipe.upipe_timing_read()
     high_water_delta = torch.cuda.max_memory_allocated() - mem_before
@@ -289,6 +296,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "step_ms_median": step_ms[len(step_ms) // 2],
+        "step_ms_min": step_ms[0],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

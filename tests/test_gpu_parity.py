@@ -376,6 +376,15 @@ def test_empty_sequence_zero_weight_gradients():
     torch.cuda.synchronize()
     for t in dW:
         assert torch.count_nonzero(t).item() == 0
+    say("empty sequence, output projection")
+    plan = upipe.Plan(0, 256, 4, 2, 128, 2, out_proj=True)
+    dW = [torch.full((n * 128, 256), 7.0, device="cuda") for n in (4, 2, 2)]
+    dWo = torch.full((256, 4 * 128), 7.0, device="cuda")
+    upipe.upipe_fwd_out(plan.handle, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0)
+    upipe.upipe_bwd_out(plan.handle, 0, 0, 0, 0, 0, 0, 0, 0, 0, dW[0], dW[1], dW[2], dWo, 0, 0)
+    torch.cuda.synchronize()
+    for t in dW + [dWo]:
+        assert torch.count_nonzero(t).item() == 0
     del shape
 
 

@@ -116,9 +116,12 @@ def traffic_for(kernel):
     return k.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(S_sample, D, d):
+def cpu_baseline(S_sample, D, d, S_full=None, H_full=None, G_full=None):
     """The fp64 oracle on a bounded sample of the workload: one query head and
-    its KV head at S_sample tokens, full d_model, causal, forward + backward."""
+    its KV head at S_sample tokens, full d_model, causal, forward + backward.
+    With the full layer's shape, also an extrapolated full-layer time, scaling
+    the measured time by the ratio of total work (causal attention plus
+    projections) -- an estimate, labelled as such."""
     import numpy as np
 
     import oracle
@@ -134,7 +137,14 @@ def cpu_baseline(S_sample, D, d):
     dt = time.perf_counter() - t0
     assert np.isfinite(out["dX"]).all()
     flops = attn_flops(S_sample, 1, d)
+    extra = {}
+    if S_full and H_full and G_full:
+        work = lambda S, H, G: attn_flops(S, H, d) + 8.0 * S * D * (H + 2 * G) * d
+        extra["extrapolated_full_layer_s"] = dt * work(S_full, H_full, G_full) / work(S_sample, 1, 1)
+        extra["extrapolation"] = ("sample time x (full-layer / sample) work, work = 7 d S(S+1) H "
+                                  "+ 8 S D (H + 2G) d; an estimate, not a measurement")
     return {
+        **extra,
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": nthreads,
@@ -326,7 +336,7 @@ def main():
     }
     if not args.skip_cpu_baseline:
         print("bench: timing the oracle on the host (bounded sample)", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(args.cpu_baseline_S, D, d)
+        result["cpu_baseline"] = cpu_baseline(args.cpu_baseline_S, D, d, S, H, G)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result))

@@ -729,6 +729,9 @@ __global__ __launch_bounds__(fw::NT, 1) void attn_fwd_kernel(AttnArgs a) {
 
   // Matrix phase of tile j: O^T += V^T P^T of tile j - 1, then S^T = K Q^T of tile j.
   auto matrix_phase = [&](int j) {
+    // raised priority: the SIMD issues this wave's MFMAs ahead of the partner
+    // wave's softmax arithmetic (2% faster than equal priorities)
+    __builtin_amdgcn_s_setprio(1);
     if (j >= 1 && active(j - 1)) {
       // step k4 outermost so the four accumulators alternate (each still
       // sums k4 = 0..3 in order); V operands requested 3 groups ahead.
@@ -767,6 +770,7 @@ __global__ __launch_bounds__(fw::NT, 1) void attn_fwd_kernel(AttnArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
   // Softmax phase of tile j: mask, lazy running max, P = exp2(S c - m), row sums.
   auto softmax_phase = [&](int j) {

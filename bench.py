@@ -159,8 +159,9 @@ def cpu_baseline(S_sample, D, d, S_full=None, H_full=None, G_full=None):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU's share of the layer; runs on more than one GPU are "
-              "not part of this build (use --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU's share of the layer; the multi-GPU layer (head shards "
+              "with all-to-all exchanges between devices) is not implemented (use --gpus 1)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -346,3 +346,14 @@ def test_out_proj_plan_workspace_and_validation():
                            None) == upipe.UPIPE_ERR_WORKSPACE
     assert L.upipe_bwd_out(outp.handle, *fake[:13], ws + 8, outp.peak_bytes,
                            None) == upipe.UPIPE_ERR_WORKSPACE
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU's share; --gpus N > 1 exits with a message
+    before touching any device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)

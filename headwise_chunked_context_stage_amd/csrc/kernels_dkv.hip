@@ -84,15 +84,20 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
   const int qt0 = a.causal ? static_cast<int>((static_cast<int64_t>(kt) * BN) / BM) : 0;
   const int per_head = nqt - qt0;
   const int niter = (h_hi - h_lo) * per_head;
-  // Loop state, the same in every wave: tile t is query tile qt0 + t % per_head
-  // of head h_lo + t / per_head.  Cursors step through (head, query tile)
+  // Loop state, the same in every wave: tile t is query tile
+  // nqt - 1 - t % per_head of head h_lo + t / per_head.  The query tiles are
+  // walked from the end of the sequence down to the diagonal, so the key
+  // tiles running together on one XCD (32 consecutive ones) all start on the
+  // same query tile and stream the same Q / dO rows at once; walking up from
+  // their diagonals kept 63 tiles (8 MB) in flight per XCD and fetched 11 GB
+  // per launch instead of 7.  Cursors step through (head, query tile)
   // without divisions; slot counters track t % NQ and t % NG.
   struct Cur {
     int h, qt;
   };
   auto adv = [&](Cur& x) {
-    if (++x.qt == nqt) {
-      x.qt = qt0;
+    if (--x.qt < qt0) {
+      x.qt = nqt - 1;
       ++x.h;
     }
   };
@@ -151,7 +156,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
       }
     }
   };
-  Cur cc{h_lo, qt0};  // tile it
+  Cur cc{h_lo, nqt - 1};  // tile it
   Cur nc = cc;        // tile it + 1
   adv(nc);
   int sq = 0, sg = 0;  // it % NQ, it % NG

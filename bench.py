@@ -259,7 +259,7 @@ def main():
         if kind in ("attn_fwd", "attn_dkv", "attn_dq", "proj", "dw", "dx", "oproj", "dout",
                     "dwo") and U >= r:
             ent["tflops"] = work / (avg_ms * 1e-3) / 1e12
-        elif kind in ("bwd_pre",):
+        elif kind in ("bwd_pre", "fill"):
             ent["gbps"] = work / (avg_ms * 1e-3) / 1e9
         kernels[kind] = ent
     attn_ms = sum(kernels.get(k, {}).get("ms_per_step", 0.0)

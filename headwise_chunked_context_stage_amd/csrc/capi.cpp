@@ -614,20 +614,23 @@ int run_bwd(const Plan& p, const BwdIn& in, hipStream_t s, const OutProj* op) {
   }
   UPIPE_TRY(timed(UPIPE_K_FILL, s,
                   [&] { return fill_zero(in.dX, static_cast<size_t>(p.S) * p.D * 4, s); }));
-  if (op) UPIPE_TRY(layer_dwo(p, K, *op, s));  // reads only the inputs dY and O
   if (p.pipeline) {
     UPIPE_TRY(bwd_pipelined(p, K, in, s, hs, E, op));
-    return UPIPE_OK;
+  } else {
+    for (const Stage& st : p.stages) {
+      UPIPE_TRY(stage_projection(p, st, K, in.X, in.Wq, in.Wk, in.Wv, in.ws, s));
+      if (op) UPIPE_TRY(stage_dout(p, st, K, in.ws, *op, s));
+      const AttnArgs a =
+          op ? with_stage_do(p, st, in.ws, bwd_args(p, st, in)) : bwd_args(p, st, in);
+      UPIPE_TRY(timed(UPIPE_K_BWD_PRE, s, [&] { return K.bwd_pre(a, s); }));
+      UPIPE_TRY(timed(UPIPE_K_ATTN_DKV, s, [&] { return K.attn_dkv(a, s); }));
+      UPIPE_TRY(timed(UPIPE_K_ATTN_DQ, s, [&] { return K.attn_dq(a, s); }));
+      UPIPE_TRY(stage_gradients(p, st, K, in, s));
+    }
   }
-  for (const Stage& st : p.stages) {
-    UPIPE_TRY(stage_projection(p, st, K, in.X, in.Wq, in.Wk, in.Wv, in.ws, s));
-    if (op) UPIPE_TRY(stage_dout(p, st, K, in.ws, *op, s));
-    const AttnArgs a = op ? with_stage_do(p, st, in.ws, bwd_args(p, st, in)) : bwd_args(p, st, in);
-    UPIPE_TRY(timed(UPIPE_K_BWD_PRE, s, [&] { return K.bwd_pre(a, s); }));
-    UPIPE_TRY(timed(UPIPE_K_ATTN_DKV, s, [&] { return K.attn_dkv(a, s); }));
-    UPIPE_TRY(timed(UPIPE_K_ATTN_DQ, s, [&] { return K.attn_dq(a, s); }));
-    UPIPE_TRY(stage_gradients(p, st, K, in, s));
-  }
+  // dWo reads only the inputs dY and O; last, on the caller's stream (after
+  // the pipelined path has joined its helper stream)
+  if (op) UPIPE_TRY(layer_dwo(p, K, *op, s));
   return UPIPE_OK;
 }
 

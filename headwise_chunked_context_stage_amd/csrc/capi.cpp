@@ -218,7 +218,7 @@ AttnArgs bwd_args(const Plan& p, const Stage& st, const BwdIn& in) {
 // then its dV.  Every U walks this same sequence, so dX is summed in the same
 // order.
 hipError_t stage_gradients(const Plan& p, const Stage& st, const Kernels& K, const BwdIn& in,
-                           hipStream_t s) {
+                           bool first_stage, hipStream_t s) {
   const size_t e = p.elem();
   const size_t wrows = static_cast<size_t>(p.d) * p.D * e;
   const size_t dwrows = static_cast<size_t>(p.d) * p.D;  // fp32 elements of one head's dW rows
@@ -253,6 +253,7 @@ hipError_t stage_gradients(const Plan& p, const Stage& st, const Kernels& K, con
       t.w[i] = chunks[b + i].w;
       t.dw[i] = chunks[b + i].dw;
     }
+    t.czero = first_stage && b == 0;  // the first dX launch starts the running sum
     hipError_t err = timed(UPIPE_K_DW, s, [&] { return K.dw(in.X, p.S, p.D, p.d, t, s); });
     if (err != hipSuccess) return err;
     err = timed(UPIPE_K_DX, s, [&] { return K.dx(in.dX, p.S, p.D, p.d, t, s); });
@@ -306,17 +307,18 @@ Stage all_heads(const Plan& p) {
 }
 
 // Forward, after the last stage: Y = O Wo^T over all heads, ascending, with
-// Y (zeroed first) as the fp32 running sum.  Summing the stages' O_s Wo_s^T
+// Y as the fp32 running sum (the first launch starts it from zero).  Summing the stages' O_s Wo_s^T
 // into Y one stage at a time gives the same bits (the sum runs through Y in
 // fp32 in the same head order), at 8 x the read-modify-write of Y.
 hipError_t layer_oproj(const Plan& p, const Kernels& K, const void* O, const OutProj& op,
                        hipStream_t s) {
   const int64_t ld = static_cast<int64_t>(p.H) * p.d;
-  hipError_t e = timed(UPIPE_K_FILL, s,
-                       [&] { return fill_zero(op.Y, static_cast<size_t>(p.S) * p.D * 4, s); });
-  if (e != hipSuccess) return e;
+  bool first = true;  // the first launch starts Y's running sum (no zero fill)
   return per_head_chunks(p, all_heads(p), O, op.Wo, nullptr, nullptr, [&](const ChunkTable& t) {
-    return timed(UPIPE_K_OPROJ, s, [&] { return K.oproj(op.Y, p.S, p.D, p.d, t, ld, s); });
+    ChunkTable tt = t;
+    tt.czero = first ? 1 : 0;
+    first = false;
+    return timed(UPIPE_K_OPROJ, s, [&] { return K.oproj(op.Y, p.S, p.D, p.d, tt, ld, s); });
   });
 }
 
@@ -450,7 +452,7 @@ hipError_t bwd_pipelined(const Plan& p, const Kernels& K, const BwdIn& in, hipSt
   hipEvent_t start = E.ev[0], proj_done[2] = {E.ev[1], E.ev[2]}, dq_done[2] = {E.ev[3], E.ev[4]},
              dx_done[2] = {E.ev[5], E.ev[6]};
   const int n = static_cast<int>(p.stages.size());
-  hipError_t e = order(start, s, h);  // dX cleared and inputs written on the caller's stream
+  hipError_t e = order(start, s, h);  // inputs written on the caller's stream
   if (e != hipSuccess) return e;
   e = stage_projection(p, p.stages[0], K, in.X, in.Wq, in.Wk, in.Wv, in.ws, h);
   if (e == hipSuccess) e = hipEventRecord(proj_done[0], h);
@@ -473,7 +475,7 @@ hipError_t bwd_pipelined(const Plan& p, const Kernels& K, const BwdIn& in, hipSt
       if (e == hipSuccess) e = hipEventRecord(proj_done[(i + 1) % 2], h);
     }
     if (e == hipSuccess) e = hipStreamWaitEvent(h, dq_done[i % 2], 0);
-    if (e == hipSuccess) e = stage_gradients(p, st, K, in, h);
+    if (e == hipSuccess) e = stage_gradients(p, st, K, in, i == 0, h);
     if (e == hipSuccess) e = hipEventRecord(dx_done[i % 2], h);
   }
   if (e == hipSuccess) e = hipStreamWaitEvent(s, dx_done[(n - 1) % 2], 0);  // join
@@ -612,12 +614,12 @@ int run_bwd(const Plan& p, const BwdIn& in, hipStream_t s, const OutProj* op) {
     UPIPE_TRY(helper_stream(&hs));
     UPIPE_TRY(E.take());
   }
-  UPIPE_TRY(timed(UPIPE_K_FILL, s,
-                  [&] { return fill_zero(in.dX, static_cast<size_t>(p.S) * p.D * 4, s); }));
+  // dX needs no zero fill: the first stage's dX launch starts the running sum
   if (p.pipeline) {
     UPIPE_TRY(bwd_pipelined(p, K, in, s, hs, E, op));
   } else {
     for (const Stage& st : p.stages) {
+      const bool first_stage = &st == &p.stages.front();
       UPIPE_TRY(stage_projection(p, st, K, in.X, in.Wq, in.Wk, in.Wv, in.ws, s));
       if (op) UPIPE_TRY(stage_dout(p, st, K, in.ws, *op, s));
       const AttnArgs a =
@@ -625,7 +627,7 @@ int run_bwd(const Plan& p, const BwdIn& in, hipStream_t s, const OutProj* op) {
       UPIPE_TRY(timed(UPIPE_K_BWD_PRE, s, [&] { return K.bwd_pre(a, s); }));
       UPIPE_TRY(timed(UPIPE_K_ATTN_DKV, s, [&] { return K.attn_dkv(a, s); }));
       UPIPE_TRY(timed(UPIPE_K_ATTN_DQ, s, [&] { return K.attn_dq(a, s); }));
-      UPIPE_TRY(stage_gradients(p, st, K, in, s));
+      UPIPE_TRY(stage_gradients(p, st, K, in, first_stage, s));
     }
   }
   // dWo reads only the inputs dY and O; last, on the caller's stream (after

@@ -430,7 +430,7 @@ __global__ __launch_bounds__(256, 2) void dx_kernel(float* __restrict__ dX, int6
       for (int i = 0; i < 16; ++i) {
         const int64_t gi = i0 + 64 * wm + 32 * mb + 8 * (i / 4) + 4 * hf + (i % 4);
         const int64_t k = k0 + 64 * wn + 32 * nb + col;
-        acc[mb][nb][i] = gi < S ? dX[gi * D + k] : 0.f;
+        acc[mb][nb][i] = (gi < S && !t.czero) ? dX[gi * D + k] : 0.f;
       }
 
   const int nsteps = t.n * (DH / GK);
@@ -534,7 +534,7 @@ __global__ __launch_bounds__(256, 2) void oproj_kernel(float* __restrict__ Y, in
       for (int i = 0; i < 16; ++i) {
         const int64_t gi = i0 + 64 * wm + 32 * mb + 8 * (i / 4) + 4 * hf + (i % 4);
         const int64_t k = k0 + 64 * wn + 32 * nb + col;
-        acc[mb][nb][i] = gi < S ? Y[gi * D + k] : 0.f;
+        acc[mb][nb][i] = (gi < S && !t.czero) ? Y[gi * D + k] : 0.f;
       }
 
   const int nsteps = t.n * (DH / GK);

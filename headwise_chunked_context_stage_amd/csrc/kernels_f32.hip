@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void dx_kernel(float* __restrict__ dX, int64_t
   const int64_t k = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t i = blockIdx.y;
   if (k >= D || i >= S) return;
-  float acc = dX[i * D + k];
+  float acc = t.czero ? 0.f : dX[i * D + k];
   for (int ch = 0; ch < t.n; ++ch) {
     const float* A = static_cast<const float*>(t.a[ch]);
     const float* W = static_cast<const float*>(t.w[ch]);
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(256) void oproj_kernel(float* __restrict__ Y, int64
   const int64_t k = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t i = blockIdx.y;
   if (k >= D) return;
-  float acc = Y[i * D + k];
+  float acc = t.czero ? 0.f : Y[i * D + k];
   for (int ch = 0; ch < t.n; ++ch) {
     const float* o = static_cast<const float*>(t.a[ch]) + i * ld;
     const float* w = static_cast<const float*>(t.w[ch]) + k * ld;

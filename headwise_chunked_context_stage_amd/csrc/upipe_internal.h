@@ -83,6 +83,8 @@ constexpr int kMaxChunks = 64;
 struct ChunkTable {
   int n;
   uint64_t rot;               // projection: bit i set = rotate chunk i's rows (queries, keys)
+  int czero;                  // dX / Y running sums: this launch starts the sum (its C input is
+                              // zero and the output is not read); same bits as reading zeros
   const void* w[kMaxChunks];  // weight rows [d][D] of this chunk
   void* a[kMaxChunks];        // [S][d] activation / gradient buffer of this chunk
   float* dw[kMaxChunks];      // [d][D] fp32 weight-gradient rows (dW launches only)

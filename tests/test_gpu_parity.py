@@ -94,6 +94,7 @@ def check_against_oracle(out, ref, dtype, inp=None, shape=None, causal=True, rop
     for k in ("O", "LSE", "dX", "dWq", "dWk", "dWv"):
         got = host(out[k])
         floor = np.abs(emu[k].double().numpy() - ref[k])
+        floor_fr = rel_frob(emu[k].double().numpy(), ref[k])
         err = np.abs(got - ref[k])
         fr = rel_frob(got, ref[k])
         say("  %-4s max %.3e mean %.3e relfrob %.3e | floor max %.3e mean %.3e"
@@ -106,7 +107,9 @@ def check_against_oracle(out, ref, dtype, inp=None, shape=None, causal=True, rop
             if np.linalg.norm(ref[k]) == 0.0:  # e.g. dWq at S = 1: dQ of row 0 is exactly 0
                 assert err.max() <= 1e-3, (k, err.max())
             else:
-                assert fr <= 1e-2, (k, fr)
+                # 1e-2 for Gaussian weights (their floor is 3-4e-3); inputs whose
+                # own floor is higher (e.g. identity weights) get 1.25x that floor
+                assert fr <= max(1e-2, 1.25 * floor_fr), (k, fr, floor_fr)
 
 
 def assert_same_bits(a, b, what):
@@ -163,6 +166,30 @@ def test_bf16_matches_oracle_and_is_U_invariant(S, D, H, G):
             assert_same_bits(first, out, "U=%d" % U)
     again = run_layer(shape, "bf16", legal_us(H, G)[-1], inp)
     assert_same_bits(first, again, "rerun")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_attention_core_on_given_qkv(dtype):
+    """The attention kernels on given Q, K, V: with X = [A | B] and selector
+    weights (Wq head 0 = [I 0], head 1 = [0 I], Wk = [I 0], Wv = [0 I]) the
+    projections copy the blocks exactly (Q0 = K = A, Q1 = V = B), so O, LSE
+    and the gradients test the forward, D, dK/dV and dQ kernels on those
+    operands against the oracle."""
+    d = 128 if dtype == "bf16" else 64
+    S, H, G = 1000, 2, 1
+    shape = LayerShape(S=S, D=2 * d, H=H, G=G, d=d)
+    inp = make_inputs(shape, dtype, seed=23, device="cpu")
+    eye, zero = torch.eye(d), torch.zeros(d, d)
+    td = inp["X"].dtype
+    inp["Wq"] = torch.cat([torch.cat([eye, zero], 1), torch.cat([zero, eye], 1)], 0).to(td)
+    inp["Wk"] = torch.cat([eye, zero], 1).to(td)
+    inp["Wv"] = torch.cat([zero, eye], 1).to(td)
+    ref = oracle_full(shape, inp)
+    dev = {k: v.cuda() for k, v in inp.items()}
+    say("attention core on given Q, K, V (%s)" % dtype)
+    out = run_layer(shape, dtype, 1, dev)
+    check_against_oracle(out, ref, dtype, inp, shape)
+    assert_same_bits(out, run_layer(shape, dtype, 2, dev), "U=2")
 
 
 @pytest.mark.parametrize("S", [1, 33, 130])

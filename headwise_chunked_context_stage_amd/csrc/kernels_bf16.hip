@@ -25,9 +25,11 @@
 // from LSE: P = exp(s - LSE), dS = P (dP - D), D = rowsum(dO * O).
 //
 // Rounding points (bf16, round-to-nearest-even): stage Q/K/V, O, P and dS at
-// the MFMA inputs, dQ/dK/dV before the weight/input-gradient GEMMs.  All
-// accumulation is fp32.  No atomics: every output element has one owner and a
-// fixed summation order, so results are identical run to run and for every U.
+// the MFMA inputs, dQ/dK/dV before the weight/input-gradient GEMMs, and (with
+// the output projection) the stage's dO.  The optional rotary embedding is
+// applied in fp32 before the rounding of Q/K and of dQ/dK.  All accumulation
+// is fp32.  No atomics: every output element has one owner and a fixed
+// summation order, so results are identical run to run and for every U.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>

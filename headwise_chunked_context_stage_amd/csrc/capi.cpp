@@ -16,6 +16,7 @@
 // A pipelined plan also uses one helper stream per device: the projections
 // of the next stage and the gradient GEMMs of the current one run there,
 // ordered against the attention kernels on the caller's stream by events.
+#include <atomic>
 #include <cstdio>
 #include <cstring>
 #include <map>
@@ -27,10 +28,6 @@
 
 using namespace upipe;
 
-struct upipe_plan {
-  Plan p;
-};
-
 namespace {
 
 // ------------------------------------------------------------------ timing
@@ -39,7 +36,8 @@ struct TimingRec {
   hipEvent_t a, b;
 };
 std::mutex g_tmu;
-bool g_timing = false;
+// read without the lock on every launch, written under it by upipe_timing_enable
+std::atomic<bool> g_timing{false};
 std::vector<TimingRec> g_recs;
 std::vector<hipEvent_t> g_pool;
 TimingRec g_open{-1, nullptr, nullptr};
@@ -487,8 +485,9 @@ hipError_t bwd_pipelined(const Plan& p, const Kernels& K, const BwdIn& in, hipSt
 namespace upipe {
 
 void timing_begin(int kind, hipStream_t st) {
-  if (!g_timing) return;
+  if (!g_timing.load()) return;
   std::lock_guard<std::mutex> g(g_tmu);
+  if (!g_timing.load()) return;
   g_open.kind = kind;
   g_open.a = take_event();
   g_open.b = take_event();
@@ -496,7 +495,7 @@ void timing_begin(int kind, hipStream_t st) {
 }
 
 void timing_end(int kind, hipStream_t st) {
-  if (!g_timing) return;
+  if (!g_timing.load()) return;
   std::lock_guard<std::mutex> g(g_tmu);
   if (g_open.kind != kind || !g_open.a || !g_open.b) return;
   hipEventRecord(g_open.b, st);
@@ -713,7 +712,7 @@ int upipe_bwd_out(const upipe_plan* h, const void* dY, const void* X, const void
 
 int upipe_timing_enable(int on) {
   std::lock_guard<std::mutex> g(g_tmu);
-  g_timing = on != 0;
+  g_timing.store(on != 0);
   return UPIPE_OK;
 }
 

@@ -178,3 +178,8 @@ void timing_begin(int kind, hipStream_t st);
 void timing_end(int kind, hipStream_t st);
 
 }  // namespace upipe
+
+// The opaque handle of the public header.
+struct upipe_plan {
+  upipe::Plan p;
+};

@@ -251,8 +251,35 @@ def upipe_auto_u(S: int, d_model: int, H: int, G: int, d_head: int, budget_bytes
     return out.value
 
 
+def _check_layout(t, name, shape, dtype):
+    """Refuse a tensor the library would read or write out of bounds: not a
+    tensor, wrong shape or element type, not contiguous."""
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s: expected a torch tensor, got %s" % (name, type(t).__name__))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s: shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise TypeError("%s: dtype %s, expected %s" % (name, t.dtype, dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s: not contiguous" % name)
+
+
+def _check_place(t, name, device, align=16):
+    """... or one in host memory, on another device, or misaligned."""
+    if t.device.type != "cuda" or t.device != device:
+        raise ValueError("%s: on %s, expected a GPU tensor on %s" % (name, t.device, device))
+    if t.numel() and t.data_ptr() % align:
+        raise ValueError("%s: data pointer not %d-byte aligned" % (name, align))
+
+
 class Plan:
-    """Owns a plan handle; the layer's shape and stage size U are fixed here."""
+    """Owns a plan handle; the layer's shape and stage size U are fixed here.
+
+    The methods check every tensor against the plan (shape, element type,
+    contiguity, device, alignment) before calling the library, which itself
+    can only check pointers for null and alignment."""
 
     def __init__(self, S, d_model, H, G, d_head, U, causal=True, dtype="bf16", pipeline=False,
                  rope_theta=0.0, out_proj=False):
@@ -295,16 +322,48 @@ class Plan:
     def stage_info(self, s: int) -> dict:
         return upipe_stage_info(self.handle, s)
 
+    def _check(self, phase, ws, ws_bytes, **tensors):
+        import torch
+
+        S, D, H, G, d = self.S, self.D, self.H, self.G, self.d
+        el = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        f32 = torch.float32
+        expect = {
+            "X": ((S, D), el), "Wq": ((H * d, D), el), "Wk": ((G * d, D), el),
+            "Wv": ((G * d, D), el), "O": ((S, H * d), el), "LSE": ((H, S), f32),
+            "dO": ((S, H * d), el), "dX": ((S, D), f32), "dWq": ((H * d, D), f32),
+            "dWk": ((G * d, D), f32), "dWv": ((G * d, D), f32), "Wo": ((D, H * d), el),
+            "Y": ((S, D), f32), "dY": ((S, D), el), "dWo": ((D, H * d), f32),
+        }
+        for name, t in tensors.items():
+            _check_layout(t, name, *expect[name])
+        if not isinstance(ws, torch.Tensor) or not ws.is_contiguous():
+            raise TypeError("ws: expected a contiguous torch tensor")
+        have = ws.numel() * ws.element_size()
+        need = self.peak_bytes_phase(phase)
+        if (ws_bytes if ws_bytes is not None else have) > have or have < need:
+            raise ValueError("ws: %d bytes, the plan needs %d" % (have, need))
+        device = tensors["X"].device
+        for name, t in tensors.items():
+            _check_place(t, name, device)
+        _check_place(ws, "ws", device, align=256)
+
     def fwd(self, X, Wq, Wk, Wv, O, LSE, ws, ws_bytes=None, stream=None):
+        self._check(0, ws, ws_bytes, X=X, Wq=Wq, Wk=Wk, Wv=Wv, O=O, LSE=LSE)
         upipe_fwd(self.handle, X, Wq, Wk, Wv, O, LSE, ws, ws_bytes, stream)
 
     def bwd(self, dO, X, Wq, Wk, Wv, O, LSE, dX, dWq, dWk, dWv, ws, ws_bytes=None, stream=None):
+        self._check(1, ws, ws_bytes, X=X, Wq=Wq, Wk=Wk, Wv=Wv, O=O, LSE=LSE, dO=dO, dX=dX,
+                    dWq=dWq, dWk=dWk, dWv=dWv)
         upipe_bwd(self.handle, dO, X, Wq, Wk, Wv, O, LSE, dX, dWq, dWk, dWv, ws, ws_bytes, stream)
 
     def fwd_out(self, X, Wq, Wk, Wv, Wo, O, LSE, Y, ws, ws_bytes=None, stream=None):
+        self._check(0, ws, ws_bytes, X=X, Wq=Wq, Wk=Wk, Wv=Wv, Wo=Wo, O=O, LSE=LSE, Y=Y)
         upipe_fwd_out(self.handle, X, Wq, Wk, Wv, Wo, O, LSE, Y, ws, ws_bytes, stream)
 
     def bwd_out(self, dY, X, Wq, Wk, Wv, Wo, O, LSE, dX, dWq, dWk, dWv, dWo, ws, ws_bytes=None,
                 stream=None):
+        self._check(1, ws, ws_bytes, X=X, Wq=Wq, Wk=Wk, Wv=Wv, Wo=Wo, O=O, LSE=LSE, dY=dY, dX=dX,
+                    dWq=dWq, dWk=dWk, dWv=dWv, dWo=dWo)
         upipe_bwd_out(self.handle, dY, X, Wq, Wk, Wv, Wo, O, LSE, dX, dWq, dWk, dWv, dWo, ws,
                       ws_bytes, stream)

@@ -39,7 +39,10 @@
  * enqueues anything; on failure it returns a nonzero code and enqueues
  * nothing.  A failed HIP launch returns UPIPE_ERR_HIP.  Faults that happen on
  * the device surface at the caller's next synchronisation.  No entry point
- * allocates device memory, synchronises the stream or prints.
+ * allocates device memory or prints, and none synchronises the stream, with
+ * two exceptions that exist for benchmarks: upipe_timing_read waits for the
+ * timing events it reads (hipEventSynchronize), and upipe_mfma_ceiling waits
+ * for its own launch.
  */
 #ifndef UPIPE_H
 #define UPIPE_H

@@ -357,3 +357,41 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_binding_rejects_bad_tensors_before_calling_the_library():
+    """Plan.fwd / bwd / fwd_out / bwd_out check every tensor against the plan
+    (shape, element type, contiguity, GPU device, alignment, workspace size)
+    and raise before any pointer reaches the library; a host tensor would
+    otherwise be handed to the kernels as a device address."""
+    import torch
+
+    S, D, H, G, d = 64, 128, 2, 1, 128
+    plan = upipe.Plan(S, D, H, G, d, 1, dtype="bf16", out_proj=True)
+    bf, f32 = torch.bfloat16, torch.float32
+    t = {"X": torch.zeros(S, D, dtype=bf), "Wq": torch.zeros(H * d, D, dtype=bf),
+         "Wk": torch.zeros(G * d, D, dtype=bf), "Wv": torch.zeros(G * d, D, dtype=bf),
+         "O": torch.zeros(S, H * d, dtype=bf), "LSE": torch.zeros(H, S, dtype=f32),
+         "ws": torch.zeros(plan.peak_bytes, dtype=torch.uint8)}
+    with pytest.raises(ValueError, match="GPU tensor"):  # host memory is never passed on
+        plan.fwd(t["X"], t["Wq"], t["Wk"], t["Wv"], t["O"], t["LSE"], t["ws"])
+    with pytest.raises(ValueError, match="shape"):
+        plan.fwd(t["X"][:, :64], t["Wq"], t["Wk"], t["Wv"], t["O"], t["LSE"], t["ws"])
+    with pytest.raises(TypeError, match="dtype"):
+        plan.fwd(t["X"].float(), t["Wq"], t["Wk"], t["Wv"], t["O"], t["LSE"], t["ws"])
+    with pytest.raises(ValueError, match="contiguous"):
+        plan.fwd(t["X"].t().contiguous().t(), t["Wq"], t["Wk"], t["Wv"], t["O"], t["LSE"],
+                 t["ws"])
+    with pytest.raises(ValueError, match="bytes"):
+        plan.fwd(t["X"], t["Wq"], t["Wk"], t["Wv"], t["O"], t["LSE"], t["ws"][:16])
+    with pytest.raises(TypeError, match="torch tensor"):
+        plan.fwd(t["X"].data_ptr(), t["Wq"], t["Wk"], t["Wv"], t["O"], t["LSE"], t["ws"])
+    with pytest.raises(TypeError, match="dtype"):  # LSE is fp32
+        plan.fwd(t["X"], t["Wq"], t["Wk"], t["Wv"], t["O"], t["LSE"].to(bf), t["ws"])
+    with pytest.raises(ValueError, match="shape"):  # dX is [S][D] fp32
+        plan.bwd(t["O"], t["X"], t["Wq"], t["Wk"], t["Wv"], t["O"], t["LSE"],
+                 torch.zeros(S, D + 128, dtype=f32), torch.zeros(H * d, D, dtype=f32),
+                 torch.zeros(G * d, D, dtype=f32), torch.zeros(G * d, D, dtype=f32), t["ws"])
+    with pytest.raises(ValueError, match="shape"):  # Wo is [D][H*d]
+        plan.fwd_out(t["X"], t["Wq"], t["Wk"], t["Wv"], torch.zeros(H * d, D, dtype=bf), t["O"],
+                     t["LSE"], torch.zeros(S, D, dtype=f32), t["ws"])

@@ -34,12 +34,16 @@ def _rotate(x, cs, sn, sign):
 
 
 def bf16_path_emulation(inp, H: int, G: int, d: int, causal: bool = True,
-                        rope_theta: float = 0.0, out_proj: bool = False) -> dict:
+                        rope_theta: float = 0.0, out_proj: bool = False,
+                        round_grads: bool = True) -> dict:
     """With rope_theta > 0, queries and keys are rotated in fp32 before their
     rounding, and dQ, dK take the transposed rotation before theirs.  With
     out_proj, Y = O Wo^T and dWo = dY^T O in fp32 from the stored O, and the
-    attention backward runs with dO = dY Wo rounded to bf16 once."""
+    attention backward runs with dO = dY Wo rounded to bf16 once.
+    round_grads=False keeps dQ, dK, dV in fp32 for the gradient products (a
+    variant the kernels do not implement; it isolates that rounding point)."""
     bf = lambda t: t.to(torch.bfloat16).float()
+    bfg = bf if round_grads else (lambda t: t)
     X, Wq, Wk, Wv = [inp[k].detach().cpu().float() for k in ("X", "Wq", "Wk", "Wv")]
     if out_proj:
         Wo, dY = inp["Wo"].detach().cpu().float(), inp["dY"].detach().cpu().float()
@@ -71,11 +75,11 @@ def bf16_path_emulation(inp, H: int, G: int, d: int, causal: bool = True,
     P = torch.exp(s - lse[..., None])
     dP = go @ V.transpose(1, 2).contiguous()
     dS = P * (dP - Dd)
-    dQ = bf(rot(tau * (bf(dS) @ K), -1))
+    dQ = bfg(rot(tau * (bf(dS) @ K), -1))
     dKh = bf(dS).transpose(1, 2).contiguous() @ Q
     dVh = bf(P).transpose(1, 2).contiguous() @ go
-    dK = bf(rot(tau * dKh.reshape(G, r, S, d).sum(1), -1))
-    dV = bf(dVh.reshape(G, r, S, d).sum(1))
+    dK = bfg(rot(tau * dKh.reshape(G, r, S, d).sum(1), -1))
+    dV = bfg(dVh.reshape(G, r, S, d).sum(1))
     dQf = dQ.transpose(0, 1).reshape(S, H * d)
     dKf = dK.transpose(0, 1).reshape(S, G * d)
     dVf = dV.transpose(0, 1).reshape(S, G * d)

@@ -59,6 +59,12 @@ def _load():
         lib.oracle_dx_tail.restype = i32
         lib.oracle_out_proj.argtypes = [i64, i64, i64, i32, dp, vp, vp, dp, dp, dp, i32]
         lib.oracle_out_proj.restype = i32
+        lib.oracle_forward_qkn.argtypes = [i64, i64, i32, i32, i32, i32, f64, f64, i32, vp, vp, vp,
+                                           vp, vp, vp, dp, dp, i32]
+        lib.oracle_forward_qkn.restype = i32
+        lib.oracle_backward_qkn.argtypes = [i64, i64, i32, i32, i32, i32, f64, f64, i32, vp, vp, vp,
+                                            vp, vp, vp, vp, dp, dp, dp, dp, dp, dp, dp, dp, i32]
+        lib.oracle_backward_qkn.restype = i32
         _lib = lib
     return _lib
 
@@ -93,17 +99,29 @@ def _ptr(a: np.ndarray):
 
 
 def forward(X, Wq, Wk, Wv, H: int, G: int, d: int, causal: bool = True, nthreads: int | None = None,
-            rope_theta: float = 0.0):
+            rope_theta: float = 0.0, q_norm=None, k_norm=None, qk_eps: float = 1e-6):
     """Return (O [S][H*d], LSE [H][S]) in fp64.  rope_theta > 0 applies the
-    rotary embedding to queries and keys (see the C++ header)."""
-    (X, Wq, Wk, Wv), enc = _prep([X, Wq, Wk, Wv])
+    rotary embedding to queries and keys; q_norm and k_norm ([d], same
+    encoding as X) apply QK-norm with qk_eps (see the C++ header)."""
+    norm = q_norm is not None
+    if norm != (k_norm is not None):
+        raise ValueError("QK-norm needs both q_norm and k_norm")
+    arrs, enc = _prep([X, Wq, Wk, Wv] + ([q_norm, k_norm] if norm else []))
+    X, Wq, Wk, Wv = arrs[:4]
     S, D = X.shape
     _check_shapes(S, D, H, G, d, Wq, Wk, Wv)
     O = np.empty((S, H * d), np.float64)
     LSE = np.empty((H, S), np.float64)
-    rc = _load().oracle_forward(S, D, H, G, d, int(bool(causal)), float(rope_theta), enc, _ptr(X),
-                                _ptr(Wq), _ptr(Wk),
-                                _ptr(Wv), _ptr(O), _ptr(LSE), nthreads or default_threads())
+    if norm:
+        _check_norm(arrs[4], arrs[5], d)
+        rc = _load().oracle_forward_qkn(S, D, H, G, d, int(bool(causal)), float(rope_theta),
+                                        float(qk_eps), enc, _ptr(X), _ptr(Wq), _ptr(Wk), _ptr(Wv),
+                                        _ptr(arrs[4]), _ptr(arrs[5]), _ptr(O), _ptr(LSE),
+                                        nthreads or default_threads())
+    else:
+        rc = _load().oracle_forward(S, D, H, G, d, int(bool(causal)), float(rope_theta), enc,
+                                    _ptr(X), _ptr(Wq), _ptr(Wk), _ptr(Wv), _ptr(O), _ptr(LSE),
+                                    nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle_forward rejected the shape")
     return O, LSE
@@ -132,12 +150,18 @@ def forward_rows(X, Wq, Wk, Wv, H: int, G: int, d: int, rows, causal: bool = Tru
 
 
 def backward(X, Wq, Wk, Wv, dO, H: int, G: int, d: int, causal: bool = True,
-             nthreads: int | None = None, rope_theta: float = 0.0):
+             nthreads: int | None = None, rope_theta: float = 0.0, q_norm=None, k_norm=None,
+             qk_eps: float = 1e-6):
     """Forward + backward of L = sum(O * dO).
 
-    Returns a dict of fp64 arrays: O, LSE, dX, dWq, dWk, dWv.
+    Returns a dict of fp64 arrays: O, LSE, dX, dWq, dWk, dWv, and with QK-norm
+    (q_norm, k_norm given) also dq_norm, dk_norm.
     """
-    (X, Wq, Wk, Wv, dO), enc = _prep([X, Wq, Wk, Wv, dO])
+    norm = q_norm is not None
+    if norm != (k_norm is not None):
+        raise ValueError("QK-norm needs both q_norm and k_norm")
+    arrs, enc = _prep([X, Wq, Wk, Wv, dO] + ([q_norm, k_norm] if norm else []))
+    X, Wq, Wk, Wv, dO = arrs[:5]
     S, D = X.shape
     _check_shapes(S, D, H, G, d, Wq, Wk, Wv)
     if dO.shape != (S, H * d):
@@ -150,11 +174,22 @@ def backward(X, Wq, Wk, Wv, dO, H: int, G: int, d: int, causal: bool = True,
         "dWk": np.empty((G * d, D), np.float64),
         "dWv": np.empty((G * d, D), np.float64),
     }
-    rc = _load().oracle_backward(S, D, H, G, d, int(bool(causal)), float(rope_theta), enc, _ptr(X),
-                                 _ptr(Wq), _ptr(Wk),
-                                 _ptr(Wv), _ptr(dO), _ptr(out["O"]), _ptr(out["LSE"]),
-                                 _ptr(out["dX"]), _ptr(out["dWq"]), _ptr(out["dWk"]),
-                                 _ptr(out["dWv"]), nthreads or default_threads())
+    if norm:
+        _check_norm(arrs[5], arrs[6], d)
+        out["dq_norm"] = np.empty(d, np.float64)
+        out["dk_norm"] = np.empty(d, np.float64)
+        rc = _load().oracle_backward_qkn(S, D, H, G, d, int(bool(causal)), float(rope_theta),
+                                         float(qk_eps), enc, _ptr(X), _ptr(Wq), _ptr(Wk), _ptr(Wv),
+                                         _ptr(arrs[5]), _ptr(arrs[6]), _ptr(dO), _ptr(out["O"]),
+                                         _ptr(out["LSE"]), _ptr(out["dX"]), _ptr(out["dWq"]),
+                                         _ptr(out["dWk"]), _ptr(out["dWv"]), _ptr(out["dq_norm"]),
+                                         _ptr(out["dk_norm"]), nthreads or default_threads())
+    else:
+        rc = _load().oracle_backward(S, D, H, G, d, int(bool(causal)), float(rope_theta), enc,
+                                     _ptr(X), _ptr(Wq), _ptr(Wk), _ptr(Wv), _ptr(dO),
+                                     _ptr(out["O"]), _ptr(out["LSE"]), _ptr(out["dX"]),
+                                     _ptr(out["dWq"]), _ptr(out["dWk"]), _ptr(out["dWv"]),
+                                     nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle_backward rejected the shape")
     return out
@@ -227,6 +262,11 @@ def backward_out(X, Wq, Wk, Wv, Wo, dY, H: int, G: int, d: int, causal: bool = T
     out["Y"] = Y
     out["dWo"] = dWo
     return out
+
+
+def _check_norm(gq, gk, d):
+    if gq.shape != (d,) or gk.shape != (d,):
+        raise ValueError("q_norm and k_norm must be [d_head]")
 
 
 def _check_shapes(S, D, H, G, d, Wq, Wk, Wv):

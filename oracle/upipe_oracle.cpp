@@ -37,6 +37,16 @@
 // Values are not rotated.  The backward applies the transposed rotation to
 // the gradients of the rotated rows.
 //
+// QK-norm (optional, the *_qkn entry points; not on the pages, it belongs to
+// the Qwen3 family the pages train): every projected query and key row x of a
+// head (d values) is RMS-normalised and scaled by a weight shared by all
+// heads, gamma_q for queries and gamma_k for keys, before the rotary
+// embedding:
+//   r = 1 / sqrt(sum_c x_c^2 / d + eps),  xhat = x r,  y_c = gamma_c xhat_c.
+// Its backward, for the gradient gy of y:
+//   gx_c = r (gamma_c gy_c - xhat_c (sum_e gamma_e gy_e xhat_e) / d),
+//   dgamma_c = sum over heads and rows of gy_c xhat_c.
+//
 // Output projection (optional, oracle_out_proj; not on the pages' step list,
 // it is the linear map that follows attention in the Llama and Qwen blocks):
 // Y = O Wo^T with Wo [d_model][H*d]; for L = sum(Y * dY) the attention output
@@ -138,18 +148,131 @@ void rotate_rows(double* x, int64_t nrows, const int64_t* pos, const Shape& s, i
   }
 }
 
+// QK-norm weights (decoded), off when empty.
+struct QkNorm {
+  double eps = 0.0;
+  std::vector<double> gq, gk;  // [d] each
+  bool on() const { return !gq.empty(); }
+};
+
+// RMS-normalise rows [0, nrows) of a [nrows][d] block in place and scale by
+// gamma; xhat (the normalised rows) and rinv (1/rms per row) are kept when
+// given, for the backward.
+void normalize_rows(double* x, int64_t nrows, int d, const std::vector<double>& gamma, double eps,
+                    double* xhat, double* rinv) {
+  for (int64_t t = 0; t < nrows; ++t) {
+    double* row = x + t * d;
+    double ss = 0.0;
+    for (int c = 0; c < d; ++c) ss += row[c] * row[c];
+    const double r = 1.0 / std::sqrt(ss / d + eps);
+    if (rinv) rinv[t] = r;
+    for (int c = 0; c < d; ++c) {
+      const double xh = row[c] * r;
+      if (xhat) xhat[t * d + c] = xh;
+      row[c] = gamma[c] * xh;
+    }
+  }
+}
+
+// Backward of normalize_rows: g holds the gradient of the scaled rows on
+// entry and that of the unnormalised rows on exit; dgamma accumulates
+// sum_t g_t * xhat_t (rows ascending).
+void normalize_rows_bwd(double* g, int64_t nrows, int d, const std::vector<double>& gamma,
+                        const double* xhat, const double* rinv, double* dgamma) {
+  for (int64_t t = 0; t < nrows; ++t) {
+    double* row = g + t * d;
+    const double* xh = xhat + t * d;
+    double dot_gx = 0.0;
+    for (int c = 0; c < d; ++c) {
+      dot_gx += gamma[c] * row[c] * xh[c];
+      dgamma[c] += row[c] * xh[c];
+    }
+    for (int c = 0; c < d; ++c) row[c] = rinv[t] * (gamma[c] * row[c] - xh[c] * dot_gx / d);
+  }
+}
+
 // Project rows [0, nrows) of X ([S][D]) through the rows of W that belong to
 // head `head` (W is [nh*d][D], head h = rows h*d .. h*d+d-1):
 // out[i][c] = sum_k X[i][k] * W[head*d + c][k]   (out is [nrows][d]).
+// Each output is one sum over k ascending, as dot() forms it; eight outputs
+// of a row are formed side by side (independent sums, so the same values).
 void project_head(const std::vector<double>& X, const std::vector<double>& W, const Shape& s,
                   int head, int64_t nrows, const int64_t* rows, double* out, int nthreads) {
+  constexpr int CB = 8;
   parallel_for(nrows, nthreads, [&](int64_t t) {
     int64_t i = rows ? rows[t] : t;
     const double* x = &X[static_cast<size_t>(i * s.D)];
-    for (int c = 0; c < s.d; ++c) {
+    int c = 0;
+    for (; c + CB <= s.d; c += CB) {
+      const double* w[CB];
+      double acc[CB];
+      for (int b = 0; b < CB; ++b) {
+        w[b] = &W[static_cast<size_t>((static_cast<int64_t>(head) * s.d + c + b) * s.D)];
+        acc[b] = 0.0;
+      }
+      for (int64_t k = 0; k < s.D; ++k)
+        for (int b = 0; b < CB; ++b) acc[b] += x[k] * w[b][k];
+      for (int b = 0; b < CB; ++b) out[t * s.d + c + b] = acc[b];
+    }
+    for (; c < s.d; ++c) {
       const double* w = &W[static_cast<size_t>((static_cast<int64_t>(head) * s.d + c) * s.D)];
       out[t * s.d + c] = dot(x, w, s.D);
     }
+  });
+}
+
+// dW[row][k] = sum_i grad[i][row] * X[i][k] for the nheads*d rows of a
+// gradient held as [nheads][S][d], each element summed over i ascending.
+// A block of rows is accumulated while X streams by once (the same sums in
+// the same order as one element at a time).
+void weight_grad(const std::vector<double>& grad, const std::vector<double>& X, int64_t S,
+                 int64_t D, int d, int nheads, double* dW, int nthreads) {
+  constexpr int RB = 32;
+  const int64_t nrow = static_cast<int64_t>(nheads) * d;
+  const int64_t nblk = (nrow + RB - 1) / RB;
+  parallel_for(nblk, nthreads, [&](int64_t b) {
+    const int64_t r0 = b * RB, r1 = std::min(nrow, r0 + RB);
+    std::vector<double> acc(static_cast<size_t>((r1 - r0) * D), 0.0);
+    for (int64_t i = 0; i < S; ++i) {
+      const double* x = &X[static_cast<size_t>(i * D)];
+      for (int64_t row = r0; row < r1; ++row) {
+        const int64_t h = row / d, c = row % d;
+        const double g = grad[static_cast<size_t>((h * S + i) * d + c)];
+        double* a = &acc[static_cast<size_t>((row - r0) * D)];
+        for (int64_t k = 0; k < D; ++k) a[k] += g * x[k];
+      }
+    }
+    std::copy(acc.begin(), acc.end(), dW + r0 * D);
+  });
+}
+
+// dX[i][k] = sum_h sum_c dQ_h[i][c] Wq[h*d+c][k]
+//          + sum_g sum_c (dK_g[i][c] Wk[g*d+c][k] + dV_g[i][c] Wv[g*d+c][k]),
+// the terms added in that order (query heads, then per KV head and column the
+// key and value terms as one pair).  Row i of dX is accumulated while the
+// weight rows stream by (the same sums, in the same order, per element).
+// dQ is [H][n][d] and dK, dV are [G][n][d]; rows t of those give dX row t.
+void input_grad(const std::vector<double>& dQ, const std::vector<double>& dK,
+                const std::vector<double>& dV, const std::vector<double>& Wq,
+                const std::vector<double>& Wk, const std::vector<double>& Wv, int64_t n,
+                int64_t D, int H, int G, int d, double* dX, int nthreads) {
+  parallel_for(n, nthreads, [&](int64_t t) {
+    double* acc = dX + t * D;
+    for (int64_t k = 0; k < D; ++k) acc[k] = 0.0;
+    for (int h = 0; h < H; ++h)
+      for (int c = 0; c < d; ++c) {
+        const double g = dQ[static_cast<size_t>((h * n + t) * d + c)];
+        const double* w = &Wq[static_cast<size_t>((static_cast<int64_t>(h) * d + c) * D)];
+        for (int64_t k = 0; k < D; ++k) acc[k] += g * w[k];
+      }
+    for (int g = 0; g < G; ++g)
+      for (int c = 0; c < d; ++c) {
+        const double gk = dK[static_cast<size_t>((g * n + t) * d + c)];
+        const double gv = dV[static_cast<size_t>((g * n + t) * d + c)];
+        const double* wk = &Wk[static_cast<size_t>((static_cast<int64_t>(g) * d + c) * D)];
+        const double* wv = &Wv[static_cast<size_t>((static_cast<int64_t>(g) * d + c) * D)];
+        for (int64_t k = 0; k < D; ++k) acc[k] += gk * wk[k] + gv * wv[k];
+      }
   });
 }
 
@@ -179,14 +302,24 @@ double attend_row(const double* q, const double* K, const double* V, const Shape
 
 extern "C" {
 
-// Forward.  X [S][D], Wq [H*d][D], Wk/Wv [G*d][D] in encoding `enc`.
-// Outputs (fp64, caller-owned): O [S][H*d] (column h*d+c), LSE [H][S].
-// Returns 0, or 1 on an invalid shape.
-int oracle_forward(int64_t S, int64_t D, int H, int G, int d, int causal, double rope_theta,
-                   int enc, const void* Xp, const void* Wqp, const void* Wkp, const void* Wvp,
-                   double* O, double* LSE, int nthreads) {
-  Shape s{S, D, H, G, d, causal, rope_theta};
-  if (!shape_ok(s)) return 1;
+}  // extern "C"
+
+namespace {
+
+QkNorm decode_norm(const void* gqp, const void* gkp, int enc, int d, double eps) {
+  QkNorm n;
+  if (gqp && gkp) {
+    n.eps = eps;
+    n.gq = decode(gqp, enc, d);
+    n.gk = decode(gkp, enc, d);
+  }
+  return n;
+}
+
+int forward_impl(const Shape& s, const QkNorm& nrm, int enc, const void* Xp, const void* Wqp,
+                 const void* Wkp, const void* Wvp, double* O, double* LSE, int nthreads) {
+  const int64_t S = s.S, D = s.D;
+  const int H = s.H, G = s.G, d = s.d;
   std::vector<double> X = decode(Xp, enc, S * D);
   std::vector<double> Wq = decode(Wqp, enc, static_cast<int64_t>(H) * d * D);
   std::vector<double> Wk = decode(Wkp, enc, static_cast<int64_t>(G) * d * D);
@@ -196,9 +329,11 @@ int oracle_forward(int64_t S, int64_t D, int H, int G, int d, int causal, double
   for (int g = 0; g < G; ++g) {
     project_head(X, Wk, s, g, S, nullptr, K.data(), nthreads);
     project_head(X, Wv, s, g, S, nullptr, V.data(), nthreads);
+    if (nrm.on()) normalize_rows(K.data(), S, d, nrm.gk, nrm.eps, nullptr, nullptr);
     rotate_rows(K.data(), S, nullptr, s, +1);
     for (int h = g * s.r(); h < (g + 1) * s.r(); ++h) {
       project_head(X, Wq, s, h, S, nullptr, Q.data(), nthreads);
+      if (nrm.on()) normalize_rows(Q.data(), S, d, nrm.gq, nrm.eps, nullptr, nullptr);
       rotate_rows(Q.data(), S, nullptr, s, +1);
       parallel_for(S, nthreads, [&](int64_t i) {
         std::vector<double> scores;
@@ -210,6 +345,32 @@ int oracle_forward(int64_t S, int64_t D, int H, int G, int d, int causal, double
     }
   }
   return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Forward.  X [S][D], Wq [H*d][D], Wk/Wv [G*d][D] in encoding `enc`.
+// Outputs (fp64, caller-owned): O [S][H*d] (column h*d+c), LSE [H][S].
+// Returns 0, or 1 on an invalid shape.
+int oracle_forward(int64_t S, int64_t D, int H, int G, int d, int causal, double rope_theta,
+                   int enc, const void* Xp, const void* Wqp, const void* Wkp, const void* Wvp,
+                   double* O, double* LSE, int nthreads) {
+  Shape s{S, D, H, G, d, causal, rope_theta};
+  if (!shape_ok(s)) return 1;
+  return forward_impl(s, QkNorm(), enc, Xp, Wqp, Wkp, Wvp, O, LSE, nthreads);
+}
+
+// Forward with QK-norm: gamma_q, gamma_k [d] in encoding `enc`, eps >= 0.
+int oracle_forward_qkn(int64_t S, int64_t D, int H, int G, int d, int causal, double rope_theta,
+                       double eps, int enc, const void* Xp, const void* Wqp, const void* Wkp,
+                       const void* Wvp, const void* gqp, const void* gkp, double* O, double* LSE,
+                       int nthreads) {
+  Shape s{S, D, H, G, d, causal, rope_theta};
+  if (!shape_ok(s) || !gqp || !gkp || !(eps >= 0.0)) return 1;
+  return forward_impl(s, decode_norm(gqp, gkp, enc, d, eps), enc, Xp, Wqp, Wkp, Wvp, O, LSE,
+                      nthreads);
 }
 
 // Forward on a subset of query rows and of query heads [h0, h1).  rows[0..nrows)
@@ -274,12 +435,16 @@ int oracle_forward_rows(int64_t S, int64_t D, int H, int G, int d, int causal,
 // Row quantities (dQ) are computed by a pass over query rows, column
 // quantities (dK, dV) by a pass over key rows; each recomputes P and dP from
 // Q, K, V, LSE and dO, so no two threads ever write the same element.
-int oracle_backward(int64_t S, int64_t D, int H, int G, int d, int causal, double rope_theta,
-                    int enc, const void* Xp, const void* Wqp, const void* Wkp, const void* Wvp,
-                    const void* dOp, double* O, double* LSE, double* dX, double* dWq,
-                    double* dWk, double* dWv, int nthreads) {
-  Shape s{S, D, H, G, d, causal, rope_theta};
-  if (!shape_ok(s)) return 1;
+}  // extern "C"
+
+namespace {
+
+int backward_impl(const Shape& s, const QkNorm& nrm, int enc, const void* Xp, const void* Wqp,
+                  const void* Wkp, const void* Wvp, const void* dOp, double* O, double* LSE,
+                  double* dX, double* dWq, double* dWk, double* dWv, double* dgq, double* dgk,
+                  int nthreads) {
+  const int64_t S = s.S, D = s.D;
+  const int H = s.H, G = s.G, d = s.d, causal = s.causal;
   const int64_t Hd = static_cast<int64_t>(H) * d;
   const int r = s.r();
   std::vector<double> X = decode(Xp, enc, S * D);
@@ -291,14 +456,24 @@ int oracle_backward(int64_t S, int64_t D, int H, int G, int d, int causal, doubl
   // Projections for every head (the oracle is not memory-frugal).
   std::vector<double> Q(static_cast<size_t>(H * S * d)), K(static_cast<size_t>(G * S * d)),
       V(static_cast<size_t>(G * S * d));
-  // Q and K are kept rotated (when rope_theta > 0): the attention sees them so.
+  // Q and K are kept normalised (QK-norm) and rotated (when rope_theta > 0):
+  // the attention sees them so.
+  std::vector<double> xq, rq, xk, rk;  // QK-norm: normalised rows and 1/rms, for the backward
+  if (nrm.on()) {
+    xq.resize(static_cast<size_t>(H * S * d));
+    rq.resize(static_cast<size_t>(H * S));
+    xk.resize(static_cast<size_t>(G * S * d));
+    rk.resize(static_cast<size_t>(G * S));
+  }
   for (int h = 0; h < H; ++h) {
     project_head(X, Wq, s, h, S, nullptr, &Q[h * S * d], nthreads);
+    if (nrm.on()) normalize_rows(&Q[h * S * d], S, d, nrm.gq, nrm.eps, &xq[h * S * d], &rq[h * S]);
     rotate_rows(&Q[h * S * d], S, nullptr, s, +1);
   }
   for (int g = 0; g < G; ++g) {
     project_head(X, Wk, s, g, S, nullptr, &K[g * S * d], nthreads);
     project_head(X, Wv, s, g, S, nullptr, &V[g * S * d], nthreads);
+    if (nrm.on()) normalize_rows(&K[g * S * d], S, d, nrm.gk, nrm.eps, &xk[g * S * d], &rk[g * S]);
     rotate_rows(&K[g * S * d], S, nullptr, s, +1);
   }
 
@@ -368,36 +543,51 @@ int oracle_backward(int64_t S, int64_t D, int H, int G, int d, int causal, doubl
   // them through the transposed rotation.
   for (int h = 0; h < H; ++h) rotate_rows(&dQ[h * S * d], S, nullptr, s, -1);
   for (int g = 0; g < G; ++g) rotate_rows(&dK[g * S * d], S, nullptr, s, -1);
+  // QK-norm: then back through the normalisation (heads ascending, rows
+  // ascending in the weight gradients).
+  if (nrm.on()) {
+    for (int c = 0; c < d; ++c) dgq[c] = dgk[c] = 0.0;
+    for (int h = 0; h < H; ++h)
+      normalize_rows_bwd(&dQ[h * S * d], S, d, nrm.gq, &xq[h * S * d], &rq[h * S], dgq);
+    for (int g = 0; g < G; ++g)
+      normalize_rows_bwd(&dK[g * S * d], S, d, nrm.gk, &xk[g * S * d], &rk[g * S], dgk);
+  }
 
   // Weight gradients: dW[row][k] = sum_i grad[i][row] * X[i][k].
-  auto weight_grad = [&](const std::vector<double>& grad, int nheads, double* dW) {
-    parallel_for(static_cast<int64_t>(nheads) * d, nthreads, [&](int64_t row) {
-      const int64_t h = row / d, c = row % d;
-      for (int64_t k = 0; k < D; ++k) {
-        double acc = 0.0;
-        for (int64_t i = 0; i < S; ++i) acc += grad[(h * S + i) * d + c] * X[i * D + k];
-        dW[row * D + k] = acc;
-      }
-    });
-  };
-  weight_grad(dQ, H, dWq);
-  weight_grad(dK, G, dWk);
-  weight_grad(dV, G, dWv);
+  weight_grad(dQ, X, S, D, d, H, dWq, nthreads);
+  weight_grad(dK, X, S, D, d, G, dWk, nthreads);
+  weight_grad(dV, X, S, D, d, G, dWv, nthreads);
 
   // Input gradient: dX[i][k] = sum over projected rows of grad * W.
-  parallel_for(S, nthreads, [&](int64_t i) {
-    for (int64_t k = 0; k < D; ++k) {
-      double acc = 0.0;
-      for (int h = 0; h < H; ++h)
-        for (int c = 0; c < d; ++c) acc += dQ[(h * S + i) * d + c] * Wq[(h * d + c) * D + k];
-      for (int g = 0; g < G; ++g)
-        for (int c = 0; c < d; ++c)
-          acc += dK[(g * S + i) * d + c] * Wk[(g * d + c) * D + k] +
-                 dV[(g * S + i) * d + c] * Wv[(g * d + c) * D + k];
-      dX[i * D + k] = acc;
-    }
-  });
+  input_grad(dQ, dK, dV, Wq, Wk, Wv, S, D, H, G, d, dX, nthreads);
   return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int oracle_backward(int64_t S, int64_t D, int H, int G, int d, int causal, double rope_theta,
+                    int enc, const void* Xp, const void* Wqp, const void* Wkp, const void* Wvp,
+                    const void* dOp, double* O, double* LSE, double* dX, double* dWq,
+                    double* dWk, double* dWv, int nthreads) {
+  Shape s{S, D, H, G, d, causal, rope_theta};
+  if (!shape_ok(s)) return 1;
+  return backward_impl(s, QkNorm(), enc, Xp, Wqp, Wkp, Wvp, dOp, O, LSE, dX, dWq, dWk, dWv,
+                       nullptr, nullptr, nthreads);
+}
+
+// Backward with QK-norm (gamma_q, gamma_k [d] in encoding `enc`, eps >= 0);
+// also writes dgamma_q, dgamma_k [d] (fp64).
+int oracle_backward_qkn(int64_t S, int64_t D, int H, int G, int d, int causal, double rope_theta,
+                        double eps, int enc, const void* Xp, const void* Wqp, const void* Wkp,
+                        const void* Wvp, const void* gqp, const void* gkp, const void* dOp,
+                        double* O, double* LSE, double* dX, double* dWq, double* dWk, double* dWv,
+                        double* dgq, double* dgk, int nthreads) {
+  Shape s{S, D, H, G, d, causal, rope_theta};
+  if (!shape_ok(s) || !gqp || !gkp || !dgq || !dgk || !(eps >= 0.0)) return 1;
+  return backward_impl(s, decode_norm(gqp, gkp, enc, d, eps), enc, Xp, Wqp, Wkp, Wvp, dOp, O,
+                       LSE, dX, dWq, dWk, dWv, dgq, dgk, nthreads);
 }
 
 // Input gradient at the last rows [t0, S) of a causal layer, from the same
@@ -485,18 +675,7 @@ int oracle_dx_tail(int64_t S, int64_t D, int H, int G, int d, double rope_theta,
   }
   for (int h = 0; h < H; ++h) rotate_rows(&dQ[h * n * d], n, rows.data(), s, -1);
   for (int g = 0; g < G; ++g) rotate_rows(&dK[g * n * d], n, rows.data(), s, -1);
-  parallel_for(n, nthreads, [&](int64_t t) {
-    for (int64_t k = 0; k < D; ++k) {
-      double acc = 0.0;
-      for (int h = 0; h < H; ++h)
-        for (int c = 0; c < d; ++c) acc += dQ[(h * n + t) * d + c] * Wq[(h * d + c) * D + k];
-      for (int g = 0; g < G; ++g)
-        for (int c = 0; c < d; ++c)
-          acc += dK[(g * n + t) * d + c] * Wk[(g * d + c) * D + k] +
-                 dV[(g * n + t) * d + c] * Wv[(g * d + c) * D + k];
-      dXt[t * D + k] = acc;
-    }
-  });
+  input_grad(dQ, dK, dV, Wq, Wk, Wv, n, D, H, G, d, dXt, nthreads);
   return 0;
 }
 

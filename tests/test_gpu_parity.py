@@ -101,9 +101,22 @@ def check_against_oracle(out, ref, dtype, inp=None, shape=None, causal=True, rop
             % (k, err.max(), err.mean(), fr, floor.max(), floor.mean()))
         assert err.max() <= 1.25 * floor.max() + 1e-3, (k, "max above the bf16 floor")
         assert err.mean() <= 1.25 * floor.mean() + 1e-5, (k, "mean above the bf16 floor")
-        if k.startswith("d"):
+        if k == "dX":
+            # the literal mean bound, wherever the bf16 floor itself allows it;
+            # at S = 1 the floor's own mean is 2.06e-3 (dV of a group is the
+            # sum of its heads' dO, rounded to bf16), a recorded deviation
+            if 1.25 * floor.mean() <= 2e-3:
+                assert err.mean() <= 2e-3, (k, "mean above 2e-3", err.mean())
+            else:
+                say("       literal mean bound: the floor (%.3e) is above it at this shape"
+                    % floor.mean())
+        if k.startswith("dW"):
+            # a recorded deviation: the bf16 floor of the weight gradients is
+            # above the literal bounds for any implementation (bf16 storage of
+            # Q, K, V, O alone puts their mean error near 1e-2)
             say("       literal bounds (2e-2 / 2e-3): %s" %
-                ("met" if err.max() <= 2e-2 and err.mean() <= 2e-3 else "not met (floor)"))
+                ("met" if err.max() <= 2e-2 and err.mean() <= 2e-3 else
+                 "not met -- known deviation, floor max %.3e mean %.3e" % (floor.max(), floor.mean())))
             if np.linalg.norm(ref[k]) == 0.0:  # e.g. dWq at S = 1: dQ of row 0 is exactly 0
                 assert err.max() <= 1e-3, (k, err.max())
             else:
@@ -587,21 +600,83 @@ def test_full_size_qwen32b_s64k_U_invariant_and_peak_bytes():
     assert 8 * ws[8][0] == ws[64][0]
 
 
+@pytest.mark.timeout(900)
 def test_full_size_llama8b_share_s1m():
     """One GPU's share of Llama3-8B at S = 1M tokens (4 query heads + 1 KV
-    head, U = 1): forward rows against the oracle (early rows of all heads
-    and rows near 64K), the scaling identities, finite outputs and the
+    head, U = 1): forward rows of all heads against the oracle, early and
+    past 2^19 tokens (where element offsets of X [S][4096] and O pass 2^31),
+    up to the last row; dX of the last 8 tokens (offsets near 2^32) against
+    the oracle's exact tail; the scaling identities, finite outputs and the
     measured workspace."""
     cfg = CONFIGS["llama8b_share_s1m"]
     shape = cfg["shape"]
+    S = shape.S
     inp = make_inputs(shape, "bf16", seed=0, device="cuda")
     say("llama8b share S=1048576 U=1")
     out, ws = run_measured(shape, 1, inp)
     say("  workspace fwd %d bwd %d bytes" % ws)
     assert ws[0] == 2 * shape.S * shape.d * 3
-    sampled_rows_check(shape, inp, out, [0, 1, 1023, 4095], [65535, 65534, 32767], (0, 4))
+    sampled_rows_check(shape, inp, out,
+                       [0, 1, 1023, 4095, 32767, 65535, (1 << 19) + 3, 3 << 18, S - 4096,
+                        S - 2, S - 1], [], None)
+    dx_tail_check(shape, inp, out, 8)
     e = identities(out, inp)
     say("  identities %.2e %.2e %.2e" % e)
     assert max(e) < 1e-4
     for k in OUTS:
         assert torch.isfinite(out[k]).all(), k
+
+
+# ---------------------------------------------------------------- full d_model sub-layer
+def test_full_dmodel_sublayer_s32k_every_output_against_oracle():
+    """One KV group of the Llama3-8B shape at full d_model and S = 32768 (4
+    query heads, 1 KV head, D = 4096): every output against the fp64 oracle's
+    full backward, stored by tests/golden/make_sublayer_s32k.py -- sampled
+    rows of dWq, dWk, dWv element by element (each a sum over all 32768
+    tokens through the split contraction of the weight-gradient kernel), dX,
+    O and LSE at rows across the sequence -- for every legal U, bit-identical
+    across U."""
+    import os
+    import sys
+
+    golden = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    sys.path.insert(0, golden)
+    from make_sublayer_s32k import input_hash
+
+    fx = np.load(os.path.join(golden, "sublayer_s32k.npz"))
+    S, D, H, G, d = (int(v) for v in fx["shape"])
+    shape = LayerShape(S=S, D=D, H=H, G=G, d=d)
+    cpu_inp = make_inputs(shape, "bf16", seed=int(fx["seed"]), device="cpu")
+    assert input_hash(cpu_inp) == str(fx["input_sha256"]), "inputs differ from the fixture's"
+    inp = {k: v.cuda() for k, v in cpu_inp.items()}
+    del cpu_inp
+    rows = fx["token_rows"]
+    first = None
+    for U in legal_us(H, G):
+        say("sub-layer S=%d D=%d H=%d G=%d U=%d" % (S, D, H, G, U))
+        out = run_layer(shape, "bf16", U, inp)
+        if first is not None:
+            assert_same_bits(first, out, "U=%d" % U)
+            continue
+        first = out
+        compare("O", host(out["O"][rows]), fx["O"].astype(np.float64), 2e-2, 2e-3)
+        compare("LSE", host(out["LSE"][:, rows]), fx["LSE"].astype(np.float64), 2e-2, 2e-3)
+        got = host(out["dX"][rows])
+        ref = fx["dX"].astype(np.float64)
+        err = np.abs(got - ref)
+        say("  dX   max %.3e mean %.3e relfrob %.3e" % (err.max(), err.mean(), rel_frob(got, ref)))
+        assert err.mean() <= 2e-3 and rel_frob(got, ref) <= 1e-2 and err.max() <= 5e-2
+        for k, rk in (("dWq", "dwq_rows"), ("dWk", "dwk_rows"), ("dWv", "dwv_rows")):
+            got = host(out[k][fx[rk]])
+            ref = fx[k].astype(np.float64)
+            err = np.abs(got - ref)
+            fr = rel_frob(got, ref)
+            say("  %-4s max %.3e mean %.3e relfrob %.3e (literal bounds: known deviation)"
+                % (k, err.max(), err.mean(), fr))
+            assert fr <= 1e-2, (k, fr)
+            for i in range(ref.shape[0]):  # row by row, and no single element far off
+                rms = float(np.sqrt(np.mean(ref[i] ** 2)))
+                assert rel_frob(got[i], ref[i]) <= 1.5e-2, (k, i, rel_frob(got[i], ref[i]))
+                assert err[i].max() <= 0.1 * rms, (k, i, err[i].max(), rms)
+    del first
+    torch.cuda.empty_cache()

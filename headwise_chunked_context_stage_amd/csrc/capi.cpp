@@ -57,6 +57,9 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 bool ptr_ok(const void* p) { return p != nullptr && aligned(p, 16); }
 
+// A pointer the plan uses must be valid, one it does not use must be null.
+bool need(const void* p, bool used) { return used ? ptr_ok(p) : p == nullptr; }
+
 char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
 const char* at(const void* base, size_t off) { return static_cast<const char*>(base) + off; }
 
@@ -92,10 +95,20 @@ struct Kernels {
 // producing kernel (the bf16 kernels apply it in their epilogues, before
 // rounding).  fp32 storage is exact, so both orders give the same values.
 hipError_t f32_proj(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t,
-                    const Rope& rope, hipStream_t st) {
+                    const Rope& rope, const NormArgs& nrm, hipStream_t st) {
   hipError_t e = f32::proj(X, S, D, d, t, st);
-  for (int i = 0; i < t.n && e == hipSuccess; ++i)
-    if ((t.rot >> i) & 1) e = f32::rope(static_cast<float*>(t.a[i]), 1, S, d, rope, +1, st);
+  for (int i = 0; i < t.n && e == hipSuccess; ++i) {
+    const int k = t.nkind[i];
+    if (k) {  // QK-norm, then the rotary embedding, as the bf16 epilogue does
+      const int64_t idx = t.nidx[i];
+      e = norm::fwd_f32(static_cast<float*>(t.a[i]), 1, S, d,
+                        static_cast<const float*>(nrm.gamma[k - 1]), nrm.eps,
+                        nrm.store ? nrm.xh[k - 1] + idx * S * d : nullptr,
+                        nrm.store ? nrm.ri[k - 1] + idx * S : nullptr, st);
+    }
+    if (e == hipSuccess && ((t.rot >> i) & 1))
+      e = f32::rope(static_cast<float*>(t.a[i]), 1, S, d, rope, +1, st);
+  }
   return e;
 }
 
@@ -124,9 +137,22 @@ Kernels kernels_for(int dtype) {
 
 // Project the stage's query heads (and its KV heads when it opens their group)
 // into the stage buffers.  Chunks: one per head, d rows of the weight each.
+// QK-norm weights and their gradients for one call (null when the plan has
+// no QK-norm; the gradients only in the backward).
+struct NormIn {
+  const void* gq;
+  const void* gk;
+  float* dgq;
+  float* dgk;
+};
+
+// Project the stage's query heads (and its KV heads when it opens their group)
+// into the stage buffers.  Chunks: one per head, d rows of the weight each.
+// With QK-norm, queries and keys are normalised (and with `store` their
+// normalised rows and 1/rms kept in the workspace for the backward).
 hipError_t stage_projection(const Plan& p, const Stage& st, const Kernels& K, const void* X,
                             const void* Wq, const void* Wk, const void* Wv, void* ws,
-                            hipStream_t s) {
+                            hipStream_t s, const NormIn& nin, bool store) {
   const size_t e = p.elem();
   const size_t wrows = static_cast<size_t>(p.d) * p.D * e;  // bytes of one head's weight rows
   const size_t hbuf = static_cast<size_t>(p.S) * p.d * e;   // bytes of one head's [S][d] buffer
@@ -134,15 +160,31 @@ hipError_t stage_projection(const Plan& p, const Stage& st, const Kernels& K, co
     const void* w;
     void* a;
     bool rotate;  // queries and keys take the rotary embedding, values do not
+    int kind, idx;  // QK-norm: 1 = query head idx, 2 = key head idx, 0 = none
   };
   const bool rope = p.rope.on != 0;
+  const int qn = p.qk_norm ? 1 : 0, kn = p.qk_norm ? 2 : 0;
   std::vector<Job> jobs;
   for (int h = 0; h < st.nq; ++h)
-    jobs.push_back({at(Wq, (st.q0 + h) * wrows), at(ws, p.ws.q[st.slot] + h * hbuf), rope});
+    jobs.push_back({at(Wq, (st.q0 + h) * wrows), at(ws, p.ws.q[st.slot] + h * hbuf), rope, qn, h});
   if (st.load) {
     for (int g = 0; g < st.nkv; ++g) {
-      jobs.push_back({at(Wk, (st.kv0 + g) * wrows), at(ws, p.ws.k[st.kvslot] + g * hbuf), rope});
-      jobs.push_back({at(Wv, (st.kv0 + g) * wrows), at(ws, p.ws.v[st.kvslot] + g * hbuf), false});
+      jobs.push_back({at(Wk, (st.kv0 + g) * wrows), at(ws, p.ws.k[st.kvslot] + g * hbuf), rope, kn, g});
+      jobs.push_back({at(Wv, (st.kv0 + g) * wrows), at(ws, p.ws.v[st.kvslot] + g * hbuf), false, 0, 0});
+    }
+  }
+  NormArgs nrm;
+  std::memset(&nrm, 0, sizeof(nrm));
+  if (p.qk_norm) {
+    nrm.gamma[0] = nin.gq;
+    nrm.gamma[1] = nin.gk;
+    nrm.eps = static_cast<float>(p.qk_eps);
+    nrm.store = store ? 1 : 0;
+    if (store) {
+      nrm.xh[0] = reinterpret_cast<float*>(at(ws, p.ws.xq[st.slot]));
+      nrm.ri[0] = reinterpret_cast<float*>(at(ws, p.ws.rq[st.slot]));
+      nrm.xh[1] = reinterpret_cast<float*>(at(ws, p.ws.xk[st.kvslot]));
+      nrm.ri[1] = reinterpret_cast<float*>(at(ws, p.ws.rk[st.kvslot]));
     }
   }
   for (size_t b = 0; b < jobs.size(); b += kMaxChunks) {
@@ -153,9 +195,11 @@ hipError_t stage_projection(const Plan& p, const Stage& st, const Kernels& K, co
       t.w[i] = jobs[b + i].w;
       t.a[i] = jobs[b + i].a;
       if (jobs[b + i].rotate) t.rot |= uint64_t(1) << i;
+      t.nkind[i] = static_cast<unsigned char>(jobs[b + i].kind);
+      t.nidx[i] = static_cast<unsigned char>(jobs[b + i].idx);
     }
     hipError_t err =
-        timed(UPIPE_K_PROJ, s, [&] { return K.proj(X, p.S, p.D, p.d, t, p.rope, s); });
+        timed(UPIPE_K_PROJ, s, [&] { return K.proj(X, p.S, p.D, p.d, t, p.rope, nrm, s); });
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
@@ -208,7 +252,38 @@ AttnArgs bwd_args(const Plan& p, const Stage& st, const BwdIn& in) {
     a.dk_acc = reinterpret_cast<float*>(at(in.ws, p.ws.dk_acc));
     a.dv_acc = reinterpret_cast<float*>(at(in.ws, p.ws.dv_acc));
   }
+  if (p.qk_norm && p.dtype == UPIPE_BF16) {  // fp32 gradients for the normalisation's backward
+    a.dq32 = reinterpret_cast<float*>(at(in.ws, p.ws.gq32[st.slot]));
+    a.dk32 = reinterpret_cast<float*>(at(in.ws, p.ws.gk32[st.kvslot]));
+  }
   return a;
+}
+
+// QK-norm backward of a stage, after its dK/dV and dQ: the gradients of the
+// normalised query rows (and, when the stage completes its KV heads, key
+// rows) go back through the normalisation into the buffers the gradient
+// GEMMs read, and their per-block products are added into dgamma in order.
+hipError_t stage_norm_bwd(const Plan& p, const Stage& st, const BwdIn& in, const NormIn& nin,
+                          bool first_q, bool first_k, hipStream_t s) {
+  const bool bf = p.dtype == UPIPE_BF16;
+  auto f = [&](size_t off) { return reinterpret_cast<float*>(at(in.ws, off)); };
+  hipError_t e = timed(UPIPE_K_NORM, s, [&] {
+    const float* g = bf ? f(p.ws.gq32[st.slot]) : f(p.ws.dq[st.slot]);
+    hipError_t r = norm::bwd(g, f(p.ws.xq[st.slot]), f(p.ws.rq[st.slot]), nin.gq, bf ? 1 : 0,
+                             at(in.ws, p.ws.dq[st.slot]), bf ? 1 : 0, f(p.ws.pq), st.nq, p.S, p.d,
+                             s);
+    if (r == hipSuccess) r = norm::gamma_sum(nin.dgq, f(p.ws.pq), st.nq, p.S, p.d, first_q, s);
+    return r;
+  });
+  if (e != hipSuccess || !st.done) return e;
+  return timed(UPIPE_K_NORM, s, [&] {
+    const float* g = bf ? f(p.ws.gk32[st.kvslot]) : f(p.ws.dk[st.kvslot]);
+    hipError_t r = norm::bwd(g, f(p.ws.xk[st.kvslot]), f(p.ws.rk[st.kvslot]), nin.gk, bf ? 1 : 0,
+                             at(in.ws, p.ws.dk[st.kvslot]), bf ? 1 : 0, f(p.ws.pk), st.nkv, p.S,
+                             p.d, s);
+    if (r == hipSuccess) r = norm::gamma_sum(nin.dgk, f(p.ws.pk), st.nkv, p.S, p.d, first_k, s);
+    return r;
+  });
 }
 
 // Weight and input gradients of one stage, in the one global order used for
@@ -414,12 +489,12 @@ hipError_t order(hipEvent_t ev, hipStream_t signaller, hipStream_t waiter) {
 // s mod 2, so the projection of s + 1 waits only for the attention of s - 1.
 hipError_t fwd_pipelined(const Plan& p, const Kernels& K, const void* X, const void* Wq,
                          const void* Wk, const void* Wv, void* O, float* LSE, void* ws,
-                         hipStream_t s, hipStream_t h, SyncEvents& E) {
+                         hipStream_t s, hipStream_t h, SyncEvents& E, const NormIn& nin) {
   hipEvent_t start = E.ev[0], proj_done[2] = {E.ev[1], E.ev[2]}, attn_done[2] = {E.ev[3], E.ev[4]};
   const int n = static_cast<int>(p.stages.size());
   hipError_t e = order(start, s, h);  // inputs written on the caller's stream
   if (e != hipSuccess) return e;
-  e = stage_projection(p, p.stages[0], K, X, Wq, Wk, Wv, ws, h);
+  e = stage_projection(p, p.stages[0], K, X, Wq, Wk, Wv, ws, h, nin, false);
   if (e == hipSuccess) e = hipEventRecord(proj_done[0], h);
   for (int i = 0; i < n && e == hipSuccess; ++i) {
     const Stage& st = p.stages[i];
@@ -433,7 +508,7 @@ hipError_t fwd_pipelined(const Plan& p, const Kernels& K, const void* X, const v
     if (e != hipSuccess || i + 1 == n) break;
     // copy (i + 1) mod 2 was last read by the attention of stage i - 1
     if (i >= 1) e = hipStreamWaitEvent(h, attn_done[(i - 1) % 2], 0);
-    if (e == hipSuccess) e = stage_projection(p, p.stages[i + 1], K, X, Wq, Wk, Wv, ws, h);
+    if (e == hipSuccess) e = stage_projection(p, p.stages[i + 1], K, X, Wq, Wk, Wv, ws, h, nin, false);
     if (e == hipSuccess) e = hipEventRecord(proj_done[(i + 1) % 2], h);
   }
   return e;
@@ -446,14 +521,15 @@ hipError_t fwd_pipelined(const Plan& p, const Kernels& K, const void* X, const v
 // s mod 2 of dQ once dX of stage s - 2 has.  dK/dV use the K/V copy of their
 // group; the group two loads back finished its dX by stage s - 2 as well.
 hipError_t bwd_pipelined(const Plan& p, const Kernels& K, const BwdIn& in, hipStream_t s,
-                         hipStream_t h, SyncEvents& E, const OutProj* op) {
+                         hipStream_t h, SyncEvents& E, const OutProj* op, const NormIn& nin) {
   hipEvent_t start = E.ev[0], proj_done[2] = {E.ev[1], E.ev[2]}, dq_done[2] = {E.ev[3], E.ev[4]},
              dx_done[2] = {E.ev[5], E.ev[6]};
   const int n = static_cast<int>(p.stages.size());
   hipError_t e = order(start, s, h);  // inputs written on the caller's stream
   if (e != hipSuccess) return e;
-  e = stage_projection(p, p.stages[0], K, in.X, in.Wq, in.Wk, in.Wv, in.ws, h);
+  e = stage_projection(p, p.stages[0], K, in.X, in.Wq, in.Wk, in.Wv, in.ws, h, nin, true);
   if (e == hipSuccess) e = hipEventRecord(proj_done[0], h);
+  bool k_started = false;  // dgamma_k's running sum (QK-norm)
   for (int i = 0; i < n && e == hipSuccess; ++i) {
     const Stage& st = p.stages[i];
     // the stage dO buffer is single: its GEMMs run on this stream, after
@@ -465,11 +541,15 @@ hipError_t bwd_pipelined(const Plan& p, const Kernels& K, const BwdIn& in, hipSt
     if (e == hipSuccess && i >= 2) e = hipStreamWaitEvent(s, dx_done[i % 2], 0);
     if (e == hipSuccess) e = timed(UPIPE_K_ATTN_DKV, s, [&] { return K.attn_dkv(a, s); });
     if (e == hipSuccess) e = timed(UPIPE_K_ATTN_DQ, s, [&] { return K.attn_dq(a, s); });
+    if (e == hipSuccess && p.qk_norm) {
+      e = stage_norm_bwd(p, st, in, nin, i == 0, !k_started, s);
+      k_started = k_started || st.done;
+    }
     if (e == hipSuccess) e = hipEventRecord(dq_done[i % 2], s);
     if (e == hipSuccess && i + 1 < n) {
       if (i >= 1) e = hipStreamWaitEvent(h, dq_done[(i - 1) % 2], 0);
       if (e == hipSuccess)
-        e = stage_projection(p, p.stages[i + 1], K, in.X, in.Wq, in.Wk, in.Wv, in.ws, h);
+        e = stage_projection(p, p.stages[i + 1], K, in.X, in.Wq, in.Wk, in.Wv, in.ws, h, nin, true);
       if (e == hipSuccess) e = hipEventRecord(proj_done[(i + 1) % 2], h);
     }
     if (e == hipSuccess) e = hipStreamWaitEvent(h, dq_done[i % 2], 0);
@@ -519,11 +599,20 @@ int upipe_create_ex(upipe_plan** out, int64_t S, int64_t d_model, int H, int G, 
 
 int upipe_create_rope(upipe_plan** out, int64_t S, int64_t d_model, int H, int G, int d_head, int U,
                       int causal, int dtype, int flags, double rope_theta) {
+  if (flags & UPIPE_QK_NORM) return UPIPE_ERR_ARG;  // needs an eps: upipe_create_opt
+  const upipe_options o{flags, rope_theta, 0.0};
+  return upipe_create_opt(out, S, d_model, H, G, d_head, U, causal, dtype, &o);
+}
+
+int upipe_create_opt(upipe_plan** out, int64_t S, int64_t d_model, int H, int G, int d_head,
+                     int U, int causal, int dtype, const upipe_options* opt) {
   if (!out) return UPIPE_ERR_ARG;
   *out = nullptr;
+  const upipe_options o = opt ? *opt : upipe_options{0, 0.0, 0.0};
   upipe_plan* h = new (std::nothrow) upipe_plan;
   if (!h) return UPIPE_ERR_ARG;
-  int rc = make_plan(h->p, S, d_model, H, G, d_head, U, causal, dtype, flags, rope_theta);
+  int rc = make_plan(h->p, S, d_model, H, G, d_head, U, causal, dtype, o.flags, o.rope_theta,
+                     o.qk_norm_eps);
   if (rc != UPIPE_OK) {
     delete h;
     return rc;
@@ -582,17 +671,17 @@ namespace {
 // Forward of every stage; `op` adds the output projection.  Arguments are
 // validated by the callers.
 int run_fwd(const Plan& p, const void* X, const void* Wq, const void* Wk, const void* Wv,
-            void* O, float* LSE, void* ws, hipStream_t s, const OutProj* op) {
+            void* O, float* LSE, void* ws, hipStream_t s, const OutProj* op, const NormIn& nin) {
   const Kernels K = kernels_for(p.dtype);
   if (p.pipeline) {
     hipStream_t hs = nullptr;
     SyncEvents E;
     UPIPE_TRY(helper_stream(&hs));
     UPIPE_TRY(E.take());
-    UPIPE_TRY(fwd_pipelined(p, K, X, Wq, Wk, Wv, O, LSE, ws, s, hs, E));
+    UPIPE_TRY(fwd_pipelined(p, K, X, Wq, Wk, Wv, O, LSE, ws, s, hs, E, nin));
   } else {
     for (const Stage& st : p.stages) {
-      UPIPE_TRY(stage_projection(p, st, K, X, Wq, Wk, Wv, ws, s));
+      UPIPE_TRY(stage_projection(p, st, K, X, Wq, Wk, Wv, ws, s, nin, false));
       AttnArgs a = attn_args(p, st, ws);
       a.o = O;
       a.lse = LSE;
@@ -605,7 +694,7 @@ int run_fwd(const Plan& p, const void* X, const void* Wq, const void* Wk, const 
 
 // Backward of every stage; `op` adds the output projection (dO of each stage
 // from dY; in.dO unused).  Arguments are validated by the callers.
-int run_bwd(const Plan& p, const BwdIn& in, hipStream_t s, const OutProj* op) {
+int run_bwd(const Plan& p, const BwdIn& in, hipStream_t s, const OutProj* op, const NormIn& nin) {
   const Kernels K = kernels_for(p.dtype);
   hipStream_t hs = nullptr;
   SyncEvents E;
@@ -615,17 +704,22 @@ int run_bwd(const Plan& p, const BwdIn& in, hipStream_t s, const OutProj* op) {
   }
   // dX needs no zero fill: the first stage's dX launch starts the running sum
   if (p.pipeline) {
-    UPIPE_TRY(bwd_pipelined(p, K, in, s, hs, E, op));
+    UPIPE_TRY(bwd_pipelined(p, K, in, s, hs, E, op, nin));
   } else {
+    bool k_started = false;  // dgamma_k's running sum (QK-norm)
     for (const Stage& st : p.stages) {
       const bool first_stage = &st == &p.stages.front();
-      UPIPE_TRY(stage_projection(p, st, K, in.X, in.Wq, in.Wk, in.Wv, in.ws, s));
+      UPIPE_TRY(stage_projection(p, st, K, in.X, in.Wq, in.Wk, in.Wv, in.ws, s, nin, true));
       if (op) UPIPE_TRY(stage_dout(p, st, K, in.ws, *op, s));
       const AttnArgs a =
           op ? with_stage_do(p, st, in.ws, bwd_args(p, st, in)) : bwd_args(p, st, in);
       UPIPE_TRY(timed(UPIPE_K_BWD_PRE, s, [&] { return K.bwd_pre(a, s); }));
       UPIPE_TRY(timed(UPIPE_K_ATTN_DKV, s, [&] { return K.attn_dkv(a, s); }));
       UPIPE_TRY(timed(UPIPE_K_ATTN_DQ, s, [&] { return K.attn_dq(a, s); }));
+      if (p.qk_norm) {
+        UPIPE_TRY(stage_norm_bwd(p, st, in, nin, first_stage, !k_started, s));
+        k_started = k_started || st.done;
+      }
       UPIPE_TRY(stage_gradients(p, st, K, in, first_stage, s));
     }
   }
@@ -653,19 +747,20 @@ extern "C" {
 
 int upipe_fwd(const upipe_plan* h, const void* X, const void* Wq, const void* Wk, const void* Wv,
               void* O, float* LSE, void* ws, size_t ws_bytes, void* stream) {
-  if (!h) return UPIPE_ERR_ARG;
+  if (!h || h->p.qk_norm) return UPIPE_ERR_ARG;
   const Plan& p = h->p;
   if (p.S == 0) return UPIPE_OK;
   if (!ptr_ok(X) || !ptr_ok(Wq) || !ptr_ok(Wk) || !ptr_ok(Wv) || !ptr_ok(O) || !ptr_ok(LSE))
     return UPIPE_ERR_ARG;
   if (!ws || !aligned(ws, kAlign) || ws_bytes < p.ws.fwd_bytes) return UPIPE_ERR_WORKSPACE;
-  return run_fwd(p, X, Wq, Wk, Wv, O, LSE, ws, static_cast<hipStream_t>(stream), nullptr);
+  return run_fwd(p, X, Wq, Wk, Wv, O, LSE, ws, static_cast<hipStream_t>(stream), nullptr,
+                 NormIn{});
 }
 
 int upipe_fwd_out(const upipe_plan* h, const void* X, const void* Wq, const void* Wk,
                   const void* Wv, const void* Wo, void* O, float* LSE, float* Y, void* ws,
                   size_t ws_bytes, void* stream) {
-  if (!h || !h->p.out_proj) return UPIPE_ERR_ARG;
+  if (!h || !h->p.out_proj || h->p.qk_norm) return UPIPE_ERR_ARG;
   const Plan& p = h->p;
   if (p.S == 0) return UPIPE_OK;
   if (!ptr_ok(X) || !ptr_ok(Wq) || !ptr_ok(Wk) || !ptr_ok(Wv) || !ptr_ok(Wo) || !ptr_ok(O) ||
@@ -673,13 +768,13 @@ int upipe_fwd_out(const upipe_plan* h, const void* X, const void* Wq, const void
     return UPIPE_ERR_ARG;
   if (!ws || !aligned(ws, kAlign) || ws_bytes < p.ws.fwd_bytes) return UPIPE_ERR_WORKSPACE;
   const OutProj op{Wo, Y, nullptr, nullptr, nullptr};
-  return run_fwd(p, X, Wq, Wk, Wv, O, LSE, ws, static_cast<hipStream_t>(stream), &op);
+  return run_fwd(p, X, Wq, Wk, Wv, O, LSE, ws, static_cast<hipStream_t>(stream), &op, NormIn{});
 }
 
 int upipe_bwd(const upipe_plan* h, const void* dO, const void* X, const void* Wq, const void* Wk,
               const void* Wv, const void* O, const float* LSE, float* dX, float* dWq, float* dWk,
               float* dWv, void* ws, size_t ws_bytes, void* stream) {
-  if (!h) return UPIPE_ERR_ARG;
+  if (!h || h->p.qk_norm) return UPIPE_ERR_ARG;
   const Plan& p = h->p;
   if (!ptr_ok(dWq) || !ptr_ok(dWk) || !ptr_ok(dWv)) return UPIPE_ERR_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -689,14 +784,14 @@ int upipe_bwd(const upipe_plan* h, const void* dO, const void* X, const void* Wq
     return UPIPE_ERR_ARG;
   if (!ws || !aligned(ws, kAlign) || ws_bytes < p.ws.bwd_bytes) return UPIPE_ERR_WORKSPACE;
   const BwdIn in{dO, X, Wq, Wk, Wv, O, LSE, dX, dWq, dWk, dWv, ws};
-  return run_bwd(p, in, s, nullptr);
+  return run_bwd(p, in, s, nullptr, NormIn{});
 }
 
 int upipe_bwd_out(const upipe_plan* h, const void* dY, const void* X, const void* Wq,
                   const void* Wk, const void* Wv, const void* Wo, const void* O, const float* LSE,
                   float* dX, float* dWq, float* dWk, float* dWv, float* dWo, void* ws,
                   size_t ws_bytes, void* stream) {
-  if (!h || !h->p.out_proj) return UPIPE_ERR_ARG;
+  if (!h || !h->p.out_proj || h->p.qk_norm) return UPIPE_ERR_ARG;
   const Plan& p = h->p;
   if (!ptr_ok(dWq) || !ptr_ok(dWk) || !ptr_ok(dWv) || !ptr_ok(dWo)) return UPIPE_ERR_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -707,7 +802,55 @@ int upipe_bwd_out(const upipe_plan* h, const void* dY, const void* X, const void
   if (!ws || !aligned(ws, kAlign) || ws_bytes < p.ws.bwd_bytes) return UPIPE_ERR_WORKSPACE;
   const BwdIn in{nullptr, X, Wq, Wk, Wv, O, LSE, dX, dWq, dWk, dWv, ws};
   const OutProj op{Wo, nullptr, dY, O, dWo};
-  return run_bwd(p, in, s, &op);
+  return run_bwd(p, in, s, &op, NormIn{});
+}
+
+int upipe_fwd_ex(const upipe_plan* h, const upipe_fwd_io* io, void* ws, size_t ws_bytes,
+                 void* stream) {
+  if (!h || !io) return UPIPE_ERR_ARG;
+  const Plan& p = h->p;
+  // what the plan uses must be given, what it does not use must be null
+  if (!need(io->q_norm, p.qk_norm) || !need(io->k_norm, p.qk_norm) || !need(io->Wo, p.out_proj) ||
+      !need(io->Y, p.out_proj))
+    return UPIPE_ERR_ARG;
+  if (p.S == 0) return UPIPE_OK;
+  if (!ptr_ok(io->X) || !ptr_ok(io->Wq) || !ptr_ok(io->Wk) || !ptr_ok(io->Wv) || !ptr_ok(io->O) ||
+      !ptr_ok(io->LSE))
+    return UPIPE_ERR_ARG;
+  if (!ws || !aligned(ws, kAlign) || ws_bytes < p.ws.fwd_bytes) return UPIPE_ERR_WORKSPACE;
+  const OutProj op{io->Wo, io->Y, nullptr, nullptr, nullptr};
+  const NormIn nin{io->q_norm, io->k_norm, nullptr, nullptr};
+  return run_fwd(p, io->X, io->Wq, io->Wk, io->Wv, io->O, io->LSE, ws,
+                 static_cast<hipStream_t>(stream), p.out_proj ? &op : nullptr, nin);
+}
+
+int upipe_bwd_ex(const upipe_plan* h, const upipe_bwd_io* io, void* ws, size_t ws_bytes,
+                 void* stream) {
+  if (!h || !io) return UPIPE_ERR_ARG;
+  const Plan& p = h->p;
+  if (!need(io->q_norm, p.qk_norm) || !need(io->k_norm, p.qk_norm) ||
+      !need(io->dq_norm, p.qk_norm) || !need(io->dk_norm, p.qk_norm) ||
+      !need(io->Wo, p.out_proj) || !need(io->dY, p.out_proj) || !need(io->dWo, p.out_proj) ||
+      !need(io->dO, !p.out_proj))
+    return UPIPE_ERR_ARG;
+  if (!ptr_ok(io->dWq) || !ptr_ok(io->dWk) || !ptr_ok(io->dWv)) return UPIPE_ERR_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.S == 0) {
+    const int rc = zero_weight_grads(p, io->dWq, io->dWk, io->dWv, io->dWo, s);
+    if (rc != UPIPE_OK || !p.qk_norm) return rc;
+    UPIPE_TRY(timed(UPIPE_K_FILL, s, [&] { return fill_zero(io->dq_norm, p.d * 4, s); }));
+    UPIPE_TRY(timed(UPIPE_K_FILL, s, [&] { return fill_zero(io->dk_norm, p.d * 4, s); }));
+    return UPIPE_OK;
+  }
+  if (!ptr_ok(io->X) || !ptr_ok(io->Wq) || !ptr_ok(io->Wk) || !ptr_ok(io->Wv) || !ptr_ok(io->O) ||
+      !ptr_ok(io->LSE) || !ptr_ok(io->dX))
+    return UPIPE_ERR_ARG;
+  if (!ws || !aligned(ws, kAlign) || ws_bytes < p.ws.bwd_bytes) return UPIPE_ERR_WORKSPACE;
+  const BwdIn in{io->dO, io->X, io->Wq, io->Wk, io->Wv, io->O, io->LSE, io->dX, io->dWq, io->dWk,
+                 io->dWv, ws};
+  const OutProj op{io->Wo, nullptr, io->dY, io->O, io->dWo};
+  const NormIn nin{io->q_norm, io->k_norm, io->dq_norm, io->dk_norm};
+  return run_bwd(p, in, s, p.out_proj ? &op : nullptr, nin);
 }
 
 int upipe_timing_enable(int on) {
@@ -744,7 +887,7 @@ int upipe_mfma_ceiling(int waves_per_simd, int iters, double* tflops, void* stre
 const char* upipe_kernel_name(int kind) {
   static const char* names[UPIPE_K_COUNT] = {"proj", "attn_fwd", "bwd_pre", "attn_dkv",
                                              "attn_dq", "dw", "dx", "fill",
-                                             "oproj", "dout", "dwo"};
+                                             "oproj", "dout", "dwo", "norm"};
   if (kind < 0 || kind >= UPIPE_K_COUNT) return "unknown";
   return names[kind];
 }

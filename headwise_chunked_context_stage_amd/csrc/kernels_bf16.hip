@@ -52,9 +52,11 @@ constexpr int GBUF = 2 * GB * GS;             // elements per buffer (two operan
 // store through a ring of register sets, so each has several steps of MFMA
 // time to arrive (one step ahead, the loop waited on HBM latency).
 // Chunks marked in t.rot (queries and keys under a rotary embedding) are
-// rotated in fp32 before their single rounding to bf16.
+// rotated, and chunks with t.nkind set (QK-norm) RMS-normalised and scaled
+// by gamma first, in fp32 before their single rounding to bf16.
 __global__ __launch_bounds__(256, 2) void proj_kernel(const u16* __restrict__ X, int64_t S,
-                                                      int64_t D, ChunkTable t, int nrb, Rope rope) {
+                                                      int64_t D, ChunkTable t, int nrb, Rope rope,
+                                                      NormArgs nrm) {
   __shared__ __attribute__((aligned(16))) u16 lds[2 * GBUF];
   const int total = nrb * t.n;
   const int lid = xcd_remap(blockIdx.x, total);
@@ -133,11 +135,16 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(const u16* __restrict__ X,
   if (kb < nk) body(kb, std::integral_constant<int, 1 % NRR>{});
   if (kb + 1 < nk) body(kb + 1, std::integral_constant<int, 2 % NRR>{});
   if (NRR > 3 && kb + 2 < nk) body(kb + 2, std::integral_constant<int, 3 % NRR>{});
-  if ((t.rot >> ch) & 1) {
-    // Rotated chunk: C (fp32) -> LDS tile [128][132]; each thread then reads
-    // 8 consecutive columns of a row and the 8 columns d/2 away, rotates the
-    // pairs and stores 8 bf16 (16 bytes).  The column group is fixed per
-    // thread, so its 8 frequencies are read once.
+  const bool rot = (t.rot >> ch) & 1;
+  const int nkd = t.nkind[ch];
+  if (rot || nkd) {
+    // Rotated or normalised chunk: C (fp32) -> LDS tile [128][132]; each
+    // thread then reads 8 consecutive columns of a row and the 8 columns d/2
+    // away, (QK-norm) scales both by gamma / rms of the row -- the 16 threads
+    // of a row sum their squares with an xor butterfly, which leaves every
+    // one of them the same sum --, rotates the pairs and stores 8 bf16
+    // (16 bytes).  The column group is fixed per thread, so its 8
+    // frequencies and gamma values are read once.
     constexpr int CF = GB + 4;
     float* cf = reinterpret_cast<float*>(lds);
 #pragma unroll
@@ -155,21 +162,67 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(const u16* __restrict__ X,
     double fw[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) fw[k] = rope.fw[(c0 % 64) + k];
+    float go[8], gp[8];  // gamma at the own and the partner columns
+    if (nkd) {
+      const u16* gam = static_cast<const u16*>(nrm.gamma[nkd - 1]);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        go[k] = __uint_as_float(static_cast<unsigned>(gam[c0 + k]) << 16);
+        gp[k] = __uint_as_float(static_cast<unsigned>(gam[(c0 ^ 64) + k]) << 16);
+      }
+    }
+    float* xh = nkd && nrm.store ? nrm.xh[nkd - 1] + static_cast<int64_t>(t.nidx[ch]) * S * DH : nullptr;
+    float* ri = nkd && nrm.store ? nrm.ri[nkd - 1] + static_cast<int64_t>(t.nidx[ch]) * S : nullptr;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       const int row = tid / 16 + 16 * m;
       const int64_t gi = i0 + row;
+      // the 16 threads of a row (one 16-lane group) skip it together, so the
+      // butterfly below only ever combines lanes that all take part
       if (gi >= S) continue;
       const float* own = cf + row * CF + c0;
       const float* other = cf + row * CF + (c0 ^ 64);
+      float xo[8], xp[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        xo[k] = own[k];
+        xp[k] = other[k];
+      }
+      if (nkd) {
+        float ss = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) ss += xo[k] * xo[k];
+#pragma unroll
+        for (int msk = 1; msk < 16; msk <<= 1) ss += __shfl_xor(ss, msk);
+        const float r = 1.f / sqrtf(ss * (1.f / DH) + nrm.eps);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          xo[k] *= r;
+          xp[k] *= r;
+        }
+        if (xh) {
+          st16(xh + gi * DH + c0, __builtin_bit_cast(u32x4, f32x4{xo[0], xo[1], xo[2], xo[3]}));
+          st16(xh + gi * DH + c0 + 4, __builtin_bit_cast(u32x4, f32x4{xo[4], xo[5], xo[6], xo[7]}));
+          if (chunk == 0) ri[gi] = r;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          xo[k] *= go[k];
+          xp[k] *= gp[k];
+        }
+      }
       float y[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        float cs, sn;
-        rope_cs(gi, fw[k], cs, sn);
-        float lo = upper ? other[k] : own[k], hi = upper ? own[k] : other[k];
-        rope_fwd(lo, hi, cs, sn);
-        y[k] = upper ? hi : lo;
+        if (rot) {
+          float cs, sn;
+          rope_cs(gi, fw[k], cs, sn);
+          float lo = upper ? xp[k] : xo[k], hi = upper ? xo[k] : xp[k];
+          rope_fwd(lo, hi, cs, sn);
+          y[k] = upper ? hi : lo;
+        } else {
+          y[k] = xo[k];
+        }
       }
       u32x4 v;
 #pragma unroll
@@ -1127,6 +1180,16 @@ __global__ __launch_bounds__(dqk::NT, 1) void attn_dq_kernel(AttnArgs a) {
           dq[d4 + 2][i] = hi;
         }
     }
+    if (a.dq32) {  // QK-norm: fp32, for the normalisation's backward
+      float* o32 = a.dq32 + (static_cast<int64_t>(u) * S + myq) * DH;
+#pragma unroll
+      for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          *reinterpret_cast<f32x4*>(o32 + 32 * d4 + 8 * g4 + 4 * hf) =
+              f32x4{dq[d4][4 * g4], dq[d4][4 * g4 + 1], dq[d4][4 * g4 + 2], dq[d4][4 * g4 + 3]};
+      return;
+    }
 #pragma unroll
     for (int d4 = 0; d4 < 4; ++d4)
 #pragma unroll
@@ -1194,12 +1257,16 @@ inline unsigned cdiv(int64_t a, int64_t b) { return static_cast<unsigned>((a + b
 namespace bf16 {
 
 hipError_t proj(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t, const Rope& rope,
-                hipStream_t st) {
+                const NormArgs& nrm, hipStream_t st) {
   if (d != DH || D % GK != 0) return hipErrorInvalidValue;
   if (t.rot != 0 && !rope.on) return hipErrorInvalidValue;
+  for (int i = 0; i < t.n; ++i)
+    if (t.nkind[i] > 2 || (t.nkind[i] && !nrm.gamma[t.nkind[i] - 1]) ||
+        (t.nkind[i] && nrm.store && (!nrm.xh[t.nkind[i] - 1] || !nrm.ri[t.nkind[i] - 1])))
+      return hipErrorInvalidValue;
   const int nrb = static_cast<int>(cdiv(S, GB));
   hipLaunchKernelGGL(proj_kernel, dim3(nrb * t.n), dim3(256), 0, st, static_cast<const u16*>(X), S,
-                     D, t, nrb, rope);
+                     D, t, nrb, rope, nrm);
   return hipGetLastError();
 }
 

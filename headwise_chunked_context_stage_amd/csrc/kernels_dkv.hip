@@ -315,7 +315,9 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
         const int64_t kr = wk0 + 8 * (i / 4) + 4 * hf + (i % 4);
         if (kr >= S) continue;
         const int64_t off = (static_cast<int64_t>(gl) * S + kr) * DH + 32 * d4 + col;
-        if (a.last_of_group)
+        if (a.last_of_group && !pwave && a.dk32)
+          a.dk32[off] = acc[d4][i];  // QK-norm: fp32, for the normalisation's backward
+        else if (a.last_of_group)
           out[off] = __builtin_bit_cast(u16, static_cast<__bf16>(acc[d4][i]));
         else
           carry[off] = acc[d4][i];

@@ -25,10 +25,12 @@
 namespace upipe {
 
 int make_plan(Plan& p, int64_t S, int64_t D, int H, int G, int d, int U, int causal, int dtype,
-              int flags, double rope_theta) {
-  if ((flags & ~(UPIPE_PIPELINE | UPIPE_OUT_PROJ)) != 0) return UPIPE_ERR_ARG;
+              int flags, double rope_theta, double qk_eps) {
+  if ((flags & ~(UPIPE_PIPELINE | UPIPE_OUT_PROJ | UPIPE_QK_NORM)) != 0) return UPIPE_ERR_ARG;
   // rope_theta: 0 (no rotary embedding) or a finite positive base
   if (!(rope_theta >= 0.0) || !std::isfinite(rope_theta)) return UPIPE_ERR_ARG;
+  // QK-norm eps: finite and >= 0 (checked only when the flag is set)
+  if ((flags & UPIPE_QK_NORM) && (!(qk_eps >= 0.0) || !std::isfinite(qk_eps))) return UPIPE_ERR_ARG;
   if (S < 0 || D <= 0 || H <= 0 || G <= 0 || d <= 0 || U <= 0) return UPIPE_ERR_ARG;
   if (causal != 0 && causal != 1) return UPIPE_ERR_ARG;
   if (dtype != UPIPE_BF16 && dtype != UPIPE_F32) return UPIPE_ERR_ARG;
@@ -59,6 +61,8 @@ int make_plan(Plan& p, int64_t S, int64_t D, int H, int G, int d, int U, int cau
   p.kv_per_stage = std::max(1, U / r);
   p.pipeline = (flags & UPIPE_PIPELINE) ? 1 : 0;
   p.out_proj = (flags & UPIPE_OUT_PROJ) ? 1 : 0;
+  p.qk_norm = (flags & UPIPE_QK_NORM) ? 1 : 0;
+  p.qk_eps = p.qk_norm ? qk_eps : 0.0;
   // Rotary embedding: w_c = theta^(-2c/d) for c < d/2, kept as turns per
   // position (w_c / 2 pi) in fp64.
   p.rope_theta = rope_theta;
@@ -125,6 +129,25 @@ int make_plan(Plan& p, int64_t S, int64_t D, int H, int G, int d, int U, int cau
   }
   // With the output projection the backward forms each stage's dO from dY.
   w.dob = p.out_proj ? take(U * Sd * e) : 0;
+  // QK-norm: the normalised rows and 1/rms of the stage's queries and keys
+  // (written by the backward's projections, read by the norm's backward),
+  // the fp32 gradients before that backward (bf16 only; fp32 plans keep them
+  // in dQ / dK), and the per-block sums of dgamma.
+  for (int c = 0; c < 2; ++c) w.xq[c] = w.rq[c] = w.xk[c] = w.rk[c] = w.gq32[c] = w.gk32[c] = 0;
+  w.pq = w.pk = 0;
+  if (p.qk_norm) {
+    const size_t nb = (static_cast<size_t>(S) + kNormBlock - 1) / kNormBlock;
+    take2(w.xq, U * Sd * 4);
+    take2(w.rq, static_cast<size_t>(U) * S * 4);
+    take2(w.xk, nkv * Sd * 4);
+    take2(w.rk, nkv * static_cast<size_t>(S) * 4);
+    if (dtype == UPIPE_BF16) {
+      take2(w.gq32, U * Sd * 4);
+      take2(w.gk32, nkv * Sd * 4);
+    }
+    w.pq = take(static_cast<size_t>(U) * nb * d * 4);
+    w.pk = take(nkv * nb * d * 4);
+  }
   w.bwd_bytes = off;
   return UPIPE_OK;
 }

@@ -42,7 +42,25 @@ struct WsLayout {
   size_t dk_acc, dv_acc;       // fp32 carry of dK, dV across a group's stages (bf16 and U < r)
   size_t dob;                  // dO of the stage's heads [U][S][d] (element type), from dY through
                                // the output projection (plans with UPIPE_OUT_PROJ; else 0)
+  // QK-norm (plans with UPIPE_QK_NORM; else 0), backward only:
+  size_t xq[2], rq[2];         // normalised query rows [U][S][d] fp32, 1/rms [U][S] fp32
+  size_t xk[2], rk[2];         // the same for the stage's keys [kv][S][d], [kv][S]
+  size_t gq32[2], gk32[2];     // bf16: fp32 gradients of the normalised rows before their
+                               // backward, [U][S][d] and [kv][S][d] (fp32 plans use dq/dk)
+  size_t pq, pk;               // per-256-token-block sums for dgamma: [U][nb][d], [kv][nb][d]
   size_t fwd_bytes, bwd_bytes;
+};
+
+// QK-norm operands of the projection epilogues: chunks with kind 1 (queries)
+// or 2 (keys) are normalised with gamma[kind - 1]; with `store` set, the
+// normalised rows and 1/rms of chunk i go to xh[kind - 1] + idx * S * d and
+// ri[kind - 1] + idx * S (the backward's recomputation keeps them).
+struct NormArgs {
+  const void* gamma[2];
+  float* xh[2];
+  float* ri[2];
+  float eps;
+  int store;
 };
 
 // Rotary position embedding of queries and keys (rotate-half form): the pair
@@ -64,6 +82,8 @@ struct Plan {
   int out_proj;      // the workspace holds the stage dO buffer of upipe_bwd_out
   double rope_theta; // 0: no rotary embedding
   Rope rope;         // frequencies derived from rope_theta and d
+  int qk_norm;       // UPIPE_QK_NORM
+  double qk_eps;
   std::vector<Stage> stages;
   WsLayout ws;
   size_t elem() const { return dtype == UPIPE_BF16 ? 2 : 4; }
@@ -71,7 +91,9 @@ struct Plan {
 
 // Validates and builds; returns a UPIPE_* code.
 int make_plan(Plan& p, int64_t S, int64_t D, int H, int G, int d, int U, int causal, int dtype,
-              int flags = 0, double rope_theta = 0.0);
+              int flags = 0, double rope_theta = 0.0, double qk_eps = 0.0);
+
+constexpr int kNormBlock = 256;  // tokens per partial sum of dgamma
 int choose_u(int64_t S, int64_t D, int H, int G, int d, int causal, int dtype, size_t budget,
              int* U);
 
@@ -88,6 +110,8 @@ struct ChunkTable {
   const void* w[kMaxChunks];  // weight rows [d][D] of this chunk
   void* a[kMaxChunks];        // [S][d] activation / gradient buffer of this chunk
   float* dw[kMaxChunks];      // [d][D] fp32 weight-gradient rows (dW launches only)
+  unsigned char nkind[kMaxChunks];  // projection: 0, or QK-norm with gamma[nkind - 1]
+  unsigned char nidx[kMaxChunks];   // projection: row block of the chunk in NormArgs' buffers
 };
 
 struct AttnArgs {
@@ -119,6 +143,8 @@ struct AttnArgs {
   void* dv;
   float* dk_acc;        // fp32 carry (bf16 only), may be null when not needed
   float* dv_acc;
+  float* dq32;          // bf16 with QK-norm: dQ goes here in fp32 (after the rotary
+  float* dk32;          //   transpose) instead of dq; the finished dK likewise
   int first_of_group;   // this launch starts the group's dK/dV accumulation
   int last_of_group;    // this launch completes it
   // rotary embedding: the bf16 kernels map the gradients of the rotated
@@ -132,7 +158,7 @@ struct AttnArgs {
 namespace bf16 {
 // Chunks with their bit set in t.rot are rotated (rope) before rounding.
 hipError_t proj(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t, const Rope& rope,
-                hipStream_t st);
+                const NormArgs& nrm, hipStream_t st);
 hipError_t attn_fwd(const AttnArgs& a, hipStream_t st);
 hipError_t bwd_pre(const AttnArgs& a, hipStream_t st);
 hipError_t attn_dkv(const AttnArgs& a, hipStream_t st);
@@ -172,6 +198,24 @@ hipError_t dwo(const void* dY, int64_t S, int64_t D, int d, const ChunkTable& t,
                hipStream_t st);
 }  // namespace f32
 hipError_t fill_zero(void* p, size_t bytes, hipStream_t st);
+
+// QK-norm kernels (kernels_norm.hip), d = d_head <= 128.
+namespace norm {
+// fp32 plans: normalise n [S][d] buffers at `x` in place (x = gamma * xhat);
+// xhat / rinv (may be null) keep the normalised rows and 1/rms.
+hipError_t fwd_f32(float* x, int n, int64_t S, int d, const float* gamma, float eps, float* xhat,
+                   float* rinv, hipStream_t st);
+// Backward of n rows blocks: g [n][S][d] fp32 gradients of the normalised
+// rows -> out [n][S][d] (element type `out_bf16 ? bf16 : fp32`; may alias g
+// when fp32), and part [n][nb][d] (nb = ceil(S / kNormBlock)) = per-block
+// sums of g * xhat.  gamma in the element type.
+hipError_t bwd(const float* g, const float* xhat, const float* rinv, const void* gamma,
+               int gamma_bf16, void* out, int out_bf16, float* part, int n, int64_t S, int d,
+               hipStream_t st);
+// dg[c] = (first ? 0 : dg[c]) + sum over n * nb partial rows in order.
+hipError_t gamma_sum(float* dg, const float* part, int n, int64_t S, int d, int first,
+                     hipStream_t st);
+}  // namespace norm
 
 // Kernel timing hooks (capi.cpp).
 void timing_begin(int kind, hipStream_t st);

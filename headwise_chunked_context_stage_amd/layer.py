@@ -61,3 +61,35 @@ def run_out(plan, inp, backward_pass: bool = True, stream=None):
                      out["LSE"], out["dX"], out["dWq"], out["dWk"], out["dWv"], out["dWo"],
                      out["ws"], stream=stream)
     return out
+
+
+def run_ex(plan, inp, backward_pass: bool = True, stream=None):
+    """Any plan through upipe_fwd_ex / upipe_bwd_ex: the QK-norm weights
+    (q_norm, k_norm) and the output projection (Wo, dY) are taken from `inp`
+    when the plan uses them; returns O, LSE (and Y) and, for the backward,
+    dX, dWq, dWk, dWv (and dq_norm, dk_norm, dWo)."""
+    dev = inp["X"].device
+    out = alloc_outputs(plan, dev, backward=backward_pass)
+    io = {k: inp[k] for k in ("X", "Wq", "Wk", "Wv")}
+    io.update(O=out["O"], LSE=out["LSE"])
+    if plan.qk_norm:
+        io.update(q_norm=inp["q_norm"], k_norm=inp["k_norm"])
+    if plan.out_proj:
+        out["Y"] = torch.empty((plan.S, plan.D), dtype=torch.float32, device=dev)
+        io.update(Wo=inp["Wo"], Y=out["Y"])
+    plan.fwd_ex(io, out["ws"], stream=stream)
+    if backward_pass:
+        bio = {k: io[k] for k in ("X", "Wq", "Wk", "Wv", "O", "LSE")}
+        bio.update({k: out[k] for k in ("dX", "dWq", "dWk", "dWv")})
+        if plan.qk_norm:
+            out["dq_norm"] = torch.empty((plan.d,), dtype=torch.float32, device=dev)
+            out["dk_norm"] = torch.empty((plan.d,), dtype=torch.float32, device=dev)
+            bio.update(q_norm=inp["q_norm"], k_norm=inp["k_norm"], dq_norm=out["dq_norm"],
+                       dk_norm=out["dk_norm"])
+        if plan.out_proj:
+            out["dWo"] = torch.empty((plan.D, plan.H * plan.d), dtype=torch.float32, device=dev)
+            bio.update(Wo=inp["Wo"], dY=inp["dY"], dWo=out["dWo"])
+        else:
+            bio["dO"] = inp["dO"]
+        plan.bwd_ex(bio, out["ws"], stream=stream)
+    return out

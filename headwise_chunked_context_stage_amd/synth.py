@@ -62,13 +62,16 @@ def torch_dtype(dtype: str) -> torch.dtype:
 
 
 def make_inputs(shape: LayerShape, dtype: str = "bf16", seed: int = 0, device: str = "cpu",
-                with_grad_out: bool = True, wq_zero: bool = False, out_proj: bool = False):
+                with_grad_out: bool = True, wq_zero: bool = False, out_proj: bool = False,
+                qk_norm: bool = False):
     """Draw X, Wq, Wk, Wv (and dO) for `shape`.
 
     Returns a dict of tensors on `device` in the storage dtype.  `wq_zero`
     replaces Wq by zeros after drawing (the draw order is unchanged).
     `out_proj` also draws, after the others, the output projection
     Wo [D][H*d] ~ N(0, 1/(H*d)) and the output gradient dY [S][D] ~ N(0, 1).
+    `qk_norm` then draws the QK-norm weights q_norm, k_norm [d] ~ 1 + N(0, 0.2^2)
+    (trained RMSNorm weights scatter around 1).
     """
     dev = torch.device(device)
     gen = torch.Generator(device=dev)
@@ -94,6 +97,10 @@ def make_inputs(shape: LayerShape, dtype: str = "bf16", seed: int = 0, device: s
     if out_proj:
         out["Wo"] = draw(D, H * d, 1.0 / ((H * d) ** 0.5))
         out["dY"] = draw(S, D, 1.0)
+    if qk_norm:
+        for k in ("q_norm", "k_norm"):
+            t = torch.randn((d,), generator=gen, device=dev, dtype=torch.float32)
+            out[k] = (1.0 + 0.2 * t).to(td)
     if wq_zero:
         out["Wq"].zero_()
     return out

@@ -17,15 +17,38 @@ UPIPE_BF16, UPIPE_F32 = 0, 1
 UPIPE_OK, UPIPE_ERR_ARG, UPIPE_ERR_UNSUPPORTED, UPIPE_ERR_WORKSPACE, UPIPE_ERR_HIP = 0, 1, 2, 3, 4
 UPIPE_PIPELINE = 1  # plan flag: stage pipelining on a second stream
 UPIPE_OUT_PROJ = 2  # plan flag: workspace for upipe_bwd_out (output projection)
+UPIPE_QK_NORM = 4   # plan flag: per-head RMSNorm of queries and keys (upipe_fwd_ex / upipe_bwd_ex)
 KERNEL_KINDS = ("proj", "attn_fwd", "bwd_pre", "attn_dkv", "attn_dq", "dw", "dx", "fill",
-                "oproj", "dout", "dwo")
+                "oproj", "dout", "dwo", "norm")
 
 EXPORTS = ("upipe_create", "upipe_create_ex", "upipe_create_rope", "upipe_destroy", "upipe_peak_bytes", "upipe_peak_bytes_phase",
            "upipe_fwd", "upipe_bwd", "upipe_strerror", "upipe_num_stages", "upipe_stage_info",
            "upipe_timing_enable", "upipe_timing_read", "upipe_kernel_name", "upipe_mfma_ceiling",
-           "upipe_auto_u", "upipe_fwd_out", "upipe_bwd_out")
+           "upipe_auto_u", "upipe_fwd_out", "upipe_bwd_out", "upipe_create_opt",
+           "upipe_fwd_ex", "upipe_bwd_ex")
 
 _lib = None
+
+
+class Options(ctypes.Structure):
+    """upipe_options"""
+    _fields_ = [("flags", ctypes.c_int), ("rope_theta", ctypes.c_double),
+                ("qk_norm_eps", ctypes.c_double)]
+
+
+FWD_IO_FIELDS = ("X", "Wq", "Wk", "Wv", "q_norm", "k_norm", "Wo", "O", "LSE", "Y")
+BWD_IO_FIELDS = ("dO", "dY", "X", "Wq", "Wk", "Wv", "q_norm", "k_norm", "Wo", "O", "LSE", "dX",
+                 "dWq", "dWk", "dWv", "dq_norm", "dk_norm", "dWo")
+
+
+class FwdIO(ctypes.Structure):
+    """upipe_fwd_io: every member a device address (0 = NULL)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in FWD_IO_FIELDS]
+
+
+class BwdIO(ctypes.Structure):
+    """upipe_bwd_io"""
+    _fields_ = [(n, ctypes.c_void_p) for n in BWD_IO_FIELDS]
 
 
 class UpipeError(RuntimeError):
@@ -81,6 +104,13 @@ def lib():
     L.upipe_mfma_ceiling.restype = i32
     L.upipe_auto_u.argtypes = [i64, i64, i32, i32, i32, i32, i32, sz, ctypes.POINTER(i32)]
     L.upipe_auto_u.restype = i32
+    L.upipe_create_opt.argtypes = [ctypes.POINTER(vp), i64, i64, i32, i32, i32, i32, i32, i32,
+                                   ctypes.POINTER(Options)]
+    L.upipe_create_opt.restype = i32
+    L.upipe_fwd_ex.argtypes = [vp, ctypes.POINTER(FwdIO), vp, sz, vp]
+    L.upipe_fwd_ex.restype = i32
+    L.upipe_bwd_ex.argtypes = [vp, ctypes.POINTER(BwdIO), vp, sz, vp]
+    L.upipe_bwd_ex.restype = i32
     _lib = L
     return L
 
@@ -154,6 +184,33 @@ def upipe_create_rope(S, d_model, H, G, d_head, U, causal=1, dtype="bf16", flags
                                    _dtype_code(dtype), int(flags), float(rope_theta)),
            "upipe_create_rope")
     return h.value
+
+
+def upipe_create_opt(S, d_model, H, G, d_head, U, causal=1, dtype="bf16", flags=0,
+                     rope_theta=0.0, qk_norm_eps=0.0) -> int:
+    h = ctypes.c_void_p()
+    opt = Options(int(flags), float(rope_theta), float(qk_norm_eps))
+    _check(lib().upipe_create_opt(ctypes.byref(h), S, d_model, H, G, d_head, U, int(causal),
+                                  _dtype_code(dtype), ctypes.byref(opt)), "upipe_create_opt")
+    return h.value
+
+
+def upipe_fwd_ex(plan, io: dict, ws, ws_bytes=None, stream=None) -> None:
+    """io: tensors (or addresses) by the names of upipe_fwd_io; missing = NULL."""
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if hasattr(ws, "numel") else 0
+    s = FwdIO(*[_addr(io.get(n)) for n in FWD_IO_FIELDS])
+    _check(lib().upipe_fwd_ex(plan, ctypes.byref(s), _addr(ws), ws_bytes,
+                              _stream(stream, io.get("X"), io.get("O"))), "upipe_fwd_ex")
+
+
+def upipe_bwd_ex(plan, io: dict, ws, ws_bytes=None, stream=None) -> None:
+    """io: tensors (or addresses) by the names of upipe_bwd_io; missing = NULL."""
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if hasattr(ws, "numel") else 0
+    s = BwdIO(*[_addr(io.get(n)) for n in BWD_IO_FIELDS])
+    _check(lib().upipe_bwd_ex(plan, ctypes.byref(s), _addr(ws), ws_bytes,
+                              _stream(stream, io.get("dX"), io.get("dWq"))), "upipe_bwd_ex")
 
 
 def upipe_destroy(plan) -> None:
@@ -282,15 +339,21 @@ class Plan:
     can only check pointers for null and alignment."""
 
     def __init__(self, S, d_model, H, G, d_head, U, causal=True, dtype="bf16", pipeline=False,
-                 rope_theta=0.0, out_proj=False):
+                 rope_theta=0.0, out_proj=False, qk_norm=False, qk_norm_eps=1e-6):
         self.S, self.D, self.H, self.G, self.d, self.U = S, d_model, H, G, d_head, U
         self.causal = bool(causal)
         self.pipeline = bool(pipeline)
         self.out_proj = bool(out_proj)
+        self.qk_norm = bool(qk_norm)
+        self.qk_norm_eps = float(qk_norm_eps)
         self.rope_theta = float(rope_theta)
         self.dtype = "bf16" if _dtype_code(dtype) == UPIPE_BF16 else "f32"
         flags = (UPIPE_PIPELINE if self.pipeline else 0) | (UPIPE_OUT_PROJ if self.out_proj else 0)
-        if self.rope_theta != 0.0 or self.out_proj:
+        if self.qk_norm:
+            self.handle = upipe_create_opt(S, d_model, H, G, d_head, U, int(self.causal), dtype,
+                                           flags | UPIPE_QK_NORM, self.rope_theta,
+                                           self.qk_norm_eps)
+        elif self.rope_theta != 0.0 or self.out_proj:
             self.handle = upipe_create_rope(S, d_model, H, G, d_head, U, int(self.causal), dtype,
                                             flags, self.rope_theta)
         elif self.pipeline:
@@ -334,6 +397,8 @@ class Plan:
             "dO": ((S, H * d), el), "dX": ((S, D), f32), "dWq": ((H * d, D), f32),
             "dWk": ((G * d, D), f32), "dWv": ((G * d, D), f32), "Wo": ((D, H * d), el),
             "Y": ((S, D), f32), "dY": ((S, D), el), "dWo": ((D, H * d), f32),
+            "q_norm": ((d,), el), "k_norm": ((d,), el), "dq_norm": ((d,), f32),
+            "dk_norm": ((d,), f32),
         }
         for name, t in tensors.items():
             _check_layout(t, name, *expect[name])
@@ -356,6 +421,29 @@ class Plan:
         self._check(1, ws, ws_bytes, X=X, Wq=Wq, Wk=Wk, Wv=Wv, O=O, LSE=LSE, dO=dO, dX=dX,
                     dWq=dWq, dWk=dWk, dWv=dWv)
         upipe_bwd(self.handle, dO, X, Wq, Wk, Wv, O, LSE, dX, dWq, dWk, dWv, ws, ws_bytes, stream)
+
+    def fwd_ex(self, io: dict, ws, ws_bytes=None, stream=None):
+        """Forward of any plan; io holds the tensors of upipe_fwd_io by name
+        (the ones the plan uses: q_norm, k_norm with QK-norm; Wo, Y with the
+        output projection)."""
+        want = ["X", "Wq", "Wk", "Wv", "O", "LSE"] + (["q_norm", "k_norm"] if self.qk_norm else []) \
+            + (["Wo", "Y"] if self.out_proj else [])
+        extra = set(k for k, v in io.items() if v is not None) - set(want)
+        if extra:
+            raise ValueError("tensors this plan does not use: %s" % sorted(extra))
+        self._check(0, ws, ws_bytes, **{k: io.get(k) for k in want})
+        upipe_fwd_ex(self.handle, io, ws, ws_bytes, stream)
+
+    def bwd_ex(self, io: dict, ws, ws_bytes=None, stream=None):
+        """Backward of any plan; io holds the tensors of upipe_bwd_io by name."""
+        want = ["X", "Wq", "Wk", "Wv", "O", "LSE", "dX", "dWq", "dWk", "dWv"] \
+            + (["q_norm", "k_norm", "dq_norm", "dk_norm"] if self.qk_norm else []) \
+            + (["Wo", "dY", "dWo"] if self.out_proj else ["dO"])
+        extra = set(k for k, v in io.items() if v is not None) - set(want)
+        if extra:
+            raise ValueError("tensors this plan does not use: %s" % sorted(extra))
+        self._check(1, ws, ws_bytes, **{k: io.get(k) for k in want})
+        upipe_bwd_ex(self.handle, io, ws, ws_bytes, stream)
 
     def fwd_out(self, X, Wq, Wk, Wv, Wo, O, LSE, Y, ws, ws_bytes=None, stream=None):
         self._check(0, ws, ws_bytes, X=X, Wq=Wq, Wk=Wk, Wv=Wv, Wo=Wo, O=O, LSE=LSE, Y=Y)

@@ -96,8 +96,28 @@ enum {
    * and Qwen blocks, which a drop-in attention module has to include.  The
    * workspace of the backward grows by the stage's dO buffer
    * (U * S * d_head elements); upipe_fwd and upipe_bwd work as before. */
-  UPIPE_OUT_PROJ = 2
+  UPIPE_OUT_PROJ = 2,
+  /* QK-norm (upipe_create_opt; not on the pages: the Qwen3 attention whose
+   * shape the pages train normalises each projected query and key row of a
+   * head before the rotary embedding).  For a row x of d_head values:
+   *   r = 1 / sqrt(sum_c x_c^2 / d_head + eps),  y_c = gamma_c * x_c * r,
+   * with gamma_q [d_head] for every query head and gamma_k [d_head] for
+   * every key head.  In bf16 the normalisation happens in fp32 before the
+   * stage buffers' single rounding.  The backward also returns dgamma_q and
+   * dgamma_k (fp32), each summed over heads ascending and 256-token blocks
+   * ascending (the same bits for every U).  Such plans run only through
+   * upipe_fwd_ex / upipe_bwd_ex, which take gamma; the backward's workspace
+   * grows by the fp32 normalised rows of the stage's queries and keys and
+   * their fp32 gradients (about 8 * S * d_head * (U + kv) bytes). */
+  UPIPE_QK_NORM = 4
 };
+
+/* Options of upipe_create_opt. */
+typedef struct {
+  int flags;           /* a combination of UPIPE_PIPELINE, UPIPE_OUT_PROJ, UPIPE_QK_NORM */
+  double rope_theta;   /* rotary embedding base, as for upipe_create_rope; 0 = none */
+  double qk_norm_eps;  /* with UPIPE_QK_NORM: eps of the normalisation (finite, >= 0) */
+} upipe_options;
 
 /* upipe_create with flags (a combination of the values above; 0 gives the
  * same plan as upipe_create).  Unknown flag bits return UPIPE_ERR_ARG. */
@@ -120,6 +140,13 @@ int upipe_create_ex(upipe_plan** out, int64_t S, int64_t d_model, int H, int G, 
  * workspace does not change. */
 int upipe_create_rope(upipe_plan** out, int64_t S, int64_t d_model, int H, int G, int d_head,
                       int U, int causal, int dtype, int flags, double rope_theta);
+
+/* upipe_create_rope with every option in one struct (opt may be NULL: no
+ * options).  UPIPE_ERR_ARG for unknown flag bits, a bad rope_theta (as for
+ * upipe_create_rope) or, with UPIPE_QK_NORM, a negative, NaN or infinite
+ * qk_norm_eps. */
+int upipe_create_opt(upipe_plan** out, int64_t S, int64_t d_model, int H, int G, int d_head,
+                     int U, int causal, int dtype, const upipe_options* opt);
 
 /* Chunk size from a memory budget (host only).  The pages (paper.rainbus.top
  * summary of "Untied Ulysses", section 独立分析的弱点) propose choosing U from
@@ -144,6 +171,10 @@ size_t upipe_peak_bytes(const upipe_plan* p);
 
 /* Per phase: 0 = forward only, 1 = backward. */
 size_t upipe_peak_bytes_phase(const upipe_plan* p, int phase);
+
+/* upipe_fwd, upipe_bwd, upipe_fwd_out and upipe_bwd_out return
+ * UPIPE_ERR_ARG for a plan with UPIPE_QK_NORM (they have no gamma
+ * arguments); upipe_fwd_ex / upipe_bwd_ex serve every plan. */
 
 /* Forward.  Writes O [S][H*d] and LSE [H][S] (natural log of the softmax
  * denominator of the scaled scores).  Enqueued on `stream` (a hipStream_t;
@@ -180,6 +211,55 @@ int upipe_bwd_out(const upipe_plan* p, const void* dY, const void* X, const void
                   float* dX, float* dWq, float* dWk, float* dWv, float* dWo, void* ws,
                   size_t ws_bytes, void* stream);
 
+/* Tensors of one forward call of upipe_fwd_ex (device pointers, caller
+ * owned; layouts and element types as for upipe_fwd / upipe_fwd_out).
+ * Members a plan does not use must be NULL. */
+typedef struct {
+  const void* X;
+  const void* Wq;
+  const void* Wk;
+  const void* Wv;
+  const void* q_norm; /* UPIPE_QK_NORM: gamma_q [d_head], element type */
+  const void* k_norm; /* UPIPE_QK_NORM: gamma_k [d_head], element type */
+  const void* Wo;     /* UPIPE_OUT_PROJ: [d_model][H*d] */
+  void* O;            /* [S][H*d] */
+  float* LSE;         /* [H][S] */
+  float* Y;           /* UPIPE_OUT_PROJ: [S][d_model] fp32 */
+} upipe_fwd_io;
+
+/* Tensors of one backward call of upipe_bwd_ex.  dO is the gradient of O
+ * ([S][H*d]); with UPIPE_OUT_PROJ the plan takes dY ([S][d_model]) instead
+ * and dO must be NULL.  Outputs are overwritten. */
+typedef struct {
+  const void* dO;
+  const void* dY;
+  const void* X;
+  const void* Wq;
+  const void* Wk;
+  const void* Wv;
+  const void* q_norm;
+  const void* k_norm;
+  const void* Wo;
+  const void* O;
+  const float* LSE;
+  float* dX;
+  float* dWq;
+  float* dWk;
+  float* dWv;
+  float* dq_norm; /* UPIPE_QK_NORM: dgamma_q [d_head] fp32 */
+  float* dk_norm; /* UPIPE_QK_NORM: dgamma_k [d_head] fp32 */
+  float* dWo;     /* UPIPE_OUT_PROJ: [d_model][H*d] fp32 */
+} upipe_bwd_io;
+
+/* Forward / backward of any plan (every flag combination): what upipe_fwd,
+ * upipe_bwd, upipe_fwd_out and upipe_bwd_out do, plus QK-norm.  A required
+ * pointer that is NULL or misaligned, or an unused one that is not NULL,
+ * returns UPIPE_ERR_ARG before anything is enqueued. */
+int upipe_fwd_ex(const upipe_plan* p, const upipe_fwd_io* io, void* ws, size_t ws_bytes,
+                 void* stream);
+int upipe_bwd_ex(const upipe_plan* p, const upipe_bwd_io* io, void* ws, size_t ws_bytes,
+                 void* stream);
+
 /* Text for an error code (static storage). */
 const char* upipe_strerror(int code);
 
@@ -212,7 +292,8 @@ enum {
   UPIPE_K_OPROJ = 8,    /* output projection Y += O Wo^T */
   UPIPE_K_DOUT = 9,     /* dO = dY Wo */
   UPIPE_K_DWO = 10,     /* dWo = dY^T O */
-  UPIPE_K_COUNT = 11
+  UPIPE_K_NORM = 11,    /* QK-norm backward and its weight-gradient sums */
+  UPIPE_K_COUNT = 12
 };
 int upipe_timing_enable(int on);
 int upipe_timing_read(double* ms, int64_t* launches, int n);

@@ -248,17 +248,21 @@ def decode_exact(a) -> np.ndarray:
 
 
 def backward_out(X, Wq, Wk, Wv, Wo, dY, H: int, G: int, d: int, causal: bool = True,
-                 nthreads: int | None = None, rope_theta: float = 0.0):
+                 nthreads: int | None = None, rope_theta: float = 0.0, q_norm=None, k_norm=None,
+                 qk_eps: float = 1e-6):
     """The layer followed by its output projection, forward + backward of
     L = sum(Y * dY) with Y = O Wo^T.  Composes the definitions: attention
     forward, Y = O Wo^T, dO = dY Wo, then the attention backward with that dO
     (every input decoded exactly to fp64 first), and dWo = dY^T O.
     Returns a dict of fp64 arrays: O, LSE, Y, dX, dWq, dWk, dWv, dWo."""
+    nk = dict(q_norm=q_norm, k_norm=k_norm, qk_eps=qk_eps)
     O, LSE = forward(X, Wq, Wk, Wv, H, G, d, causal=causal, nthreads=nthreads,
-                     rope_theta=rope_theta)
+                     rope_theta=rope_theta, **nk)
     Y, dO, dWo = out_proj(O, Wo, dY, nthreads=nthreads)
     ex = [decode_exact(a) for a in (X, Wq, Wk, Wv)]
-    out = backward(*ex, dO, H, G, d, causal=causal, nthreads=nthreads, rope_theta=rope_theta)
+    if q_norm is not None:
+        nk.update(q_norm=decode_exact(q_norm), k_norm=decode_exact(k_norm))
+    out = backward(*ex, dO, H, G, d, causal=causal, nthreads=nthreads, rope_theta=rope_theta, **nk)
     out["Y"] = Y
     out["dWo"] = dWo
     return out

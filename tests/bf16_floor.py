@@ -33,15 +33,31 @@ def _rotate(x, cs, sn, sign):
     return torch.cat([a * cs - b * sn, b * cs + a * sn], dim=-1)
 
 
+def _rms_fwd(x, gamma, eps):
+    """QK-norm in fp32: returns gamma * xhat, xhat and 1/rms [..., 1]."""
+    r = torch.rsqrt(x.pow(2).mean(-1, keepdim=True) + eps)
+    xh = x * r
+    return xh * gamma, xh, r
+
+
+def _rms_bwd(g, xh, r, gamma):
+    """gradient of the unnormalised rows for g = gradient of gamma * xhat."""
+    t = (gamma * g * xh).sum(-1, keepdim=True) / xh.shape[-1]
+    return r * (gamma * g - xh * t)
+
+
 def bf16_path_emulation(inp, H: int, G: int, d: int, causal: bool = True,
                         rope_theta: float = 0.0, out_proj: bool = False,
-                        round_grads: bool = True) -> dict:
+                        round_grads: bool = True, qk_norm_eps=None) -> dict:
     """With rope_theta > 0, queries and keys are rotated in fp32 before their
     rounding, and dQ, dK take the transposed rotation before theirs.  With
     out_proj, Y = O Wo^T and dWo = dY^T O in fp32 from the stored O, and the
     attention backward runs with dO = dY Wo rounded to bf16 once.
     round_grads=False keeps dQ, dK, dV in fp32 for the gradient products (a
-    variant the kernels do not implement; it isolates that rounding point)."""
+    variant the kernels do not implement; it isolates that rounding point).
+    qk_norm_eps (with inp["q_norm"], inp["k_norm"]) adds QK-norm in fp32
+    before the rotation and rounding; its backward runs on the fp32
+    gradients, and dq_norm / dk_norm are returned as well."""
     bf = lambda t: t.to(torch.bfloat16).float()
     bfg = bf if round_grads else (lambda t: t)
     X, Wq, Wk, Wv = [inp[k].detach().cpu().float() for k in ("X", "Wq", "Wk", "Wv")]
@@ -58,8 +74,15 @@ def bf16_path_emulation(inp, H: int, G: int, d: int, causal: bool = True,
         rot = lambda t, sign: _rotate(t, cs, sn, sign)
     else:
         rot = lambda t, sign: t
-    Q = bf(rot((X @ Wq.T).reshape(S, H, d).transpose(0, 1), 1))
-    K = bf(rot((X @ Wk.T).reshape(S, G, d).transpose(0, 1), 1)).repeat_interleave(r, 0)
+    qn = qk_norm_eps is not None
+    qp = (X @ Wq.T).reshape(S, H, d).transpose(0, 1)
+    kp = (X @ Wk.T).reshape(S, G, d).transpose(0, 1)
+    if qn:
+        gq, gk = inp["q_norm"].detach().cpu().float(), inp["k_norm"].detach().cpu().float()
+        qp, xq, rq = _rms_fwd(qp, gq, qk_norm_eps)
+        kp, xk, rk = _rms_fwd(kp, gk, qk_norm_eps)
+    Q = bf(rot(qp, 1))
+    K = bf(rot(kp, 1)).repeat_interleave(r, 0)
     V = bf(X @ Wv.T).reshape(S, G, d).transpose(0, 1).repeat_interleave(r, 0)
     s = (Q @ K.transpose(1, 2).contiguous()) * tau
     if causal:
@@ -75,18 +98,25 @@ def bf16_path_emulation(inp, H: int, G: int, d: int, causal: bool = True,
     P = torch.exp(s - lse[..., None])
     dP = go @ V.transpose(1, 2).contiguous()
     dS = P * (dP - Dd)
-    dQ = bfg(rot(tau * (bf(dS) @ K), -1))
+    dQ = rot(tau * (bf(dS) @ K), -1)
     dKh = bf(dS).transpose(1, 2).contiguous() @ Q
     dVh = bf(P).transpose(1, 2).contiguous() @ go
-    dK = bfg(rot(tau * dKh.reshape(G, r, S, d).sum(1), -1))
+    dK = rot(tau * dKh.reshape(G, r, S, d).sum(1), -1)
+    extra = {}
+    if qn:
+        extra["dq_norm"] = (dQ * xq).sum((0, 1))
+        extra["dk_norm"] = (dK * xk).sum((0, 1))
+        dQ = _rms_bwd(dQ, xq, rq, gq)
+        dK = _rms_bwd(dK, xk, rk, gk)
+    dQ = bfg(dQ)
+    dK = bfg(dK)
     dV = bfg(dVh.reshape(G, r, S, d).sum(1))
     dQf = dQ.transpose(0, 1).reshape(S, H * d)
     dKf = dK.transpose(0, 1).reshape(S, G * d)
     dVf = dV.transpose(0, 1).reshape(S, G * d)
-    extra = {}
     if out_proj:
         Of = O.transpose(0, 1).reshape(S, H * d)
-        extra = {"Y": Of @ Wo.T, "dWo": dY.T @ Of}
+        extra.update({"Y": Of @ Wo.T, "dWo": dY.T @ Of})
     return {
         **extra,
         "O": O.transpose(0, 1).reshape(S, H * d),

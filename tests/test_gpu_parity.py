@@ -407,6 +407,108 @@ def test_out_proj_matches_oracle_and_is_U_invariant(S, D, H, G, d, dtype, theta)
     assert torch.equal(plain["O"], first["O"]) and torch.equal(plain["LSE"], first["LSE"])
 
 
+# ---------------------------------------------------------------- QK-norm
+# Per-head RMSNorm of the projected queries and keys before the rotary
+# embedding (the Qwen3 attention; not on the pages), through upipe_fwd_ex /
+# upipe_bwd_ex: every output, dgamma_q and dgamma_k included, against the
+# oracle; bit-identical across U and with the pipelined plan.
+QKN_KEYS = ("O", "LSE", "dX", "dWq", "dWk", "dWv", "dq_norm", "dk_norm")
+QKN_CASES = [
+    # S, D, H, G, d, dtype, theta, out_proj
+    (1000, 1024, 4, 1, 128, "bf16", 0.0, False),      # ragged, one group (U = 1 carries dK)
+    (768, 512, 8, 2, 128, "bf16", 1000000.0, False),  # two groups, Qwen3's rotary base
+    (512, 1536, 8, 8, 128, "bf16", 1000000.0, True),  # MHA with the output projection
+    (320, 256, 4, 2, 64, "f32", 10000.0, False),
+    (256, 256, 4, 2, 64, "f32", 0.0, True),
+]
+
+
+def run_layer_ex(shape, dtype, U, inp, pipeline=False, rope_theta=0.0, out_proj=False):
+    from headwise_chunked_context_stage_amd.layer import run_ex
+
+    plan = upipe.Plan(shape.S, shape.D, shape.H, shape.G, shape.d, U, dtype=dtype,
+                      pipeline=pipeline, rope_theta=rope_theta, out_proj=out_proj, qk_norm=True,
+                      qk_norm_eps=1e-6)
+    out = run_ex(plan, inp)
+    torch.cuda.synchronize()
+    out.pop("ws")
+    return out
+
+
+@pytest.mark.parametrize("S,D,H,G,d,dtype,theta,oproj", QKN_CASES)
+def test_qk_norm_matches_oracle_and_is_U_invariant(S, D, H, G, d, dtype, theta, oproj):
+    shape = LayerShape(S=S, D=D, H=H, G=G, d=d)
+    cpu_inp = make_inputs(shape, dtype, seed=31, device="cpu", qk_norm=True, out_proj=oproj)
+    ex = {k: to_numpy_exact(cpu_inp[k]) for k in cpu_inp}
+    nk = dict(q_norm=ex["q_norm"], k_norm=ex["k_norm"], qk_eps=1e-6, rope_theta=theta)
+    if oproj:
+        ref = oracle.backward_out(ex["X"], ex["Wq"], ex["Wk"], ex["Wv"], ex["Wo"], ex["dY"],
+                                  H, G, d, **nk)
+    else:
+        ref = oracle.backward(ex["X"], ex["Wq"], ex["Wk"], ex["Wv"], ex["dO"], H, G, d, **nk)
+    keys = QKN_KEYS + (("Y", "dWo") if oproj else ())
+    inp = {k: v.cuda() for k, v in cpu_inp.items()}
+    emu = None
+    if dtype == "bf16":
+        emu = bf16_path_emulation(cpu_inp, H, G, d, rope_theta=theta, out_proj=oproj,
+                                  qk_norm_eps=1e-6)
+    first = None
+    for U in legal_us(H, G):
+        say("qk-norm %s theta=%g out_proj=%d S=%d D=%d H=%d G=%d U=%d"
+            % (dtype, theta, oproj, S, D, H, G, U))
+        out = run_layer_ex(shape, dtype, U, inp, rope_theta=theta, out_proj=oproj)
+        if first is not None:
+            assert_same_bits(first, out, "U=%d" % U)
+            continue
+        first = out
+        for k in keys:
+            got = host(out[k])
+            if dtype == "f32":
+                compare(k, got, ref[k], 2e-2, 2e-3)
+                continue
+            err = np.abs(got - ref[k])
+            floor = np.abs(emu[k].double().numpy() - ref[k])
+            fr = rel_frob(got, ref[k])
+            say("  %-7s max %.3e mean %.3e relfrob %.3e | floor max %.3e mean %.3e"
+                % (k, err.max(), err.mean(), fr, floor.max(), floor.mean()))
+            assert err.max() <= 1.25 * floor.max() + 1e-3, (k, "max above the bf16 floor")
+            assert err.mean() <= 1.25 * floor.mean() + 1e-5, (k, "mean above the floor")
+            if k in ("O", "LSE", "Y"):
+                compare(k, got, ref[k], 2e-2, 2e-3)
+            elif k == "dX":
+                assert err.mean() <= 2e-3, (k, err.mean())
+            else:
+                assert fr <= max(1e-2, 1.25 * rel_frob(emu[k].double().numpy(), ref[k])), (k, fr)
+    say("qk-norm pipelined U=%d" % legal_us(H, G)[-1])
+    assert_same_bits(first, run_layer_ex(shape, dtype, legal_us(H, G)[-1], inp, pipeline=True,
+                                         rope_theta=theta, out_proj=oproj), "pipelined")
+
+
+def test_qk_norm_entry_points_reject_mismatched_arguments():
+    """A QK-norm plan refuses the entry points without gamma, and
+    upipe_fwd_ex / upipe_bwd_ex refuse a missing gamma or a tensor the plan
+    does not use, before anything is enqueued."""
+    shape = LayerShape(S=128, D=256, H=2, G=1, d=128)
+    inp = {k: v.cuda() for k, v in make_inputs(shape, "bf16", seed=2, device="cpu",
+                                                qk_norm=True).items()}
+    plan = upipe.Plan(128, 256, 2, 1, 128, 1, qk_norm=True)
+    out = alloc_outputs(plan, inp["X"].device)
+    with pytest.raises(upipe.UpipeError):
+        upipe.upipe_fwd(plan.handle, inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], out["O"],
+                        out["LSE"], out["ws"])
+    io = dict(X=inp["X"], Wq=inp["Wq"], Wk=inp["Wk"], Wv=inp["Wv"], O=out["O"], LSE=out["LSE"])
+    with pytest.raises(upipe.UpipeError):  # gamma missing
+        upipe.upipe_fwd_ex(plan.handle, io, out["ws"])
+    plain = upipe.Plan(128, 256, 2, 1, 128, 1)
+    with pytest.raises(upipe.UpipeError):  # gamma given to a plan without QK-norm
+        upipe.upipe_fwd_ex(plain.handle, dict(io, q_norm=inp["q_norm"], k_norm=inp["k_norm"]),
+                           out["ws"])
+    upipe.upipe_fwd_ex(plain.handle, io, out["ws"])  # the plain plan through the same entry
+    torch.cuda.synchronize()
+    ref = run_layer(shape, "bf16", 1, inp, backward=False)
+    assert torch.equal(out["O"], ref["O"]) and torch.equal(out["LSE"], ref["LSE"])
+
+
 def test_empty_sequence_zero_weight_gradients():
     shape = LayerShape(S=0, D=256, H=4, G=2, d=128)
     plan = upipe.Plan(0, 256, 4, 2, 128, 2)

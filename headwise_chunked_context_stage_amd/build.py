@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libupipe.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["plan.cpp", "capi.cpp", "kernels_f32.hip", "kernels_bf16.hip", "kernels_dkv.hip",
-           "kernels_norm.hip"]
+           "kernels_norm.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -24,8 +24,8 @@ KERNEL_KINDS = ("proj", "attn_fwd", "bwd_pre", "attn_dkv", "attn_dq", "dw", "dx"
 EXPORTS = ("upipe_create", "upipe_create_ex", "upipe_create_rope", "upipe_destroy", "upipe_peak_bytes", "upipe_peak_bytes_phase",
            "upipe_fwd", "upipe_bwd", "upipe_strerror", "upipe_num_stages", "upipe_stage_info",
            "upipe_timing_enable", "upipe_timing_read", "upipe_kernel_name", "upipe_mfma_ceiling",
-           "upipe_auto_u", "upipe_fwd_out", "upipe_bwd_out", "upipe_create_opt",
-           "upipe_fwd_ex", "upipe_bwd_ex")
+           "upipe_auto_u", "upipe_fwd_out", "upipe_bwd_out", "upipe_fwd_noalloc",
+           "upipe_noalloc_max_bytes", "upipe_create_opt", "upipe_fwd_ex", "upipe_bwd_ex")
 
 _lib = None
 
@@ -111,6 +111,10 @@ def lib():
     L.upipe_fwd_ex.restype = i32
     L.upipe_bwd_ex.argtypes = [vp, ctypes.POINTER(BwdIO), vp, sz, vp]
     L.upipe_bwd_ex.restype = i32
+    L.upipe_fwd_noalloc.argtypes = [vp] * 8
+    L.upipe_fwd_noalloc.restype = i32
+    L.upipe_noalloc_max_bytes.argtypes = []
+    L.upipe_noalloc_max_bytes.restype = sz
     _lib = L
     return L
 
@@ -257,6 +261,17 @@ def upipe_bwd_out(plan, dY, X, Wq, Wk, Wv, Wo, O, LSE, dX, dWq, dWk, dWv, dWo, w
                                _addr(Wo), _addr(O), _addr(LSE), _addr(dX), _addr(dWq), _addr(dWk),
                                _addr(dWv), _addr(dWo), _addr(ws), ws_bytes,
                                _stream(stream, dX, dWq)), "upipe_bwd_out")
+
+
+def upipe_fwd_noalloc(plan, X, Wq, Wk, Wv, O, LSE, stream=None) -> None:
+    """upipe_fwd without a workspace: the library's static device array holds
+    the stage buffers (no allocation; calls overlapping on one GPU race)."""
+    _check(lib().upipe_fwd_noalloc(plan, _addr(X), _addr(Wq), _addr(Wk), _addr(Wv), _addr(O),
+                                   _addr(LSE), _stream(stream, X, O)), "upipe_fwd_noalloc")
+
+
+def upipe_noalloc_max_bytes() -> int:
+    return int(lib().upipe_noalloc_max_bytes())
 
 
 def upipe_strerror(code: int) -> str:
@@ -444,6 +459,20 @@ class Plan:
             raise ValueError("tensors this plan does not use: %s" % sorted(extra))
         self._check(1, ws, ws_bytes, **{k: io.get(k) for k in want})
         upipe_bwd_ex(self.handle, io, ws, ws_bytes, stream)
+
+    def fwd_noalloc(self, X, Wq, Wk, Wv, O, LSE, stream=None):
+        tensors = dict(X=X, Wq=Wq, Wk=Wk, Wv=Wv, O=O, LSE=LSE)
+        import torch
+
+        el = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        S, D, H, G, d = self.S, self.D, self.H, self.G, self.d
+        expect = {"X": ((S, D), el), "Wq": ((H * d, D), el), "Wk": ((G * d, D), el),
+                  "Wv": ((G * d, D), el), "O": ((S, H * d), el), "LSE": ((H, S), torch.float32)}
+        for name, t in tensors.items():
+            _check_layout(t, name, *expect[name])
+        for name, t in tensors.items():
+            _check_place(t, name, X.device)
+        upipe_fwd_noalloc(self.handle, X, Wq, Wk, Wv, O, LSE, stream)
 
     def fwd_out(self, X, Wq, Wk, Wv, Wo, O, LSE, Y, ws, ws_bytes=None, stream=None):
         self._check(0, ws, ws_bytes, X=X, Wq=Wq, Wk=Wk, Wv=Wv, Wo=Wo, O=O, LSE=LSE, Y=Y)

@@ -211,6 +211,25 @@ int upipe_bwd_out(const upipe_plan* p, const void* dY, const void* X, const void
                   float* dX, float* dWq, float* dWk, float* dWv, float* dWo, void* ws,
                   size_t ws_bytes, void* stream);
 
+/* The forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same results as upipe_fwd (the same
+ * kernels run); the stage buffers live in a static device array of
+ * upipe_noalloc_max_bytes() bytes (256 MiB) that each GPU the library runs
+ * on holds from the first call on it until the process ends.  The call
+ * allocates nothing.  `stream` must belong to the current device.
+ * Returns UPIPE_ERR_WORKSPACE when upipe_peak_bytes_phase(p, 0) exceeds the
+ * array, UPIPE_ERR_ARG for a pipelined plan (UPIPE_PIPELINE) or a stream of
+ * another device, and otherwise what upipe_fwd returns.  Every call on one
+ * GPU uses the same array: calls that overlap in time on one GPU (two
+ * streams, two host threads) race.  Nothing in the array has to start at
+ * zero; a call never reads what an earlier one left there. */
+int upipe_fwd_noalloc(const upipe_plan* p, const void* X, const void* Wq, const void* Wk,
+                      const void* Wv, void* O, float* LSE, void* stream);
+
+/* Size in bytes of the static array upipe_fwd_noalloc works in. */
+size_t upipe_noalloc_max_bytes(void);
+
 /* Tensors of one forward call of upipe_fwd_ex (device pointers, caller
  * owned; layouts and element types as for upipe_fwd / upipe_fwd_out).
  * Members a plan does not use must be NULL. */

@@ -43,6 +43,8 @@ def parse():
                     help="rotary embedding of queries and keys with this base (0: none)")
     ap.add_argument("--out-proj", action="store_true",
                     help="the layer with its output projection (upipe_fwd_out / upipe_bwd_out)")
+    ap.add_argument("--qk-norm", action="store_true",
+                    help="QK-norm of queries and keys (eps 1e-6), through upipe_fwd_ex / upipe_bwd_ex")
     ap.add_argument("--skip-cpu-baseline", action="store_true",
                     help="omit the oracle timing (profiling runs only)")
     ap.add_argument("--cpu-baseline-S", type=int, default=8192)
@@ -116,6 +118,28 @@ def traffic_for(kernel):
     return k.get("hbm_bytes_per_launch")
 
 
+def host_cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def gpu_sclk_sample(out: dict):
+    """The shader clock as rocm-smi reports it (run in a child process while
+    the timed steps execute); stores the text of its sclk lines."""
+    import subprocess
+
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30)
+        out["sclk"] = [ln.strip() for ln in r.stdout.splitlines() if "sclk" in ln.lower()] or None
+    except (OSError, subprocess.SubprocessError):
+        out["sclk"] = None
+
+
 def cpu_baseline(S_sample, D, d, S_full=None, H_full=None, G_full=None):
     """The fp64 oracle on a bounded sample of the workload: one query head and
     its KV head at S_sample tokens, full d_model, causal, forward + backward.
@@ -148,6 +172,7 @@ def cpu_baseline(S_sample, D, d, S_full=None, H_full=None, G_full=None):
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": nthreads,
+        "cpu_model": host_cpu_model(),
         "kind": "oracle",
         "sample": ("1 query head + its KV head, S=%d, d_model=%d, d_head=%d, causal, fwd+bwd "
                    "incl. projections and weight/input gradients; %.1f s; TFLOP/s counts causal "
@@ -195,18 +220,35 @@ def main():
         torch.cuda.synchronize()
         print("bench: calibration copy of %d bytes" % n, file=sys.stderr, flush=True)
         del src, dst
-    inp = make_inputs(shape, cfg["dtype"], seed=0, device="cuda", out_proj=args.out_proj)
+    inp = make_inputs(shape, cfg["dtype"], seed=0, device="cuda", out_proj=args.out_proj,
+                      qk_norm=args.qk_norm)
     plan = upipe.Plan(S, D, H, G, d, U, causal=True, dtype=cfg["dtype"], pipeline=args.pipeline,
-                      rope_theta=args.rope_theta, out_proj=args.out_proj)
+                      rope_theta=args.rope_theta, out_proj=args.out_proj, qk_norm=args.qk_norm)
     out = alloc_outputs(plan, dev)
     if args.out_proj:
         out["Y"] = torch.empty((S, D), dtype=torch.float32, device=dev)
         out["dWo"] = torch.empty((D, H * d), dtype=torch.float32, device=dev)
+    fio = bio = None
+    if args.qk_norm:  # every option through the io-struct entry points
+        out["dq_norm"] = torch.empty((d,), dtype=torch.float32, device=dev)
+        out["dk_norm"] = torch.empty((d,), dtype=torch.float32, device=dev)
+        fio = dict(X=inp["X"], Wq=inp["Wq"], Wk=inp["Wk"], Wv=inp["Wv"], q_norm=inp["q_norm"],
+                   k_norm=inp["k_norm"], O=out["O"], LSE=out["LSE"])
+        bio = dict(fio, dX=out["dX"], dWq=out["dWq"], dWk=out["dWk"], dWv=out["dWv"],
+                   dq_norm=out["dq_norm"], dk_norm=out["dk_norm"])
+        if args.out_proj:
+            fio.update(Wo=inp["Wo"], Y=out["Y"])
+            bio.update(Wo=inp["Wo"], dY=inp["dY"], dWo=out["dWo"])
+        else:
+            bio["dO"] = inp["dO"]
     torch.cuda.synchronize()
     mem_before = torch.cuda.memory_allocated()
 
     def step():
-        if args.out_proj:
+        if args.qk_norm:
+            plan.fwd_ex(fio, out["ws"])
+            plan.bwd_ex(bio, out["ws"])
+        elif args.out_proj:
             plan.fwd_out(inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], out["O"],
                          out["LSE"], out["Y"], out["ws"])
             plan.bwd_out(inp["dY"], inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"],
@@ -228,13 +270,19 @@ def main():
     # current stream: the library runs there unless pipelined, and a
     # pipelined call joins its helper stream back before returning)
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    import threading
+
+    clock = {}
+    sampler = threading.Thread(target=gpu_sclk_sample, args=(clock,), daemon=True)
     t0 = time.perf_counter()
     marks[0].record()
+    sampler.start()
     for i in range(args.steps):
         step()
         marks[i + 1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    sampler.join(timeout=60)
     step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     upipe.upipe_timing_enable(False)
     ktimes = upipe.upipe_timing_read()
@@ -257,7 +305,7 @@ def main():
         ent = {"ms_per_step": rec["ms"] / args.steps, "launches_per_step": n_per_step,
                "avg_launch_ms": avg_ms}
         if kind in ("attn_fwd", "attn_dkv", "attn_dq", "proj", "dw", "dx", "oproj", "dout",
-                    "dwo") and U >= r:
+                    "dwo") and (U >= r or kind in ("attn_fwd", "attn_dkv", "attn_dq")):
             ent["tflops"] = work / (avg_ms * 1e-3) / 1e12
         elif kind in ("bwd_pre", "fill"):
             ent["gbps"] = work / (avg_ms * 1e-3) / 1e9
@@ -318,8 +366,9 @@ def main():
                                "shape" if args.config.startswith("llama") else args.config,
                    "name": args.config, "S": S, "d_model": D, "H": H, "G": G, "d_head": d,
                    "U": U, "pipeline": args.pipeline, "rope_theta": args.rope_theta,
-                   "out_proj": args.out_proj, "causal": True,
+                   "out_proj": args.out_proj, "qk_norm": args.qk_norm, "causal": True,
                    "seed": 0},
+        "host": {"cpu_model": host_cpu_model(), "gpu_sclk_during_steps": clock.get("sclk")},
         "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "attn_kernels_tflops": aflops / (attn_ms * 1e-3) / 1e12 if attn_ms > 0 else None,
         "attn_kernels_pct_peak": (100.0 * aflops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS

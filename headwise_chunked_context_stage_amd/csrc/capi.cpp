@@ -571,14 +571,15 @@ void timing_begin(int kind, hipStream_t st) {
   g_open.kind = kind;
   g_open.a = take_event();
   g_open.b = take_event();
-  if (g_open.a) hipEventRecord(g_open.a, st);
+  // a failed record shows up as a failed read in upipe_timing_read
+  if (g_open.a) (void)hipEventRecord(g_open.a, st);
 }
 
 void timing_end(int kind, hipStream_t st) {
   if (!g_timing.load()) return;
   std::lock_guard<std::mutex> g(g_tmu);
   if (g_open.kind != kind || !g_open.a || !g_open.b) return;
-  hipEventRecord(g_open.b, st);
+  (void)hipEventRecord(g_open.b, st);
   g_recs.push_back(g_open);
   g_open = TimingRec{-1, nullptr, nullptr};
 }

@@ -47,7 +47,7 @@ def parse():
                     help="QK-norm of queries and keys (eps 1e-6), through upipe_fwd_ex / upipe_bwd_ex")
     ap.add_argument("--skip-cpu-baseline", action="store_true",
                     help="omit the oracle timing (profiling runs only)")
-    ap.add_argument("--cpu-baseline-S", type=int, default=8192)
+    ap.add_argument("--cpu-baseline-S", type=int, default=16384)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (HBM counter calibration)")
     return ap.parse_args()
@@ -128,16 +128,22 @@ def host_cpu_model():
     return None
 
 
-def gpu_sclk_sample(out: dict):
-    """The shader clock as rocm-smi reports it (run in a child process while
-    the timed steps execute); stores the text of its sclk lines."""
-    import subprocess
+def gpu_sclk_sample(out: dict, delay_s: float = 0.5):
+    """The shader clock the driver reports while the timed steps execute: the
+    current level ('*') of each card's pp_dpm_sclk in sysfs (what
+    rocm-smi --showclocks prints), read from this process after delay_s."""
+    import glob
 
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30)
-        out["sclk"] = [ln.strip() for ln in r.stdout.splitlines() if "sclk" in ln.lower()] or None
-    except (OSError, subprocess.SubprocessError):
-        out["sclk"] = None
+    time.sleep(delay_s)
+    found = []
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            cur = [ln.strip() for ln in open(f) if ln.strip().endswith("*")]
+        except OSError:
+            continue
+        if cur:
+            found.append("%s: %s" % (f.split("/")[4], cur[0]))
+    out["sclk"] = found or None
 
 
 def cpu_baseline(S_sample, D, d, S_full=None, H_full=None, G_full=None):

@@ -737,15 +737,23 @@ __global__ __launch_bounds__(256, 2) void dout_kernel(const u16* __restrict__ dY
 // per-lane scalar.  Waves w and w + 4 share a SIMD and run "ping-pong": each
 // alternates a matrix phase and a softmax phase, one barrier phase apart, so
 // one wave's MFMAs meet the other's exponentials.
+//
+// Small grids (fewer than two rounds of 256-row workgroups, e.g. one head of
+// a 32K-token sequence) run the same code with 4 waves and 128 query rows per
+// workgroup, two workgroups per CU: each wave still owns 32 query rows and
+// visits the same key tiles in the same order with the same arithmetic, so
+// the results are bit-identical to the 8-wave form; the waves then run matrix
+// and softmax phases in turn and the other workgroup on the CU fills the gaps.
 namespace fw {
-constexpr int BM = 256, BN = 64;
-constexpr int NT = 512;         // threads
+constexpr int BN = 64;
 constexpr int TILE = BN * 128;  // elements of one swizzled 64-row tile
 constexpr float kLazy = 8.f;    // keep a stale running max while the new one exceeds it by <= 8 (log2)
 }  // namespace fw
 
-__global__ __launch_bounds__(fw::NT, 1) void attn_fwd_kernel(AttnArgs a) {
+template <int NW>  // waves per workgroup: 8 (256 query rows, ping-pong) or 4 (128 rows)
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(AttnArgs a) {
   using namespace fw;
+  constexpr int BM = 32 * NW;
   __shared__ __attribute__((aligned(256))) u16 kbuf[2 * TILE];
   __shared__ __attribute__((aligned(256))) u16 vbuf[2 * TILE];
   const int64_t S = a.S;
@@ -764,8 +772,11 @@ __global__ __launch_bounds__(fw::NT, 1) void attn_fwd_kernel(AttnArgs a) {
   const u16* V = static_cast<const u16*>(a.v) + static_cast<int64_t>(gl) * S * DH;
 
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, col = lane % 32, hf = lane / 32;
-  const bool first = wave < 4;  // waves w and w + 4 share a SIMD; the second runs one phase later
-  const int st = tid & 255;     // copy index within the group: the first waves copy K tiles, the second V tiles
+  // 8 waves: waves w and w + 4 share a SIMD, and the second runs one phase later
+  const bool first = NW == 4 || wave < 4;
+  // copy index within the group: with 8 waves the first waves copy K tiles and
+  // the second V tiles; with 4 waves every wave copies both
+  const int st = tid & 255;
   const int64_t qfirst = static_cast<int64_t>(qb) * BM;
   const int64_t wq0 = qfirst + 32 * wave;
   const int64_t myq = wq0 + col;
@@ -918,7 +929,23 @@ __global__ __launch_bounds__(fw::NT, 1) void attn_fwd_kernel(AttnArgs a) {
   }
   dma_wait();
   __syncthreads();
-  if (first) {
+  if constexpr (NW == 4) {
+    // no partner wave: K(j + 1) and V(j) are copied while tile j runs
+    for (int j = 0; j <= ntiles; ++j) {
+      if (j + 1 < ntiles) {
+        copy_tile(K, j + 1, kbuf + ((j + 1) & 1) * TILE, 0);
+        copy_tile(K, j + 1, kbuf + ((j + 1) & 1) * TILE, 1);
+      }
+      if (j < ntiles) {
+        copy_tile(V, j, vbuf + (j & 1) * TILE, 0);
+        copy_tile(V, j, vbuf + (j & 1) * TILE, 1);
+      }
+      matrix_phase(j);
+      softmax_phase(j);
+      dma_wait();
+      __syncthreads();
+    }
+  } else if (first) {
     for (int j = 0; j <= ntiles; ++j) {
       if (j + 1 < ntiles) copy_tile(K, j + 1, kbuf + ((j + 1) & 1) * TILE, 0);
       matrix_phase(j);
@@ -994,16 +1021,20 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(AttnArgs a) {
 // and filled by 4-row direct copies issued by the first wave of each SIMD:
 // with two waves per SIMD the first (older) wave finishes its tiles well
 // ahead of the second, so it has the time to issue them.
+// Small grids run the same code with 4 waves (128 query rows, two
+// workgroups per CU) and one K/V tile pair between barriers: each wave's rows,
+// tiles and arithmetic are those of the 8-wave form, so the bits are too.
 namespace dqk {
-constexpr int BM = 256, BN = 64;
-constexpr int NT = 512;  // threads
+constexpr int BN = 64;
 constexpr int TILE = BN * 128;  // swizzled 64-row tile (elements)
 constexpr int BUF = 2 * TILE;   // K and V
 }  // namespace dqk
 
-__global__ __launch_bounds__(dqk::NT, 1) void attn_dq_kernel(AttnArgs a) {
+template <int NW>  // waves per workgroup: 8 (256 query rows) or 4 (128 rows)
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_dq_kernel(AttnArgs a) {
   using namespace dqk;
-  __shared__ __attribute__((aligned(256))) u16 lds[4 * BUF];
+  constexpr int BM = 32 * NW, NT = 64 * NW;
+  __shared__ __attribute__((aligned(256))) u16 lds[(NW == 8 ? 4 : 2) * BUF];
   const int64_t S = a.S;
   const int nqb = static_cast<int>((S + BM - 1) / BM);
   const int lid = xcd_snake(blockIdx.x, gridDim.x);  // as in the forward (9.2 -> 2.5 GB fetched)
@@ -1053,7 +1084,7 @@ __global__ __launch_bounds__(dqk::NT, 1) void attn_dq_kernel(AttnArgs a) {
   auto stage_regs = [&](const u16* src, int j, u16* dst) {  // every thread, synchronous
     const int64_t r0 = static_cast<int64_t>(j) * BN;
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
+    for (int m = 0; m < BN * 16 / NT; ++m) {
       const int e = tid + NT * m, row = e >> 4, ck = e & 15;
       const u32x4 v = r0 + row < S ? ld16(src + (r0 + row) * DH + 8 * ck) : u32x4{0, 0, 0, 0};
       st16(dst + swz_off(row, ck), v);
@@ -1088,7 +1119,21 @@ __global__ __launch_bounds__(dqk::NT, 1) void attn_dq_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) dq[i] = zero16();
 
-  issue_pair(0, 0);
+  // 4 waves: tile j (K and V) in slot j & 1, copied one tile ahead
+  auto issue_one = [&](int j, int slot) {
+    if (whole(j)) {
+      copy_tile(K, j, lds + slot * BUF);
+      copy_tile(V, j, lds + slot * BUF + TILE);
+    } else {
+      stage_regs(K, j, lds + slot * BUF);
+      stage_regs(V, j, lds + slot * BUF + TILE);
+    }
+  };
+  if constexpr (NW == 4) {
+    if (ntiles > 0) issue_one(0, 0);
+  } else {
+    issue_pair(0, 0);
+  }
   dma_wait();
   __syncthreads();
   auto process = [&](int j, int cur) {
@@ -1150,13 +1195,22 @@ __global__ __launch_bounds__(dqk::NT, 1) void attn_dq_kernel(AttnArgs a) {
       }
     }
   };
-  for (int j0 = 0; j0 < ntiles; j0 += 2) {
-    const int p = (j0 >> 1) & 1;  // pair slot of tiles j0, j0 + 1
-    if (j0 + 2 < ntiles) issue_pair(j0 + 2, p ^ 1);
-    process(j0, 2 * p);
-    if (j0 + 1 < ntiles) process(j0 + 1, 2 * p + 1);
-    dma_wait();
-    __syncthreads();
+  if constexpr (NW == 4) {
+    for (int j = 0; j < ntiles; ++j) {
+      if (j + 1 < ntiles) issue_one(j + 1, (j + 1) & 1);
+      process(j, j & 1);
+      dma_wait();
+      __syncthreads();
+    }
+  } else {
+    for (int j0 = 0; j0 < ntiles; j0 += 2) {
+      const int p = (j0 >> 1) & 1;  // pair slot of tiles j0, j0 + 1
+      if (j0 + 2 < ntiles) issue_pair(j0 + 2, p ^ 1);
+      process(j0, 2 * p);
+      if (j0 + 1 < ntiles) process(j0 + 1, 2 * p + 1);
+      dma_wait();
+      __syncthreads();
+    }
   }
 
   if (myq < S) {
@@ -1311,9 +1365,16 @@ hipError_t dout(const void* dY, int64_t S, int64_t D, int d, const ChunkTable& t
   return hipGetLastError();
 }
 
+// Fewer than two rounds of 256-row workgroups: 128-row workgroups (the same
+// bits, see the kernel).
+static bool small_grid(const AttnArgs& a) { return cdiv(a.S, 256) * a.nq < 512; }
+
 hipError_t attn_fwd(const AttnArgs& a, hipStream_t st) {
   if (a.d != DH) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3(cdiv(a.S, fw::BM) * a.nq), dim3(fw::NT), 0, st, a);
+  if (small_grid(a))
+    hipLaunchKernelGGL(attn_fwd_kernel<4>, dim3(cdiv(a.S, 128) * a.nq), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(attn_fwd_kernel<8>, dim3(cdiv(a.S, 256) * a.nq), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 
@@ -1355,7 +1416,10 @@ hipError_t mfma_ceiling(int waves_per_simd, int iters, double* tflops, hipStream
 
 hipError_t attn_dq(const AttnArgs& a, hipStream_t st) {
   if (a.d != DH) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_dq_kernel, dim3(cdiv(a.S, dqk::BM) * a.nq), dim3(dqk::NT), 0, st, a);
+  if (small_grid(a))
+    hipLaunchKernelGGL(attn_dq_kernel<4>, dim3(cdiv(a.S, 128) * a.nq), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(attn_dq_kernel<8>, dim3(cdiv(a.S, 256) * a.nq), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 

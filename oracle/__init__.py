@@ -65,6 +65,9 @@ def _load():
         lib.oracle_backward_qkn.argtypes = [i64, i64, i32, i32, i32, i32, f64, f64, i32, vp, vp, vp,
                                             vp, vp, vp, vp, dp, dp, dp, dp, dp, dp, dp, dp, i32]
         lib.oracle_backward_qkn.restype = i32
+        lib.oracle_forward_rows_qkn.argtypes = [i64, i64, i32, i32, i32, i32, f64, f64, i32, vp, vp,
+                                                vp, vp, vp, vp, vp, i64, i32, i32, dp, dp, i32]
+        lib.oracle_forward_rows_qkn.restype = i32
         _lib = lib
     return _lib
 
@@ -128,11 +131,16 @@ def forward(X, Wq, Wk, Wv, H: int, G: int, d: int, causal: bool = True, nthreads
 
 
 def forward_rows(X, Wq, Wk, Wv, H: int, G: int, d: int, rows, causal: bool = True,
-                 heads=None, nthreads: int | None = None, rope_theta: float = 0.0):
+                 heads=None, nthreads: int | None = None, rope_theta: float = 0.0, q_norm=None,
+                 k_norm=None, qk_eps: float = 1e-6):
     """Forward at the token rows `rows` only, for query heads range(*heads)
     (default: all): (O_rows [n][H*d], LSE_rows [H][n]) in fp64; entries of
-    heads outside the range are NaN."""
-    (X, Wq, Wk, Wv), enc = _prep([X, Wq, Wk, Wv])
+    heads outside the range are NaN.  q_norm / k_norm as for forward()."""
+    norm = q_norm is not None
+    if norm != (k_norm is not None):
+        raise ValueError("QK-norm needs both q_norm and k_norm")
+    arrs, enc = _prep([X, Wq, Wk, Wv] + ([q_norm, k_norm] if norm else []))
+    X, Wq, Wk, Wv = arrs[:4]
     S, D = X.shape
     _check_shapes(S, D, H, G, d, Wq, Wk, Wv)
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
@@ -140,10 +148,18 @@ def forward_rows(X, Wq, Wk, Wv, H: int, G: int, d: int, rows, causal: bool = Tru
     h0, h1 = heads if heads is not None else (0, H)
     O = np.full((n, H * d), np.nan, np.float64)
     LSE = np.full((H, n), np.nan, np.float64)
-    rc = _load().oracle_forward_rows(S, D, H, G, d, int(bool(causal)), float(rope_theta), enc,
-                                     _ptr(X), _ptr(Wq),
-                                     _ptr(Wk), _ptr(Wv), _ptr(rows), n, int(h0), int(h1), _ptr(O),
-                                     _ptr(LSE), nthreads or default_threads())
+    if norm:
+        _check_norm(arrs[4], arrs[5], d)
+        rc = _load().oracle_forward_rows_qkn(S, D, H, G, d, int(bool(causal)), float(rope_theta),
+                                             float(qk_eps), enc, _ptr(X), _ptr(Wq), _ptr(Wk),
+                                             _ptr(Wv), _ptr(arrs[4]), _ptr(arrs[5]), _ptr(rows), n,
+                                             int(h0), int(h1), _ptr(O), _ptr(LSE),
+                                             nthreads or default_threads())
+    else:
+        rc = _load().oracle_forward_rows(S, D, H, G, d, int(bool(causal)), float(rope_theta), enc,
+                                         _ptr(X), _ptr(Wq), _ptr(Wk), _ptr(Wv), _ptr(rows), n,
+                                         int(h0), int(h1), _ptr(O), _ptr(LSE),
+                                         nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle_forward_rows rejected the shape or rows")
     return O, LSE

@@ -377,12 +377,16 @@ int oracle_forward_qkn(int64_t S, int64_t D, int H, int G, int d, int causal, do
 // are token indices; keys/values are projected only for the KV heads of those
 // query heads and the positions those rows see.  Outputs: Orows [nrows][H*d],
 // LSErows [H][nrows] (fp64); entries of other heads are left untouched.
-int oracle_forward_rows(int64_t S, int64_t D, int H, int G, int d, int causal,
-                        double rope_theta, int enc, const void* Xp, const void* Wqp,
-                        const void* Wkp, const void* Wvp, const int64_t* rows, int64_t nrows,
-                        int h0, int h1, double* Orows, double* LSErows, int nthreads) {
-  Shape s{S, D, H, G, d, causal, rope_theta};
-  if (!shape_ok(s) || nrows < 0 || h0 < 0 || h1 > H || h0 >= h1) return 1;
+}  // extern "C"
+
+namespace {
+
+int forward_rows_impl(const Shape& s, const QkNorm& nrm, int enc, const void* Xp, const void* Wqp,
+                      const void* Wkp, const void* Wvp, const int64_t* rows, int64_t nrows, int h0,
+                      int h1, double* Orows, double* LSErows, int nthreads) {
+  const int64_t S = s.S, D = s.D;
+  const int H = s.H, G = s.G, d = s.d;
+  if (nrows < 0 || h0 < 0 || h1 > H || h0 >= h1) return 1;
   int64_t need = 0;  // keys needed: [0, need)
   for (int64_t t = 0; t < nrows; ++t) {
     if (rows[t] < 0 || rows[t] >= S) return 1;
@@ -406,9 +410,11 @@ int oracle_forward_rows(int64_t S, int64_t D, int H, int G, int d, int causal,
   for (int g = s.kv(h0); g <= s.kv(h1 - 1); ++g) {
     project_head(X, Wk, sk, g, need, nullptr, K.data(), nthreads);
     project_head(X, Wv, sk, g, need, nullptr, V.data(), nthreads);
+    if (nrm.on()) normalize_rows(K.data(), need, d, nrm.gk, nrm.eps, nullptr, nullptr);
     rotate_rows(K.data(), need, nullptr, s, +1);
     for (int h = std::max(h0, g * s.r()); h < std::min(h1, (g + 1) * s.r()); ++h) {
       project_head(Xq, Wq, sq, h, nrows, nullptr, Q.data(), nthreads);
+      if (nrm.on()) normalize_rows(Q.data(), nrows, d, nrm.gq, nrm.eps, nullptr, nullptr);
       rotate_rows(Q.data(), nrows, rows, s, +1);
       parallel_for(nrows, nthreads, [&](int64_t t) {
         std::vector<double> scores;
@@ -420,6 +426,32 @@ int oracle_forward_rows(int64_t S, int64_t D, int H, int G, int d, int causal,
     }
   }
   return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int oracle_forward_rows(int64_t S, int64_t D, int H, int G, int d, int causal,
+                        double rope_theta, int enc, const void* Xp, const void* Wqp,
+                        const void* Wkp, const void* Wvp, const int64_t* rows, int64_t nrows,
+                        int h0, int h1, double* Orows, double* LSErows, int nthreads) {
+  Shape s{S, D, H, G, d, causal, rope_theta};
+  if (!shape_ok(s)) return 1;
+  return forward_rows_impl(s, QkNorm(), enc, Xp, Wqp, Wkp, Wvp, rows, nrows, h0, h1, Orows,
+                           LSErows, nthreads);
+}
+
+// Sampled rows with QK-norm (gamma_q, gamma_k [d] in encoding `enc`, eps >= 0).
+int oracle_forward_rows_qkn(int64_t S, int64_t D, int H, int G, int d, int causal,
+                            double rope_theta, double eps, int enc, const void* Xp,
+                            const void* Wqp, const void* Wkp, const void* Wvp, const void* gqp,
+                            const void* gkp, const int64_t* rows, int64_t nrows, int h0, int h1,
+                            double* Orows, double* LSErows, int nthreads) {
+  Shape s{S, D, H, G, d, causal, rope_theta};
+  if (!shape_ok(s) || !gqp || !gkp || !(eps >= 0.0)) return 1;
+  return forward_rows_impl(s, decode_norm(gqp, gkp, enc, d, eps), enc, Xp, Wqp, Wkp, Wvp, rows,
+                           nrows, h0, h1, Orows, LSErows, nthreads);
 }
 
 // Forward + backward of L = sum(O * dO).

@@ -6,15 +6,19 @@ bf16 inputs.  Each stage of the pages' method projects its heads from X and
 attends over the full sequence (paper.rainbus.top summary of "Untied
 Ulysses", section 方法步骤详情); the oracle computes the unchunked layer.
 
+With the argument `qwen3`, the same for one KV group of the Qwen3-32B
+attention shape: d_model 5120, 8 query heads sharing 1 KV head (written to
+sublayer_s32k_qwen3.npz).
+
 Inputs come from the seeded CPU generator of the package's input module
 (seed 0, drawn in the order X, Wq, Wk, Wv, dO), so the GPU test can draw the
 same bits again.  The oracle's full forward and backward run once (minutes
 on a few host cores); sampled rows of every output are stored, with the
-shape, the seed and a hash of the inputs, in sublayer_s32k.npz.  Values are
+shape, the seed and a hash of the inputs, in the .npz file.  Values are
 stored as float32 (relative rounding 6e-8, far below the comparison gates).
 
 This script calls only the oracle and the input generator:
-    python tests/golden/make_sublayer_s32k.py
+    python tests/golden/make_sublayer_s32k.py [qwen3]
 """
 from __future__ import annotations
 
@@ -29,11 +33,15 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(os.path.dirname(HERE))
 sys.path.insert(0, ROOT)
 
-OUT = os.path.join(HERE, "sublayer_s32k.npz")
-SHAPE = dict(S=32768, D=4096, H=4, G=1, d=128)
 SEED = 0
-# sampled rows: first/last rows of heads and blocks, and a few inside
-DWQ_ROWS = [0, 1, 126, 127, 133, 320, 484, 511]
+# name -> (output file, shape, sampled dWq rows); rows are first/last rows of
+# heads and blocks and a few inside
+VARIANTS = {
+    "llama3": ("sublayer_s32k.npz", dict(S=32768, D=4096, H=4, G=1, d=128),
+               [0, 1, 126, 127, 133, 320, 484, 511]),
+    "qwen3": ("sublayer_s32k_qwen3.npz", dict(S=32768, D=5120, H=8, G=1, d=128),
+              [0, 1, 127, 133, 320, 575, 896, 1023]),
+}
 DWK_ROWS = [0, 37, 64, 127]
 DWV_ROWS = [0, 50, 99, 127]
 TOKEN_ROWS = [0, 1, 4095, 4096, 16383, 16391, 32766, 32767]
@@ -49,13 +57,15 @@ def input_hash(inp) -> str:
     return h.hexdigest()
 
 
-def main():
+def main(variant="llama3"):
     import torch
 
     import oracle
     from headwise_chunked_context_stage_amd.synth import LayerShape, make_inputs, to_numpy_exact
 
-    shape = LayerShape(**SHAPE)
+    fname, shape_args, DWQ_ROWS = VARIANTS[variant]
+    OUT = os.path.join(HERE, fname)
+    shape = LayerShape(**shape_args)
     inp = make_inputs(shape, "bf16", seed=SEED, device="cpu")
     digest = input_hash(inp)
     oracle.build(force=False)
@@ -83,4 +93,4 @@ def main():
 
 
 if __name__ == "__main__":
-    main()
+    main(sys.argv[1] if len(sys.argv) > 1 else "llama3")

@@ -484,6 +484,51 @@ def test_qk_norm_matches_oracle_and_is_U_invariant(S, D, H, G, d, dtype, theta, 
                                          rope_theta=theta, out_proj=oproj), "pipelined")
 
 
+@pytest.mark.timeout(900)
+def test_full_size_qwen32b_s64k_qk_norm_rope_U_invariant():
+    """The Qwen3-32B attention block's own options at its shape (S = 65536,
+    d_model 5120, 64 query heads, 8 KV heads): QK-norm and the rotary
+    embedding with base 1e6, bit-identical for U in {1, 8, 64}; forward rows
+    of two groups' heads against the oracle (early rows and the last ones);
+    the Q/K scale invariance <dgamma_q, gamma_q> = <dgamma_k, gamma_k> (exact
+    for the exact layer) and finite outputs."""
+    cfg = CONFIGS["qwen32b_s64k"]
+    shape = cfg["shape"]
+    S, r = shape.S, shape.H // shape.G
+    inp = make_inputs(shape, "bf16", seed=0, device="cuda", qk_norm=True)
+    first = None
+    for U in cfg["U"]:
+        say("qwen32b S=65536 QK-norm + rope 1e6, U=%d" % U)
+        out = run_layer_ex(shape, "bf16", U, inp, rope_theta=1e6)
+        if first is not None:
+            assert_same_bits(first, out, "U=%d" % U)
+            del out
+            torch.cuda.empty_cache()
+            continue
+        first = out
+        n = S
+        np_in = [to_numpy_exact(inp["X"][:n])] + [to_numpy_exact(inp[k]) for k in ("Wq", "Wk", "Wv")]
+        nk = dict(rope_theta=1e6, q_norm=to_numpy_exact(inp["q_norm"]),
+                  k_norm=to_numpy_exact(inp["k_norm"]), qk_eps=1e-6)
+        rows = [0, 1, 1023, 4095, S - 1000, S - 2, S - 1]
+        for heads in ((0, r), (7 * r, 8 * r)):
+            say("  oracle rows %s heads %s" % (rows[:4], heads))
+            Or, Lr = oracle.forward_rows(*np_in, shape.H, shape.G, shape.d, rows, heads=heads, **nk)
+            c0, c1 = heads[0] * shape.d, heads[1] * shape.d
+            compare("O", host(out["O"][rows])[:, c0:c1], Or[:, c0:c1], 2e-2, 2e-3)
+            compare("LSE", host(out["LSE"][heads[0]:heads[1]][:, rows]), Lr[heads[0]:heads[1]], 2e-2, 2e-3)
+        gq, gk = inp["q_norm"].double(), inp["k_norm"].double()
+        dq, dk = out["dq_norm"].double(), out["dk_norm"].double()
+        a, b = float((dq * gq).sum()), float((dk * gk).sum())
+        scale = float(dq.norm() * gq.norm() + dk.norm() * gk.norm())
+        say("  <dgq,gq> %.6e  <dgk,gk> %.6e  relative %.2e" % (a, b, abs(a - b) / scale))
+        assert abs(a - b) <= 1e-2 * scale, (a, b, scale)
+        for k in QKN_KEYS:
+            assert torch.isfinite(out[k]).all(), k
+    del first
+    torch.cuda.empty_cache()
+
+
 def test_qk_norm_entry_points_reject_mismatched_arguments():
     """A QK-norm plan refuses the entry points without gamma, and
     upipe_fwd_ex / upipe_bwd_ex refuse a missing gamma or a tensor the plan
@@ -730,14 +775,15 @@ def test_full_size_llama8b_share_s1m():
 
 
 # ---------------------------------------------------------------- full d_model sub-layer
-def test_full_dmodel_sublayer_s32k_every_output_against_oracle():
-    """One KV group of the Llama3-8B shape at full d_model and S = 32768 (4
-    query heads, 1 KV head, D = 4096): every output against the fp64 oracle's
-    full backward, stored by tests/golden/make_sublayer_s32k.py -- sampled
-    rows of dWq, dWk, dWv element by element (each a sum over all 32768
-    tokens through the split contraction of the weight-gradient kernel), dX,
-    O and LSE at rows across the sequence -- for every legal U, bit-identical
-    across U."""
+@pytest.mark.parametrize("fixture", ["sublayer_s32k.npz", "sublayer_s32k_qwen3.npz"])
+def test_full_dmodel_sublayer_s32k_every_output_against_oracle(fixture):
+    """One KV group at full d_model and S = 32768 -- of the Llama3-8B shape (4
+    query heads, 1 KV head, D = 4096) and of the Qwen3-32B shape (8 query
+    heads, D = 5120): every output against the fp64 oracle's full backward,
+    stored by tests/golden/make_sublayer_s32k.py -- sampled rows of dWq, dWk,
+    dWv element by element (each a sum over all 32768 tokens through the split
+    contraction of the weight-gradient kernel), dX, O and LSE at rows across
+    the sequence -- for every legal U, bit-identical across U."""
     import os
     import sys
 
@@ -745,7 +791,7 @@ def test_full_dmodel_sublayer_s32k_every_output_against_oracle():
     sys.path.insert(0, golden)
     from make_sublayer_s32k import input_hash
 
-    fx = np.load(os.path.join(golden, "sublayer_s32k.npz"))
+    fx = np.load(os.path.join(golden, fixture))
     S, D, H, G, d = (int(v) for v in fx["shape"])
     shape = LayerShape(S=S, D=D, H=H, G=G, d=d)
     cpu_inp = make_inputs(shape, "bf16", seed=int(fx["seed"]), device="cpu")

@@ -85,6 +85,11 @@ def test_qknorm_against_torch_library(oracle_mod, shape, causal, theta):
     np.testing.assert_array_equal(LSE, got["LSE"])
     plain = oracle_mod.forward(X, Wq, Wk, Wv, H, G, d, causal=causal, rope_theta=theta)[0]
     assert np.abs(plain - O).max() > 1e-3  # the normalisation is applied
+    rows = [0, 3, S // 2, S - 1]
+    Or, Lr = oracle_mod.forward_rows(X, Wq, Wk, Wv, H, G, d, rows, causal=causal, rope_theta=theta,
+                                     q_norm=gq, k_norm=gk, qk_eps=EPS)
+    close(Or, O[rows])
+    close(Lr, LSE[:, rows])
 
 
 def test_qknorm_finite_differences(oracle_mod):

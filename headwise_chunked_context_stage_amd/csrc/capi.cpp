@@ -327,7 +327,8 @@ hipError_t stage_gradients(const Plan& p, const Stage& st, const Kernels& K, con
       t.dw[i] = chunks[b + i].dw;
     }
     t.czero = first_stage && b == 0;  // the first dX launch starts the running sum
-    hipError_t err = timed(UPIPE_K_DW, s, [&] { return K.dw(in.X, p.S, p.D, p.d, t, s); });
+    float* dws = reinterpret_cast<float*>(at(in.ws, p.ws.dws));
+    hipError_t err = timed(UPIPE_K_DW, s, [&] { return K.dw(in.X, p.S, p.D, p.d, t, dws, s); });
     if (err != hipSuccess) return err;
     err = timed(UPIPE_K_DX, s, [&] { return K.dx(in.dX, p.S, p.D, p.d, t, s); });
     if (err != hipSuccess) return err;
@@ -407,10 +408,11 @@ hipError_t stage_dout(const Plan& p, const Stage& st, const Kernels& K, void* ws
 
 // Backward: dWo = dY^T O for every head (one launch fills the chip; a
 // stage's heads alone would leave it half idle).
-hipError_t layer_dwo(const Plan& p, const Kernels& K, const OutProj& op, hipStream_t s) {
+hipError_t layer_dwo(const Plan& p, const Kernels& K, const OutProj& op, void* ws, hipStream_t s) {
   const int64_t ld = static_cast<int64_t>(p.H) * p.d;
+  float* dws = reinterpret_cast<float*>(at(ws, p.ws.dws));
   return per_head_chunks(p, all_heads(p), op.O, op.Wo, op.dWo, nullptr, [&](const ChunkTable& t) {
-    return timed(UPIPE_K_DWO, s, [&] { return K.dwo(op.dY, p.S, p.D, p.d, t, ld, s); });
+    return timed(UPIPE_K_DWO, s, [&] { return K.dwo(op.dY, p.S, p.D, p.d, t, ld, dws, s); });
   });
 }
 
@@ -726,7 +728,7 @@ int run_bwd(const Plan& p, const BwdIn& in, hipStream_t s, const OutProj* op, co
   }
   // dWo reads only the inputs dY and O; last, on the caller's stream (after
   // the pipelined path has joined its helper stream)
-  if (op) UPIPE_TRY(layer_dwo(p, K, *op, s));
+  if (op) UPIPE_TRY(layer_dwo(p, K, *op, in.ws, s));
   return UPIPE_OK;
 }
 

@@ -259,10 +259,12 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(const u16* __restrict__ X,
 // row-major into LDS in the attention tile layout (64 rows of 128 columns,
 // 16-byte chunks, no transposes) and read as column operands with the
 // transposing LDS reads; A and B then present the same k-slot order.  A launch
-// has few output tiles and a long contraction, so each workgroup splits K: two
-// groups of four waves sum the first and the second half of the k-steps (the
-// split point depends on S only), and the halves are added in that order
-// through LDS.
+// has few output tiles and a long contraction, so K is split twice, at points
+// that depend on S only: into dw_parts(S) parts of the k-steps, one workgroup
+// each (part 0 writes dW, part p > 0 scratch tile p - 1 of its chunk, and
+// dw_fold_kernel adds the parts in order), and inside a workgroup into two
+// halves, summed by two groups of four waves and added in that order through
+// LDS.
 namespace dwk {
 constexpr int ROWS = 64;            // contraction rows per k-step
 constexpr int TILE = ROWS * RS;     // one operand tile
@@ -271,17 +273,24 @@ constexpr int NRR = 3;              // k-steps of global loads in flight
 
 // TR (the output projection's weight gradient): A has row stride `ld`
 // (a head's columns of O [S][H*d]) and the result is stored transposed,
-// dW[k][c] at t.dw[ch] + k * ld + c (dWo [d_model][H*d]).
+// dW[k][c] at t.dw[ch] + k * ld + c (dWo [d_model][H*d]).  A scratch tile
+// holds a part in the output's layout with its own row stride: [128][D], or
+// [D][128] for TR.
 template <bool TR>
 __global__ __launch_bounds__(512, 1) void dw_kernel(const u16* __restrict__ X, int64_t S, int64_t D,
-                                                    ChunkTable t, int ncb, int64_t ld) {
+                                                    ChunkTable t, int ncb, int64_t ld, int nparts,
+                                                    float* __restrict__ scratch) {
   using namespace dwk;
   __shared__ __attribute__((aligned(16))) u16 lds[2][2][2 * TILE];  // [group][buffer][A tile, X tile]
-  const int total = ncb * t.n;
-  const int lid = xcd_remap(blockIdx.x, total);
-  const int cb = lid / t.n, ch = lid % t.n;
+  // logical id = (part, column block, chunk), chunk fastest: the chunks of a
+  // column block read the same X rows; each XCD takes a contiguous range
+  const int per_part = ncb * t.n;
+  const int lid = xcd_remap(blockIdx.x, per_part * nparts);
+  const int part = lid / per_part, rem = lid % per_part;
+  const int cb = rem / t.n, ch = rem % t.n;
   const u16* A = static_cast<const u16*>(t.a[ch]);
-  float* dW = t.dw[ch];
+  float* dW = part == 0 ? t.dw[ch] : scratch + (static_cast<int64_t>(part - 1) * t.n + ch) * GB * D;
+  const int64_t ldw = TR ? (part == 0 ? ld : GB) : D;  // row stride of dW's layout
   const int64_t k0 = static_cast<int64_t>(cb) * GB;  // column block of D
   const int grp = threadIdx.x / 256, tid = threadIdx.x % 256;
   const int wave = tid / 64, lane = tid % 64, col = lane % 32, hf = lane / 32;
@@ -291,11 +300,13 @@ __global__ __launch_bounds__(512, 1) void dw_kernel(const u16* __restrict__ X, i
   const int srow = tid >> 4, sc = tid & 15;
 
   u32x4 rr[NRR][8];
-  const int nk_all = static_cast<int>((S + ROWS - 1) / ROWS);
-  const int half = (nk_all + 1) / 2;
-  const int kfirst = grp ? half : 0;          // first k-step of this group
-  const int nk = grp ? nk_all - half : half;  // k-steps of this group
-  const int nk_max = half;                    // rounds run by both groups
+  const int64_t nk_all = (S + ROWS - 1) / ROWS;
+  const int p0 = static_cast<int>(nk_all * part / nparts);  // this part's k-steps [p0, p1)
+  const int p1 = static_cast<int>(nk_all * (part + 1) / nparts);
+  const int half = (p1 - p0 + 1) / 2;
+  const int kfirst = p0 + (grp ? half : 0);       // first k-step of this group
+  const int nk = grp ? p1 - p0 - half : half;     // k-steps of this group
+  const int nk_max = half;                        // rounds run by both groups
   auto load = [&](int set, int kb) {
     const int64_t s0 = static_cast<int64_t>(kfirst + kb) * ROWS;
 #pragma unroll
@@ -386,7 +397,7 @@ __global__ __launch_bounds__(512, 1) void dw_kernel(const u16* __restrict__ X, i
           if constexpr (TR) {  // registers 4 i4 .. 4 i4 + 3 hold four consecutive c
             const int c = 64 * wm + 32 * mb + 8 * i4 + 4 * hf;
             const int64_t k = k0 + 64 * wn + 32 * nb + col;
-            *reinterpret_cast<f32x4*>(dW + k * ld + c) =
+            *reinterpret_cast<f32x4*>(dW + k * ldw + c) =
                 f32x4{acc[mb][nb][4 * i4] + o[0], acc[mb][nb][4 * i4 + 1] + o[1],
                       acc[mb][nb][4 * i4 + 2] + o[2], acc[mb][nb][4 * i4 + 3] + o[3]};
           } else {
@@ -395,11 +406,31 @@ __global__ __launch_bounds__(512, 1) void dw_kernel(const u16* __restrict__ X, i
               const int i = 4 * i4 + e;
               const int c = 64 * wm + 32 * mb + 8 * (i / 4) + 4 * hf + (i % 4);
               const int64_t k = k0 + 64 * wn + 32 * nb + col;
-              dW[static_cast<int64_t>(c) * D + k] = acc[mb][nb][i] + o[e];
+              dW[static_cast<int64_t>(c) * ldw + k] = acc[mb][nb][i] + o[e];
             }
           }
         }
   }
+}
+
+// dW of each chunk = part 0 (in dW) + part 1 + ... + part P - 1 (scratch), in
+// that order.  Grid (float4 groups of a chunk's 128 x D block / 256, chunks).
+template <bool TR>
+__global__ __launch_bounds__(256) void dw_fold_kernel(ChunkTable t, const float* __restrict__ scratch,
+                                                      int64_t D, int64_t ld, int nparts) {
+  const int ch = blockIdx.y;
+  const int64_t e = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;  // index in the tile
+  if (e >= GB * D) return;
+  // tile layout [128][D] (dW rows), or [D][128] for TR (dW at k * ld + c)
+  const int64_t out = TR ? (e / GB) * ld + e % GB : e;
+  f32x4 v = *reinterpret_cast<const f32x4*>(t.dw[ch] + out);
+  for (int p = 1; p < nparts; ++p) {
+    const f32x4 s = *reinterpret_cast<const f32x4*>(
+        scratch + (static_cast<int64_t>(p - 1) * t.n + ch) * GB * D + e);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] += s[j];
+  }
+  *reinterpret_cast<f32x4*>(t.dw[ch] + out) = v;
 }
 
 // ---- input gradient: dX[i][k] += sum over chunks (table order) of
@@ -1324,21 +1355,46 @@ hipError_t proj(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t,
   return hipGetLastError();
 }
 
-hipError_t dw(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t, hipStream_t st) {
-  if (d != DH || D % GB != 0) return hipErrorInvalidValue;
+// Weight gradients, dw_batch(P) chunks per launch: the parts' GEMM, then
+// (P > 1) the fold of the parts into dW.
+template <bool TR>
+hipError_t dw_launch(const u16* B, int64_t S, int64_t D, const ChunkTable& t, int64_t ld,
+                     float* scratch, hipStream_t st) {
+  if (t.n <= 0) return hipSuccess;
   const int ncb = static_cast<int>(D / GB);
-  hipLaunchKernelGGL(dw_kernel<false>, dim3(ncb * t.n), dim3(512), 0, st, static_cast<const u16*>(X),
-                     S, D, t, ncb, int64_t(DH));
-  return hipGetLastError();
+  const int P = dw_parts(S), nb = dw_batch(P) < t.n ? dw_batch(P) : t.n;
+  if (P > 1 && !scratch) return hipErrorInvalidValue;
+  for (int b = 0; b < t.n; b += nb) {
+    ChunkTable u = t;
+    u.n = t.n - b < nb ? t.n - b : nb;
+    for (int i = 0; i < u.n; ++i) {
+      u.a[i] = t.a[b + i];
+      u.w[i] = t.w[b + i];
+      u.dw[i] = t.dw[b + i];
+    }
+    hipLaunchKernelGGL(dw_kernel<TR>, dim3(ncb * u.n * P), dim3(512), 0, st, B, S, D, u, ncb, ld, P,
+                       scratch);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (P > 1) {
+      hipLaunchKernelGGL(dw_fold_kernel<TR>, dim3(cdiv(GB * D / 4, 256), u.n), dim3(256), 0, st, u,
+                         scratch, D, ld, P);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+hipError_t dw(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t, float* scratch,
+              hipStream_t st) {
+  if (d != DH || D % GB != 0) return hipErrorInvalidValue;
+  return dw_launch<false>(static_cast<const u16*>(X), S, D, t, int64_t(DH), scratch, st);
 }
 
 hipError_t dwo(const void* dY, int64_t S, int64_t D, int d, const ChunkTable& t, int64_t ld,
-               hipStream_t st) {
+               float* scratch, hipStream_t st) {
   if (d != DH || D % GB != 0 || ld % 4 != 0) return hipErrorInvalidValue;
-  const int ncb = static_cast<int>(D / GB);
-  hipLaunchKernelGGL(dw_kernel<true>, dim3(ncb * t.n), dim3(512), 0, st, static_cast<const u16*>(dY),
-                     S, D, t, ncb, ld);
-  return hipGetLastError();
+  return dw_launch<true>(static_cast<const u16*>(dY), S, D, t, ld, scratch, st);
 }
 
 hipError_t dx(float* dX, int64_t S, int64_t D, int d, const ChunkTable& t, hipStream_t st) {

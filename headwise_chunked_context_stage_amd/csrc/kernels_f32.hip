@@ -318,7 +318,8 @@ hipError_t proj(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t,
   return hipGetLastError();
 }
 
-hipError_t dw(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t, hipStream_t st) {
+hipError_t dw(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t, float* /*scratch*/,
+              hipStream_t st) {
   hipLaunchKernelGGL(dw_kernel, dim3(cdiv(D, 256), d, t.n), dim3(256), 0, st,
                      static_cast<const float*>(X), S, D, d, t);
   return hipGetLastError();
@@ -355,7 +356,7 @@ hipError_t dout(const void* dY, int64_t S, int64_t D, int d, const ChunkTable& t
 }
 
 hipError_t dwo(const void* dY, int64_t S, int64_t D, int d, const ChunkTable& t, int64_t ld,
-               hipStream_t st) {
+               float* /*scratch*/, hipStream_t st) {
   hipLaunchKernelGGL(dwo_kernel, dim3(cdiv(D, 4), cdiv(d, 64), t.n), dim3(256), 0, st,
                      static_cast<const float*>(dY), S, D, d, t, ld);
   return hipGetLastError();

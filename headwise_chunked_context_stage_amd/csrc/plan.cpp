@@ -148,6 +148,15 @@ int make_plan(Plan& p, int64_t S, int64_t D, int H, int G, int d, int U, int cau
     w.pq = take(static_cast<size_t>(U) * nb * d * 4);
     w.pk = take(nkv * nb * d * 4);
   }
+  // bf16 weight gradients: partial sums of the token parts after the first,
+  // for the most chunks one call passes (a stage's heads, plus its group's K
+  // and V; with the output projection, the heads of the dWo launches)
+  int nmax = 0;
+  for (const Stage& st : p.stages) nmax = std::max(nmax, st.nq + (st.done ? 2 * st.nkv : 0));
+  if (p.out_proj) nmax = std::max(nmax, H);
+  nmax = std::min(nmax, kMaxChunks);
+  const size_t dws = dtype == UPIPE_BF16 ? dw_scratch_bytes(S, D, nmax) : 0;
+  w.dws = dws ? take(dws) : 0;
   w.bwd_bytes = off;
   return UPIPE_OK;
 }

@@ -48,6 +48,8 @@ struct WsLayout {
   size_t gq32[2], gk32[2];     // bf16: fp32 gradients of the normalised rows before their
                                // backward, [U][S][d] and [kv][S][d] (fp32 plans use dq/dk)
   size_t pq, pk;               // per-256-token-block sums for dgamma: [U][nb][d], [kv][nb][d]
+  size_t dws;                  // bf16: partial weight gradients of the token parts after the
+                               // first, dw_scratch_bytes(S, D, nmax) (none when S < 8192)
   size_t fwd_bytes, bwd_bytes;
 };
 
@@ -102,6 +104,22 @@ int choose_u(int64_t S, int64_t D, int H, int G, int d, int causal, int dtype, s
 // the projection (out[i] = X * W[i]^T), the weight gradient
 // (dW[i] = a[i]^T X) and the input gradient (dX += sum_i a[i] W[i]).
 constexpr int kMaxChunks = 64;
+
+// bf16 weight gradients: the token range (the contraction of dW = a^T X) is
+// cut into dw_parts(S) parts of equal k-step counts, a number fixed by S alone
+// so that every U sums in the same order.  Each part is its own fp32 sum (its
+// own workgroups, so a thin stage still fills the chip); the first goes to dW,
+// the others to (P - 1) scratch tiles of [d = 128][D] fp32 per chunk, and a
+// fold adds parts 1 .. P - 1 to dW in that order.  A launch takes up to
+// dw_batch(P) chunks (the chunks of a launch share their reads of X), so the
+// scratch holds at most 16 tiles; `nmax` is the most chunks one call passes.
+inline int dw_parts(int64_t S) { return S < 8192 ? 1 : static_cast<int>(S >= 32768 ? 8 : S / 4096); }
+inline int dw_batch(int parts) { return parts == 1 ? kMaxChunks : (16 / (parts - 1) > 0 ? 16 / (parts - 1) : 1); }
+inline size_t dw_scratch_bytes(int64_t S, int64_t D, int nmax) {
+  const int P = dw_parts(S);
+  const int nb = dw_batch(P) < nmax ? dw_batch(P) : nmax;
+  return P == 1 ? 0 : static_cast<size_t>(P - 1) * nb * 128 * static_cast<size_t>(D) * 4;
+}
 struct ChunkTable {
   int n;
   uint64_t rot;               // projection: bit i set = rotate chunk i's rows (queries, keys)
@@ -163,7 +181,9 @@ hipError_t attn_fwd(const AttnArgs& a, hipStream_t st);
 hipError_t bwd_pre(const AttnArgs& a, hipStream_t st);
 hipError_t attn_dkv(const AttnArgs& a, hipStream_t st);
 hipError_t attn_dq(const AttnArgs& a, hipStream_t st);
-hipError_t dw(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t, hipStream_t st);
+// `scratch`: dw_scratch_bytes(S, D, t.n) bytes or more (may be null when that is 0).
+hipError_t dw(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t, float* scratch,
+              hipStream_t st);
 hipError_t dx(float* dX, int64_t S, int64_t D, int d, const ChunkTable& t, hipStream_t st);
 // Output projection (chunks = heads ascending; a[ch] / w[ch] point at the
 // head's columns of O and Wo, row stride ld = H*d):
@@ -175,7 +195,7 @@ hipError_t oproj(float* Y, int64_t S, int64_t D, int d, const ChunkTable& t, int
 hipError_t dout(const void* dY, int64_t S, int64_t D, int d, const ChunkTable& t, int64_t ld,
                 hipStream_t st);
 hipError_t dwo(const void* dY, int64_t S, int64_t D, int d, const ChunkTable& t, int64_t ld,
-               hipStream_t st);
+               float* scratch, hipStream_t st);
 // dense MFMA stream on every CU; TFLOP/s (synchronous)
 hipError_t mfma_ceiling(int waves_per_simd, int iters, double* tflops, hipStream_t st);
 }  // namespace bf16
@@ -185,7 +205,9 @@ hipError_t attn_fwd(const AttnArgs& a, hipStream_t st);
 hipError_t bwd_pre(const AttnArgs& a, hipStream_t st);
 hipError_t attn_dkv(const AttnArgs& a, hipStream_t st);
 hipError_t attn_dq(const AttnArgs& a, hipStream_t st);
-hipError_t dw(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t, hipStream_t st);
+// `scratch` is not used (same signature as the bf16 launcher).
+hipError_t dw(const void* X, int64_t S, int64_t D, int d, const ChunkTable& t, float* scratch,
+              hipStream_t st);
 hipError_t dx(float* dX, int64_t S, int64_t D, int d, const ChunkTable& t, hipStream_t st);
 // In-place rotation of n [S][d] fp32 buffers at `buf` (consecutive): sign +1
 // rotates queries/keys, -1 applies the transposed rotation to gradients.
@@ -195,7 +217,7 @@ hipError_t oproj(float* Y, int64_t S, int64_t D, int d, const ChunkTable& t, int
 hipError_t dout(const void* dY, int64_t S, int64_t D, int d, const ChunkTable& t, int64_t ld,
                 hipStream_t st);
 hipError_t dwo(const void* dY, int64_t S, int64_t D, int d, const ChunkTable& t, int64_t ld,
-               hipStream_t st);
+               float* scratch, hipStream_t st);
 }  // namespace f32
 hipError_t fill_zero(void* p, size_t bytes, hipStream_t st);
 

@@ -42,11 +42,11 @@ hipError_t attn_fwd(const AttnArgs&, hipStream_t) { return launched(); }
 hipError_t bwd_pre(const AttnArgs&, hipStream_t) { return launched(); }
 hipError_t attn_dkv(const AttnArgs&, hipStream_t) { return launched(); }
 hipError_t attn_dq(const AttnArgs&, hipStream_t) { return launched(); }
-hipError_t dw(const void*, int64_t, int64_t, int, const ChunkTable&, hipStream_t) { return launched(); }
+hipError_t dw(const void*, int64_t, int64_t, int, const ChunkTable&, float*, hipStream_t) { return launched(); }
 hipError_t dx(float*, int64_t, int64_t, int, const ChunkTable&, hipStream_t) { return launched(); }
 hipError_t oproj(float*, int64_t, int64_t, int, const ChunkTable&, int64_t, hipStream_t) { return launched(); }
 hipError_t dout(const void*, int64_t, int64_t, int, const ChunkTable&, int64_t, hipStream_t) { return launched(); }
-hipError_t dwo(const void*, int64_t, int64_t, int, const ChunkTable&, int64_t, hipStream_t) { return launched(); }
+hipError_t dwo(const void*, int64_t, int64_t, int, const ChunkTable&, int64_t, float*, hipStream_t) { return launched(); }
 hipError_t mfma_ceiling(int, int, double*, hipStream_t) { return launched(); }
 }  // namespace bf16
 namespace f32 {
@@ -55,12 +55,12 @@ hipError_t attn_fwd(const AttnArgs&, hipStream_t) { return launched(); }
 hipError_t bwd_pre(const AttnArgs&, hipStream_t) { return launched(); }
 hipError_t attn_dkv(const AttnArgs&, hipStream_t) { return launched(); }
 hipError_t attn_dq(const AttnArgs&, hipStream_t) { return launched(); }
-hipError_t dw(const void*, int64_t, int64_t, int, const ChunkTable&, hipStream_t) { return launched(); }
+hipError_t dw(const void*, int64_t, int64_t, int, const ChunkTable&, float*, hipStream_t) { return launched(); }
 hipError_t dx(float*, int64_t, int64_t, int, const ChunkTable&, hipStream_t) { return launched(); }
 hipError_t rope(float*, int, int64_t, int, const Rope&, int, hipStream_t) { return launched(); }
 hipError_t oproj(float*, int64_t, int64_t, int, const ChunkTable&, int64_t, hipStream_t) { return launched(); }
 hipError_t dout(const void*, int64_t, int64_t, int, const ChunkTable&, int64_t, hipStream_t) { return launched(); }
-hipError_t dwo(const void*, int64_t, int64_t, int, const ChunkTable&, int64_t, hipStream_t) { return launched(); }
+hipError_t dwo(const void*, int64_t, int64_t, int, const ChunkTable&, int64_t, float*, hipStream_t) { return launched(); }
 }  // namespace f32
 namespace norm {
 hipError_t fwd_f32(float*, int, int64_t, int, const float*, float, float*, float*, hipStream_t) { return launched(); }

@@ -341,6 +341,38 @@ def test_rope_long_positions():
         assert torch.isfinite(out[k]).all(), k
 
 
+# Weight gradients over token parts: from 8192 tokens on, the bf16 dW sums
+# run over dw_parts(S) = min(8, S // 4096) parts of the token range, one
+# workgroup each, folded in part order (a split fixed by S, so every U sums
+# alike).  These cases cross 2, 3 and 4 parts, one with a ragged last k-step.
+PART_CASES = [
+    # S, D, H, G (d = 128)
+    (8192, 256, 2, 1),    # 2 parts
+    (12000, 256, 2, 1),   # 2 parts, ragged
+    (12288, 384, 4, 2),   # 3 parts, two groups
+    (16384, 256, 2, 1),   # 4 parts
+]
+
+
+@pytest.mark.parametrize("S,D,H,G", PART_CASES)
+def test_bf16_weight_gradient_token_parts(S, D, H, G):
+    shape = LayerShape(S=S, D=D, H=H, G=G, d=128)
+    cpu_inp = make_inputs(shape, "bf16", seed=23, device="cpu")
+    ref = oracle_full(shape, cpu_inp)
+    inp = {k: v.cuda() for k, v in cpu_inp.items()}
+    first = None
+    for U in legal_us(H, G):
+        say("bf16 token parts S=%d D=%d H=%d G=%d U=%d" % (S, D, H, G, U))
+        out = run_layer(shape, "bf16", U, inp)
+        if first is None:
+            check_against_oracle(out, ref, "bf16", cpu_inp, shape)
+            first = out
+        else:
+            assert_same_bits(first, out, "U=%d" % U)
+    say("bf16 token parts pipelined U=1")
+    assert_same_bits(first, run_layer(shape, "bf16", 1, inp, pipeline=True), "pipelined")
+
+
 # ---------------------------------------------------------------- output projection
 # Y = O Wo^T after the attention (the Llama / Qwen attention block's output map;
 # not on the pages' step list): forward into Y (fp32, summed stage by stage),
@@ -351,6 +383,7 @@ OUT_CASES = [
     (1000, 1024, 4, 1, 128, "bf16", 0.0),       # ragged
     (768, 512, 8, 2, 128, "bf16", 500000.0),    # two groups, with the rotary embedding
     (512, 1536, 8, 8, 128, "bf16", 0.0),        # MHA, d_model (1536) wider than H*d (1024)
+    (8192, 256, 2, 1, 128, "bf16", 0.0),        # dWo over 2 token parts (transposed fold)
     (320, 256, 4, 2, 64, "f32", 10000.0),
 ]
 

@@ -173,8 +173,14 @@ def test_qwen3_32b_reduction_matches_pages():
     ratio = u_small.peak_bytes_phase(0) / u_all.peak_bytes_phase(0)
     assert ratio == g["upipe_coeff"] / g["ulysses_coeff"]
     assert 100.0 * (1.0 - ratio) == g["reduction_percent"]
-    # the backward's stage buffers scale the same way
-    assert u_small.peak_bytes_phase(1) / u_all.peak_bytes_phase(1) == pytest.approx(1 / 8, rel=1e-3)
+    # the backward's stage buffers scale the same way; the weight-gradient
+    # scratch (partial sums of 7 token parts, 128 x D fp32 each) is the same
+    # for every U
+    # (U = 8: 10 chunks per stage, U = 64: 64 per call; both take 2 per launch)
+    scratch = dw_scratch_closed_form(S, D, 10)
+    assert scratch == dw_scratch_closed_form(S, D, 64) == 14 * 128 * D * 4
+    ratio_b = (u_small.peak_bytes_phase(1) - scratch) / (u_all.peak_bytes_phase(1) - scratch)
+    assert ratio_b == pytest.approx(1 / 8, rel=1e-3)
 
 
 FAKE = 1 << 20  # a 256-aligned non-null address; never dereferenced (validation fails first)
@@ -268,6 +274,42 @@ def test_auto_u_rejects_bad_shapes_and_null_output():
     assert e.value.code == upipe.UPIPE_ERR_UNSUPPORTED
     L = upipe.lib()
     assert L.upipe_auto_u(4096, 1024, 32, 8, 128, 1, 0, 1 << 40, None) == upipe.UPIPE_ERR_ARG
+
+
+def dw_scratch_closed_form(S, D, nmax):
+    """bf16 weight-gradient scratch: the token range is cut into P parts
+    (P = 1 below 8192 tokens, S // 4096 up to 8 parts, 8 from 32768 tokens on);
+    parts 1..P-1 of up to min(nmax, max(1, 16 // (P - 1))) chunks at a time are
+    kept as 128 x D fp32 tiles (nmax: the most chunks of one call)."""
+    P = 1 if S < 8192 else (8 if S >= 32768 else S // 4096)
+    if P == 1:
+        return 0
+    return (P - 1) * min(nmax, max(1, 16 // (P - 1))) * 128 * D * 4
+
+
+def test_dw_scratch_is_fixed_by_s_and_d():
+    """The weight-gradient scratch is a backward-only region: the token parts
+    depend on S only (so every U sums dW over the same parts), the tiles on
+    d_model and on the chunks one stage passes (its heads, plus K and V of the
+    group it finishes): bwd bytes(U) - the stage buffers' closed form."""
+    d, D, H, G = 128, 1024, 8, 2
+    r = H // G
+    for S in (4096, 8191, 8192, 12288, 16384, 20480, 32768, 65536):
+        for U in legal_us(H, G):
+            kv_s = max(1, U // r)
+            qkv = 2 * S * d * (U + 2 * kv_s)
+            single = 2 * 4 * S * U + (2 * 4 * S * d if U < r else 0)
+            p = upipe.Plan(S, D, H, G, d, U)
+            extra = p.peak_bytes_phase(1) - (2 * qkv + single)
+            want = dw_scratch_closed_form(S, D, U + 2 * kv_s)
+            # regions are 256-byte aligned (S = 8191 rounds up)
+            assert want <= extra < want + 16 * 256, (S, U, extra, want)
+            assert p.peak_bytes_phase(0) == qkv
+    # fp32 plans use their own weight-gradient kernel: no scratch
+    p = upipe.Plan(32768, 256, 4, 2, 64, 2, dtype="f32")
+    S, d, U, kv_s = 32768, 64, 2, 1
+    qkv = 4 * S * d * (U + 2 * kv_s)
+    assert p.peak_bytes_phase(1) == 2 * qkv + 2 * 4 * S * U
 
 
 def test_pipelined_plan_doubles_the_per_stage_buffers():

@@ -473,11 +473,16 @@ __global__ __launch_bounds__(256, 2) void dx_kernel(float* __restrict__ dX, int6
   const int wm = wave / 2, wn = wave % 2;
 
   // A: thread tid moves 16-column groups (row tid / 4 + 64 m, group tid % 4), m < 2;
-  // W: rows tid / 16 + 16 m (m < 4), 16-byte chunk tid % 16.
+  // W: rows tid / 16 + 16 m (m < 4), 16-byte chunk tid % 16.  Global loads run
+  // NRR k-steps ahead of their LDS store through a ring of register sets (a
+  // stage has few k-steps, 2 per chunk, each too short to hide a load).
+  constexpr int NRR = 3;
   const int arow = tid >> 2, agrp = tid & 3;
   const int wrow = tid >> 4, wc = tid & 15;
-  u32x4 ra[2][2], rw[4];
-  auto load = [&](int step) {
+  const int nsteps = t.n * (DH / GK);
+  u32x4 ra[NRR][2][2], rw[NRR][4];
+  auto load = [&](int set, int step) {
+    if (step >= nsteps) return;
     const int ch = step / (DH / GK), c0 = (step % (DH / GK)) * GK;
     const u16* Ap = static_cast<const u16*>(t.a[ch]);
     const u16* Wp = static_cast<const u16*>(t.w[ch]);
@@ -485,28 +490,40 @@ __global__ __launch_bounds__(256, 2) void dx_kernel(float* __restrict__ dX, int6
     for (int m = 0; m < 2; ++m) {
       const int64_t gi = i0 + arow + 64 * m;
       const u16* src = Ap + gi * DH + c0 + 16 * agrp;
-      ra[m][0] = gi < S ? ld16(src) : u32x4{0, 0, 0, 0};
-      ra[m][1] = gi < S ? ld16(src + 8) : u32x4{0, 0, 0, 0};
+      ra[set][m][0] = gi < S ? ld16(src) : u32x4{0, 0, 0, 0};
+      ra[set][m][1] = gi < S ? ld16(src + 8) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int m = 0; m < 4; ++m) rw[m] = ld16(Wp + static_cast<int64_t>(c0 + wrow + 16 * m) * D + k0 + wc * 8);
+    for (int m = 0; m < 4; ++m)
+      rw[set][m] = ld16(Wp + static_cast<int64_t>(c0 + wrow + 16 * m) * D + k0 + wc * 8);
   };
-  auto store = [&](int b) {
+  auto store = [&](int set, int b) {
     u16* as = lds + b * (AT + WT);
     u16* wt = as + AT;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       // logical columns [0-3 | 4-7] [8-11 | 12-15] -> physical [0-3 | 8-11] [4-7 | 12-15]
-      const u32x4 lo = {ra[m][0][0], ra[m][0][1], ra[m][1][0], ra[m][1][1]};
-      const u32x4 hi = {ra[m][0][2], ra[m][0][3], ra[m][1][2], ra[m][1][3]};
+      const u32x4 lo = {ra[set][m][0][0], ra[set][m][0][1], ra[set][m][1][0], ra[set][m][1][1]};
+      const u32x4 hi = {ra[set][m][0][2], ra[set][m][0][3], ra[set][m][1][2], ra[set][m][1][3]};
       u16* dst = as + (arow + 64 * m) * GS + 16 * agrp;
       st16(dst, lo);
       st16(dst + 8, hi);
     }
 #pragma unroll
-    for (int m = 0; m < 4; ++m) st16(wt + toff(wrow + 16 * m, wc * 8), rw[m]);
+    for (int m = 0; m < 4; ++m) st16(wt + toff(wrow + 16 * m, wc * 8), rw[set][m]);
   };
 
+  // the first k-steps' operands, then the running dX (the C input), all in flight together.
+  // C element (mb, nb, i) is row 64 wm + 32 mb + 8 (i / 4) + 4 hf + i % 4, column
+  // 64 wn + 32 nb + col of the tile: a per-lane offset plus a wave-uniform row offset
+  // (a scalar address) plus 32 nb.
+#pragma unroll
+  for (int i = 0; i < NRR; ++i) load(i, i);
+  float* const ctile = dX + i0 * D;
+  const int coff = (64 * wm + 4 * hf) * static_cast<int>(D) + static_cast<int>(k0) + 64 * wn + col;
+  const bool cfull = i0 + GB <= S;  // no row of the tile past S
+  const int crow_lim = static_cast<int>(S - i0) - (64 * wm + 4 * hf);  // row r of the lane is in when r < lim
+  auto crow = [&](int mb, int i) { return 32 * mb + 8 * (i / 4) + (i % 4); };
   f32x16 acc[2][2];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
@@ -514,18 +531,18 @@ __global__ __launch_bounds__(256, 2) void dx_kernel(float* __restrict__ dX, int6
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int64_t gi = i0 + 64 * wm + 32 * mb + 8 * (i / 4) + 4 * hf + (i % 4);
-        const int64_t k = k0 + 64 * wn + 32 * nb + col;
-        acc[mb][nb][i] = (gi < S && !t.czero) ? dX[gi * D + k] : 0.f;
+        const float* rp = ctile + static_cast<int64_t>(crow(mb, i)) * D;
+        const bool in = cfull || crow(mb, i) < crow_lim;
+        acc[mb][nb][i] = (in && !t.czero) ? rp[coff + 32 * nb] : 0.f;
       }
 
-  const int nsteps = t.n * (DH / GK);
-  load(0);
-  store(0);
+  store(0, 0);
+  load(0, NRR);
   __syncthreads();
-  for (int sidx = 0; sidx < nsteps; ++sidx) {
+  // step sidx's data sits in register set sidx % NRR until its LDS store
+  auto body = [&](int sidx, auto setc) {  // setc = (sidx + 1) % NRR, a compile-time constant
+    constexpr int SN = decltype(setc)::value;
     const int cur = sidx & 1;
-    if (sidx + 1 < nsteps) load(sidx + 1);
     const u16* as = lds + cur * (AT + WT);
     const TileAddr tw = tile_addr(lds + cur * (AT + WT) + AT, lane);
 #pragma unroll
@@ -540,18 +557,29 @@ __global__ __launch_bounds__(256, 2) void dx_kernel(float* __restrict__ dX, int6
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma(fa[mb], fb[nb], acc[mb][nb]);
     }
-    if (sidx + 1 < nsteps) store(cur ^ 1);
+    if (sidx + 1 < nsteps) store(SN, cur ^ 1);
+    load(SN, sidx + 1 + NRR);  // the set just stored takes step sidx + 1 + NRR
     __syncthreads();
+  };
+  static_assert(NRR == 3 || NRR == 4, "the loop below is unrolled for 3 or 4 register sets");
+  int sidx = 0;
+  for (; sidx + NRR <= nsteps; sidx += NRR) {
+    body(sidx, std::integral_constant<int, 1 % NRR>{});
+    body(sidx + 1, std::integral_constant<int, 2 % NRR>{});
+    body(sidx + 2, std::integral_constant<int, 3 % NRR>{});
+    if constexpr (NRR > 3) body(sidx + 3, std::integral_constant<int, 4 % NRR>{});
   }
+  if (sidx < nsteps) body(sidx, std::integral_constant<int, 1 % NRR>{});
+  if (sidx + 1 < nsteps) body(sidx + 1, std::integral_constant<int, 2 % NRR>{});
+  if (NRR > 3 && sidx + 2 < nsteps) body(sidx + 2, std::integral_constant<int, 3 % NRR>{});
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int64_t gi = i0 + 64 * wm + 32 * mb + 8 * (i / 4) + 4 * hf + (i % 4);
-        const int64_t k = k0 + 64 * wn + 32 * nb + col;
-        if (gi < S) dX[gi * D + k] = acc[mb][nb][i];
+        float* rp = ctile + static_cast<int64_t>(crow(mb, i)) * D;
+        if (cfull || crow(mb, i) < crow_lim) rp[coff + 32 * nb] = acc[mb][nb][i];
       }
 }
 

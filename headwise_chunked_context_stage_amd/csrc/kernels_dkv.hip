@@ -18,8 +18,9 @@ namespace {
 // Eight waves: each 32-key block has a pair of waves on one SIMD.  With the
 // key in the lane (registers = query rows), the first wave of a pair computes
 // S = Q K^T, P = exp(S - LSE) and dV += P^T dO; the second computes
-// dP = dO V^T, dS = P (dP - D) with the first wave's fp32 P (exchanged
-// through LDS lane for lane) and dK += dS^T Q.  P^T and dS^T are A operands
+// dP - D = dO V^T (its accumulators start from -D, the MFMA C input),
+// dS = P (dP - D) with the first wave's fp32 P (exchanged through LDS lane
+// for lane) and dK += dS^T Q.  P^T and dS^T are A operands
 // straight from registers; dO and Q are read as column operands of the same
 // row-major tiles.  Each tile takes two barrier phases: in the first, the
 // second wave runs dK of the previous tile while the first wave evaluates the
@@ -170,7 +171,6 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
   // 32x64 C blocks of one tile: rows (query) x keys of this wave, two chains
   // over the 128 head columns; row operands from LDS two steps ahead.
   auto row_pass = [&](const SwzAddr& xa, f32x16 (&sv)[2]) {
-    sv[0] = sv[1] = zero16();
     bf16x8 fa[3][2];
     auto row_ops = [&](int t, bf16x8 (&f)[2]) {
       f[0] = swz_row_frag(xa, 0, t);
@@ -220,6 +220,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
         f32x4 l4[8];  // requested before the S MFMAs, so they are ready for the exponentials
 #pragma unroll
         for (int j = 0; j < 8; ++j) l4[j] = *reinterpret_cast<const f32x4*>(&stat[sg][0][8 * j + 4 * hf]);
+        sv[0] = sv[1] = zero16();
         row_pass(swz_addr(qs + sq * TILE, lane), sv);
         const int64_t q0 = static_cast<int64_t>(cc.qt) * BM;
         const bool need_mask = a.causal && q0 < wk0 + 31;
@@ -253,24 +254,30 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
     f32x16 sv[2];  // dP of the current tile
     for (int it = 0; it <= niter; ++it) {
       if (it + 1 < niter) issue(nc, sq + 1 == NQ ? 0 : sq + 1, sg ^ 1);
-      if (it < niter) row_pass(swz_addr(gs + sg * TILE, lane), sv);  // dP = dO V^T
+      if (it < niter) {
+        // dP - D = dO V^T with the accumulators starting from -D (rows in C layout)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&stat[sg][1][8 * j + 4 * hf]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sv[j / 4][4 * (j % 4) + e] = -d4[e];
+        }
+        row_pass(swz_addr(gs + sg * TILE, lane), sv);
+      }
       if (it >= 1) col_pass(swz_addr(qs + (sq == 0 ? NQ - 1 : sq - 1) * TILE, lane), op);  // dK += dS^T Q, tile it - 1
       __syncthreads();
       if (it < niter) {
         // dS = P (dP - D) with the partner's fp32 P
-        f32x4 d4[8], p4[8];
+        f32x4 p4[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          d4[j] = *reinterpret_cast<const f32x4*>(&stat[sg][1][8 * j + 4 * hf]);
-          p4[j] = pxch[kb][j][lane];
-        }
+        for (int j = 0; j < 8; ++j) p4[j] = pxch[kb][j][lane];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
             const int j = 4 * qb + g4;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sv[qb][4 * g4 + e] = p4[j][e] * (sv[qb][4 * g4 + e] - d4[j][e]);
+            for (int e = 0; e < 4; ++e) sv[qb][4 * g4 + e] = p4[j][e] * sv[qb][4 * g4 + e];
           }
 #pragma unroll
         for (int k4 = 0; k4 < 4; ++k4) op[k4] = pack8(sv[k4 / 2], k4 % 2);

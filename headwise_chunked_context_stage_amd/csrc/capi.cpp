@@ -252,6 +252,11 @@ AttnArgs bwd_args(const Plan& p, const Stage& st, const BwdIn& in) {
     a.dk_acc = reinterpret_cast<float*>(at(in.ws, p.ws.dk_acc));
     a.dv_acc = reinterpret_cast<float*>(at(in.ws, p.ws.dv_acc));
   }
+  a.kv_split = 1;
+  if (p.dtype == UPIPE_BF16 && dkv_split(p.S) == 2) {
+    a.kv_split = 2;
+    a.kvp = reinterpret_cast<float*>(at(in.ws, p.ws.kvp));
+  }
   if (p.qk_norm && p.dtype == UPIPE_BF16) {  // fp32 gradients for the normalisation's backward
     a.dq32 = reinterpret_cast<float*>(at(in.ws, p.ws.gq32[st.slot]));
     a.dk32 = reinterpret_cast<float*>(at(in.ws, p.ws.gk32[st.kvslot]));

@@ -42,7 +42,10 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
   __shared__ __attribute__((aligned(16))) f32x4 pxch[4][8][64];  // P of each key block: [block][reg/4][lane]
   const int64_t S = a.S;
   const int lid = xcd_snake(blockIdx.x, gridDim.x);
-  const int kt = lid / nkv, gl = lid % nkv;  // key tile 0 (most work) first
+  // logical id = (key tile, half, KV head): key tile 0 (most work) first;
+  // half 1 exists only with a.kv_split == 2 (then nkv == 1)
+  const int per_kt = nkv * a.kv_split;
+  const int kt = lid / per_kt, half = (lid % per_kt) / nkv, gl = lid % nkv;
   const int g = a.kv_head0 + gl;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, col = lane % 32, hf = lane / 32;
   const int kb = wave & 3;      // key block of this wave (waves kb and kb + 4 share a SIMD)
@@ -65,8 +68,11 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
   // dV (first wave) or dK (second) sums: C layout, lane = d column within
   // the 32-column block d4, registers = key rows
   f32x16 acc[4];
+  // split: this half's fp32 sums of one KV head, [half][dK, dV][S][d]
+  float* const part =
+      a.kv_split == 2 ? a.kvp + (static_cast<int64_t>(half) * 2 + (pwave ? 1 : 0)) * S * DH : nullptr;
   {
-    const float* carry = pwave ? a.dv_acc : a.dk_acc;
+    const float* carry = part ? part : (pwave ? a.dv_acc : a.dk_acc);
 #pragma unroll
     for (int d4 = 0; d4 < 4; ++d4) acc[d4] = zero16();
     if (!a.first_of_group) {
@@ -83,10 +89,20 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
   const int h_lo = max(a.q_head0, g * a.r), h_hi = min(a.q_head0 + a.nq, (g + 1) * a.r);
   const int nqt = static_cast<int>((S + BM - 1) / BM);
   const int qt0 = a.causal ? static_cast<int>((static_cast<int64_t>(kt) * BN) / BM) : 0;
-  const int per_head = nqt - qt0;
+  // query tiles [qlo, qhi) of this workgroup: all from the diagonal on, or
+  // with the split the upper (half 0) or lower (half 1) part of them
+  int qlo = qt0, qhi = nqt;
+  if (a.kv_split == 2) {
+    const int mid = qt0 + (nqt - qt0 + 1) / 2;
+    if (half == 0)
+      qlo = mid;
+    else
+      qhi = mid;
+  }
+  const int per_head = qhi - qlo;
   const int niter = (h_hi - h_lo) * per_head;
   // Loop state, the same in every wave: tile t is query tile
-  // nqt - 1 - t % per_head of head h_lo + t / per_head.  The query tiles are
+  // qhi - 1 - t % per_head of head h_lo + t / per_head.  The query tiles are
   // walked from the end of the sequence down to the diagonal, so the key
   // tiles running together on one XCD (32 consecutive ones) all start on the
   // same query tile and stream the same Q / dO rows at once; walking up from
@@ -97,8 +113,8 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
     int h, qt;
   };
   auto adv = [&](Cur& x) {
-    if (--x.qt < qt0) {
-      x.qt = nqt - 1;
+    if (--x.qt < qlo) {
+      x.qt = qhi - 1;
       ++x.h;
     }
   };
@@ -157,7 +173,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
       }
     }
   };
-  Cur cc{h_lo, nqt - 1};  // tile it
+  Cur cc{h_lo, qhi - 1};  // tile it
   Cur nc = cc;        // tile it + 1
   adv(nc);
   int sq = 0, sg = 0;  // it % NQ, it % NG
@@ -288,7 +304,15 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
     }
   }
 
-  {
+  if (part) {  // split: this half's sum as it stands; dkv_combine_kernel finishes the group
+#pragma unroll
+    for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t kr = wk0 + 8 * (i / 4) + 4 * hf + (i % 4);
+        if (kr < S) part[kr * DH + 32 * d4 + col] = acc[d4][i];
+      }
+  } else {
     float* carry = pwave ? a.dv_acc : a.dk_acc;
     u16* out = static_cast<u16*>(pwave ? a.dv : a.dk);
     const float scale = pwave ? 1.f : tau;
@@ -332,6 +356,36 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
   }
 }
 
+// Split dK/dV of one KV head, its group finished: dK = tau (upper + lower),
+// then the transposed rotation of the pairs (c, c + 64) with the rotary
+// embedding, rounded to bf16 (or kept in fp32 for the QK-norm backward);
+// dV = upper + lower, rounded.  One thread per (key row, pair).
+__global__ __launch_bounds__(256) void dkv_combine_kernel(AttnArgs a) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t row = idx / 64;
+  const int c = static_cast<int>(idx % 64);
+  if (row >= a.S) return;
+  const int64_t Sd = a.S * DH, o = row * DH + c;
+  const float* P = a.kvp;  // [half][dK, dV][S][d]
+  const float tau = 1.f / sqrtf(static_cast<float>(DH));
+  float klo = (P[o] + P[2 * Sd + o]) * tau, khi = (P[o + 64] + P[2 * Sd + o + 64]) * tau;
+  if (a.rope.on) {
+    float cs, sn;
+    rope_cs(row, a.rope.fw[c], cs, sn);
+    rope_bwd(klo, khi, cs, sn);
+  }
+  if (a.dk32) {
+    a.dk32[o] = klo;
+    a.dk32[o + 64] = khi;
+  } else {
+    static_cast<u16*>(a.dk)[o] = __builtin_bit_cast(u16, static_cast<__bf16>(klo));
+    static_cast<u16*>(a.dk)[o + 64] = __builtin_bit_cast(u16, static_cast<__bf16>(khi));
+  }
+  const float vlo = P[Sd + o] + P[3 * Sd + o], vhi = P[Sd + o + 64] + P[3 * Sd + o + 64];
+  static_cast<u16*>(a.dv)[o] = __builtin_bit_cast(u16, static_cast<__bf16>(vlo));
+  static_cast<u16*>(a.dv)[o + 64] = __builtin_bit_cast(u16, static_cast<__bf16>(vhi));
+}
+
 }  // namespace
 
 namespace bf16 {
@@ -340,8 +394,39 @@ hipError_t attn_dkv(const AttnArgs& a, hipStream_t st) {
   if (a.d != DH) return hipErrorInvalidValue;
   const int nkv = a.nq >= a.r ? a.nq / a.r : 1;
   const unsigned nkt = static_cast<unsigned>((a.S + kv::BN - 1) / kv::BN);
-  hipLaunchKernelGGL(attn_dkv_kernel, dim3(nkt * nkv), dim3(512), 0, st, a, nkv);
-  return hipGetLastError();
+  if (a.kv_split != 2) {
+    hipLaunchKernelGGL(attn_dkv_kernel, dim3(nkt * nkv), dim3(512), 0, st, a, nkv);
+    return hipGetLastError();
+  }
+  // split: one launch per KV group of the stage (the two halves' sums of one
+  // KV head at a time), then the combine when the group is finished
+  if (!a.kvp || a.kv_split != dkv_split(a.S)) return hipErrorInvalidValue;
+  const int64_t Sd = a.S * DH;
+  for (int g = 0; g < nkv; ++g) {
+    AttnArgs b = a;
+    if (nkv > 1) {  // the stage holds whole groups: group g's r query heads
+      b.nq = a.r;
+      b.q_head0 = a.q_head0 + g * a.r;
+      b.kv_head0 = a.kv_head0 + g;
+      b.q = static_cast<const u16*>(a.q) + static_cast<int64_t>(g) * a.r * Sd;
+      b.k = static_cast<const u16*>(a.k) + g * Sd;
+      b.v = static_cast<const u16*>(a.v) + g * Sd;
+      b.dd = a.dd + static_cast<int64_t>(g) * a.r * a.S;
+      b.lse2 = a.lse2 + static_cast<int64_t>(g) * a.r * a.S;
+      b.dk = static_cast<u16*>(a.dk) + g * Sd;
+      b.dv = static_cast<u16*>(a.dv) + g * Sd;
+      b.dk32 = a.dk32 ? a.dk32 + g * Sd : nullptr;
+    }
+    hipLaunchKernelGGL(attn_dkv_kernel, dim3(nkt * 2), dim3(512), 0, st, b, 1);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (b.last_of_group && a.S > 0) {
+      hipLaunchKernelGGL(dkv_combine_kernel, dim3(static_cast<unsigned>((a.S * 64 + 255) / 256)), dim3(256),
+                         0, st, b);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
 }
 
 }  // namespace bf16

@@ -121,11 +121,12 @@ int make_plan(Plan& p, int64_t S, int64_t D, int H, int G, int d, int U, int cau
   take2(w.dq, U * Sd * e);
   take2(w.dk, nkv * Sd * e);
   take2(w.dv, nkv * Sd * e);
-  if (dtype == UPIPE_BF16 && U < r) {
+  w.dk_acc = w.dv_acc = w.kvp = 0;
+  if (dtype == UPIPE_BF16 && dkv_split(S) == 2) {
+    w.kvp = take(4 * Sd * 4);  // two halves x (dK, dV) of one KV head, fp32
+  } else if (dtype == UPIPE_BF16 && U < r) {
     w.dk_acc = take(Sd * 4);
     w.dv_acc = take(Sd * 4);
-  } else {
-    w.dk_acc = w.dv_acc = 0;
   }
   // With the output projection the backward forms each stage's dO from dY.
   w.dob = p.out_proj ? take(U * Sd * e) : 0;

@@ -39,7 +39,9 @@ struct WsLayout {
   size_t lse2;                 // LSE * log2(e) [U][S] fp32                    (backward)
   size_t dq[2];                // dQ [U][S][d] (element type)                  (backward)
   size_t dk[2], dv[2];         // dK, dV [kv][S][d] (element type)             (backward)
-  size_t dk_acc, dv_acc;       // fp32 carry of dK, dV across a group's stages (bf16 and U < r)
+  size_t dk_acc, dv_acc;       // fp32 carry of dK, dV across a group's stages (bf16, U < r, no split)
+  size_t kvp;                  // bf16 with dkv_split(S) == 2: the two halves' fp32 dK, dV sums of
+                               // one KV head, [half][dK, dV][S][d] (also their carry when U < r)
   size_t dob;                  // dO of the stage's heads [U][S][d] (element type), from dY through
                                // the output projection (plans with UPIPE_OUT_PROJ; else 0)
   // QK-norm (plans with UPIPE_QK_NORM; else 0), backward only:
@@ -132,6 +134,14 @@ struct ChunkTable {
   unsigned char nidx[kMaxChunks];   // projection: row block of the chunk in NormArgs' buffers
 };
 
+// dK/dV with fewer than 512 key tiles (S <= 65408): each key tile's query
+// tiles are split into an upper and a lower half, one workgroup each, so
+// that the triangular causal work does not leave the longest key tile alone
+// on the critical path.  Each half is its own fp32 sum (over the group's heads
+// and stages), and a combine kernel adds upper + lower.  Fixed by S alone, so
+// every U sums alike.
+inline int dkv_split(int64_t S) { return (S + 127) / 128 < 512 ? 2 : 1; }
+
 struct AttnArgs {
   int64_t S;
   int H;          // total query heads (row stride of O/dO is H*d)
@@ -161,6 +171,8 @@ struct AttnArgs {
   void* dv;
   float* dk_acc;        // fp32 carry (bf16 only), may be null when not needed
   float* dv_acc;
+  int kv_split;         // bf16: dkv_split(S); with 2, dK/dV sums go to kvp (one KV head per
+  float* kvp;           //   launch, [half][dK, dV][S][d] fp32) and a combine kernel finishes them
   float* dq32;          // bf16 with QK-norm: dQ goes here in fp32 (after the rotary
   float* dk32;          //   transpose) instead of dq; the finished dK likewise
   int first_of_group;   // this launch starts the group's dK/dV accumulation

@@ -276,6 +276,17 @@ def test_auto_u_rejects_bad_shapes_and_null_output():
     assert L.upipe_auto_u(4096, 1024, 32, 8, 128, 1, 0, 1 << 40, None) == upipe.UPIPE_ERR_ARG
 
 
+def kv_sum_bytes(S, d, U, r):
+    """bf16 dK/dV sums in fp32: below 512 key tiles of 128 (S <= 65408) each
+    key tile's query range is split into two halves with sums of their own,
+    [half][dK, dV][S][d] for one KV head at a time (they also carry the sums
+    across a group's stages); from 512 key tiles on, one fp32 carry of dK and
+    dV [S][d] when a group spans stages (U < r)."""
+    if (S + 127) // 128 < 512:
+        return 4 * 4 * S * d
+    return 2 * 4 * S * d if U < r else 0
+
+
 def dw_scratch_closed_form(S, D, nmax):
     """bf16 weight-gradient scratch: the token range is cut into P parts
     (P = 1 below 8192 tokens, S // 4096 up to 8 parts, 8 from 32768 tokens on);
@@ -298,7 +309,7 @@ def test_dw_scratch_is_fixed_by_s_and_d():
         for U in legal_us(H, G):
             kv_s = max(1, U // r)
             qkv = 2 * S * d * (U + 2 * kv_s)
-            single = 2 * 4 * S * U + (2 * 4 * S * d if U < r else 0)
+            single = 2 * 4 * S * U + kv_sum_bytes(S, d, U, r)
             p = upipe.Plan(S, D, H, G, d, U)
             extra = p.peak_bytes_phase(1) - (2 * qkv + single)
             want = dw_scratch_closed_form(S, D, U + 2 * kv_s)
@@ -315,7 +326,7 @@ def test_dw_scratch_is_fixed_by_s_and_d():
 def test_pipelined_plan_doubles_the_per_stage_buffers():
     """Stage pipelining (the pages' overlap suggestion, paper.rainbus.top summary,
     sections 局限与改进 and 独立分析的弱点) keeps two copies of the Q/K/V stage
-    buffers and of the dQ/dK/dV buffers; the D, LSE*log2(e) and fp32 dK/dV carry
+    buffers and of the dQ/dK/dV buffers; the D, LSE*log2(e) and fp32 dK/dV sum
     regions stay single.  Closed forms in element counts, every region a multiple
     of 256 bytes at these sizes."""
     S, d = 4096, 128
@@ -326,7 +337,7 @@ def test_pipelined_plan_doubles_the_per_stage_buffers():
             plain = upipe.Plan(S, 1024, H, G, d, U)
             pipe = upipe.Plan(S, 1024, H, G, d, U, pipeline=True)
             qkv = 2 * S * d * (U + 2 * kv_s)
-            single = 2 * 4 * S * U + (2 * 4 * S * d if U < r else 0)  # D, LSE*log2 e, carry
+            single = 2 * 4 * S * U + kv_sum_bytes(S, d, U, r)  # D, LSE*log2 e, dK/dV sums
             assert plain.peak_bytes_phase(0) == qkv
             assert pipe.peak_bytes_phase(0) == 2 * qkv
             assert plain.peak_bytes_phase(1) == 2 * qkv + single

@@ -27,6 +27,10 @@ namespace {
 // exponentials, so the SIMD's matrix unit stays busy; in the second, the
 // first wave runs dV while the second forms dS.  The fp32 sums stay in
 // registers, and across the stages of a group in the fp32 carry buffers.
+// Below 512 key tiles (dkv_split) each key tile's query tiles are split into
+// an upper and a lower half, one workgroup each with fp32 sums of its own
+// (kept, and carried across stages, in the half-sum buffers), and
+// dkv_combine_kernel adds upper + lower when the group is finished.
 namespace kv {
 constexpr int BN = 128, BM = 64;
 constexpr int TILE = BM * 128;  // one swizzled 64-row tile

@@ -19,6 +19,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -92,11 +93,25 @@ def kernel_work(kind, S, D, d, U, r, causal=True):
 KERNEL_SOURCES = ("bf16_common.h", "kernels_bf16.hip", "kernels_dkv.hip", "rope_device.h")
 
 
+def _code_only(text):
+    """C++ source without its comments and blank-line / trailing-space
+    differences, so that editing a comment keeps the hash."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    out = []
+    for line in text.splitlines():
+        code = re.sub(r"//.*$", "", line).rstrip()
+        if code:
+            out.append(code)
+    return "\n".join(out)
+
+
 def source_sha():
-    """First 16 hex digits of the sha256 over the bf16 kernel sources."""
+    """First 16 hex digits of the sha256 over the code (comments stripped) of
+    the bf16 kernel sources."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        h.update(open(os.path.join(ROOT, "headwise_chunked_context_stage_amd", "csrc", name), "rb").read())
+        with open(os.path.join(ROOT, "headwise_chunked_context_stage_amd", "csrc", name)) as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

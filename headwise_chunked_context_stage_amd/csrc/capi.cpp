@@ -494,9 +494,51 @@ hipError_t order(hipEvent_t ev, hipStream_t signaller, hipStream_t waiter) {
 // Forward, pipelined: stage s + 1's projection (helper stream) runs while
 // stage s's attention (caller's stream) does.  Stage s uses buffer copy
 // s mod 2, so the projection of s + 1 waits only for the attention of s - 1.
+// Small attention grids instead alternate whole stages between the two
+// streams (stage s on the caller's stream when s is even): one stage's
+// attention starts while the previous one's longest query blocks finish, in
+// the CUs they leave idle.  Stage s's Q copy s mod 2 was last read by stage
+// s - 2 on the same stream.  A stage that loads K/V into a copy first waits
+// for the other stream's latest stage if that stream read the copy since its
+// last load; a stage of a group loaded on the other stream waits for the load.
+hipError_t fwd_alternating(const Plan& p, const Kernels& K, const void* X, const void* Wq,
+                           const void* Wk, const void* Wv, void* O, float* LSE, void* ws,
+                           hipStream_t s, hipStream_t h, SyncEvents& E, const NormIn& nin) {
+  hipEvent_t start = E.ev[0], kv_ready[2] = {E.ev[1], E.ev[2]}, attn_done[2] = {E.ev[3], E.ev[4]};
+  const int n = static_cast<int>(p.stages.size());
+  hipError_t e = order(start, s, h);  // inputs written on the caller's stream
+  int load_stream[2] = {-1, -1};      // stream (0: caller's, 1: helper) of the last load into each copy
+  int readers[2] = {0, 0};            // streams that read each copy since its last load (bit mask)
+  for (int i = 0; i < n && e == hipSuccess; ++i) {
+    const Stage& st = p.stages[i];
+    const int xi = i % 2, k = st.kvslot;
+    hipStream_t x = xi == 0 ? s : h;
+    if (st.load && (readers[k] & (1 << (1 - xi)))) e = hipStreamWaitEvent(x, attn_done[1 - xi], 0);
+    if (e == hipSuccess) e = stage_projection(p, st, K, X, Wq, Wk, Wv, ws, x, nin, false);
+    if (e == hipSuccess && st.load) {
+      e = hipEventRecord(kv_ready[k], x);
+      load_stream[k] = xi;
+      readers[k] = 0;
+    } else if (e == hipSuccess && load_stream[k] != xi) {
+      e = hipStreamWaitEvent(x, kv_ready[k], 0);
+    }
+    readers[k] |= 1 << xi;
+    if (e != hipSuccess) break;
+    AttnArgs a = attn_args(p, st, ws);
+    a.o = O;
+    a.lse = LSE;
+    e = timed(UPIPE_K_ATTN_FWD, x, [&] { return K.attn_fwd(a, x); });
+    if (e == hipSuccess) e = hipEventRecord(attn_done[i % 2], x);
+  }
+  if (e == hipSuccess && n >= 2) e = hipStreamWaitEvent(s, attn_done[1], 0);  // join the helper stream
+  return e;
+}
+
 hipError_t fwd_pipelined(const Plan& p, const Kernels& K, const void* X, const void* Wq,
                          const void* Wk, const void* Wv, void* O, float* LSE, void* ws,
                          hipStream_t s, hipStream_t h, SyncEvents& E, const NormIn& nin) {
+  if (p.dtype == UPIPE_BF16 && attn_small_grid(p.S, p.U))
+    return fwd_alternating(p, K, X, Wq, Wk, Wv, O, LSE, ws, s, h, E, nin);
   hipEvent_t start = E.ev[0], proj_done[2] = {E.ev[1], E.ev[2]}, attn_done[2] = {E.ev[3], E.ev[4]};
   const int n = static_cast<int>(p.stages.size());
   hipError_t e = order(start, s, h);  // inputs written on the caller's stream

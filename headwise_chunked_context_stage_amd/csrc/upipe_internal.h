@@ -142,6 +142,11 @@ struct ChunkTable {
 // every U sums alike.
 inline int dkv_split(int64_t S) { return (S + 127) / 128 < 512 ? 2 : 1; }
 
+// Attention grids under two rounds of 256-row query blocks (x heads): the
+// forward and dQ kernels then run 128-row workgroups (the same bits), and a
+// pipelined plan's forward alternates stages between its two streams.
+inline bool attn_small_grid(int64_t S, int nq) { return (S + 255) / 256 * nq < 512; }
+
 struct AttnArgs {
   int64_t S;
   int H;          // total query heads (row stride of O/dO is H*d)

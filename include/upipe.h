@@ -82,10 +82,14 @@ enum {
    * The stage buffers get two copies, and each call runs the projection
    * GEMMs of stage s + 1 and, in the backward, the weight- and
    * input-gradient GEMMs of stage s on a second stream while stage s + 1's
-   * attention kernels run on the caller's stream.  Every kernel, its inputs
-   * and the order of every accumulation are those of the plain plan, so the
-   * results are bit-identical; upipe_peak_bytes grows by one more copy of
-   * the Q, K, V (and dQ, dK, dV) stage buffers.  The second stream (default
+   * attention kernels run on the caller's stream.  When the attention grid
+   * is small (fewer than 512 query blocks of 256 rows over the stage's
+   * heads), the forward instead alternates whole stages (projection and
+   * attention) between the two streams, so one stage's attention fills the
+   * CUs the previous one's last query blocks leave idle.  Every kernel, its
+   * inputs and the order of every accumulation are those of the plain plan,
+   * so the results are bit-identical; upipe_peak_bytes grows by one more
+   * copy of the Q, K, V (and dQ, dK, dV) stage buffers.  The second stream (default
    * priority, one per device, created on the first pipelined call on the
    * current device, which must be the device of `stream`) and a pool of
    * events are kept until the process ends; the calls allocate no device

@@ -491,19 +491,24 @@ hipError_t order(hipEvent_t ev, hipStream_t signaller, hipStream_t waiter) {
   return hipStreamWaitEvent(waiter, ev, 0);
 }
 
-// Forward, pipelined: stage s + 1's projection (helper stream) runs while
-// stage s's attention (caller's stream) does.  Stage s uses buffer copy
-// s mod 2, so the projection of s + 1 waits only for the attention of s - 1.
-// Small attention grids instead alternate whole stages between the two
-// streams (stage s on the caller's stream when s is even): one stage's
-// attention starts while the previous one's longest query blocks finish, in
-// the CUs they leave idle.  Stage s's Q copy s mod 2 was last read by stage
-// s - 2 on the same stream.  A stage that loads K/V into a copy first waits
-// for the other stream's latest stage if that stream read the copy since its
-// last load; a stage of a group loaded on the other stream waits for the load.
-hipError_t fwd_alternating(const Plan& p, const Kernels& K, const void* X, const void* Wq,
-                           const void* Wk, const void* Wv, void* O, float* LSE, void* ws,
-                           hipStream_t s, hipStream_t h, SyncEvents& E, const NormIn& nin) {
+// A pipelined plan overlaps stages only where the attention grid is small
+// (fewer than two rounds of 256-row query blocks over the stage's heads):
+// there the last query blocks of a stage run alone and leave CUs idle.  With
+// larger grids the overlap measured slower (the concurrent work disturbs the
+// attention kernels' L2 sharing), and the stages run in order on the
+// caller's stream as in the plain plan.
+bool overlap_stages(const Plan& p) { return p.pipeline && attn_small_grid(p.S, p.U); }
+
+// Forward, pipelined: whole stages alternate between the two streams (stage
+// s on the caller's stream when s is even), so one stage's attention starts
+// while the previous one's longest query blocks finish, in the CUs they
+// leave idle.  Stage s's Q copy s mod 2 was last read by stage s - 2 on the
+// same stream.  A stage that loads K/V into a copy first waits for the other
+// stream's latest stage if that stream read the copy since its last load; a
+// stage of a group loaded on the other stream waits for the load.
+hipError_t fwd_pipelined(const Plan& p, const Kernels& K, const void* X, const void* Wq,
+                         const void* Wk, const void* Wv, void* O, float* LSE, void* ws,
+                         hipStream_t s, hipStream_t h, SyncEvents& E, const NormIn& nin) {
   hipEvent_t start = E.ev[0], kv_ready[2] = {E.ev[1], E.ev[2]}, attn_done[2] = {E.ev[3], E.ev[4]};
   const int n = static_cast<int>(p.stages.size());
   hipError_t e = order(start, s, h);  // inputs written on the caller's stream
@@ -531,35 +536,6 @@ hipError_t fwd_alternating(const Plan& p, const Kernels& K, const void* X, const
     if (e == hipSuccess) e = hipEventRecord(attn_done[i % 2], x);
   }
   if (e == hipSuccess && n >= 2) e = hipStreamWaitEvent(s, attn_done[1], 0);  // join the helper stream
-  return e;
-}
-
-hipError_t fwd_pipelined(const Plan& p, const Kernels& K, const void* X, const void* Wq,
-                         const void* Wk, const void* Wv, void* O, float* LSE, void* ws,
-                         hipStream_t s, hipStream_t h, SyncEvents& E, const NormIn& nin) {
-  if (p.dtype == UPIPE_BF16 && attn_small_grid(p.S, p.U))
-    return fwd_alternating(p, K, X, Wq, Wk, Wv, O, LSE, ws, s, h, E, nin);
-  hipEvent_t start = E.ev[0], proj_done[2] = {E.ev[1], E.ev[2]}, attn_done[2] = {E.ev[3], E.ev[4]};
-  const int n = static_cast<int>(p.stages.size());
-  hipError_t e = order(start, s, h);  // inputs written on the caller's stream
-  if (e != hipSuccess) return e;
-  e = stage_projection(p, p.stages[0], K, X, Wq, Wk, Wv, ws, h, nin, false);
-  if (e == hipSuccess) e = hipEventRecord(proj_done[0], h);
-  for (int i = 0; i < n && e == hipSuccess; ++i) {
-    const Stage& st = p.stages[i];
-    e = hipStreamWaitEvent(s, proj_done[i % 2], 0);
-    if (e != hipSuccess) break;
-    AttnArgs a = attn_args(p, st, ws);
-    a.o = O;
-    a.lse = LSE;
-    e = timed(UPIPE_K_ATTN_FWD, s, [&] { return K.attn_fwd(a, s); });
-    if (e == hipSuccess) e = hipEventRecord(attn_done[i % 2], s);
-    if (e != hipSuccess || i + 1 == n) break;
-    // copy (i + 1) mod 2 was last read by the attention of stage i - 1
-    if (i >= 1) e = hipStreamWaitEvent(h, attn_done[(i - 1) % 2], 0);
-    if (e == hipSuccess) e = stage_projection(p, p.stages[i + 1], K, X, Wq, Wk, Wv, ws, h, nin, false);
-    if (e == hipSuccess) e = hipEventRecord(proj_done[(i + 1) % 2], h);
-  }
   return e;
 }
 
@@ -723,7 +699,7 @@ namespace {
 int run_fwd(const Plan& p, const void* X, const void* Wq, const void* Wk, const void* Wv,
             void* O, float* LSE, void* ws, hipStream_t s, const OutProj* op, const NormIn& nin) {
   const Kernels K = kernels_for(p.dtype);
-  if (p.pipeline) {
+  if (overlap_stages(p)) {
     hipStream_t hs = nullptr;
     SyncEvents E;
     UPIPE_TRY(helper_stream(&hs));
@@ -748,12 +724,13 @@ int run_bwd(const Plan& p, const BwdIn& in, hipStream_t s, const OutProj* op, co
   const Kernels K = kernels_for(p.dtype);
   hipStream_t hs = nullptr;
   SyncEvents E;
-  if (p.pipeline) {  // before anything is enqueued
+  const bool overlap = overlap_stages(p);
+  if (overlap) {  // before anything is enqueued
     UPIPE_TRY(helper_stream(&hs));
     UPIPE_TRY(E.take());
   }
   // dX needs no zero fill: the first stage's dX launch starts the running sum
-  if (p.pipeline) {
+  if (overlap) {
     UPIPE_TRY(bwd_pipelined(p, K, in, s, hs, E, op, nin));
   } else {
     bool k_started = false;  // dgamma_k's running sum (QK-norm)

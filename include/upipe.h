@@ -79,17 +79,20 @@ int upipe_create(upipe_plan** out, int64_t S, int64_t d_model, int H, int G, int
 enum {
   /* Stage pipelining (the pages' suggested improvement of overlapping the
    * stages; paper.rainbus.top summary, sections 局限与改进 and 独立分析的弱点).
-   * The stage buffers get two copies, and each call runs the projection
-   * GEMMs of stage s + 1 and, in the backward, the weight- and
-   * input-gradient GEMMs of stage s on a second stream while stage s + 1's
-   * attention kernels run on the caller's stream.  When the attention grid
-   * is small (fewer than 512 query blocks of 256 rows over the stage's
-   * heads), the forward instead alternates whole stages (projection and
-   * attention) between the two streams, so one stage's attention fills the
-   * CUs the previous one's last query blocks leave idle.  Every kernel, its
-   * inputs and the order of every accumulation are those of the plain plan,
-   * so the results are bit-identical; upipe_peak_bytes grows by one more
-   * copy of the Q, K, V (and dQ, dK, dV) stage buffers.  The second stream (default
+   * The stage buffers get two copies.  Where the attention grid is small
+   * (fewer than 512 query blocks of 256 rows over a stage's U heads, e.g.
+   * U = 1 at up to 64K tokens), consecutive stages overlap: the forward
+   * alternates whole stages (projection and attention) between the caller's
+   * stream and a second stream, so one stage's attention fills the CUs the
+   * previous one's last query blocks leave idle, and the backward runs the
+   * projection of stage s + 1 and the weight- and input-gradient GEMMs of
+   * stage s on the second stream while stage s + 1's attention kernels run
+   * on the caller's stream.  With larger grids the stages run in order on
+   * the caller's stream, as in the plain plan (overlapping them measured
+   * slower there).  Every kernel, its inputs and the order of every
+   * accumulation are those of the plain plan, so the results are
+   * bit-identical; upipe_peak_bytes grows by one more copy of the Q, K, V
+   * (and dQ, dK, dV) stage buffers.  The second stream (default
    * priority, one per device, created on the first pipelined call on the
    * current device, which must be the device of `stream`) and a pool of
    * events are kept until the process ends; the calls allocate no device

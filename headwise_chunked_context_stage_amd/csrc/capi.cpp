@@ -241,8 +241,8 @@ AttnArgs bwd_args(const Plan& p, const Stage& st, const BwdIn& in) {
   a.do_h0 = 0;
   a.o_in = in.O;
   a.lse_in = in.LSE;
-  a.dd = reinterpret_cast<float*>(at(in.ws, p.ws.dd));
-  a.lse2 = reinterpret_cast<float*>(at(in.ws, p.ws.lse2));
+  a.dd = reinterpret_cast<float*>(at(in.ws, p.ws.dd[st.slot]));
+  a.lse2 = reinterpret_cast<float*>(at(in.ws, p.ws.lse2[st.slot]));
   a.dq = at(in.ws, p.ws.dq[st.slot]);
   // dK/dV belong to the KV group: the fp32 variant carries them across the
   // group's stages in these buffers, so they follow the K/V copy
@@ -457,7 +457,7 @@ hipError_t helper_stream(hipStream_t* out) {
 // enqueues, and gives them back before it returns: a wait binds to the record
 // that precedes it on the host, so a later call may record the same events
 // again while earlier work is still in flight.
-constexpr int kSyncEvents = 7;
+constexpr int kSyncEvents = 8;
 std::mutex g_emu;
 std::vector<hipEvent_t> g_sync_pool;
 
@@ -539,8 +539,65 @@ hipError_t fwd_pipelined(const Plan& p, const Kernels& K, const void* X, const v
   return e;
 }
 
-// Backward, pipelined.  Caller's stream: D pre-pass, dK/dV and dQ of each
-// stage.  Helper stream: the projection of stage s + 1, then the dW and dX
+// Backward, pipelined on small grids: whole stages alternate between the two
+// streams as in the forward, so one stage's dQ (whose last query blocks run
+// alone) overlaps the next stage's work.  Per stage, on its stream: the
+// projection, the D pre-pass, dQ, dK/dV, the QK-norm backward and the dW and
+// dX GEMMs.  Q, dQ, D and LSE*log2(e) use the stage's copy (s mod 2, last
+// used by stage s - 2 on the same stream); K/V copies follow the forward's
+// rule.  What stays single runs as a chain in stage order, each link waiting
+// for the previous stage's: dK/dV (its fp32 sums carry across a group's
+// stages), the QK-norm backward (dgamma's running sums) and the GEMMs (dX's
+// running sum and the dW part sums) -- so every sum keeps its order.
+hipError_t bwd_alternating(const Plan& p, const Kernels& K, const BwdIn& in, hipStream_t s,
+                           hipStream_t h, SyncEvents& E, const NormIn& nin) {
+  hipEvent_t start = E.ev[0], kv_ready[2] = {E.ev[1], E.ev[2]}, stage_done[2] = {E.ev[3], E.ev[4]};
+  hipEvent_t dkv_done = E.ev[5], norm_done = E.ev[6], grad_done = E.ev[7];
+  const int n = static_cast<int>(p.stages.size());
+  hipError_t e = order(start, s, h);  // inputs written on the caller's stream
+  int load_stream[2] = {-1, -1};      // stream (0: caller's, 1: helper) of the last load into each copy
+  int readers[2] = {0, 0};            // streams that used each K/V copy since its last load (bit mask)
+  bool k_started = false;             // dgamma_k's running sum (QK-norm)
+  for (int i = 0; i < n && e == hipSuccess; ++i) {
+    const Stage& st = p.stages[i];
+    const int xi = i % 2, k = st.kvslot;
+    hipStream_t x = xi == 0 ? s : h;
+    const bool other = i >= 1;  // the previous stage ran on the other stream
+    if (st.load && (readers[k] & (1 << (1 - xi)))) e = hipStreamWaitEvent(x, stage_done[1 - xi], 0);
+    if (e == hipSuccess) e = stage_projection(p, st, K, in.X, in.Wq, in.Wk, in.Wv, in.ws, x, nin, true);
+    if (e == hipSuccess && st.load) {
+      e = hipEventRecord(kv_ready[k], x);
+      load_stream[k] = xi;
+      readers[k] = 0;
+    } else if (e == hipSuccess && load_stream[k] != xi) {
+      e = hipStreamWaitEvent(x, kv_ready[k], 0);
+    }
+    readers[k] |= 1 << xi;
+    if (e != hipSuccess) break;
+    const AttnArgs a = bwd_args(p, st, in);
+    e = timed(UPIPE_K_BWD_PRE, x, [&] { return K.bwd_pre(a, x); });
+    if (e == hipSuccess) e = timed(UPIPE_K_ATTN_DQ, x, [&] { return K.attn_dq(a, x); });
+    if (e == hipSuccess && other) e = hipStreamWaitEvent(x, dkv_done, 0);
+    if (e == hipSuccess) e = timed(UPIPE_K_ATTN_DKV, x, [&] { return K.attn_dkv(a, x); });
+    if (e == hipSuccess) e = hipEventRecord(dkv_done, x);
+    if (e == hipSuccess && p.qk_norm) {
+      if (other) e = hipStreamWaitEvent(x, norm_done, 0);
+      if (e == hipSuccess) e = stage_norm_bwd(p, st, in, nin, i == 0, !k_started, x);
+      if (e == hipSuccess) e = hipEventRecord(norm_done, x);
+      k_started = k_started || st.done;
+    }
+    if (e == hipSuccess && other) e = hipStreamWaitEvent(x, grad_done, 0);
+    if (e == hipSuccess) e = stage_gradients(p, st, K, in, i == 0, x);
+    if (e == hipSuccess) e = hipEventRecord(grad_done, x);
+    if (e == hipSuccess) e = hipEventRecord(stage_done[xi], x);
+  }
+  if (e == hipSuccess && n >= 2) e = hipStreamWaitEvent(s, stage_done[1], 0);  // join the helper stream
+  return e;
+}
+
+// Backward, pipelined, with the output projection (its stage dO buffer is
+// single, so stages cannot alternate).  Caller's stream: D pre-pass, dK/dV
+// and dQ of each stage.  Helper stream: the projection of stage s + 1, then the dW and dX
 // GEMMs of stage s, in stage order (dX keeps its one summation order).
 // Copy s mod 2 of Q/K/V is free again once dQ of stage s - 1 has run; copy
 // s mod 2 of dQ once dX of stage s - 2 has.  dK/dV use the K/V copy of their
@@ -730,7 +787,9 @@ int run_bwd(const Plan& p, const BwdIn& in, hipStream_t s, const OutProj* op, co
     UPIPE_TRY(E.take());
   }
   // dX needs no zero fill: the first stage's dX launch starts the running sum
-  if (overlap) {
+  if (overlap && !op) {
+    UPIPE_TRY(bwd_alternating(p, K, in, s, hs, E, nin));
+  } else if (overlap) {  // the stage dO buffer is single: stages keep their order
     UPIPE_TRY(bwd_pipelined(p, K, in, s, hs, E, op, nin));
   } else {
     bool k_started = false;  // dgamma_k's running sum (QK-norm)

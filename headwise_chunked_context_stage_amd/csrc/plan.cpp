@@ -116,8 +116,8 @@ int make_plan(Plan& p, int64_t S, int64_t D, int H, int G, int d, int U, int cau
   take2(w.k, nkv * Sd * e);
   take2(w.v, nkv * Sd * e);
   w.fwd_bytes = off;
-  w.dd = take(static_cast<size_t>(U) * S * 4);
-  w.lse2 = take(static_cast<size_t>(U) * S * 4);
+  take2(w.dd, static_cast<size_t>(U) * S * 4);
+  take2(w.lse2, static_cast<size_t>(U) * S * 4);
   take2(w.dq, U * Sd * e);
   take2(w.dk, nkv * Sd * e);
   take2(w.dv, nkv * Sd * e);

@@ -35,8 +35,8 @@ struct Stage {
 // stage's slot or kvslot) and one otherwise ([1] == [0]).
 struct WsLayout {
   size_t q[2], k[2], v[2];     // Q [U][S][d], K [kv][S][d], V [kv][S][d]   (element type)
-  size_t dd;                   // D = rowsum(dO*O) [U][S] fp32                 (backward)
-  size_t lse2;                 // LSE * log2(e) [U][S] fp32                    (backward)
+  size_t dd[2];                // D = rowsum(dO*O) [U][S] fp32                 (backward)
+  size_t lse2[2];              // LSE * log2(e) [U][S] fp32                    (backward)
   size_t dq[2];                // dQ [U][S][d] (element type)                  (backward)
   size_t dk[2], dv[2];         // dK, dV [kv][S][d] (element type)             (backward)
   size_t dk_acc, dv_acc;       // fp32 carry of dK, dV across a group's stages (bf16, U < r, no split)

@@ -84,15 +84,16 @@ enum {
    * U = 1 at up to 64K tokens), consecutive stages overlap: the forward
    * alternates whole stages (projection and attention) between the caller's
    * stream and a second stream, so one stage's attention fills the CUs the
-   * previous one's last query blocks leave idle, and the backward runs the
-   * projection of stage s + 1 and the weight- and input-gradient GEMMs of
-   * stage s on the second stream while stage s + 1's attention kernels run
-   * on the caller's stream.  With larger grids the stages run in order on
+   * previous one's last query blocks leave idle.  The backward alternates
+   * whole stages the same way (with UPIPE_OUT_PROJ, whose stage dO buffer is
+   * single, it instead runs the projection of stage s + 1 and the weight-
+   * and input-gradient GEMMs of stage s on the second stream while stage
+   * s + 1's attention kernels run on the caller's stream).  With larger grids the stages run in order on
    * the caller's stream, as in the plain plan (overlapping them measured
    * slower there).  Every kernel, its inputs and the order of every
    * accumulation are those of the plain plan, so the results are
    * bit-identical; upipe_peak_bytes grows by one more copy of the Q, K, V
-   * (and dQ, dK, dV) stage buffers.  The second stream (default
+   * (and dQ, dK, dV, D and LSE) stage buffers.  The second stream (default
    * priority, one per device, created on the first pipelined call on the
    * current device, which must be the device of `stream`) and a pool of
    * events are kept until the process ends; the calls allocate no device

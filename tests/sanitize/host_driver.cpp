@@ -11,6 +11,7 @@
 //    (plain, pipelined, output projection, QK-norm, more than 64 chunks per
 //    launch) run their stage loops.
 // Exit status 0 when every check holds; failures are printed.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -52,6 +53,8 @@ void check_layout(const upipe::Plan& p) {
     fwd.push_back({w.k[c], nkv * Sd * e});
     fwd.push_back({w.v[c], nkv * Sd * e});
     bwd.push_back({w.dq[c], p.U * Sd * e});
+    bwd.push_back({w.dd[c], static_cast<size_t>(p.U) * p.S * 4});
+    bwd.push_back({w.lse2[c], static_cast<size_t>(p.U) * p.S * 4});
     bwd.push_back({w.dk[c], nkv * Sd * e});
     bwd.push_back({w.dv[c], nkv * Sd * e});
     if (p.qk_norm) {
@@ -65,11 +68,17 @@ void check_layout(const upipe::Plan& p) {
       }
     }
   }
-  bwd.push_back({w.dd, static_cast<size_t>(p.U) * p.S * 4});
-  bwd.push_back({w.lse2, static_cast<size_t>(p.U) * p.S * 4});
   if (w.dk_acc) {
     bwd.push_back({w.dk_acc, Sd * 4});
     bwd.push_back({w.dv_acc, Sd * 4});
+  }
+  if (p.dtype == UPIPE_BF16 && upipe::dkv_split(p.S) == 2) bwd.push_back({w.kvp, 4 * Sd * 4});
+  if (p.dtype == UPIPE_BF16) {  // the weight gradients' part sums, for the most chunks of one call
+    int nmax = 0;
+    for (const upipe::Stage& st : p.stages) nmax = std::max(nmax, st.nq + (st.done ? 2 * st.nkv : 0));
+    if (p.out_proj) nmax = std::max(nmax, p.H);
+    nmax = std::min(nmax, upipe::kMaxChunks);
+    bwd.push_back({w.dws, upipe::dw_scratch_bytes(p.S, p.D, nmax)});
   }
   if (p.out_proj) bwd.push_back({w.dob, p.U * Sd * e});
   if (p.qk_norm) {

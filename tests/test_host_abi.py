@@ -326,9 +326,10 @@ def test_dw_scratch_is_fixed_by_s_and_d():
 def test_pipelined_plan_doubles_the_per_stage_buffers():
     """Stage pipelining (the pages' overlap suggestion, paper.rainbus.top summary,
     sections 局限与改进 and 独立分析的弱点) keeps two copies of the Q/K/V stage
-    buffers and of the dQ/dK/dV buffers; the D, LSE*log2(e) and fp32 dK/dV sum
-    regions stay single.  Closed forms in element counts, every region a multiple
-    of 256 bytes at these sizes."""
+    buffers, of the dQ/dK/dV buffers and of D and LSE*log2(e) (consecutive
+    stages may run at once); the fp32 dK/dV sum regions stay single (their sums
+    run in stage order).  Closed forms in element counts, every region a
+    multiple of 256 bytes at these sizes."""
     S, d = 4096, 128
     for H, G in [(32, 8), (8, 2), (8, 8)]:
         r = H // G
@@ -337,11 +338,12 @@ def test_pipelined_plan_doubles_the_per_stage_buffers():
             plain = upipe.Plan(S, 1024, H, G, d, U)
             pipe = upipe.Plan(S, 1024, H, G, d, U, pipeline=True)
             qkv = 2 * S * d * (U + 2 * kv_s)
-            single = 2 * 4 * S * U + kv_sum_bytes(S, d, U, r)  # D, LSE*log2 e, dK/dV sums
+            stats = 2 * 4 * S * U  # D, LSE*log2 e
+            single = kv_sum_bytes(S, d, U, r)  # dK/dV sums
             assert plain.peak_bytes_phase(0) == qkv
             assert pipe.peak_bytes_phase(0) == 2 * qkv
-            assert plain.peak_bytes_phase(1) == 2 * qkv + single
-            assert pipe.peak_bytes_phase(1) == 4 * qkv + single
+            assert plain.peak_bytes_phase(1) == 2 * qkv + stats + single
+            assert pipe.peak_bytes_phase(1) == 4 * qkv + 2 * stats + single
             assert pipe.num_stages == plain.num_stages
             for s in range(plain.num_stages):
                 assert pipe.stage_info(s) == plain.stage_info(s)

@@ -173,6 +173,16 @@ __device__ __forceinline__ void dma_row(const void* src, unsigned dst, unsigned 
 }
 #pragma clang diagnostic pop
 __device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// A register filled by a global load before a copy loop, made to arrive here.
+// Because the wait insertion does not count the copies, a register still in
+// flight where the loop starts gets an s_waitcnt vmcnt(0) before its first
+// use in every iteration, and that wait also holds the wave until the copies
+// it has just issued for the next tile have landed.  Waiting once, before the
+// loop, keeps the loop free of it.
+template <class T>
+__device__ __forceinline__ void settle(T& x) {
+  asm volatile("" : "+v"(x));
+}
 __device__ __forceinline__ unsigned lds_byte_addr(const void* p) {
   return static_cast<unsigned>(reinterpret_cast<uintptr_t>((const lds_u16*)p));
 }

@@ -845,6 +845,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
   for (int t = 0; t < 8; ++t)
     qf[t] = __builtin_bit_cast(bf16x8, myq < S ? ld16(Q + myq * DH + 16 * t + 8 * hf) : u32x4{0, 0, 0, 0});
+#pragma unroll
+  for (int t = 0; t < 8; ++t) settle(qf[t]);
 
   const int64_t kv_end = a.causal ? min(S, qfirst + BM) : S;
   const int ntiles = static_cast<int>((kv_end + BN - 1) / BN);
@@ -1122,8 +1124,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_dq_kernel(AttnArgs a) {
       gf[t] = __builtin_bit_cast(bf16x8, myq < S ? ld16(dO + myq * ldo + 16 * t + 8 * hf) : u32x4{0, 0, 0, 0});
     }
   }
-  const float lse2 = myq < S ? a.lse_in[static_cast<int64_t>(h) * S + myq] * kLog2e : INFINITY;
-  const float Dq = myq < S ? a.dd[static_cast<int64_t>(u) * S + myq] : 0.f;
+  float lse2 = myq < S ? a.lse_in[static_cast<int64_t>(h) * S + myq] * kLog2e : INFINITY;
+  float Dq = myq < S ? a.dd[static_cast<int64_t>(u) * S + myq] : 0.f;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    settle(qf[t]);
+    settle(gf[t]);
+  }
+  settle(lse2);
+  settle(Dq);
 
   const int64_t kv_end = a.causal ? min(S, qfirst + BM) : S;
   const int ntiles = static_cast<int>((kv_end + BN - 1) / BN);

@@ -89,6 +89,10 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
         }
     }
   }
+#pragma unroll
+  for (int t = 0; t < 8; ++t) settle(kvf[t]);
+#pragma unroll
+  for (int d4 = 0; d4 < 4; ++d4) settle(acc[d4]);
 
   const int h_lo = max(a.q_head0, g * a.r), h_hi = min(a.q_head0 + a.nq, (g + 1) * a.r);
   const int nqt = static_cast<int>((S + BM - 1) / BM);

@@ -173,6 +173,14 @@ __device__ __forceinline__ void dma_row(const void* src, unsigned dst, unsigned 
 }
 #pragma clang diagnostic pop
 __device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// max(x[l], x[l ^ 32]) in every lane l: v_permlane32_swap exchanges the two
+// half-waves between two registers (both holding x), after which each lane
+// holds its own value in one and its partner's in the other.  This stays in
+// registers, where a 32-lane xor shuffle is an LDS permute round trip.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 // A register filled by a global load before a copy loop, made to arrive here.
 // Because the wait insertion does not count the copies, a register still in
 // flight where the loop starts gets an s_waitcnt vmcnt(0) before its first

@@ -926,7 +926,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(AttnArgs a) {
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[b][i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32)) * c;
+    mt = max_xor32(mt) * c;
     // Lazy running max: rescale only when the tile max exceeds it by more
     // than kLazy (p <= 2^kLazy stays exact in fp32 and in bf16's exponent).
     const float m_new = (mt > m_run + kLazy) ? mt : m_run;

@@ -247,7 +247,9 @@ __global__ __launch_bounds__(512, 1) void attn_dkv_kernel(AttnArgs a, int nkv) {
         sv[0] = sv[1] = zero16();
         row_pass(swz_addr(qs + sq * TILE, lane), sv);
         const int64_t q0 = static_cast<int64_t>(cc.qt) * BM;
-        const bool need_mask = a.causal && q0 < wk0 + 31;
+        // the diagonal test as a scalar, so the masking below is skipped by a
+        // branch (as a per-lane condition it ran, exec-masked, on every tile)
+        const bool need_mask = __builtin_amdgcn_readfirstlane(static_cast<int>(a.causal && q0 < wk0 + 31)) != 0;
         const int mlim = static_cast<int>(myk - q0);  // tile row r is masked when r < mlim
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)

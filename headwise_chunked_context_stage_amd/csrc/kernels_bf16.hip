@@ -959,11 +959,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(AttnArgs a) {
   // workgroup barriers.  K(j) is read in phases 2j (first waves) and 2j + 1
   // (second waves); V(j) in phases 2j + 2 and 2j + 3.  Tile copies: the first
   // waves copy K tiles, the second V tiles (swizzled), 16 rows per wave, by
-  // 4-row direct global-to-LDS copies, half at the start of each of the wave's two phases
-  // (issuing a row copy costs a wave tens of cycles, so neither phase takes
-  // all of them).  K(j + 1) is issued in phases 2j and 2j + 1 and complete at
-  // the end of 2j + 1; V(j) is issued in phases 2j and 2j + 1 and complete at
-  // the end of 2j + 1.
+  // 4-row direct global-to-LDS copies, all at the start of the wave's softmax
+  // phase: the matrix phase bounds each phase, and issuing a copy costs the
+  // issuing wave tens of cycles.  K(j + 1) is issued in phase 2j + 1 and
+  // complete at its end; V(j) is issued in phase 2j and complete at the end
+  // of 2j + 1.
   const int wv = __builtin_amdgcn_readfirstlane(wave) & 3;
   // per-lane parts of the 4-row copies into the swizzled tiles: row lane / 16
   // of the four, chunk (lane % 16) ^ (4 (lane / 16) + q)
@@ -1008,20 +1008,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(AttnArgs a) {
     }
   } else if (first) {
     for (int j = 0; j <= ntiles; ++j) {
-      if (j + 1 < ntiles) copy_tile(K, j + 1, kbuf + ((j + 1) & 1) * TILE, 0);
       matrix_phase(j);
       __syncthreads();
-      if (j + 1 < ntiles) copy_tile(K, j + 1, kbuf + ((j + 1) & 1) * TILE, 1);
+      if (j + 1 < ntiles) {
+        copy_tile(K, j + 1, kbuf + ((j + 1) & 1) * TILE, 0);
+        copy_tile(K, j + 1, kbuf + ((j + 1) & 1) * TILE, 1);
+      }
       softmax_phase(j);
       dma_wait();
       __syncthreads();
     }
   } else {
     for (int j = 0; j <= ntiles; ++j) {
-      if (j < ntiles) copy_tile(V, j, vbuf + (j & 1) * TILE, 0);
+      if (j < ntiles) {
+        copy_tile(V, j, vbuf + (j & 1) * TILE, 0);
+        copy_tile(V, j, vbuf + (j & 1) * TILE, 1);
+      }
       softmax_phase(j - 1);
       __syncthreads();
-      if (j < ntiles) copy_tile(V, j, vbuf + (j & 1) * TILE, 1);
       matrix_phase(j);
       dma_wait();
       __syncthreads();

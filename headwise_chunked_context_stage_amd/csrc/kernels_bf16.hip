@@ -70,14 +70,18 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(const u16* __restrict__ X,
   constexpr int NRR = 4;
   const int nk = static_cast<int>(D / GK);
   u32x4 rx[NRR][4], rw[NRR][4];
+  // The loads are unconditional (k-steps past the end reload the last one,
+  // rows past S reload row S - 1, zeroed when stored): a load behind a branch
+  // leaves the compiler's wait counting at the join unable to trust later
+  // loads, and it then waits for the whole ring, the loads just issued included.
+  const bool full = i0 + GB <= S;
   auto load = [&](int set, int kb) {
-    if (kb >= nk) return;
-    const int64_t k0 = static_cast<int64_t>(kb) * GK;
+    const int64_t k0 = static_cast<int64_t>(min(kb, nk - 1)) * GK;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int row = tid / 8 + 32 * m, chunk = tid % 8;
-      const int64_t gi = i0 + row;
-      rx[set][m] = gi < S ? ld16(X + gi * D + k0 + chunk * 8) : u32x4{0, 0, 0, 0};
+      const int64_t gi = min(i0 + row, S - 1);
+      rx[set][m] = ld16(X + gi * D + k0 + chunk * 8);
       rw[set][m] = ld16(W + static_cast<int64_t>(row) * D + k0 + chunk * 8);
     }
   };
@@ -87,7 +91,8 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(const u16* __restrict__ X,
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int row = tid / 8 + 32 * m, chunk = tid % 8;
-      st16(xs + row * GS + chunk * 8, rx[set][m]);
+      const u32x4 x = full || i0 + row < S ? rx[set][m] : u32x4{0, 0, 0, 0};
+      st16(xs + row * GS + chunk * 8, x);
       st16(ws + row * GS + chunk * 8, rw[set][m]);
     }
   };

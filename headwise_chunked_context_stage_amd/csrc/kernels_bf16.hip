@@ -71,7 +71,8 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(const u16* __restrict__ X,
   const int nk = static_cast<int>(D / GK);
   u32x4 rx[NRR][4], rw[NRR][4];
   // The loads are unconditional (k-steps past the end reload the last one,
-  // rows past S reload row S - 1, zeroed when stored): a load behind a branch
+  // rows past S reload row S - 1, zeroed when stored; S >= 1 here, since the
+  // entry points launch nothing for an empty sequence): a load behind a branch
   // leaves the compiler's wait counting at the join unable to trust later
   // loads, and it then waits for the whole ring, the loads just issued included.
   const bool full = i0 + GB <= S;
